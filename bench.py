@@ -1,0 +1,262 @@
+"""Benchmark of the lookahead sparse-KV decode step on one MI355X.
+
+A step is one pass of the whole hot path for every layer of one batch:
+sparse paged decode attention (verify + drafts over the resident selected
+blocks), lookahead scoring of every block, top-k selection and the
+resident-set diff with capped fetch / eviction.  The timed loop keeps all
+inputs resident in HBM and leaves the host-tier transfer out (the maps still
+update every step, so every step moves the same bytes); the workload's state is
+replicated so that the working set exceeds the 256 MB Infinity Cache and every
+step streams from HBM.
+
+Prints one JSON line: throughput in (request x layer) decode steps per second,
+the roofline of the dominant kernel (algorithmic bytes / measured duration
+against 8 TB/s), per-kernel timings, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2**20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="llama8b_32k")
+    p.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed the Infinity Cache twice")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, attended_blocks: int):
+    """Bytes each kernel must move per launch (whole batch, one layer)."""
+    e = cfg.elem_bytes
+    units = cfg.batch * cfg.kv_heads
+    N = cfg.n_blocks0
+    d = cfg.head_dim
+    score = units * N * 2 * d * e + units * N * 4 + cfg.batch * cfg.q_heads * cfg.n_draft * d * e
+    attn = (attended_blocks * 2 * 16 * d * e + cfg.batch * cfg.q_heads * cfg.T * d * (e + 4)
+            + units * cfg.k * 8)
+    return {"lookahead_score": score, "sparse_paged_decode_attn": attn,
+            "topk_select": units * N * 4 + units * cfg.k * 4,
+            "resident_diff_cap_evict": units * cfg.k * 4 * 4 + units * cfg.fetch_cap * 12}
+
+
+def attn_flops(cfg, attended_blocks: int):
+    return attended_blocks * 16 * cfg.group * cfg.T * cfg.head_dim * 4
+
+
+def cpu_baseline(cfg, target_s: float):
+    """The oracle timed on a bounded sample of the same workload (single thread)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oasis_oracle as O
+    from workload import synth
+
+    H = cfg.kv_heads
+    done_unit_steps = 0
+    units_used = 0
+    steps = min(cfg.steps, 16)
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        u = 0
+        while t_total < target_s and u < cfg.batch * H:
+            r, h = divmod(u, H)
+            ud = synth.unit_data(cfg, r, 0, h)
+            K = ud.keys()
+            t0 = time.perf_counter()
+            O.run_unit(K_at=lambda t: K, V=ud.V, queries=ud.queries, drafts_prologue=ud.drafts[0],
+                       n0=cfg.ctx, k=cfg.k, cap=cfg.fetch_cap, steps=steps,
+                       initial_slots=lambda S0: synth.initial_residency(cfg, r, 0, h, S0),
+                       append=cfg.append, max_blocks=cfg.max_blocks)
+            t_total += time.perf_counter() - t0
+            done_unit_steps += steps
+            units_used += 1
+            u += 1
+    # one (request x layer) step covers kv_heads units
+    value = (done_unit_steps / H) / t_total
+    return {"value": value, "unit": "decode steps/s (request x layer)", "cores": 1, "kind": "oracle",
+            "sample": f"{units_used} of {cfg.batch * H} (request, KV head) units of layer 0, "
+                      f"prologue + {steps} steps each, fp64 numpy, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by request or "
+              f"KV head with no exchange, so N GPUs would run N independent copies of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
+    from workload import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    # per-layer HBM state (metadata + pool) and the replica count that defeats the MALL
+    shape_meta = cfg.batch * cfg.kv_heads * cfg.max_blocks * 2 * cfg.head_dim * cfg.elem_bytes
+    shape_pool = cfg.batch * cfg.kv_heads * cfg.k * 2 * 16 * cfg.head_dim * cfg.elem_bytes
+    state_bytes = (shape_meta + shape_pool) * cfg.layers
+    replicas = args.replicas or max(1, math.ceil(2 * MALL_BYTES / state_bytes))
+    print(f"# config {cfg.name}: state {state_bytes / 2**20:.0f} MiB per replica, {replicas} replicas",
+          file=sys.stderr, flush=True)
+
+    run = SyntheticRun(cfg, replicas=replicas)
+    rt = run.rt
+    run.prologue()
+    for l in range(run.L):
+        for rep in range(1, replicas):
+            rt.state[l][rep].copy_from(rt.state[l][0])
+    torch.cuda.synchronize()
+    print("# prologue done", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    names = ["sparse_paged_decode_attn", "lookahead_score", "topk_select", "resident_diff_cap_evict"]
+
+    def one_step(i, ev=None):
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            q = run.q[l, t + 1]
+            st = rt.state[l][rep]
+            if ev is not None:
+                ev[0].record(stream)
+            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr)
+            if ev is not None:
+                ev[1].record(stream)
+            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores)
+            if ev is not None:
+                ev[2].record(stream)
+            L.oasis_topk_select(rt.h, st.scores, rt.ctx_len, st.sel)
+            if ev is not None:
+                ev[3].record(stream)
+            L.oasis_resident_diff_cap_evict(rt.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                            st.evict)
+            if ev is not None:
+                ev[4].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    def attended():
+        tot = 0
+        for l in range(run.L):
+            st = rt.state[l][0]
+            sel = st.sel.long()
+            valid = sel >= 0
+            slots = torch.gather(st.b2s, 1, sel.clamp(min=0).to(torch.int64))
+            tot += int(((slots >= 0) & valid).sum())
+        return tot // run.L
+
+    attended_before = attended()
+
+    # timed region 1: the headline loop (no per-kernel events)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # timed region 2: the same loop with HIP events between the kernels (per-kernel durations)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps * run.L)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            ev = evs[i * run.L + l]
+            q = run.q[l, t + 1]
+            st = rt.state[l][rep]
+            ev[0].record(stream)
+            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr)
+            ev[1].record(stream)
+            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores)
+            ev[2].record(stream)
+            L.oasis_topk_select(rt.h, st.scores, rt.ctx_len, st.sel)
+            ev[3].record(stream)
+            L.oasis_resident_diff_cap_evict(rt.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                            st.evict)
+            ev[4].record(stream)
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
+    per = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    attended_after = attended()
+
+    if args.calib_copy:
+        a = torch.empty(2**30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    steps_total = cfg.batch * run.L * args.steps
+    value = steps_total / elapsed
+    ab = algorithmic_bytes(cfg, attended_before)
+    kern = {}
+    for n in names:
+        gbs = ab[n] / avg[n] / 1e9
+        kern[n] = {"avg_us": avg[n] * 1e6, "bytes": ab[n], "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+    dominant = max(["sparse_paged_decode_attn", "lookahead_score"], key=lambda n: avg[n])
+    roof = {"bound": "hbm", "achieved": kern[dominant]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kern[dominant]["GB/s"] / HBM_PEAK_GBS, "traffic": None, "kernel": dominant,
+            "bytes_per_launch": ab[dominant], "avg_launch_us": avg[dominant] * 1e6}
+    res = {
+        "metric": "predict+select+sparse-attn decode steps/s at 32K ctx; % of peak HBM GB/s",
+        "value": value,
+        "unit": "decode steps/s (request x layer)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: batch {cfg.batch}, {run.L} layer(s), {cfg.q_heads}q/{cfg.kv_heads}kv "
+                               f"heads, d {cfg.head_dim}, ctx {cfg.ctx}, budget {cfg.budget_tokens} tokens, "
+                               f"{cfg.n_draft} drafts + 1 verify, cap {cfg.fetch_cap}",
+                   "batch": cfg.batch, "layers": run.L, "ctx": cfg.ctx, "replicas": replicas,
+                   "attended_blocks": [attended_before, attended_after]},
+        "roofline": roof,
+        "kernels": kern,
+        "ms_per_step_with_events": elapsed_ev / args.steps * 1e3,
+        "hbm_bytes_per_step": sum(ab[n] for n in names) * run.L,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    run.close()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

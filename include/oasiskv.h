@@ -1,0 +1,208 @@
+/*
+ * oasiskv.h - C ABI of the lookahead sparse-KV decode step for AMD MI355X (gfx950).
+ *
+ * The per-decode-step hot path of OasisKV's lookahead sparse prefetching, as
+ * described by the OasisKV pages:
+ *   [EXPL]  METAL MEDIA explainer "OasisKV: Scaling In-Decode KV Cache Beyond
+ *           HBM with Lookahead Sparse Prefetching" (arXiv 2608.08097)
+ *   [INDEX] mlsanity.com index entry for the same paper ("Builds on" list)
+ * Per layer and step: sparse attention of the verify and draft queries over
+ * the resident selected KV blocks ([EXPL] Figure 7 right), lookahead scoring of
+ * every block from the draft queries against per-block key min/max metadata
+ * ([EXPL] Figure 7), top-k selection with the sink and newest block kept,
+ * the set difference against the head-wise resident map with a per-step fetch
+ * cap and capped eviction ([EXPL] "What they did" item 3, Table 2, Figure 9),
+ * and the transfer of the missing blocks from the host tier ([EXPL] Figure 8).
+ *
+ * Conventions
+ *  - Unit = one (request r, KV head h) of one layer; unit index u = r*H + h.
+ *    Pointers are per layer: the caller offsets by layer.
+ *  - Query head hq = h*G + g serves KV head h (consecutive GQA grouping, [INDEX]
+ *    cites GQA).  Queries q are [B][H*G][T][d] with T = 1 + n_draft: row t = 0 is
+ *    the verify query, rows 1..n_draft the draft queries of the step.
+ *  - Element type (OASIS_BF16 or OASIS_F32) applies to q, block metadata, K/V
+ *    pages and appended tokens; scores and attention output are float32.
+ *  - Block metadata "meta": [B][H][max_blocks][2][d]; row 0 = per-channel key
+ *    min of the block, row 1 = per-channel key max.
+ *  - Page = one block of one unit: K rows [16][d] (token-major) followed by V
+ *    transposed [d][16] (channel-major), 2*16*d elements.  The host tier is
+ *    [B][H][max_blocks][page] (pinned host memory); the HBM pool is
+ *    [B][H][budget_blocks][page]; slot s of unit u is page u*budget_blocks + s.
+ *  - Resident maps: slot_to_block [B][H][budget_blocks] and block_to_slot
+ *    [B][H][max_blocks], int32, -1 = none; they are kept mutually inverse.
+ *  - ctx_len [B] (device, int32): context length per request.  Precondition,
+ *    not checked on the host: 1 <= ctx_len[r] <= max_blocks*16 (and < for the
+ *    append call).  N = ceil(ctx_len / 16) blocks.
+ *  - Ownership: the caller allocates and owns every buffer; the library never
+ *    allocates device or host memory.  The handle stores shapes only and is
+ *    immutable after creation (safe to share between threads).
+ *  - Asynchrony: device entry points only enqueue work on `stream` (a
+ *    hipStream_t passed as void*, NULL = default stream) and return.
+ *  - Errors: every call returns OASIS_OK or a negative status.  Arguments are
+ *    validated before anything is enqueued, so a failed call leaves no partial
+ *    work.  oasis_last_error() returns the calling thread's last message.
+ */
+#ifndef OASISKV_H
+#define OASISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OASIS_OK 0
+#define OASIS_EINVAL (-1)        /* null pointer, bad shape field, bad list entry */
+#define OASIS_EHIP (-2)          /* a HIP runtime call failed (message kept) */
+#define OASIS_EUNSUPPORTED (-3)  /* dtype / head_dim / block_size / row count not built */
+
+#define OASIS_F32 0
+#define OASIS_BF16 1
+
+typedef struct oasis_shape {
+  int32_t batch;          /* B requests */
+  int32_t kv_heads;       /* H */
+  int32_t group;          /* G query heads per KV head */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t block_size;     /* tokens per block: must be 16 */
+  int32_t max_blocks;     /* N_max: blocks allocated per unit (context capacity / 16) */
+  int32_t budget_blocks;  /* k: selected blocks = HBM slots per unit, 2..1024 */
+  int32_t n_draft;        /* D draft queries per step, >= 1 */
+  int32_t fetch_cap;      /* blocks fetched per unit per step, >= 0 */
+  int32_t dtype;          /* OASIS_BF16 or OASIS_F32 */
+} oasis_shape;
+
+typedef struct oasis_ctx* oasis_handle;
+
+/* Validates the shape (EINVAL / EUNSUPPORTED) and returns a handle.  No HIP call. */
+int oasis_create(const oasis_shape* shape, oasis_handle* out);
+int oasis_destroy(oasis_handle h);
+/* Last error message of the calling thread ("" if none). */
+const char* oasis_last_error(void);
+/* ABI version of this library. */
+int oasis_version(void);
+
+/* Byte sizes of the caller-allocated buffers of one layer (0 on a bad handle). */
+size_t oasis_page_bytes(oasis_handle h);       /* one page: 2*16*d elements */
+size_t oasis_meta_bytes(oasis_handle h);       /* B*H*max_blocks*2*d elements */
+size_t oasis_pool_bytes(oasis_handle h);       /* B*H*budget_blocks pages */
+size_t oasis_host_tier_bytes(oasis_handle h);  /* B*H*max_blocks pages */
+/* Split-K workspace of oasis_sparse_paged_decode_attn (device, 256-byte aligned). */
+size_t oasis_workspace_bytes(oasis_handle h);
+
+/*
+ * Host-side page packing (no device work).  Writes n_blocks blocks of unit u
+ * into the page layout at `pages` ([B][H][max_blocks][page], host memory).
+ * k, v: source rows [n_blocks][16][d] (token-major, element type); either may
+ * be NULL to leave that half of the pages unchanged.  blocks: destination
+ * block indices [n_blocks] (NULL = 0 .. n_blocks-1).  EINVAL on an index out of
+ * range.  This is how the prefill fills the host tier ([EXPL] Figure 7 left:
+ * the full KV cache lives in CPU memory).
+ */
+int oasis_pack_pages(oasis_handle h, const void* k, const void* v, const int32_t* blocks,
+                     int32_t n_blocks, int32_t unit, void* pages);
+
+/*
+ * Host-side append of one token per unit into the host tier (no device work).
+ * k_new, v_new: [B][H][d] host; pos: [B] host, token position per request
+ * (= context length before the append).  EINVAL if a position is out of range.
+ */
+int oasis_host_tier_append(oasis_handle h, const void* k_new, const void* v_new,
+                           const int32_t* pos, void* host_tier);
+
+/*
+ * Block metadata build (prefill, and rebuild after keys change).  For each of
+ * `count` staged pages (device, [count][page]): the page is block b of unit u,
+ * id = page_ids[i] = u*max_blocks + b (page_ids NULL: the staged pages are the
+ * whole layer, count = B*H*max_blocks, id = i).  Writes meta rows of blocks
+ * b < N(ctx_len) as the min and max over the block's tokens below ctx_len
+ * ([EXPL] Figure 7 left: per-block min/max pooling).  If pool and
+ * block_to_slot are non-NULL, a staged page whose block is resident is also
+ * copied into its pool slot.  page_ids entries must be in range (device data,
+ * not checked on the host; out-of-range ids are skipped by the kernel).
+ */
+int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* page_ids,
+                           int32_t count, const int32_t* ctx_len, void* meta, void* pool,
+                           const int32_t* block_to_slot, void* stream);
+
+/*
+ * Append one token per unit (long-output decode).  k_new, v_new: [B][H][d]
+ * device.  The token goes to position p = ctx_len_in[r]: the metadata row of
+ * block p/16 is initialised to the token (p % 16 == 0) or absorbs it by
+ * min/max; if that block is resident its pool page row is written too.
+ * ctx_len_out[r] = p + 1 (ctx_len_out must not alias ctx_len_in).
+ */
+int oasis_block_meta_update(oasis_handle h, const void* k_new, const void* v_new,
+                            const int32_t* ctx_len_in, int32_t* ctx_len_out, void* meta,
+                            void* pool, const int32_t* block_to_slot, void* stream);
+
+/*
+ * Lookahead score ([EXPL] Figure 7 right: the draft queries scan the compressed
+ * keys to predict the next step's blocks).  For every block b < N of every unit:
+ *   scores[u][b] = max over drafts t in 1..D and group heads g of
+ *                  sum_c max(q[t][g][c]*kmin[b][c], q[t][g][c]*kmax[b][c])
+ * (the Quest upper bound; Quest is in [INDEX] "Builds on").  scores:
+ * [B][H][max_blocks] float32; entries b >= N are not written.
+ */
+int oasis_lookahead_score(oasis_handle h, const void* q, const void* meta, const int32_t* ctx_len,
+                          float* scores, void* stream);
+
+/*
+ * Top-k selection.  sel [B][H][budget_blocks] int32 in rank order: the sink
+ * block 0, then the newest block N-1 (if N > 1), then the other blocks by
+ * descending score with ties broken by lower index (-0.0 ranks as +0.0), up to
+ * budget_blocks entries; the rest is -1.  With N <= budget_blocks every block
+ * is selected.
+ */
+int oasis_topk_select(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                      void* stream);
+
+/*
+ * Set difference against the resident set, capped fetch, capped eviction
+ * ([EXPL] "What they did" item 3; Figure 9).  Per unit:
+ *   missing = selected blocks with block_to_slot = -1, in rank order;
+ *   fetch   = the first min(fetch_cap, |missing|) of them;
+ *   slots   = free slots (slot_to_block = -1) in ascending order, then the
+ *             slots of victims: resident blocks outside the selection, taken
+ *             lowest score first (equal scores: higher block index first), only
+ *             as many as the free slots cannot cover;
+ *   both maps are updated in place.
+ * fetch [B][H][fetch_cap][2] = (block, slot) pairs, (-1, -1) padded; n_fetch
+ * [B][H]; evict [B][H][fetch_cap] victim blocks in eviction order, -1 padded.
+ * scores must be the ones sel was made from.
+ */
+int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const float* scores,
+                                  int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
+                                  int32_t* n_fetch, int32_t* evict, void* stream);
+
+/*
+ * Fetch issue ([EXPL] Figure 8: the transfer lands in HBM before the layer's
+ * attention at the next step).  Reads a host-visible copy of fetch / n_fetch
+ * (the caller must have synchronised its device-to-host copy) and enqueues one
+ * hipMemcpyAsync host-to-device of a page per entry, from host_tier (pinned)
+ * to its pool slot, on `stream` (normally a side stream).  All entries are
+ * validated before the first copy is enqueued (EINVAL on a bad entry).
+ */
+int oasis_fetch_issue(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch_host,
+                      const int32_t* n_fetch_host, void* stream);
+
+/*
+ * Sparse paged GQA decode attention ([EXPL] Figure 7 right: verify and draft
+ * queries attend together over the sparse working set).  For every unit, query
+ * row (g, t) and the token set J of the blocks of sel that are resident
+ * (block_to_slot >= 0), tokens below ctx_len:
+ *   out[r][h*G+g][t] = softmax_j(q . K[j] / sqrt(d)) . V[j]   (0 if J is empty)
+ * float32 accumulation, split over the selection with a log-sum-exp merge.
+ * out: [B][H*G][T][d] float32.  workspace: oasis_workspace_bytes() bytes.
+ */
+int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* pool,
+                                   const int32_t* sel, const int32_t* block_to_slot,
+                                   const int32_t* ctx_len, float* out, void* workspace,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OASISKV_H */

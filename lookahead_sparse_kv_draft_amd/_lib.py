@@ -1,0 +1,203 @@
+"""Thin ctypes binding of liboasiskv (include/oasiskv.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors and numpy arrays become raw pointers,
+streams become hipStream_t handles, a non-zero status becomes an OasisError
+carrying the library's message.  Every step of the decode path runs in the HIP
+library; if it is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liboasiskv.so")
+
+OASIS_OK = 0
+OASIS_EINVAL = -1
+OASIS_EHIP = -2
+OASIS_EUNSUPPORTED = -3
+OASIS_F32 = 0
+OASIS_BF16 = 1
+
+
+class OasisError(RuntimeError):
+    def __init__(self, func: str, code: int, msg: str):
+        super().__init__(f"{func} failed ({code}): {msg}")
+        self.code = code
+
+
+class oasis_shape(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in (
+        "batch", "kv_heads", "group", "head_dim", "block_size", "max_blocks",
+        "budget_blocks", "n_draft", "fetch_cap", "dtype")]
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_int = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); status-returning functions use c_int.
+SIGNATURES = {
+    "oasis_create": (_int, [ctypes.POINTER(oasis_shape), ctypes.POINTER(_vp)]),
+    "oasis_destroy": (_int, [_vp]),
+    "oasis_last_error": (ctypes.c_char_p, []),
+    "oasis_version": (_int, []),
+    "oasis_page_bytes": (_sz, [_vp]),
+    "oasis_meta_bytes": (_sz, [_vp]),
+    "oasis_pool_bytes": (_sz, [_vp]),
+    "oasis_host_tier_bytes": (_sz, [_vp]),
+    "oasis_workspace_bytes": (_sz, [_vp]),
+    "oasis_pack_pages": (_int, [_vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "oasis_host_tier_append": (_int, [_vp, _vp, _vp, _vp, _vp]),
+    "oasis_block_meta_build": (_int, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_block_meta_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
+    "oasis_resident_diff_cap_evict": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m lookahead_sparse_kv_draft_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    """Raw address of a torch tensor / numpy array / int (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(name: str, code: int):
+    if code != OASIS_OK:
+        msg = load().oasis_last_error().decode(errors="replace")
+        raise OasisError(name, code, msg)
+
+
+def _call(name: str, *args):
+    code = getattr(load(), name)(*args)
+    _check(name, code)
+
+
+# ----------------------------------------------------------------- handle
+def oasis_create(batch, kv_heads, group, head_dim, max_blocks, budget_blocks, n_draft, fetch_cap,
+                 dtype, block_size=16) -> int:
+    s = oasis_shape(batch=batch, kv_heads=kv_heads, group=group, head_dim=head_dim,
+                    block_size=block_size, max_blocks=max_blocks, budget_blocks=budget_blocks,
+                    n_draft=n_draft, fetch_cap=fetch_cap, dtype=dtype)
+    h = _vp()
+    _call("oasis_create", ctypes.byref(s), ctypes.byref(h))
+    return h.value
+
+
+def oasis_destroy(h):
+    _call("oasis_destroy", h)
+
+
+def oasis_last_error() -> str:
+    return load().oasis_last_error().decode(errors="replace")
+
+
+def oasis_version() -> int:
+    return load().oasis_version()
+
+
+def oasis_page_bytes(h) -> int:
+    return load().oasis_page_bytes(h)
+
+
+def oasis_meta_bytes(h) -> int:
+    return load().oasis_meta_bytes(h)
+
+
+def oasis_pool_bytes(h) -> int:
+    return load().oasis_pool_bytes(h)
+
+
+def oasis_host_tier_bytes(h) -> int:
+    return load().oasis_host_tier_bytes(h)
+
+
+def oasis_workspace_bytes(h) -> int:
+    return load().oasis_workspace_bytes(h)
+
+
+# ----------------------------------------------------------------- host side
+def oasis_pack_pages(h, k, v, blocks, n_blocks, unit, pages):
+    _call("oasis_pack_pages", h, _ptr(k), _ptr(v), _ptr(blocks), n_blocks, unit, _ptr(pages))
+
+
+def oasis_host_tier_append(h, k_new, v_new, pos, host_tier):
+    _call("oasis_host_tier_append", h, _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(host_tier))
+
+
+def oasis_fetch_issue(h, host_tier, pool, fetch_host, n_fetch_host, stream=None):
+    _call("oasis_fetch_issue", h, _ptr(host_tier), _ptr(pool), _ptr(fetch_host), _ptr(n_fetch_host),
+          _stream(stream))
+
+
+# ----------------------------------------------------------------- device side
+def oasis_block_meta_build(h, pages, page_ids, count, ctx_len, meta, pool=None, block_to_slot=None,
+                           stream=None):
+    _call("oasis_block_meta_build", h, _ptr(pages), _ptr(page_ids), count, _ptr(ctx_len), _ptr(meta),
+          _ptr(pool), _ptr(block_to_slot), _stream(stream))
+
+
+def oasis_block_meta_update(h, k_new, v_new, ctx_len_in, ctx_len_out, meta, pool, block_to_slot,
+                            stream=None):
+    _call("oasis_block_meta_update", h, _ptr(k_new), _ptr(v_new), _ptr(ctx_len_in), _ptr(ctx_len_out),
+          _ptr(meta), _ptr(pool), _ptr(block_to_slot), _stream(stream))
+
+
+def oasis_lookahead_score(h, q, meta, ctx_len, scores, stream=None):
+    _call("oasis_lookahead_score", h, _ptr(q), _ptr(meta), _ptr(ctx_len), _ptr(scores), _stream(stream))
+
+
+def oasis_topk_select(h, scores, ctx_len, sel, stream=None):
+    _call("oasis_topk_select", h, _ptr(scores), _ptr(ctx_len), _ptr(sel), _stream(stream))
+
+
+def oasis_resident_diff_cap_evict(h, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                                  stream=None):
+    _call("oasis_resident_diff_cap_evict", h, _ptr(sel), _ptr(scores), _ptr(block_to_slot),
+          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _stream(stream))
+
+
+def oasis_sparse_paged_decode_attn(h, q, pool, sel, block_to_slot, ctx_len, out, workspace, stream=None):
+    _call("oasis_sparse_paged_decode_attn", h, _ptr(q), _ptr(pool), _ptr(sel), _ptr(block_to_slot),
+          _ptr(ctx_len), _ptr(out), _ptr(workspace), _stream(stream))

@@ -1,0 +1,351 @@
+// C ABI of liboasiskv: argument validation, launch-shape selection and dispatch to
+// the HIP kernels; host-side page packing, token append and fetch issue.
+// Every entry point validates before enqueuing anything and reports errors through
+// a status code plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "oasis_internal.h"
+
+struct oasis_ctx {
+  oasis::Ctx c;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return OASIS_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(OASIS_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == '\0') return dflt;
+  return atoi(v);
+}
+
+#define CHECK_HANDLE(h) \
+  if ((h) == nullptr) return fail(OASIS_EINVAL, "%s: null handle", __func__)
+#define CHECK_PTR(p) \
+  if ((p) == nullptr) return fail(OASIS_EINVAL, "%s: %s is null", __func__, #p)
+// Device buffers read with 16-byte vector loads.
+#define CHECK_ALIGN16(p)                                   \
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)            \
+  return fail(OASIS_EINVAL, "%s: %s is not 16-byte aligned", __func__, #p)
+
+}  // namespace
+
+extern "C" {
+
+int oasis_version(void) { return 1; }
+
+const char* oasis_last_error(void) { return g_err.c_str(); }
+
+int oasis_create(const oasis_shape* shape, oasis_handle* out) {
+  CHECK_PTR(shape);
+  CHECK_PTR(out);
+  *out = nullptr;
+  const oasis_shape& s = *shape;
+  if (s.batch < 1 || s.kv_heads < 1 || s.group < 1 || s.max_blocks < 1 || s.n_draft < 1)
+    return fail(OASIS_EINVAL, "oasis_create: batch, kv_heads, group, max_blocks, n_draft must be >= 1");
+  if (s.budget_blocks < 2 || s.budget_blocks > oasis::kMaxBudget)
+    return fail(OASIS_EINVAL, "oasis_create: budget_blocks %d outside [2, %d]", s.budget_blocks,
+                oasis::kMaxBudget);
+  if (s.fetch_cap < 0) return fail(OASIS_EINVAL, "oasis_create: fetch_cap %d < 0", s.fetch_cap);
+  if (s.block_size != oasis::kBlock)
+    return fail(OASIS_EUNSUPPORTED, "oasis_create: block_size %d (only 16 is built)", s.block_size);
+  if (s.head_dim != 64 && s.head_dim != 128)
+    return fail(OASIS_EUNSUPPORTED, "oasis_create: head_dim %d (64 or 128 are built)", s.head_dim);
+  if (s.dtype != OASIS_BF16 && s.dtype != OASIS_F32)
+    return fail(OASIS_EUNSUPPORTED, "oasis_create: dtype %d", s.dtype);
+  if (s.max_blocks > 65536)
+    return fail(OASIS_EUNSUPPORTED, "oasis_create: max_blocks %d > 65536", s.max_blocks);
+  const long long units = static_cast<long long>(s.batch) * s.kv_heads;
+  if (units > (1 << 24)) return fail(OASIS_EUNSUPPORTED, "oasis_create: too many units");
+  const int T = 1 + s.n_draft;
+  const int rows_score = s.n_draft * s.group;
+  const int rows_attn = T * s.group;
+  if (rows_attn > oasis::kMaxRows)
+    return fail(OASIS_EUNSUPPORTED, "oasis_create: (1 + n_draft) * group = %d query rows > %d",
+                rows_attn, oasis::kMaxRows);
+
+  oasis_ctx* h = new (std::nothrow) oasis_ctx;
+  if (h == nullptr) return fail(OASIS_EINVAL, "oasis_create: out of host memory");
+  oasis::Ctx& c = h->c;
+  c.s = s;
+  c.T = T;
+  c.rows_score = rows_score;
+  c.rows_attn = rows_attn;
+  c.elem_bytes = (s.dtype == OASIS_BF16) ? 2 : 4;
+  c.page_elems = static_cast<size_t>(2) * oasis::kBlock * s.head_dim;
+  c.units = static_cast<int>(units);
+
+  // Attention split-K: enough (unit, split) wavefronts to fill 256 CUs, at
+  // least 8 selection entries per split, at most 64 (one per lane).
+  int splits = env_int("OASIS_ATTN_SPLITS", 0);
+  if (splits <= 0) {
+    const int want = (1024 + c.units - 1) / c.units;
+    splits = std::min(want, (s.budget_blocks + 7) / 8);
+  }
+  splits = std::max(1, std::min(splits, s.budget_blocks));
+  int split_len = (s.budget_blocks + splits - 1) / splits;
+  if (split_len > oasis::kWave) split_len = oasis::kWave;
+  c.attn_split_len = split_len;
+  c.attn_splits = (s.budget_blocks + split_len - 1) / split_len;
+
+  // Score kernel: 16-block tiles per wavefront, ~2048 wavefronts per launch.
+  int tpw = env_int("OASIS_SCORE_TPW", 0);
+  if (tpw <= 0) {
+    const long long tiles = units * ((s.max_blocks + 15) / 16);
+    tpw = static_cast<int>(std::max(1LL, std::min(16LL, tiles / 2048)));
+  }
+  c.score_tpw = tpw;
+  *out = h;
+  return ok();
+}
+
+int oasis_destroy(oasis_handle h) {
+  delete h;
+  return ok();
+}
+
+size_t oasis_page_bytes(oasis_handle h) {
+  return h ? h->c.page_elems * h->c.elem_bytes : 0;
+}
+
+size_t oasis_meta_bytes(oasis_handle h) {
+  return h ? static_cast<size_t>(h->c.units) * h->c.s.max_blocks * 2 * h->c.s.head_dim * h->c.elem_bytes : 0;
+}
+
+size_t oasis_pool_bytes(oasis_handle h) {
+  return h ? static_cast<size_t>(h->c.units) * h->c.s.budget_blocks * oasis_page_bytes(h) : 0;
+}
+
+size_t oasis_host_tier_bytes(oasis_handle h) {
+  return h ? static_cast<size_t>(h->c.units) * h->c.s.max_blocks * oasis_page_bytes(h) : 0;
+}
+
+size_t oasis_workspace_bytes(oasis_handle h) { return h ? oasis::attn_workspace_bytes(h->c) : 0; }
+
+int oasis_pack_pages(oasis_handle h, const void* k, const void* v, const int32_t* blocks,
+                     int32_t n_blocks, int32_t unit, void* pages) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(pages);
+  const oasis::Ctx& c = h->c;
+  if (n_blocks < 0) return fail(OASIS_EINVAL, "oasis_pack_pages: n_blocks %d < 0", n_blocks);
+  if (unit < 0 || unit >= c.units) return fail(OASIS_EINVAL, "oasis_pack_pages: unit %d out of range", unit);
+  if (n_blocks > 0 && k == nullptr && v == nullptr)
+    return fail(OASIS_EINVAL, "oasis_pack_pages: k and v are both null");
+  if (blocks == nullptr && n_blocks > c.s.max_blocks)
+    return fail(OASIS_EINVAL, "oasis_pack_pages: n_blocks %d > max_blocks", n_blocks);
+  if (blocks != nullptr)
+    for (int i = 0; i < n_blocks; ++i)
+      if (blocks[i] < 0 || blocks[i] >= c.s.max_blocks)
+        return fail(OASIS_EINVAL, "oasis_pack_pages: block %d out of range", blocks[i]);
+  const int d = c.s.head_dim;
+  const size_t eb = c.elem_bytes;
+  const size_t row_bytes = d * eb;
+  char* base = static_cast<char*>(pages) + static_cast<size_t>(unit) * c.s.max_blocks * c.page_elems * eb;
+  for (int i = 0; i < n_blocks; ++i) {
+    const int b = blocks ? blocks[i] : i;
+    char* pg = base + static_cast<size_t>(b) * c.page_elems * eb;
+    if (k != nullptr)
+      memcpy(pg, static_cast<const char*>(k) + static_cast<size_t>(i) * oasis::kBlock * row_bytes,
+             oasis::kBlock * row_bytes);
+    if (v != nullptr) {
+      const char* src = static_cast<const char*>(v) + static_cast<size_t>(i) * oasis::kBlock * row_bytes;
+      char* vt = pg + oasis::kBlock * row_bytes;  // V^T [d][16]
+      for (int t = 0; t < oasis::kBlock; ++t)
+        for (int ch = 0; ch < d; ++ch)
+          memcpy(vt + (static_cast<size_t>(ch) * oasis::kBlock + t) * eb, src + (static_cast<size_t>(t) * d + ch) * eb, eb);
+    }
+  }
+  return ok();
+}
+
+int oasis_host_tier_append(oasis_handle h, const void* k_new, const void* v_new, const int32_t* pos,
+                           void* host_tier) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(k_new);
+  CHECK_PTR(v_new);
+  CHECK_PTR(pos);
+  CHECK_PTR(host_tier);
+  const oasis::Ctx& c = h->c;
+  for (int r = 0; r < c.s.batch; ++r)
+    if (pos[r] < 0 || pos[r] >= c.s.max_blocks * oasis::kBlock)
+      return fail(OASIS_EINVAL, "oasis_host_tier_append: position %d of request %d out of range", pos[r], r);
+  const int d = c.s.head_dim;
+  const size_t eb = c.elem_bytes;
+  for (int u = 0; u < c.units; ++u) {
+    const int p = pos[u / c.s.kv_heads];
+    const int b = p / oasis::kBlock, j = p % oasis::kBlock;
+    char* pg = static_cast<char*>(host_tier) + (static_cast<size_t>(u) * c.s.max_blocks + b) * c.page_elems * eb;
+    const char* kr = static_cast<const char*>(k_new) + static_cast<size_t>(u) * d * eb;
+    const char* vr = static_cast<const char*>(v_new) + static_cast<size_t>(u) * d * eb;
+    memcpy(pg + static_cast<size_t>(j) * d * eb, kr, d * eb);
+    char* vt = pg + static_cast<size_t>(oasis::kBlock) * d * eb;
+    for (int ch = 0; ch < d; ++ch)
+      memcpy(vt + (static_cast<size_t>(ch) * oasis::kBlock + j) * eb, vr + static_cast<size_t>(ch) * eb, eb);
+  }
+  return ok();
+}
+
+int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* page_ids, int32_t count,
+                           const int32_t* ctx_len, void* meta, void* pool,
+                           const int32_t* block_to_slot, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(pages);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(meta);
+  CHECK_ALIGN16(pages);
+  CHECK_ALIGN16(pool);
+  const oasis::Ctx& c = h->c;
+  if (count < 0) return fail(OASIS_EINVAL, "oasis_block_meta_build: count %d < 0", count);
+  if (page_ids == nullptr && static_cast<long long>(count) != static_cast<long long>(c.units) * c.s.max_blocks)
+    return fail(OASIS_EINVAL, "oasis_block_meta_build: without page_ids count must be B*H*max_blocks");
+  if ((pool == nullptr) != (block_to_slot == nullptr))
+    return fail(OASIS_EINVAL, "oasis_block_meta_build: pool and block_to_slot must both be set or both null");
+  return hip_status(oasis::launch_meta_build(c, pages, page_ids, count, ctx_len, meta, pool, block_to_slot,
+                                             static_cast<hipStream_t>(stream)),
+                    "oasis_block_meta_build");
+}
+
+int oasis_block_meta_update(oasis_handle h, const void* k_new, const void* v_new, const int32_t* ctx_len_in,
+                            int32_t* ctx_len_out, void* meta, void* pool, const int32_t* block_to_slot,
+                            void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(k_new);
+  CHECK_PTR(v_new);
+  CHECK_PTR(ctx_len_in);
+  CHECK_PTR(ctx_len_out);
+  CHECK_PTR(meta);
+  CHECK_PTR(pool);
+  CHECK_PTR(block_to_slot);
+  if (static_cast<const void*>(ctx_len_in) == static_cast<const void*>(ctx_len_out))
+    return fail(OASIS_EINVAL, "oasis_block_meta_update: ctx_len_out aliases ctx_len_in");
+  return hip_status(oasis::launch_meta_update(h->c, k_new, v_new, ctx_len_in, ctx_len_out, meta, pool,
+                                              block_to_slot, static_cast<hipStream_t>(stream)),
+                    "oasis_block_meta_update");
+}
+
+int oasis_lookahead_score(oasis_handle h, const void* q, const void* meta, const int32_t* ctx_len,
+                          float* scores, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(meta);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(scores);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(meta);
+  return hip_status(oasis::launch_score(h->c, q, meta, ctx_len, scores, static_cast<hipStream_t>(stream)),
+                    "oasis_lookahead_score");
+}
+
+int oasis_topk_select(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                      void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(sel);
+  return hip_status(oasis::launch_topk(h->c, scores, ctx_len, sel, static_cast<hipStream_t>(stream)),
+                    "oasis_topk_select");
+}
+
+int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const float* scores,
+                                  int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
+                                  int32_t* n_fetch, int32_t* evict, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(sel);
+  CHECK_PTR(scores);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(n_fetch);
+  if (h->c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  return hip_status(oasis::launch_diff(h->c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch,
+                                       evict, static_cast<hipStream_t>(stream)),
+                    "oasis_resident_diff_cap_evict");
+}
+
+int oasis_fetch_issue(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch_host,
+                      const int32_t* n_fetch_host, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(host_tier);
+  CHECK_PTR(pool);
+  CHECK_PTR(n_fetch_host);
+  const oasis::Ctx& c = h->c;
+  const int cap = c.s.fetch_cap;
+  if (cap > 0) CHECK_PTR(fetch_host);
+  for (int u = 0; u < c.units; ++u) {
+    const int nf = n_fetch_host[u];
+    if (nf < 0 || nf > cap) return fail(OASIS_EINVAL, "oasis_fetch_issue: n_fetch %d of unit %d", nf, u);
+    for (int i = 0; i < nf; ++i) {
+      const int b = fetch_host[(static_cast<size_t>(u) * cap + i) * 2];
+      const int s = fetch_host[(static_cast<size_t>(u) * cap + i) * 2 + 1];
+      if (b < 0 || b >= c.s.max_blocks || s < 0 || s >= c.s.budget_blocks)
+        return fail(OASIS_EINVAL, "oasis_fetch_issue: entry (%d, %d) of unit %d out of range", b, s, u);
+    }
+  }
+  const size_t pb = c.page_elems * c.elem_bytes;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int u = 0; u < c.units; ++u) {
+    const int nf = n_fetch_host[u];
+    for (int i = 0; i < nf; ++i) {
+      const int b = fetch_host[(static_cast<size_t>(u) * cap + i) * 2];
+      const int s = fetch_host[(static_cast<size_t>(u) * cap + i) * 2 + 1];
+      const char* src = static_cast<const char*>(host_tier) + (static_cast<size_t>(u) * c.s.max_blocks + b) * pb;
+      char* dst = static_cast<char*>(pool) + (static_cast<size_t>(u) * c.s.budget_blocks + s) * pb;
+      const hipError_t e = hipMemcpyAsync(dst, src, pb, hipMemcpyHostToDevice, st);
+      if (e != hipSuccess) return hip_status(e, "oasis_fetch_issue: hipMemcpyAsync");
+    }
+  }
+  return ok();
+}
+
+int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* pool, const int32_t* sel,
+                                   const int32_t* block_to_slot, const int32_t* ctx_len, float* out,
+                                   void* workspace, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_sparse_paged_decode_attn: workspace not 256-byte aligned");
+  return hip_status(oasis::launch_attn(h->c, q, pool, sel, block_to_slot, ctx_len, out, workspace,
+                                       static_cast<hipStream_t>(stream)),
+                    "oasis_sparse_paged_decode_attn");
+}
+
+}  // extern "C"

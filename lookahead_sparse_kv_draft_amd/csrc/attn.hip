@@ -1,0 +1,388 @@
+// Sparse paged GQA decode attention over the resident selected blocks (OasisKV
+// explainer, Figure 7 right: the verify query and the draft queries attend
+// together over the sparse KV working set held in HBM).
+//
+// Work unit: one (request, KV head) and one split of its selection list; the
+// splits are merged by a log-sum-exp combine kernel.  All T*G query rows of the
+// unit (verify + drafts for each grouped query head) ride in the same
+// wavefront, so every KV page is read from HBM once per step.
+//
+// bf16 path, per 16-token block and per 16-row query tile, on the MFMA units:
+//   S^T[tok][row] = K[tok][:] . Q[row][:]   v_mfma_f32_16x16x32_bf16, A = the K
+//       page rows (16 contiguous bytes per lane), B = the query rows (registers);
+//       the output leaves lane (col, grp) with tokens 4grp..4grp+3 of row col;
+//   online softmax in the log2 domain, in registers: block max over the 4
+//       tokens of the lane and two cross-lane exchanges; probabilities rounded
+//       to bf16 (the running sum adds the rounded values, so weights and
+//       normaliser agree);
+//   O^T[ch][row] += V^T[ch][tok] . P^T[tok][row]  v_mfma_f32_16x16x16_bf16, A =
+//       the page's channel-major V^T (8 contiguous bytes per lane), B = the
+//       lane's own 4 probabilities: P never leaves registers.
+// The page layout (K token-major, V channel-major) is what makes both products
+// read contiguous lane-sized pieces without an LDS transpose.  The next block's
+// page loads are issued before the current block's math.
+//
+// f32 path: VALU, query rows and logits in LDS, accumulators in registers.
+#include "oasis_internal.h"
+
+namespace oasis {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
+
+template <int D, int RT>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s,
+    const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int H, int GT, int rows, int Nmax, int kb, int splits, int split_len, float scale_log2) {
+  constexpr int KS = D / 32;  // QK k-steps of 32 channels
+  constexpr int CT = D / 16;  // PV channel tiles
+  constexpr int PAGE = 2 * kBlock * D;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int wid = blockIdx.x;  // unit * splits + split
+  const int unit = wid / splits;
+  const int split = wid - unit * splits;
+  const int n = ctx_len[unit / H];
+
+  // Resolve this split's selection entries, one per lane.
+  const int i0 = split * split_len;
+  const int cnt = min(split_len, kb - i0);
+  int my_slot = -1, my_ntok = 0;
+  if (lane < cnt) {
+    const int b = sel[static_cast<size_t>(unit) * kb + i0 + lane];
+    if (b >= 0 && b < Nmax) {
+      const int s = b2s[static_cast<size_t>(unit) * Nmax + b];
+      const int nt = min(kBlock, n - kBlock * b);
+      if (s >= 0 && s < kb && nt > 0) {
+        my_slot = s;
+        my_ntok = nt;
+      }
+    }
+  }
+  uint64_t pending = __ballot(my_slot >= 0);
+
+  // Query rows as the B operand of S^T = K Q^T: lane (col, grp) holds row
+  // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.
+  uint4 Qb[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      Qb[rt][s] = (row < rows)
+          ? *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(unit) * GT + row) * D + 8 * (4 * s + grp))
+          : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  f32x4_t acc[RT][CT];
+  float mrun[RT], lrun[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mrun[rt] = -INFINITY;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint16_t* ubase = pool + static_cast<size_t>(unit) * kb * PAGE;
+  uint4 Kc[KS], Kn[KS];
+  uint2 Vc[CT], Vn[CT];
+  int ntok = 0;
+
+  auto load_page = [&](int slot, uint4* Kt, uint2* Vt) {
+    const uint16_t* pg = ubase + static_cast<size_t>(slot) * PAGE;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      Kt[s] = *reinterpret_cast<const uint4*>(pg + col * D + 8 * (4 * s + grp));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      Vt[ct] = *reinterpret_cast<const uint2*>(pg + kBlock * D + (16 * ct + col) * kBlock + 4 * grp);
+  };
+
+  if (pending) {
+    const int idx = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+    load_page(__shfl(my_slot, idx), Kc, Vc);
+    ntok = __shfl(my_ntok, idx);
+    pending &= pending - 1;
+    while (true) {
+      int nntok = 0;
+      const bool more = pending != 0;
+      if (more) {
+        const int nidx = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+        load_page(__shfl(my_slot, nidx), Kn, Vn);
+        nntok = __shfl(my_ntok, nidx);
+        pending &= pending - 1;
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Kc[s]), as_bf16x8(Qb[rt][s]), st, 0, 0, 0);
+        float x[4];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (4 * grp + i < ntok) ? st[i] * scale_log2 : -INFINITY;
+          mb = fmaxf(mb, x[i]);
+        }
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mnew = fmaxf(mrun[rt], mb);
+        const float alpha = exp2f(mrun[rt] - mnew);
+        mrun[rt] = mnew;
+        uint16_t pb[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = f32_to_bf16(exp2f(x[i] - mnew));
+          psum += bf16_to_f32(pb[i]);
+        }
+        lrun[rt] = lrun[rt] * alpha + psum;
+        const uint2 pw = make_uint2(static_cast<uint32_t>(pb[0]) | (static_cast<uint32_t>(pb[1]) << 16),
+                                    static_cast<uint32_t>(pb[2]) | (static_cast<uint32_t>(pb[3]) << 16));
+        const s16x4_t P = as_s16x4(pw);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[rt][ct] *= alpha;
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(Vc[ct]), P, acc[rt][ct], 0, 0, 0);
+        }
+      }
+      if (!more) break;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) Kc[s] = Kn[s];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) Vc[ct] = Vn[ct];
+      ntok = nntok;
+    }
+  }
+
+  // Partials: unnormalised O rows, running max (log2 domain) and sum.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float L = lrun[rt];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const int row = rt * 16 + col;
+    if (row < rows) {
+      float* wa = ws_acc + (static_cast<size_t>(wid) * rows + row) * D;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        *reinterpret_cast<float4*>(wa + 16 * ct + 4 * grp) =
+            make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
+      if (grp == 0) {
+        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = mrun[rt];
+        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// fp32 path: workgroup of 256 threads per (unit, split).
+template <int D>
+__global__ __launch_bounds__(256) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ pool, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ b2s, const int32_t* __restrict__ ctx_len,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int H, int GT, int rows, int Nmax,
+    int kb, int splits, int split_len, float scale_log2) {
+  constexpr int PAGE = 2 * kBlock * D;
+  constexpr int J = (kMaxRows * D + 255) / 256;  // accumulators per thread (upper bound)
+  extern __shared__ float smem[];
+  float* qs = smem;                   // [rows][D]
+  float* lg = qs + rows * D;          // [rows][16] logits, then probabilities
+  float* alpha_s = lg + rows * kBlock;  // [rows]
+  float* m_s = alpha_s + rows;        // [rows]
+  float* l_s = m_s + rows;            // [rows]
+  const int tid = threadIdx.x;
+  const int wid = blockIdx.x;
+  const int unit = wid / splits;
+  const int split = wid - unit * splits;
+  const int n = ctx_len[unit / H];
+  for (int i = tid; i < rows * D; i += 256) qs[i] = q[static_cast<size_t>(unit) * GT * D + i];
+  for (int i = tid; i < rows; i += 256) {
+    m_s[i] = -INFINITY;
+    l_s[i] = 0.f;
+  }
+  float acc[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) acc[j] = 0.f;
+  __syncthreads();
+  const int i0 = split * split_len;
+  const int i1 = min(kb, i0 + split_len);
+  for (int e = i0; e < i1; ++e) {
+    const int b = sel[static_cast<size_t>(unit) * kb + e];
+    if (b < 0 || b >= Nmax) continue;
+    const int slot = b2s[static_cast<size_t>(unit) * Nmax + b];
+    const int ntok = min(kBlock, n - kBlock * b);
+    if (slot < 0 || slot >= kb || ntok <= 0) continue;
+    const float* pg = pool + (static_cast<size_t>(unit) * kb + slot) * PAGE;
+    for (int i = tid; i < rows * kBlock; i += 256) {
+      const int row = i / kBlock, tok = i - (i / kBlock) * kBlock;
+      float s = -INFINITY;
+      if (tok < ntok) {
+        s = 0.f;
+        for (int c = 0; c < D; ++c) s += qs[row * D + c] * pg[tok * D + c];
+        s *= scale_log2;
+      }
+      lg[i] = s;
+    }
+    __syncthreads();
+    for (int row = tid; row < rows; row += 256) {
+      float mb = -INFINITY;
+      for (int t = 0; t < kBlock; ++t) mb = fmaxf(mb, lg[row * kBlock + t]);
+      const float mnew = fmaxf(m_s[row], mb);
+      const float a = exp2f(m_s[row] - mnew);
+      float ps = 0.f;
+      for (int t = 0; t < kBlock; ++t) {
+        const float p = exp2f(lg[row * kBlock + t] - mnew);
+        lg[row * kBlock + t] = p;
+        ps += p;
+      }
+      l_s[row] = l_s[row] * a + ps;
+      m_s[row] = mnew;
+      alpha_s[row] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int i = tid + 256 * j;
+      if (i < rows * D) {
+        const int row = i / D, c = i - (i / D) * D;
+        float a = acc[j] * alpha_s[row];
+        for (int t = 0; t < ntok; ++t) a += lg[row * kBlock + t] * pg[kBlock * D + c * kBlock + t];
+        acc[j] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = tid + 256 * j;
+    if (i < rows * D) ws_acc[static_cast<size_t>(wid) * rows * D + i] = acc[j];
+  }
+  for (int row = tid; row < rows; row += 256) {
+    ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = m_s[row];
+    ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = l_s[row];
+  }
+}
+
+// Log-sum-exp merge of the split partials; one wavefront per (unit, query row).
+template <int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ ws_acc,
+                                                          const float* __restrict__ ws_ml,
+                                                          float* __restrict__ out, int rows,
+                                                          int splits) {
+  constexpr int PER = D / kWave;
+  const int id = blockIdx.x;  // unit * rows + row
+  const int unit = id / rows;
+  const int row = id - unit * rows;
+  const int lane = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s)
+    M = fmaxf(M, ws_ml[((static_cast<size_t>(unit) * splits + s) * rows + row) * 2]);
+  float* o = out + static_cast<size_t>(id) * D;
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o[lane + kWave * j] = 0.f;
+    return;
+  }
+  float L = 0.f;
+  float a[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) a[j] = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const size_t p = (static_cast<size_t>(unit) * splits + s) * rows + row;
+    const float ms = ws_ml[p * 2];
+    if (ms == -INFINITY) continue;
+    const float w = exp2f(ms - M);
+    L += w * ws_ml[p * 2 + 1];
+    const float* src = ws_acc + p * D;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) a[j] += w * src[lane + kWave * j];
+  }
+  const float inv = 1.f / L;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) o[lane + kWave * j] = a[j] * inv;
+}
+
+struct WsLayout {
+  size_t acc_floats, ml_floats;
+};
+
+WsLayout ws_layout(const Ctx& c) {
+  const size_t parts = static_cast<size_t>(c.units) * c.attn_splits * c.rows_attn;
+  return {parts * c.s.head_dim, parts * 2};
+}
+
+template <int D, int RT>
+hipError_t mfma_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
+                  float scale_log2, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, RT>), dim3(c.units * c.attn_splits), dim3(kWave), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s,
+                     ctx_len, ws_acc, ws_ml, c.s.kv_heads, c.rows_attn, c.rows_attn,
+                     c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_split_len, scale_log2);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
+                  hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  if (c.s.dtype == OASIS_BF16) {
+    switch ((c.rows_attn + 15) / 16) {
+      case 1: return mfma_t<D, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
+      case 2: return mfma_t<D, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
+      case 3: return mfma_t<D, 3>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
+      default: return mfma_t<D, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
+    }
+  }
+  const int rows = c.rows_attn;
+  const size_t lds = (static_cast<size_t>(rows) * D + rows * kBlock + 3 * rows) * sizeof(float);
+  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(c.units * c.attn_splits), dim3(256), lds, st,
+                     static_cast<const float*>(q), static_cast<const float*>(pool), sel, b2s,
+                     ctx_len, ws_acc, ws_ml, c.s.kv_heads, c.rows_attn, rows, c.s.max_blocks,
+                     c.s.budget_blocks, c.attn_splits, c.attn_split_len, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(const Ctx& c) {
+  const WsLayout w = ws_layout(c);
+  const size_t acc_bytes = ((w.acc_floats * sizeof(float)) + 255) / 256 * 256;
+  return acc_bytes + w.ml_floats * sizeof(float);
+}
+
+hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                       const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
+                       hipStream_t st) {
+  const WsLayout w = ws_layout(c);
+  float* ws_acc = static_cast<float*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          ((w.acc_floats * sizeof(float)) + 255) / 256 * 256);
+  hipError_t e = (c.s.head_dim == 128)
+      ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, st)
+      : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, st);
+  if (e != hipSuccess) return e;
+  const int grid = c.units * c.rows_attn;
+  if (c.s.head_dim == 128)
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(grid), dim3(kWave), 0, st, ws_acc, ws_ml,
+                       out, c.rows_attn, c.attn_splits);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(grid), dim3(kWave), 0, st, ws_acc, ws_ml,
+                       out, c.rows_attn, c.attn_splits);
+  return hipGetLastError();
+}
+
+}  // namespace oasis

@@ -1,0 +1,153 @@
+// Block metadata kernels: per-block, per-channel key min/max ("compressed keys",
+// OasisKV explainer, Figure 7 left: per-block min/max pooling kept on the GPU).
+//
+//  meta_build  - one wavefront per staged page: min/max over the block's tokens
+//                below the context length; optionally patches the resident copy.
+//  meta_update - one wavefront per (request, KV head): absorbs the appended
+//                token into its block's min/max and writes it into the page if
+//                the block is resident.
+#include "oasis_internal.h"
+
+namespace oasis {
+namespace {
+
+template <typename E> struct Elem;
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t store(float f) { return f32_to_bf16(f); }
+};
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(float v) { return v; }
+  static __device__ __forceinline__ float store(float f) { return f; }
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void meta_build_kernel(
+    const E* __restrict__ pages, const int32_t* __restrict__ ids, int count,
+    const int32_t* __restrict__ ctx_len, E* __restrict__ meta, E* __restrict__ pool,
+    const int32_t* __restrict__ b2s, int units, int H, int Nmax, int kb) {
+  constexpr int PAGE = 2 * kBlock * D;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (w >= count) return;
+  const int id = ids ? ids[w] : w;
+  if (id < 0 || id >= units * Nmax) return;
+  const int unit = id / Nmax;
+  const int b = id - unit * Nmax;
+  const int n = ctx_len[unit / H];
+  const int N = min((n + kBlock - 1) / kBlock, Nmax);
+  if (b >= N) return;
+  const int ntok = min(kBlock, n - kBlock * b);
+  const E* pg = pages + static_cast<size_t>(w) * PAGE;
+  E* mrow = meta + static_cast<size_t>(id) * 2 * D;
+  for (int c = lane; c < D; c += kWave) {
+    float mn = Elem<E>::load(pg[c]);
+    float mx = mn;
+    for (int j = 1; j < ntok; ++j) {
+      const float v = Elem<E>::load(pg[j * D + c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    mrow[c] = Elem<E>::store(mn);
+    mrow[D + c] = Elem<E>::store(mx);
+  }
+  if (pool != nullptr && b2s != nullptr) {
+    const int slot = b2s[id];
+    if (slot >= 0 && slot < kb) {
+      const uint4* src = reinterpret_cast<const uint4*>(pg);
+      uint4* dst = reinterpret_cast<uint4*>(pool + (static_cast<size_t>(unit) * kb + slot) * PAGE);
+      constexpr int V4 = PAGE * static_cast<int>(sizeof(E)) / 16;
+      for (int i = lane; i < V4; i += kWave) dst[i] = src[i];
+    }
+  }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(64) void meta_update_kernel(
+    const E* __restrict__ k_new, const E* __restrict__ v_new, const int32_t* __restrict__ ctx_in,
+    int32_t* __restrict__ ctx_out, E* __restrict__ meta, E* __restrict__ pool,
+    const int32_t* __restrict__ b2s, int H, int Nmax, int kb) {
+  constexpr int PAGE = 2 * kBlock * D;
+  const int unit = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int r = unit / H;
+  const int h = unit - r * H;
+  const int p = ctx_in[r];
+  const int b = p / kBlock;
+  const int j = p - b * kBlock;
+  if (p < 0 || b >= Nmax) return;
+  const size_t id = static_cast<size_t>(unit) * Nmax + b;
+  E* mrow = meta + id * 2 * D;
+  const E* kn = k_new + static_cast<size_t>(unit) * D;
+  const E* vn = v_new + static_cast<size_t>(unit) * D;
+  for (int c = lane; c < D; c += kWave) {
+    const E kv = kn[c];
+    if (j == 0) {
+      mrow[c] = kv;
+      mrow[D + c] = kv;
+    } else {
+      const float kf = Elem<E>::load(kv);
+      mrow[c] = Elem<E>::store(fminf(Elem<E>::load(mrow[c]), kf));
+      mrow[D + c] = Elem<E>::store(fmaxf(Elem<E>::load(mrow[D + c]), kf));
+    }
+  }
+  const int slot = b2s[id];
+  if (slot >= 0 && slot < kb) {
+    E* pg = pool + (static_cast<size_t>(unit) * kb + slot) * PAGE;
+    for (int c = lane; c < D; c += kWave) {
+      pg[j * D + c] = kn[c];                  // K row j (token-major)
+      pg[kBlock * D + c * kBlock + j] = vn[c];  // V^T column j (channel-major)
+    }
+  }
+  if (h == 0 && lane == 0) ctx_out[r] = p + 1;
+}
+
+template <typename E, int D>
+hipError_t build_t(const Ctx& c, const void* pages, const int32_t* ids, int32_t count,
+                   const int32_t* ctx_len, void* meta, void* pool, const int32_t* b2s,
+                   hipStream_t st) {
+  const int waves_per_wg = 4;
+  const int grid = (count + waves_per_wg - 1) / waves_per_wg;
+  hipLaunchKernelGGL((meta_build_kernel<E, D>), dim3(grid), dim3(waves_per_wg * kWave), 0, st,
+                     static_cast<const E*>(pages), ids, count, ctx_len, static_cast<E*>(meta),
+                     static_cast<E*>(pool), b2s, c.units, c.s.kv_heads, c.s.max_blocks,
+                     c.s.budget_blocks);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t update_t(const Ctx& c, const void* k_new, const void* v_new, const int32_t* ctx_in,
+                    int32_t* ctx_out, void* meta, void* pool, const int32_t* b2s, hipStream_t st) {
+  hipLaunchKernelGGL((meta_update_kernel<E, D>), dim3(c.units), dim3(kWave), 0, st,
+                     static_cast<const E*>(k_new), static_cast<const E*>(v_new), ctx_in, ctx_out,
+                     static_cast<E*>(meta), static_cast<E*>(pool), b2s, c.s.kv_heads,
+                     c.s.max_blocks, c.s.budget_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids, int32_t count,
+                             const int32_t* ctx_len, void* meta, void* pool, const int32_t* b2s,
+                             hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const bool bf = c.s.dtype == OASIS_BF16;
+  if (c.s.head_dim == 128)
+    return bf ? build_t<uint16_t, 128>(c, pages, ids, count, ctx_len, meta, pool, b2s, st)
+              : build_t<float, 128>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
+  return bf ? build_t<uint16_t, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st)
+            : build_t<float, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
+}
+
+hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,
+                              const int32_t* ctx_in, int32_t* ctx_out, void* meta, void* pool,
+                              const int32_t* b2s, hipStream_t st) {
+  const bool bf = c.s.dtype == OASIS_BF16;
+  if (c.s.head_dim == 128)
+    return bf ? update_t<uint16_t, 128>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st)
+              : update_t<float, 128>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st);
+  return bf ? update_t<uint16_t, 64>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st)
+            : update_t<float, 64>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st);
+}
+
+}  // namespace oasis

@@ -1,0 +1,69 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of liboasiskv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oasiskv.h"
+
+namespace oasis {
+
+constexpr int kBlock = 16;     // tokens per KV block
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kMaxRows = 64;   // query rows per unit handled by the kernels (4 MFMA row tiles)
+constexpr int kMaxBudget = 1024;
+
+struct Ctx {
+  oasis_shape s;
+  int T;            // 1 + n_draft
+  int rows_score;   // n_draft * group
+  int rows_attn;    // T * group
+  int elem_bytes;   // 2 (bf16) or 4 (f32)
+  size_t page_elems;  // 2 * 16 * d
+  int units;        // batch * kv_heads
+  int attn_splits;  // split-K factor of the attention
+  int attn_split_len;  // selection entries per split
+  int score_tpw;    // 16-block tiles per wave in the score kernel
+};
+
+// ---- kernel launchers (defined in the .hip files); return a hipError_t ----
+hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids, int32_t count,
+                             const int32_t* ctx_len, void* meta, void* pool,
+                             const int32_t* b2s, hipStream_t st);
+hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,
+                              const int32_t* ctx_in, int32_t* ctx_out, void* meta, void* pool,
+                              const int32_t* b2s, hipStream_t st);
+hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
+                        float* scores, hipStream_t st);
+hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                       hipStream_t st);
+hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, int32_t* b2s,
+                       int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
+                       hipStream_t st);
+hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                       const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
+                       hipStream_t st);
+size_t attn_workspace_bytes(const Ctx& c);
+
+// ---- small device helpers ----
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// 32-bit key whose ascending order is descending score; -0.0 ranks as +0.0.
+__device__ __forceinline__ uint32_t desc_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~ord;
+}
+
+}  // namespace oasis

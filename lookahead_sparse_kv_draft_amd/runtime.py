@@ -1,0 +1,302 @@
+"""Per-layer decode-step runtime over liboasiskv.
+
+Holds the device and pinned-host buffers of each layer (torch is used only to
+allocate memory, to provide streams and events, and for plain copies) and
+enqueues the per-step chain of the OasisKV explainer's Figure 8: the draft
+queries of step t drive prediction, selection and transfer, which land in HBM
+before that layer's attention at step t+1.
+
+Per layer and step (compute stream unless noted):
+    wait for the layer's previous transfer
+    sparse_paged_decode_attn     verify + draft queries over S_t and R_t
+    [block_meta_update]          long-output decode: append the step's token
+    lookahead_score              drafts of step t against the block metadata
+    topk_select                  S_{t+1}
+    resident_diff_cap_evict      fetch / evict lists, maps -> R_{t+1}
+    fetch list -> host, fetch_issue on the side stream (transfer mode only)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+BLOCK = 16
+
+
+@dataclass(frozen=True)
+class Shape:
+    batch: int
+    kv_heads: int
+    group: int
+    head_dim: int
+    max_blocks: int
+    budget_blocks: int
+    n_draft: int
+    fetch_cap: int
+    dtype: str  # "bf16" | "f32"
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.kv_heads
+
+    @property
+    def T(self) -> int:
+        return 1 + self.n_draft
+
+    @property
+    def q_heads(self) -> int:
+        return self.kv_heads * self.group
+
+    @property
+    def code(self) -> int:
+        return L.OASIS_BF16 if self.dtype == "bf16" else L.OASIS_F32
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def np_elem(self):
+        return np.uint16 if self.dtype == "bf16" else np.float32
+
+    def handle(self, fetch_cap: int | None = None) -> int:
+        return L.oasis_create(self.batch, self.kv_heads, self.group, self.head_dim, self.max_blocks,
+                              self.budget_blocks, self.n_draft,
+                              self.fetch_cap if fetch_cap is None else fetch_cap, self.code)
+
+
+class LayerState:
+    """Device state of one layer (one replica) plus its pinned host tier."""
+
+    def __init__(self, rt: "DecodeRuntime", host_tier: torch.Tensor | None):
+        s, dev = rt.shape, rt.device
+        h = rt.h
+        u, k, N, cap = s.units, s.budget_blocks, s.max_blocks, s.fetch_cap
+        self.meta = torch.zeros(L.oasis_meta_bytes(h), dtype=torch.uint8, device=dev)
+        self.pool = torch.zeros(L.oasis_pool_bytes(h), dtype=torch.uint8, device=dev)
+        self.b2s = torch.full((u, N), -1, dtype=torch.int32, device=dev)
+        self.s2b = torch.full((u, k), -1, dtype=torch.int32, device=dev)
+        self.scores = torch.zeros((u, N), dtype=torch.float32, device=dev)
+        self.sel = torch.full((u, k), -1, dtype=torch.int32, device=dev)
+        self.fetch = torch.full((u, max(cap, 1), 2), -1, dtype=torch.int32, device=dev)
+        self.n_fetch = torch.zeros(u, dtype=torch.int32, device=dev)
+        self.evict = torch.full((u, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+        self.host_tier = host_tier
+        self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
+        self.n_fetch_host = torch.empty(u, dtype=torch.int32, pin_memory=True)
+        self.fetch_done = None  # event recorded on the side stream after the last transfer
+
+    def copy_from(self, other: "LayerState"):
+        for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict"):
+            getattr(self, name).copy_(getattr(other, name))
+
+
+class DecodeRuntime:
+    """Buffers and step chain for `layers` layers of one shape on one GPU."""
+
+    def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
+                 host_tier: bool = True):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.h = shape.handle()
+        s = shape
+        self.n_layers = layers
+        self.replicas = replicas
+        tiers = []
+        for _ in range(layers):
+            tiers.append(torch.empty(L.oasis_host_tier_bytes(self.h), dtype=torch.uint8, pin_memory=True)
+                         if host_tier else None)
+        # state[layer][replica]; replicas share the layer's host tier
+        self.state = [[LayerState(self, tiers[l]) for _ in range(replicas)] for l in range(layers)]
+        self.ctx = [torch.zeros(s.batch, dtype=torch.int32, device=self.device) for _ in range(2)]
+        self.ctx_cur = 0
+        self.ctx_host = np.zeros(s.batch, dtype=np.int32)
+        self.out = torch.zeros((s.batch, s.q_heads, s.T, s.head_dim), dtype=torch.float32, device=self.device)
+        ws = L.oasis_workspace_bytes(self.h)
+        self.ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.ws.data_ptr()) % 256
+        self.ws_ptr = self.ws.data_ptr() + off
+        self.side = torch.cuda.Stream(device=self.device)
+
+    def close(self):
+        if self.h:
+            L.oasis_destroy(self.h)
+            self.h = 0
+
+    # ------------------------------------------------------------ setup (untimed)
+    @property
+    def ctx_len(self) -> torch.Tensor:
+        return self.ctx[self.ctx_cur]
+
+    def set_ctx(self, ctx_host):
+        self.ctx_host = np.asarray(ctx_host, dtype=np.int32).copy()
+        self.ctx[self.ctx_cur].copy_(torch.from_numpy(self.ctx_host))
+
+    def host_tier_view(self, layer: int) -> torch.Tensor:
+        return self.state[layer][0].host_tier
+
+    def pack_unit(self, layer: int, unit: int, k_rows: np.ndarray, v_rows: np.ndarray | None,
+                  blocks: np.ndarray | None = None):
+        """Write blocks of one unit into the layer's host tier.
+
+        k_rows/v_rows: element-typed arrays [n_blocks * 16][d] (uint16 bf16 bits or float32);
+        blocks: destination block ids (default 0 .. n_blocks-1).
+        """
+        s = self.shape
+        k_rows = np.ascontiguousarray(k_rows, dtype=s.np_elem)
+        nb = k_rows.shape[0] // BLOCK
+        assert k_rows.shape == (nb * BLOCK, s.head_dim)
+        if v_rows is not None:
+            v_rows = np.ascontiguousarray(v_rows, dtype=s.np_elem)
+            assert v_rows.shape == k_rows.shape
+        bl = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int32)
+        L.oasis_pack_pages(self.h, k_rows, v_rows, bl, nb, unit, self.host_tier_view(layer))
+
+    def build_meta(self, layer: int, stream=None):
+        """Stage the layer's whole host tier to the device and build its block metadata."""
+        tier = self.host_tier_view(layer)
+        staged = tier.to(self.device, non_blocking=False)
+        for st in self.state[layer]:
+            L.oasis_block_meta_build(self.h, staged, None, self.shape.units * self.shape.max_blocks,
+                                     self.ctx_len, st.meta, None, None, stream)
+        torch.cuda.current_stream().synchronize()
+        del staged
+
+    def rebuild_blocks(self, layer: int, page_ids: np.ndarray):
+        """After host-tier pages changed: restage them, rebuild their metadata and patch
+        the resident copies (page_ids = unit * max_blocks + block)."""
+        s = self.shape
+        ids = np.ascontiguousarray(page_ids, dtype=np.int64)
+        if len(ids) == 0:
+            return
+        pb = L.oasis_page_bytes(self.h)
+        tier = self.host_tier_view(layer).view(-1, pb)
+        staged = tier[torch.from_numpy(ids)].to(self.device)
+        ids_dev = torch.from_numpy(ids.astype(np.int32)).to(self.device)
+        for st in self.state[layer]:
+            L.oasis_block_meta_build(self.h, staged, ids_dev, len(ids), self.ctx_len, st.meta, st.pool,
+                                     st.b2s)
+        torch.cuda.current_stream().synchronize()
+
+    def prologue(self, layer: int, q: torch.Tensor, initial_slots):
+        """Score the step -1 drafts, select S_0, install the initial residency
+        (initial_slots(unit, sel_row) -> slot_to_block row), then one diff + transfer."""
+        s = self.shape
+        for st in self.state[layer]:
+            L.oasis_lookahead_score(self.h, q, st.meta, self.ctx_len, st.scores)
+            L.oasis_topk_select(self.h, st.scores, self.ctx_len, st.sel)
+        st0 = self.state[layer][0]
+        sel = st0.sel.cpu().numpy()
+        s2b = np.stack([np.asarray(initial_slots(u, sel[u]), dtype=np.int32) for u in range(s.units)])
+        b2s = np.full((s.units, s.max_blocks), -1, dtype=np.int32)
+        for u in range(s.units):
+            for slot, b in enumerate(s2b[u]):
+                if b >= 0:
+                    b2s[u, b] = slot
+        # initial pages through the transfer path (a handle whose cap covers every slot)
+        h_all = s.handle(fetch_cap=s.budget_blocks)
+        try:
+            lst = np.full((s.units, s.budget_blocks, 2), -1, dtype=np.int32)
+            cnt = np.zeros(s.units, dtype=np.int32)
+            for u in range(s.units):
+                rows = [(int(b), slot) for slot, b in enumerate(s2b[u]) if b >= 0]
+                cnt[u] = len(rows)
+                if rows:
+                    lst[u, : len(rows)] = rows
+            for st in self.state[layer]:
+                st.s2b.copy_(torch.from_numpy(s2b))
+                st.b2s.copy_(torch.from_numpy(b2s))
+                torch.cuda.current_stream().synchronize()
+                L.oasis_fetch_issue(h_all, st.host_tier, st.pool, lst, cnt, torch.cuda.current_stream())
+                torch.cuda.current_stream().synchronize()
+        finally:
+            L.oasis_destroy(h_all)
+        for st in self.state[layer]:
+            L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                            st.evict)
+        self.transfer(layer)
+
+    # ------------------------------------------------------------ per-step chain
+    def attention(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None):
+        st = self.state[layer][replica]
+        if st.fetch_done is not None:
+            torch.cuda.current_stream().wait_event(st.fetch_done)
+            st.fetch_done = None
+        L.oasis_sparse_paged_decode_attn(self.h, q, st.pool, st.sel, st.b2s, self.ctx_len,
+                                         self.out if out is None else out, self.ws_ptr)
+
+    def append(self, layer: int, k_new_dev, v_new_dev, k_new_host=None, v_new_host=None,
+               replica: int = 0):
+        """Append one token per unit at the current context lengths (positions).
+
+        Every layer of a step appends at the same positions; the scoring that
+        follows sees the grown context (ctx_scoring) while later layers' attention
+        of the same step still sees the old one; end_step() makes it current.
+        """
+        st = self.state[layer][replica]
+        L.oasis_block_meta_update(self.h, k_new_dev, v_new_dev, self.ctx[self.ctx_cur],
+                                  self.ctx[1 - self.ctx_cur], st.meta, st.pool, st.b2s)
+        if k_new_host is not None and replica == 0:
+            L.oasis_host_tier_append(self.h, np.ascontiguousarray(k_new_host),
+                                     np.ascontiguousarray(v_new_host), self.ctx_host, st.host_tier)
+        self._appended = True
+
+    @property
+    def ctx_scoring(self) -> torch.Tensor:
+        return self.ctx[1 - self.ctx_cur] if getattr(self, "_appended", False) else self.ctx[self.ctx_cur]
+
+    def end_step(self):
+        if getattr(self, "_appended", False):
+            self.ctx_cur = 1 - self.ctx_cur
+            self.ctx_host = self.ctx_host + 1
+            self._appended = False
+
+    def predict_select(self, layer: int, q: torch.Tensor, replica: int = 0):
+        st = self.state[layer][replica]
+        ctx = self.ctx_scoring
+        L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores)
+        L.oasis_topk_select(self.h, st.scores, ctx, st.sel)
+        L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                        st.evict)
+
+    def transfer(self, layer: int, replica: int = 0):
+        """Copy the fetch list to the host, then issue the page copies on the side stream."""
+        st = self.state[layer][replica]
+        cur = torch.cuda.current_stream()
+        st.fetch_host.copy_(st.fetch, non_blocking=True)
+        st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)
+        ready = torch.cuda.Event()
+        ready.record(cur)
+        ready.synchronize()
+        self.side.wait_event(ready)
+        L.oasis_fetch_issue(self.h, st.host_tier, st.pool, st.fetch_host, st.n_fetch_host, self.side)
+        done = torch.cuda.Event()
+        done.record(self.side)
+        st.fetch_done = done
+
+    def wait_transfers(self):
+        for layer in self.state:
+            for st in layer:
+                if st.fetch_done is not None:
+                    torch.cuda.current_stream().wait_event(st.fetch_done)
+                    st.fetch_done = None
+
+    # ------------------------------------------------------------ inspection
+    def pool_pages(self, layer: int, replica: int = 0) -> torch.Tensor:
+        s = self.shape
+        st = self.state[layer][replica]
+        return st.pool.view(s.units, s.budget_blocks, -1)
+
+    def meta_view(self, layer: int, replica: int = 0) -> torch.Tensor:
+        s = self.shape
+        st = self.state[layer][replica]
+        el = st.meta.view(torch.int16 if s.dtype == "bf16" else torch.float32)
+        return el.view(s.units, s.max_blocks, 2, s.head_dim)

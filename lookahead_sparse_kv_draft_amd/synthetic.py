@@ -1,0 +1,184 @@
+"""Runs the decode chain on the seeded synthetic workloads (workload/).
+
+Fills the pinned host tier of every layer from the generator, builds the block
+metadata on the GPU, runs the prologue (first selection, initial residency,
+first transfer) and then decode steps, optionally recording the per-step
+state of selected units for parity checks.  Used by the benchmark, the smoke
+check and the GPU tests.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from workload import synth
+from workload.configs import BLOCK, Config
+
+from .runtime import DecodeRuntime, Shape
+
+
+def shape_of(cfg: Config) -> Shape:
+    return Shape(batch=cfg.batch, kv_heads=cfg.kv_heads, group=cfg.group, head_dim=cfg.head_dim,
+                 max_blocks=cfg.max_blocks, budget_blocks=cfg.k, n_draft=cfg.n_draft,
+                 fetch_cap=cfg.fetch_cap, dtype=cfg.dtype)
+
+
+def _elem(cfg: Config, x: np.ndarray) -> np.ndarray:
+    return synth.to_bf16_bits(x) if cfg.dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class SyntheticRun:
+    """The decode chain of one workload configuration on cuda:0."""
+
+    def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
+                 record_units=None, device: str = "cuda"):
+        self.cfg = cfg
+        self.L = cfg.layers if layers is None else layers
+        self.shape = shape_of(cfg)
+        self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas)
+        self.record_units = record_units  # list of (layer, unit) to record, or None
+        self.records = {}
+        B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        # queries: [layer][step + 1][B][Hq][T][d]; index 0 = the prologue's drafts (step -1)
+        self.q = torch.empty((self.L, cfg.steps + 1, B, H * G, T, d), dtype=tdt, device=device)
+        self.kv_new = None
+        self.drift = None
+        if cfg.append:
+            self.k_new_host = np.empty((self.L, cfg.steps, B, H, d), dtype=self.shape.np_elem)
+            self.v_new_host = np.empty_like(self.k_new_host)
+        self._fill()
+
+    # ----------------------------------------------------------------- setup
+    def _fill(self):
+        cfg, rt = self.cfg, self.rt
+        B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
+        N0 = cfg.n_blocks0
+        qh = np.empty((cfg.steps + 1, B, H * G, T, d), dtype=np.float32)
+        if cfg.drift_blocks:
+            self.drift = {}  # (l, u) -> (unit data, schedule)
+        for l in range(self.L):
+            def work(u, l=l):
+                r, h = divmod(u, H)
+                ud = synth.unit_data(cfg, r, l, h)
+                K = ud.keys()
+                rt.pack_unit(l, u, _elem(cfg, K[: N0 * BLOCK]), _elem(cfg, ud.V[: N0 * BLOCK]))
+                for t in range(-1, cfg.steps):
+                    qq = ud.queries(t)  # [G][T][d]
+                    if t == -1:
+                        qq = qq.copy()
+                        qq[:, 0, :] = 0.0  # the prologue scores drafts only
+                    qh[t + 1, r, h * G:(h + 1) * G] = qq
+                if cfg.append:
+                    pos = cfg.ctx + np.arange(cfg.steps)
+                    self.k_new_host[l, :, r, h] = _elem(cfg, K[pos])
+                    self.v_new_host[l, :, r, h] = _elem(cfg, ud.V[pos])
+                if self.drift is not None:
+                    self.drift[(l, u)] = (ud, synth.drift_schedule(cfg, r, l, h, ud.planted0))
+            with ThreadPoolExecutor(max_workers=_threads()) as ex:
+                list(ex.map(work, range(cfg.units_per_layer)))
+            self.q[l].copy_(torch.from_numpy(qh).to(self.q.dtype))
+        if cfg.append:
+            self.k_new_dev = torch.from_numpy(self.k_new_host.view(np.int16) if cfg.dtype == "bf16"
+                                              else self.k_new_host).to(self.rt.device)
+            self.v_new_dev = torch.from_numpy(self.v_new_host.view(np.int16) if cfg.dtype == "bf16"
+                                              else self.v_new_host).to(self.rt.device)
+        rt.set_ctx(np.full(cfg.batch, cfg.ctx, dtype=np.int32))
+        for l in range(self.L):
+            rt.build_meta(l)
+
+    def prologue(self):
+        cfg = self.cfg
+        H = cfg.kv_heads
+        for l in range(self.L):
+            def init(u, sel_row, l=l):
+                r, h = divmod(u, H)
+                return synth.initial_residency(cfg, r, l, h, sel_row)
+            self.rt.prologue(l, self.q[l, 0], init)
+        self.rt.wait_transfers()
+        self._record(-1)
+
+    # ----------------------------------------------------------------- steps
+    def _apply_drift(self, l: int, t: int):
+        cfg, rt = self.cfg, self.rt
+        ids = []
+        for u in range(cfg.units_per_layer):
+            ud, sched = self.drift[(l, u)]
+            unplant, plant, planted_after = sched[t]
+            blocks = np.concatenate([unplant, plant]).astype(np.int64)
+            if len(blocks) == 0:
+                continue
+            kb = ud.keys_of_blocks(blocks, planted_after)  # [m][16][d]
+            rt.pack_unit(l, u, _elem(cfg, kb.reshape(-1, cfg.head_dim)), None, blocks.astype(np.int32))
+            ids.append(u * cfg.max_blocks + blocks)
+        if ids:
+            rt.rebuild_blocks(l, np.concatenate(ids))
+
+    def step(self, t: int, transfer: bool = True):
+        cfg, rt = self.cfg, self.rt
+        for l in range(self.L):
+            q = self.q[l, t + 1]
+            rt.attention(l, q)
+            if self.record_units is not None:
+                self._record_out(l, t)
+            if cfg.append:
+                rt.append(l, self.k_new_dev[l, t], self.v_new_dev[l, t],
+                          self.k_new_host[l, t], self.v_new_host[l, t])
+            if self.drift is not None:
+                self._apply_drift(l, t)
+            rt.predict_select(l, q)
+            if transfer:
+                rt.transfer(l)
+        rt.end_step()
+        if transfer:
+            rt.wait_transfers()
+        self._record(t)
+
+    def run(self, steps: int | None = None, transfer: bool = True):
+        self.prologue()
+        for t in range(self.cfg.steps if steps is None else steps):
+            self.step(t, transfer=transfer)
+
+    # ----------------------------------------------------------------- records
+    def _record_out(self, l: int, t: int):
+        cfg = self.cfg
+        out = self.rt.out.cpu().numpy()
+        for (rl, u) in self.record_units:
+            if rl != l:
+                continue
+            r, h = divmod(u, cfg.kv_heads)
+            self.records.setdefault((l, u), {}).setdefault(t, {})["out"] = \
+                out[r, h * cfg.group:(h + 1) * cfg.group].copy()
+
+    def _record(self, t: int):
+        if self.record_units is None:
+            return
+        torch.cuda.synchronize()
+        cache = {}
+        for (l, u) in self.record_units:
+            if l not in cache:
+                st = self.rt.state[l][0]
+                cache[l] = {k: getattr(st, k).cpu().numpy() for k in
+                            ("sel", "scores", "fetch", "n_fetch", "evict", "s2b", "b2s")}
+            c = cache[l]
+            rec = self.records.setdefault((l, u), {}).setdefault(t, {})
+            nf = int(c["n_fetch"][u])
+            rec.update(sel=c["sel"][u].copy(), scores=c["scores"][u].copy(),
+                       fetch=[tuple(int(x) for x in p) for p in c["fetch"][u][:nf]],
+                       evict=[int(v) for v in c["evict"][u][:nf] if v >= 0],
+                       s2b=c["s2b"][u].copy(), b2s=c["b2s"][u].copy(),
+                       n_scoring=int(self.rt.ctx_len.cpu().numpy()[u // self.cfg.kv_heads]))
+
+    def close(self):
+        self.rt.close()

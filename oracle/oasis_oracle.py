@@ -224,6 +224,7 @@ class StepRecord:
     evict: list = field(default_factory=list)
     block_to_slot: np.ndarray | None = None  # after this step's update
     slot_to_block: np.ndarray | None = None
+    slot_to_block_before: np.ndarray | None = None  # before this step's update
     n_missing: int = 0
 
 
@@ -259,6 +260,7 @@ def run_unit(*, K_at, V, queries, drafts_prologue, n0: int, k: int, cap: int, st
     for s, b in enumerate(s2b):
         if b >= 0:
             b2s[b] = s
+    rec.slot_to_block_before = s2b.copy()
     res = resident_diff_cap_evict(rec.sel, rec.score, b2s, s2b, cap)
     rec.n_missing = sum(1 for b in rec.sel if b >= 0 and b2s[b] < 0)
     b2s, s2b = res.block_to_slot, res.slot_to_block
@@ -284,6 +286,7 @@ def run_unit(*, K_at, V, queries, drafts_prologue, n0: int, k: int, cap: int, st
         rec.score = lookahead_score(q[:, 1:, :], kmin, kmax)
         rec.sel = topk_select(rec.score, kmin.shape[0], k)
         rec.n_missing = sum(1 for b in rec.sel if b >= 0 and b2s[b] < 0)
+        rec.slot_to_block_before = s2b.copy()
         res = resident_diff_cap_evict(rec.sel, rec.score, b2s, s2b, cap)
         b2s, s2b = res.block_to_slot, res.slot_to_block
         rec.fetch, rec.evict = res.fetch, res.evict

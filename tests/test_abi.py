@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+validates arguments before touching the device, and packs host pages in the
+documented layout."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from lookahead_sparse_kv_draft_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oasiskv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oasis_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_set():
+    assert declared_functions() == sorted(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _shape(**kw):
+    base = dict(batch=2, kv_heads=2, group=4, head_dim=128, max_blocks=64, budget_blocks=16,
+                n_draft=4, fetch_cap=4, dtype=L.OASIS_BF16)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), L.OASIS_EINVAL),
+    (dict(budget_blocks=1), L.OASIS_EINVAL),
+    (dict(budget_blocks=2000), L.OASIS_EINVAL),
+    (dict(fetch_cap=-1), L.OASIS_EINVAL),
+    (dict(head_dim=96), L.OASIS_EUNSUPPORTED),
+    (dict(block_size=32), L.OASIS_EUNSUPPORTED),
+    (dict(dtype=7), L.OASIS_EUNSUPPORTED),
+    (dict(group=16, n_draft=4), L.OASIS_EUNSUPPORTED),   # 80 query rows
+    (dict(max_blocks=70000), L.OASIS_EUNSUPPORTED),
+])
+def test_create_rejects_bad_shapes(kw, code):
+    with pytest.raises(L.OasisError) as e:
+        L.oasis_create(**_shape(**kw))
+    assert e.value.code == code
+    assert L.oasis_last_error()
+
+
+def test_sizes_and_null_checks():
+    h = L.oasis_create(**_shape())
+    try:
+        assert L.oasis_version() == 1
+        assert L.oasis_page_bytes(h) == 2 * 16 * 128 * 2
+        assert L.oasis_meta_bytes(h) == 4 * 64 * 2 * 128 * 2
+        assert L.oasis_pool_bytes(h) == 4 * 16 * 8192
+        assert L.oasis_host_tier_bytes(h) == 4 * 64 * 8192
+        assert L.oasis_workspace_bytes(h) > 0
+        lib = L.load()
+        # null pointers are rejected before any device work
+        assert lib.oasis_lookahead_score(h, None, None, None, None, None) == L.OASIS_EINVAL
+        assert "null" in L.oasis_last_error()
+        assert lib.oasis_topk_select(h, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_resident_diff_cap_evict(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_sparse_paged_decode_attn(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_block_meta_update(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_block_meta_build(h, None, None, 0, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_lookahead_score(None, 16, 16, 16, 16, None) == L.OASIS_EINVAL
+        # misaligned device pointers
+        assert lib.oasis_lookahead_score(h, 18, 32, 16, 16, None) == L.OASIS_EINVAL
+        assert "aligned" in L.oasis_last_error()
+        # aliasing context buffers
+        assert lib.oasis_block_meta_update(h, 16, 16, 64, 64, 16, 16, 16, None) == L.OASIS_EINVAL
+    finally:
+        L.oasis_destroy(h)
+
+
+def test_fetch_issue_validates_every_entry_first():
+    h = L.oasis_create(**_shape())
+    try:
+        fetch = np.full((4, 4, 2), -1, dtype=np.int32)
+        nf = np.array([1, 0, 0, 0], dtype=np.int32)
+        fetch[0, 0] = (64, 0)  # block out of range
+        with pytest.raises(L.OasisError) as e:
+            L.oasis_fetch_issue(h, 16, 16, fetch, nf, 0)
+        assert e.value.code == L.OASIS_EINVAL
+        fetch[0, 0] = (3, 16)  # slot out of range
+        with pytest.raises(L.OasisError):
+            L.oasis_fetch_issue(h, 16, 16, fetch, nf, 0)
+        nf[0] = 5  # more entries than the cap
+        with pytest.raises(L.OasisError):
+            L.oasis_fetch_issue(h, 16, 16, fetch, nf, 0)
+        nf[:] = 0
+        L.oasis_fetch_issue(h, 16, 16, fetch, nf, 0)  # nothing to copy: no device work
+    finally:
+        L.oasis_destroy(h)
+
+
+@pytest.mark.parametrize("dtype", [L.OASIS_BF16, L.OASIS_F32])
+def test_pack_pages_layout(dtype):
+    """Page = K rows token-major [16][d], then V channel-major [d][16]."""
+    d, Nmax = 64, 6
+    h = L.oasis_create(**_shape(head_dim=d, max_blocks=Nmax, dtype=dtype))
+    try:
+        et = np.uint16 if dtype == L.OASIS_BF16 else np.float32
+        rng = np.random.default_rng(0)
+        K = rng.integers(0, 60000, size=(3 * 16, d)).astype(et)
+        V = rng.integers(0, 60000, size=(3 * 16, d)).astype(et)
+        pages = np.zeros((4, Nmax, 2 * 16 * d), dtype=et)
+        blocks = np.array([4, 0, 2], dtype=np.int32)
+        L.oasis_pack_pages(h, K, V, blocks, 3, 2, pages)
+        for i, b in enumerate(blocks):
+            kp = pages[2, b, : 16 * d].reshape(16, d)
+            vt = pages[2, b, 16 * d:].reshape(d, 16)
+            assert np.array_equal(kp, K[16 * i: 16 * i + 16])
+            assert np.array_equal(vt, V[16 * i: 16 * i + 16].T)
+        assert not pages[2, 1].any() and not pages[2, 3].any() and not pages[0].any()
+        # K only: V half untouched
+        K2 = K + 1
+        L.oasis_pack_pages(h, K2[:16], None, np.array([4], dtype=np.int32), 1, 2, pages)
+        assert np.array_equal(pages[2, 4, : 16 * d].reshape(16, d), K2[:16])
+        assert np.array_equal(pages[2, 4, 16 * d:].reshape(d, 16), V[:16].T)
+        with pytest.raises(L.OasisError):
+            L.oasis_pack_pages(h, K, V, np.array([6], dtype=np.int32), 1, 0, pages)
+        # host append: token 35 (block 2, row 3) of request 1 -> units 2, 3
+        kn = rng.integers(0, 60000, size=(2, 2, d)).astype(et)
+        vn = rng.integers(0, 60000, size=(2, 2, d)).astype(et)
+        L.oasis_host_tier_append(h, kn, vn, np.array([0, 35], dtype=np.int32), pages)
+        assert np.array_equal(pages[3, 2, : 16 * d].reshape(16, d)[3], kn[1, 1])
+        assert np.array_equal(pages[3, 2, 16 * d:].reshape(d, 16)[:, 3], vn[1, 1])
+        assert np.array_equal(pages[1, 0, : 16 * d].reshape(16, d)[0], kn[0, 1])
+    finally:
+        L.oasis_destroy(h)

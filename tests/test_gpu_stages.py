@@ -1,0 +1,334 @@
+"""Stage-wise GPU parity: each HIP kernel against the fp64 oracle on the same inputs.
+
+Inputs come from the seeded generators; discrete stages (selection, diff) must
+match bit for bit, metadata exactly, scores within the fp32 summation bound and
+attention within max-abs 2e-2 / relative-L2 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from lookahead_sparse_kv_draft_amd import _lib as L
+from lookahead_sparse_kv_draft_amd.runtime import DecodeRuntime
+from oracle import oasis_oracle as O
+from tests import gpu_util as U
+from workload.synth import random_scores
+
+pytestmark = pytest.mark.gpu
+BLK = 16
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ score
+@pytest.mark.parametrize("dtype,d,G,D,Nmax,ctxs", [
+    ("bf16", 128, 4, 4, 75, [1190, 700]),      # 16 rows, ragged tiles
+    ("bf16", 128, 8, 4, 40, [640, 17]),        # 32 rows (two row tiles)
+    ("bf16", 128, 4, 5, 33, [528, 513]),       # 20 rows (padded row tile)
+    ("bf16", 64, 4, 3, 70, [1024, 1]),         # d = 64, a one-block request
+    ("bf16", 128, 16, 3, 300, [4800, 3333]),   # 48 rows, several tiles per wave
+    ("f32", 64, 4, 3, 64, [1024, 999]),
+    ("f32", 128, 2, 2, 20, [300, 20]),
+])
+def test_score_parity(dtype, d, G, D, Nmax, ctxs):
+    B, H = len(ctxs), 2
+    sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, n_draft=D, dtype=dtype)
+    h = sh.handle()
+    rng = _rng(1)
+    units = B * H
+    a = rng.standard_normal((units, Nmax, d)).astype(np.float32)
+    b = rng.standard_normal((units, Nmax, d)).astype(np.float32)
+    kmin = U.elem_round(dtype, np.minimum(a, b) * 1.5)
+    kmax = U.elem_round(dtype, np.maximum(a, b) * 1.5)
+    q = U.elem_round(dtype, rng.standard_normal((B, H * G, 1 + D, d)).astype(np.float32))
+    meta = np.stack([kmin, kmax], axis=2)  # [units][Nmax][2][d]
+    meta_d = U.to_dev(dtype, meta)
+    q_d = U.to_dev(dtype, q)
+    ctx_d = U.i32(ctxs)
+    scores = torch.full((units, Nmax), float("nan"), device="cuda")
+    L.oasis_lookahead_score(h, q_d, meta_d, ctx_d, scores)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy().astype(np.float64)
+    for u in range(units):
+        r, hh = divmod(u, H)
+        N = (ctxs[r] + BLK - 1) // BLK
+        qd = q[r, hh * G:(hh + 1) * G, 1:, :].astype(np.float64)
+        ref = O.lookahead_score(qd, kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
+        tol = U.score_tolerance(qd.reshape(-1, d), kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
+        err = np.abs(got[u, :N] - ref)
+        assert np.all(err <= tol), (u, float(err.max()), float(tol.min()))
+        assert np.all(np.isnan(got[u, N:])), "blocks past the context must not be written"
+    L.oasis_destroy(h)
+
+
+# ------------------------------------------------------------------ top-k
+@pytest.mark.parametrize("k,ctxs,kind", [
+    (128, [32768, 16 * 130, 16 * 128, 16 * 127 + 3], "normal"),
+    (128, [32768, 16 * 3000 + 1, 17, 16], "ties"),
+    (16, [1024, 16 * 16, 16 * 17, 5], "ties"),
+    (16, [1024, 999, 33, 16 * 18], "const"),
+    (2, [1024, 16, 32, 48], "normal"),
+    (128, [131072, 131072 - 5, 16 * 129, 16 * 8191], "normal"),
+])
+def test_topk_parity(k, ctxs, kind):
+    B, H = len(ctxs), 3
+    Nmax = max((c + BLK - 1) // BLK for c in ctxs)
+    sh = U.make_shape(batch=B, kv_heads=H, max_blocks=Nmax, budget_blocks=k)
+    h = sh.handle()
+    rng = _rng(2)
+    sc = np.stack([random_scores(rng, Nmax, kind) for _ in range(B * H)])
+    sc_d = torch.from_numpy(sc).cuda()
+    sel = torch.full((B * H, k), -7, dtype=torch.int32, device="cuda")
+    L.oasis_topk_select(h, sc_d, U.i32(ctxs), sel)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    for u in range(B * H):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        ref = O.topk_select(sc[u].astype(np.float64), N, k)
+        assert list(got[u]) == ref, (u, N)
+    L.oasis_destroy(h)
+
+
+# ------------------------------------------------------------------ diff / cap / evict
+def _random_state(rng, N, k, n_res, kind):
+    """A valid selection (forced blocks first) and consistent resident maps."""
+    forced = [0] if N == 1 else [0, N - 1]
+    others = rng.permutation(np.arange(1, N - 1))[: max(0, min(k, N) - len(forced))]
+    sel = forced + [int(b) for b in others]
+    sel += [-1] * (k - len(sel))
+    s2b = np.full(k, -1, dtype=np.int64)
+    res = rng.choice(N, size=min(n_res, N, k), replace=False)
+    slots = rng.choice(k, size=len(res), replace=False)
+    s2b[slots] = res
+    b2s = np.full(N, -1, dtype=np.int64)
+    b2s[res] = slots
+    sc = random_scores(rng, N, kind)
+    return sel, sc, b2s, s2b
+
+
+@pytest.mark.parametrize("k,cap,N,kind", [
+    (128, 32, 2048, "normal"), (128, 16, 2048, "ties"), (128, 0, 2048, "normal"),
+    (128, 128, 500, "ties"), (16, 4, 64, "normal"), (16, 1, 20, "const"), (8, 8, 8, "ties"),
+    (2, 2, 1, "normal"), (128, 24, 528, "normal"), (128, 32, 8192, "ties"),
+])
+def test_diff_parity(k, cap, N, kind):
+    B, H = 3, 4
+    units = B * H
+    sh = U.make_shape(batch=B, kv_heads=H, max_blocks=N, budget_blocks=k, fetch_cap=cap)
+    h = sh.handle()
+    rng = _rng(3)
+    sels, scs, b2ss, s2bs = [], [], [], []
+    for u in range(units):
+        n_res = [0, k // 2, k, int(rng.integers(0, k + 1))][u % 4]
+        sel, sc, b2s, s2b = _random_state(rng, N, k, n_res, kind)
+        sels.append(sel), scs.append(sc), b2ss.append(b2s), s2bs.append(s2b)
+    sel_d = U.i32(sels)
+    sc_d = torch.from_numpy(np.stack(scs)).cuda()
+    b2s_d = U.i32(b2ss)
+    s2b_d = U.i32(s2bs)
+    cw = max(cap, 1)
+    fetch = torch.full((units, cw, 2), -9, dtype=torch.int32, device="cuda")
+    nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+    ev = torch.full((units, cw), -9, dtype=torch.int32, device="cuda")
+    L.oasis_resident_diff_cap_evict(h, sel_d, sc_d, b2s_d, s2b_d, fetch, nf, ev)
+    torch.cuda.synchronize()
+    g_b2s, g_s2b = b2s_d.cpu().numpy(), s2b_d.cpu().numpy()
+    g_f, g_nf, g_ev = fetch.cpu().numpy(), nf.cpu().numpy(), ev.cpu().numpy()
+    for u in range(units):
+        ref = O.resident_diff_cap_evict(sels[u], scs[u].astype(np.float64), b2ss[u], s2bs[u], cap)
+        assert g_nf[u] == len(ref.fetch)
+        exp_f = np.full((cw, 2), -9 if cap == 0 else -1)
+        for i, (b, s) in enumerate(ref.fetch):
+            exp_f[i] = (b, s)
+        if cap > 0:
+            assert np.array_equal(g_f[u], exp_f), u
+            exp_e = np.full(cap, -1)
+            exp_e[: len(ref.evict)] = ref.evict
+            assert np.array_equal(g_ev[u], exp_e), u
+        assert np.array_equal(g_b2s[u], ref.block_to_slot), u
+        assert np.array_equal(g_s2b[u], ref.slot_to_block), u
+    L.oasis_destroy(h)
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("dtype,d,G,D,k,ctxs", [
+    ("bf16", 128, 4, 4, 128, [32768, 2050]),    # 20 rows, split-K over 128 blocks
+    ("bf16", 128, 8, 4, 128, [4000, 2048]),     # 40 rows (three row tiles)
+    ("bf16", 128, 4, 5, 16, [263, 100]),        # 24 rows, partial newest block
+    ("bf16", 64, 4, 3, 16, [1024, 17]),         # d = 64
+    ("bf16", 128, 16, 3, 8, [150, 15]),         # 64 rows; one-block request with 15 tokens
+    ("f32", 64, 4, 3, 16, [1024, 250]),
+    ("f32", 128, 2, 1, 8, [200, 33]),
+])
+def test_attention_parity(dtype, d, G, D, k, ctxs):
+    B, H = len(ctxs), 2
+    T = 1 + D
+    Nmax = max((c + BLK - 1) // BLK for c in ctxs)
+    sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k,
+                      n_draft=D, fetch_cap=k, dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(4)
+    units = B * H
+    K = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32) * 1.5)
+    V = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    q = U.elem_round(dtype, rng.standard_normal((B, H * G, T, d)).astype(np.float32))
+    for u in range(units):
+        rt.pack_unit(0, u, U.to_elem_np(dtype, K[u]), U.to_elem_np(dtype, V[u]))
+    rt.set_ctx(ctxs)
+    # selection with some -1 entries and some selected blocks not resident
+    sel = np.full((units, k), -1, dtype=np.int32)
+    s2b = np.full((units, k), -1, dtype=np.int32)
+    b2s = np.full((units, Nmax), -1, dtype=np.int32)
+    fetch = np.full((units, k, 2), -1, dtype=np.int32)
+    nfe = np.zeros(units, dtype=np.int32)
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        m = min(k, N)
+        chosen = rng.choice(N, size=m, replace=False)
+        sel[u, :m] = chosen
+        if m > 2:
+            sel[u, m - 1] = -1
+        resident = [b for i, b in enumerate(chosen) if i % 5 != 3] + \
+            [b for b in rng.choice(N, size=min(N, 4), replace=False) if b not in chosen]
+        resident = resident[:k]
+        slots = rng.permutation(k)[: len(resident)]
+        for b, s in zip(resident, slots):
+            s2b[u, s] = b
+            b2s[u, b] = s
+            fetch[u, nfe[u]] = (b, s)
+            nfe[u] += 1
+    st = rt.state[0][0]
+    st.sel.copy_(torch.from_numpy(sel))
+    st.b2s.copy_(torch.from_numpy(b2s))
+    st.s2b.copy_(torch.from_numpy(s2b))
+    L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nfe, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    q_d = U.to_dev(dtype, q)
+    rt.out.fill_(float("nan"))
+    rt.attention(0, q_d)
+    torch.cuda.synchronize()
+    got = rt.out.cpu().numpy().astype(np.float64)
+    for u in range(units):
+        r, hh = divmod(u, H)
+        A = O.attended_blocks(sel[u], b2s[u])
+        ref = O.sparse_attention(q[r, hh * G:(hh + 1) * G].astype(np.float64), K[u].astype(np.float64),
+                                 V[u].astype(np.float64), A, ctxs[r])
+        g = got[r, hh * G:(hh + 1) * G]
+        ma, rl = U.attn_errors(g, ref)
+        assert ma <= U.ATTN_MAX_ABS and rl <= U.ATTN_REL_L2, (u, ma, rl)
+    rt.close()
+
+
+def test_attention_empty_selection_gives_zero():
+    sh = U.make_shape(batch=1, kv_heads=1, max_blocks=8, budget_blocks=4)
+    rt = DecodeRuntime(sh)
+    rt.set_ctx([100])
+    q = torch.ones((1, 4, 5, 128), dtype=torch.bfloat16, device="cuda")
+    rt.out.fill_(float("nan"))
+    rt.attention(0, q)  # sel all -1
+    torch.cuda.synchronize()
+    assert torch.all(rt.out == 0)
+    rt.close()
+
+
+# ------------------------------------------------------------------ metadata
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_meta_build_and_append(dtype, d):
+    B, H, Nmax, k = 2, 2, 12, 4
+    ctxs = [150, 33]
+    steps = 40
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=Nmax, budget_blocks=k, fetch_cap=k,
+                      dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(5)
+    units = B * H
+    K = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    V = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    for u in range(units):
+        rt.pack_unit(0, u, U.to_elem_np(dtype, K[u]), U.to_elem_np(dtype, V[u]))
+    rt.set_ctx(ctxs)
+    rt.build_meta(0)
+    st = rt.state[0][0]
+    # make the block holding each request's next token resident in slot 1
+    s2b = np.full((units, k), -1, dtype=np.int32)
+    b2s = np.full((units, Nmax), -1, dtype=np.int32)
+    for u in range(units):
+        b = ctxs[u // H] // BLK
+        s2b[u, 1], b2s[u, b] = b, 1
+    st.s2b.copy_(torch.from_numpy(s2b))
+    st.b2s.copy_(torch.from_numpy(b2s))
+    st.pool.zero_()
+
+    def check(n_per_req):
+        m = rt.meta_view(0)
+        mv = m.view(torch.bfloat16).float() if dtype == "bf16" else m
+        mv = mv.cpu().numpy().astype(np.float64)
+        for u in range(units):
+            n = n_per_req[u // H]
+            kmin, kmax = O.block_meta(K[u].astype(np.float64), n)
+            N = kmin.shape[0]
+            assert np.array_equal(mv[u, :N, 0], kmin) and np.array_equal(mv[u, :N, 1], kmax), (u, n)
+
+    check(ctxs)
+    n = list(ctxs)
+    for t in range(steps):
+        pos = np.array(n)
+        kn = np.stack([K[u, pos[u // H]] for u in range(units)]).reshape(B, H, d)
+        vn = np.stack([V[u, pos[u // H]] for u in range(units)]).reshape(B, H, d)
+        rt.append(0, U.to_dev(dtype, kn), U.to_dev(dtype, vn), U.to_elem_np(dtype, kn), U.to_elem_np(dtype, vn))
+        rt.end_step()
+        n = [x + 1 for x in n]
+        torch.cuda.synchronize()
+        check(n)
+        assert list(rt.ctx_len.cpu().numpy()) == n
+    # resident page rows written by the append == host tier rows
+    pages = rt.pool_pages(0).cpu().numpy()
+    eb = sh.elem_bytes
+    for u in range(units):
+        b = ctxs[u // H] // BLK
+        first = ctxs[u // H]
+        last = min(n[u // H], (b + 1) * BLK)
+        pg = pages[u, 1].view(np.uint16 if dtype == "bf16" else np.float32)
+        kp = pg[: BLK * d].reshape(BLK, d)
+        vt = pg[BLK * d:].reshape(d, BLK)
+        for j in range(first - b * BLK, last - b * BLK):
+            assert np.array_equal(kp[j], U.to_elem_np(dtype, K[u, b * BLK + j])), (u, j)
+            assert np.array_equal(vt[:, j], U.to_elem_np(dtype, V[u, b * BLK + j])), (u, j)
+        ht = rt.host_tier_view(0).numpy().view(np.uint16 if dtype == "bf16" else np.float32)
+        ht = ht.reshape(units, Nmax, 2 * BLK * d)
+        hp = ht[u, b]
+        for j in range(first - b * BLK, last - b * BLK):
+            assert np.array_equal(hp[: BLK * d].reshape(BLK, d)[j], U.to_elem_np(dtype, K[u, b * BLK + j]))
+    rt.close()
+
+
+def test_fetch_issue_copies_pages():
+    sh = U.make_shape(batch=2, kv_heads=2, max_blocks=40, budget_blocks=8, fetch_cap=5)
+    rt = DecodeRuntime(sh)
+    rng = _rng(6)
+    ht = rt.host_tier_view(0)
+    ht.copy_(torch.from_numpy(rng.integers(0, 255, size=ht.numel(), dtype=np.uint8)))
+    st = rt.state[0][0]
+    st.pool.zero_()
+    fetch = np.full((4, 5, 2), -1, dtype=np.int32)
+    nf = np.array([5, 0, 3, 1], dtype=np.int32)
+    for u in range(4):
+        blocks = rng.choice(40, size=nf[u], replace=False)
+        slots = rng.choice(8, size=nf[u], replace=False)
+        fetch[u, : nf[u]] = np.stack([blocks, slots], axis=1)
+    L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nf, rt.side)
+    rt.side.synchronize()
+    pb = L.oasis_page_bytes(rt.h)
+    host = ht.numpy().reshape(4, 40, pb)
+    pool = st.pool.cpu().numpy().reshape(4, 8, pb)
+    for u in range(4):
+        used = set()
+        for i in range(nf[u]):
+            b, s = fetch[u, i]
+            assert np.array_equal(pool[u, s], host[u, b])
+            used.add(s)
+        for s in set(range(8)) - used:
+            assert not pool[u, s].any()
+    rt.close()

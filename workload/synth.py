@@ -10,7 +10,7 @@ PCG64 streams so any unit can be regenerated alone, which lets the oracle
 check sampled units of a full-size run):
 
 * stream (r, l, h, 0), fixed draw order:
-  K_raw [ctx_max][d] ~ N(0, 1), V_raw [ctx_max][d] ~ N(0, 1),
+  K_raw [max_blocks*16][d] ~ N(0, 1), V_raw [max_blocks*16][d] ~ N(0, 1),
   q_base [G][d] ~ N(0, 1), the planted block set (uniform without replacement
   over the prompt blocks), draft noise [steps + 1][D][G][d] ~ N(0, 0.1^2).
 * u = normalize(sum_g q_base[g]), the unit mean query direction of the group.
@@ -68,8 +68,8 @@ class UnitData:
     r: int
     l: int
     h: int
-    K_base: np.ndarray    # [ctx_max][d] round(K_raw), before any shift
-    V: np.ndarray         # [ctx_max][d]
+    K_base: np.ndarray    # [max_blocks * 16][d] round(K_raw), before any shift
+    V: np.ndarray         # [max_blocks * 16][d]
     q_base: np.ndarray    # [G][d] verify query (element-typed)
     drafts: np.ndarray    # [steps + 1][D][G][d]; drafts[t + 1] are the drafts of step t
     u: np.ndarray         # [d] float32 unit mean query direction
@@ -78,9 +78,9 @@ class UnitData:
     def shift_per_token(self, planted: np.ndarray) -> np.ndarray:
         """Per-token shift multiplier s for the given planted block set."""
         cfg = self.cfg
-        s = np.zeros(cfg.ctx_max, dtype=np.float32)
+        s = np.zeros(cfg.max_blocks * BLOCK, dtype=np.float32)
         if len(planted):
-            blk = np.arange(cfg.ctx_max) // BLOCK
+            blk = np.arange(cfg.max_blocks * BLOCK) // BLOCK
             s += cfg.planted_shift * np.isin(blk, planted).astype(np.float32)
         if cfg.recency_blocks:
             start = max(0, (cfg.n_blocks0 - cfg.recency_blocks) * BLOCK)
@@ -88,7 +88,7 @@ class UnitData:
         return s
 
     def keys(self, planted: np.ndarray | None = None) -> np.ndarray:
-        """K [ctx_max][d] for a planted set (default: the initial one)."""
+        """K [max_blocks * 16][d] for a planted set (default: the initial one)."""
         if planted is None:
             planted = self.planted0
         s = self.shift_per_token(np.asarray(planted))
@@ -111,7 +111,7 @@ class UnitData:
 
 def unit_data(cfg: Config, r: int, l: int, h: int) -> UnitData:
     rng = _rng(cfg, r, l, h, 0)
-    n, d, G, D = cfg.ctx_max, cfg.head_dim, cfg.group, cfg.n_draft
+    n, d, G, D = cfg.max_blocks * BLOCK, cfg.head_dim, cfg.group, cfg.n_draft
     K_raw = rng.standard_normal((n, d), dtype=np.float32)
     V_raw = rng.standard_normal((n, d), dtype=np.float32)
     q_raw = rng.standard_normal((G, d), dtype=np.float32)
