@@ -104,16 +104,17 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.page_elems = static_cast<size_t>(2) * oasis::kBlock * s.head_dim;
   c.units = static_cast<int>(units);
 
-  // Attention split-K: enough (unit, split) wavefronts to fill 256 CUs, at
-  // least 8 selection entries per split, at most 64 (one per lane).
+  // Attention split-K: W-wavefront workgroups per (unit, split), about 1024
+  // wavefronts in total, at least 2 selection entries per wavefront and at most
+  // one per lane.
+  int waves = env_int("OASIS_ATTN_WAVES", 1);
+  if (waves != 1 && waves != 2 && waves != 4) waves = 1;
   int splits = env_int("OASIS_ATTN_SPLITS", 0);
-  if (splits <= 0) {
-    const int want = (1024 + c.units - 1) / c.units;
-    splits = std::min(want, (s.budget_blocks + 7) / 8);
-  }
-  splits = std::max(1, std::min(splits, s.budget_blocks));
+  if (splits <= 0) splits = (1024 + c.units * waves - 1) / (c.units * waves);
+  splits = std::max(1, std::min(splits, (s.budget_blocks + 2 * waves - 1) / (2 * waves)));
   int split_len = (s.budget_blocks + splits - 1) / splits;
-  if (split_len > oasis::kWave) split_len = oasis::kWave;
+  if (split_len > waves * oasis::kWave) split_len = waves * oasis::kWave;
+  c.attn_waves = waves;
   c.attn_split_len = split_len;
   c.attn_splits = (s.budget_blocks + split_len - 1) / split_len;
 

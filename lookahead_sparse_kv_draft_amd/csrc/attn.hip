@@ -35,16 +35,28 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
 
-template <int D, int RT>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(
+// LDS of the in-workgroup merge: per wave m and l for every row, plus the summed
+// accumulator [rows][D].
+template <int D, int RT, int W>
+struct AttnMergeLds {
+  float m[W][RT * 16];
+  float l[W][RT * 16];
+  float acc[RT * 16][D];
+};
+
+// W wavefronts per (unit, split) workgroup; W > 1 merges them in LDS.
+template <int D, int RT, int W>
+__global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s,
     const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    int H, int GT, int rows, int Nmax, int kb, int splits, int split_len, float scale_log2) {
+    float* __restrict__ out, int H, int GT, int rows, int Nmax, int kb, int splits, int split_len,
+    float scale_log2) {
   constexpr int KS = D / 32;  // QK k-steps of 32 channels
   constexpr int CT = D / 16;  // PV channel tiles
   constexpr int PAGE = 2 * kBlock * D;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int wid = blockIdx.x;  // unit * splits + split
@@ -52,12 +64,13 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   const int split = wid - unit * splits;
   const int n = ctx_len[unit / H];
 
-  // Resolve this split's selection entries, one per lane.
+  // This wavefront's selection entries: i0 + wv, i0 + wv + 4, ... (one per lane).
   const int i0 = split * split_len;
   const int cnt = min(split_len, kb - i0);
+  const int e = wv + W * lane;
   int my_slot = -1, my_ntok = 0;
-  if (lane < cnt) {
-    const int b = sel[static_cast<size_t>(unit) * kb + i0 + lane];
+  if (e < cnt) {
+    const int b = sel[static_cast<size_t>(unit) * kb + i0 + e];
     if (b >= 0 && b < Nmax) {
       const int s = b2s[static_cast<size_t>(unit) * Nmax + b];
       const int nt = min(kBlock, n - kBlock * b);
@@ -67,7 +80,13 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
       }
     }
   }
-  uint64_t pending = __ballot(my_slot >= 0);
+  // Compact the valid entries into lanes 0 .. nb-1 (forward lane permute).
+  const uint64_t valid = __ballot(my_slot >= 0);
+  const int nb = __popcll(valid);
+  const int pos = __popcll(valid & ((1ull << lane) - 1ull));
+  const int dst = (my_slot >= 0 ? pos : 63) * 4;
+  const int c_slot = __builtin_amdgcn_ds_permute(dst, my_slot);
+  const int c_ntok = __builtin_amdgcn_ds_permute(dst, my_ntok);
 
   // Query rows as the B operand of S^T = K Q^T: lane (col, grp) holds row
   // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.
@@ -94,96 +113,166 @@ __global__ __launch_bounds__(64) void attn_mfma_kernel(
   }
 
   const uint16_t* ubase = pool + static_cast<size_t>(unit) * kb * PAGE;
-  uint4 Kc[KS], Kn[KS];
-  uint2 Vc[CT], Vn[CT];
-  int ntok = 0;
-
-  auto load_page = [&](int slot, uint4* Kt, uint2* Vt) {
-    const uint16_t* pg = ubase + static_cast<size_t>(slot) * PAGE;
+  struct Page {
+    uint4 k[KS];
+    uint2 v[CT];
+  };
+  // Issue the loads of compacted entry j (every call loads: no branch around the
+  // loads, so each wait below covers only the older buffer).
+  auto load = [&](Page& pg, int j) {
+    const uint16_t* p = ubase + static_cast<size_t>(__shfl(c_slot, j)) * PAGE;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      Kt[s] = *reinterpret_cast<const uint4*>(pg + col * D + 8 * (4 * s + grp));
+      pg.k[s] = *reinterpret_cast<const uint4*>(p + col * D + 8 * (4 * s + grp));
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      Vt[ct] = *reinterpret_cast<const uint2*>(pg + kBlock * D + (16 * ct + col) * kBlock + 4 * grp);
+      pg.v[ct] = *reinterpret_cast<const uint2*>(p + kBlock * D + (16 * ct + col) * kBlock + 4 * grp);
+  };
+  auto process = [&](const Page& pg, int ntok) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pg.k[s]), as_bf16x8(Qb[rt][s]), st, 0, 0, 0);
+      float x[4];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (4 * grp + i < ntok) ? st[i] * scale_log2 : -INFINITY;
+        mb = fmaxf(mb, x[i]);
+      }
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mnew = fmaxf(mrun[rt], mb);
+      const float alpha = exp2f(mrun[rt] - mnew);
+      mrun[rt] = mnew;
+      uint16_t pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = f32_to_bf16(exp2f(x[i] - mnew));
+        psum += bf16_to_f32(pb[i]);
+      }
+      lrun[rt] = lrun[rt] * alpha + psum;
+      const uint2 pw = make_uint2(static_cast<uint32_t>(pb[0]) | (static_cast<uint32_t>(pb[1]) << 16),
+                                  static_cast<uint32_t>(pb[2]) | (static_cast<uint32_t>(pb[3]) << 16));
+      const s16x4_t P = as_s16x4(pw);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        acc[rt][ct] *= alpha;
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(pg.v[ct]), P, acc[rt][ct], 0, 0, 0);
+      }
+    }
   };
 
-  if (pending) {
-    const int idx = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-    load_page(__shfl(my_slot, idx), Kc, Vc);
-    ntok = __shfl(my_ntok, idx);
-    pending &= pending - 1;
-    while (true) {
-      int nntok = 0;
-      const bool more = pending != 0;
-      if (more) {
-        const int nidx = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-        load_page(__shfl(my_slot, nidx), Kn, Vn);
-        nntok = __shfl(my_ntok, nidx);
-        pending &= pending - 1;
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Kc[s]), as_bf16x8(Qb[rt][s]), st, 0, 0, 0);
-        float x[4];
-        float mb = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (4 * grp + i < ntok) ? st[i] * scale_log2 : -INFINITY;
-          mb = fmaxf(mb, x[i]);
-        }
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mnew = fmaxf(mrun[rt], mb);
-        const float alpha = exp2f(mrun[rt] - mnew);
-        mrun[rt] = mnew;
-        uint16_t pb[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = f32_to_bf16(exp2f(x[i] - mnew));
-          psum += bf16_to_f32(pb[i]);
-        }
-        lrun[rt] = lrun[rt] * alpha + psum;
-        const uint2 pw = make_uint2(static_cast<uint32_t>(pb[0]) | (static_cast<uint32_t>(pb[1]) << 16),
-                                    static_cast<uint32_t>(pb[2]) | (static_cast<uint32_t>(pb[3]) << 16));
-        const s16x4_t P = as_s16x4(pw);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          acc[rt][ct] *= alpha;
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(Vc[ct]), P, acc[rt][ct], 0, 0, 0);
-        }
-      }
-      if (!more) break;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) Kc[s] = Kn[s];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) Vc[ct] = Vn[ct];
-      ntok = nntok;
+  // Ping-pong over two page buffers: the next block's loads are in flight while
+  // the current block is processed.  Prefetch indices are clamped and an odd
+  // count is padded with a zero-token pass (a no-op for the online softmax once
+  // a real block has been seen), so the loop body has no branch and every wait
+  // covers only the older buffer.
+  if (nb > 0) {
+    Page pa, pbuf;
+    load(pa, 0);
+    for (int j = 0; j < nb; j += 2) {
+      load(pbuf, min(j + 1, nb - 1));
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+      process(pa, __shfl(c_ntok, j));
+      load(pa, min(j + 2, nb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      process(pbuf, (j + 1 < nb) ? __shfl(c_ntok, j + 1) : 0);
     }
   }
 
-  // Partials: unnormalised O rows, running max (log2 domain) and sum.
+  if constexpr (W == 1) {
+    // Single wavefront: the registers hold the whole split.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float L = lrun[rt];
+      L += __shfl_xor(L, 16);
+      L += __shfl_xor(L, 32);
+      const int row = rt * 16 + col;
+      if (row < rows) {
+        if (splits == 1) {
+          const float inv = (mrun[rt] == -INFINITY) ? 0.f : 1.f / L;
+          float* o = out + (static_cast<size_t>(unit) * rows + row) * D;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<float4*>(o + 16 * ct + 4 * grp) =
+                make_float4(acc[rt][ct][0] * inv, acc[rt][ct][1] * inv, acc[rt][ct][2] * inv, acc[rt][ct][3] * inv);
+        } else {
+          float* wa = ws_acc + (static_cast<size_t>(wid) * rows + row) * D;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<float4*>(wa + 16 * ct + 4 * grp) =
+                make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
+          if (grp == 0) {
+            ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = mrun[rt];
+            ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = L;
+          }
+        }
+      }
+    }
+    return;
+  } else {
+  __shared__ AttnMergeLds<D, RT, W> sm;
+  // ---- merge the wavefronts of the workgroup in LDS ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float L = lrun[rt];
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
-    const int row = rt * 16 + col;
-    if (row < rows) {
-      float* wa = ws_acc + (static_cast<size_t>(wid) * rows + row) * D;
+    if (grp == 0) {
+      sm.m[wv][rt * 16 + col] = mrun[rt];
+      sm.l[wv][rt * 16 + col] = L;
+    }
+  }
+  for (int i = threadIdx.x; i < RT * 16 * D; i += blockDim.x) (&sm.acc[0][0])[i] = 0.f;
+  __syncthreads();
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        *reinterpret_cast<float4*>(wa + 16 * ct + 4 * grp) =
-            make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
-      if (grp == 0) {
-        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = mrun[rt];
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.m[w][row]);
+    const float f = (mrun[rt] == -INFINITY) ? 0.f : exp2f(mrun[rt] - M);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&sm.acc[row][16 * ct + 4 * grp + i], acc[rt][ct][i] * f);
+  }
+  __syncthreads();
+  // Workgroup result per row: M, L = sum_w l_w * 2^(m_w - M), and sm.acc.
+  // One split: write the normalised output; otherwise write the partial.
+  const bool final_out = (splits == 1);
+  for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
+    const int row = i / D, c = i - row * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.m[w][row]);
+    const float a = sm.acc[row][c];
+    if (final_out) {
+      float L = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+          L += (sm.m[w][row] == -INFINITY) ? 0.f : sm.l[w][row] * exp2f(sm.m[w][row] - M);
+      }
+      out[(static_cast<size_t>(unit) * rows + row) * D + c] = (M == -INFINITY) ? 0.f : a / L;
+    } else {
+      ws_acc[(static_cast<size_t>(wid) * rows + row) * D + c] = a;
+      if (c == 0) {
+        float L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < W; ++w)
+            L += (sm.m[w][row] == -INFINITY) ? 0.f : sm.l[w][row] * exp2f(sm.m[w][row] - M);
+        }
+        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = M;
         ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = L;
       }
     }
+  }
   }
 }
 
@@ -275,37 +364,45 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials; one wavefront per (unit, query row).
+// Log-sum-exp merge of the split partials; one wavefront per (unit, query row),
+// four per workgroup.  All partial loads of a row are independent of each other.
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ ws_acc,
-                                                          const float* __restrict__ ws_ml,
-                                                          float* __restrict__ out, int rows,
-                                                          int splits) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_acc,
+                                                           const float* __restrict__ ws_ml,
+                                                           float* __restrict__ out, int rows,
+                                                           int splits, int total) {
   constexpr int PER = D / kWave;
-  const int id = blockIdx.x;  // unit * rows + row
+  const int id = blockIdx.x * 4 + threadIdx.x / kWave;  // unit * rows + row
+  if (id >= total) return;
   const int unit = id / rows;
   const int row = id - unit * rows;
-  const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s)
-    M = fmaxf(M, ws_ml[((static_cast<size_t>(unit) * splits + s) * rows + row) * 2]);
+  const int lane = threadIdx.x & (kWave - 1);
+  // lane s < splits holds split s's (m, l)
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < splits) {
+    const size_t p = (static_cast<size_t>(unit) * splits + lane) * rows + row;
+    ms = ws_ml[p * 2];
+    ls = ws_ml[p * 2 + 1];
+  }
+  float M = ms;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float* o = out + static_cast<size_t>(id) * D;
   if (M == -INFINITY) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) o[lane + kWave * j] = 0.f;
     return;
   }
-  float L = 0.f;
+  const float w_own = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+  float L = w_own * ls;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
   float a[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) a[j] = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const size_t p = (static_cast<size_t>(unit) * splits + s) * rows + row;
-    const float ms = ws_ml[p * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - M);
-    L += w * ws_ml[p * 2 + 1];
-    const float* src = ws_acc + p * D;
+    const float w = __shfl(w_own, s);
+    const float* src = ws_acc + ((static_cast<size_t>(unit) * splits + s) * rows + row) * D;
 #pragma unroll
     for (int j = 0; j < PER; ++j) a[j] += w * src[lane + kWave * j];
   }
@@ -323,28 +420,39 @@ WsLayout ws_layout(const Ctx& c) {
   return {parts * c.s.head_dim, parts * 2};
 }
 
+template <int D, int RT, int W>
+hipError_t mfma_w(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
+                  float* out, float scale_log2, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, RT, W>), dim3(c.units * c.attn_splits), dim3(W * kWave), 0,
+                     st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s,
+                     ctx_len, ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.rows_attn,
+                     c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_split_len, scale_log2);
+  return hipGetLastError();
+}
+
 template <int D, int RT>
 hipError_t mfma_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                   const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
-                  float scale_log2, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, RT>), dim3(c.units * c.attn_splits), dim3(kWave), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s,
-                     ctx_len, ws_acc, ws_ml, c.s.kv_heads, c.rows_attn, c.rows_attn,
-                     c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_split_len, scale_log2);
-  return hipGetLastError();
+                  float* out, float scale_log2, hipStream_t st) {
+  switch (c.attn_waves) {
+    case 1: return mfma_w<D, RT, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    case 2: return mfma_w<D, RT, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    default: return mfma_w<D, RT, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+  }
 }
 
 template <int D>
 hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                   const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
-                  hipStream_t st) {
+                  float* out, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   if (c.s.dtype == OASIS_BF16) {
     switch ((c.rows_attn + 15) / 16) {
-      case 1: return mfma_t<D, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
-      case 2: return mfma_t<D, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
-      case 3: return mfma_t<D, 3>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
-      default: return mfma_t<D, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, scale_log2, st);
+      case 1: return mfma_t<D, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+      case 2: return mfma_t<D, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+      case 3: return mfma_t<D, 3>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+      default: return mfma_t<D, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
     }
   }
   const int rows = c.rows_attn;
@@ -372,16 +480,19 @@ hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int3
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                           ((w.acc_floats * sizeof(float)) + 255) / 256 * 256);
   hipError_t e = (c.s.head_dim == 128)
-      ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, st)
-      : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, st);
+      ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st)
+      : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st);
   if (e != hipSuccess) return e;
-  const int grid = c.units * c.rows_attn;
+  // The bf16 kernel writes the output itself when there is a single split.
+  if (c.s.dtype == OASIS_BF16 && c.attn_splits == 1) return hipSuccess;
+  const int total = c.units * c.rows_attn;
+  const int grid = (total + 3) / 4;
   if (c.s.head_dim == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(grid), dim3(kWave), 0, st, ws_acc, ws_ml,
-                       out, c.rows_attn, c.attn_splits);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(grid), dim3(256), 0, st, ws_acc, ws_ml,
+                       out, c.rows_attn, c.attn_splits, total);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(grid), dim3(kWave), 0, st, ws_acc, ws_ml,
-                       out, c.rows_attn, c.attn_splits);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(grid), dim3(256), 0, st, ws_acc, ws_ml,
+                       out, c.rows_attn, c.attn_splits, total);
   return hipGetLastError();
 }
 

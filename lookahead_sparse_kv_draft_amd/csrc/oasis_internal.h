@@ -24,6 +24,7 @@ struct Ctx {
   int units;        // batch * kv_heads
   int attn_splits;  // split-K factor of the attention
   int attn_split_len;  // selection entries per split
+  int attn_waves;   // wavefronts per attention workgroup (1, 2 or 4)
   int score_tpw;    // 16-block tiles per wave in the score kernel
 };
 

@@ -82,27 +82,21 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
   float* sbase = scores + static_cast<size_t>(unit) * Nmax;
   constexpr int CHUNKS = 2 * D / 8;  // 16-byte chunks per block row pair
 
-  uint4 Bc[KSTEPS], Bn[KSTEPS];
-  {
-    const int b = t0 * 16 + col;
+  // Loads are unconditional (the block index is clamped to N-1; results of
+  // blocks >= N are discarded), so the waits below only cover the older buffer.
+  auto load = [&](uint4* Bt, int tile) {
+    const int b = min(tile * 16 + col, N - 1);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      Bc[s] = (b < N) ? mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  for (int tile = t0; tile < t1; ++tile) {
-    if (tile + 1 < t1) {
-      const int b = (tile + 1) * 16 + col;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        Bn[s] = (b < N) ? mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp] : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp];
+  };
+  auto compute = [&](const uint4* Bt, int tile) {
     float best = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[rt][s]), as_bf16x8(Bc[s]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[rt][s]), as_bf16x8(Bt[s]), acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rt * 16 + 4 * grp + i;
@@ -113,8 +107,20 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(
     best = fmaxf(best, __shfl_xor(best, 32));
     const int b = tile * 16 + col;
     if (grp == 0 && b < N) sbase[b] = best;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) Bc[s] = Bn[s];
+  };
+  // Ping-pong over two tile buffers.  The prefetch index is clamped and the
+  // loop body has no branch (an odd count repeats the last tile, whose store is
+  // identical), so every wait covers only the older buffer.
+  const int ntl = t1 - t0;
+  uint4 Ba[KSTEPS], Bb[KSTEPS];
+  load(Ba, t0);
+  for (int j = 0; j < ntl; j += 2) {
+    load(Bb, t0 + min(j + 1, ntl - 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+    compute(Ba, t0 + j);
+    load(Ba, t0 + min(j + 2, ntl - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(Bb, t0 + min(j + 1, ntl - 1));
   }
 }
 

@@ -162,7 +162,13 @@ def test_diff_parity(k, cap, N, kind):
     ("f32", 64, 4, 3, 16, [1024, 250]),
     ("f32", 128, 2, 1, 8, [200, 33]),
 ])
-def test_attention_parity(dtype, d, G, D, k, ctxs):
+@pytest.mark.parametrize("waves,splits", [(None, None), (1, 1), (2, 3), (4, 2)])
+def test_attention_parity(dtype, d, G, D, k, ctxs, waves, splits, monkeypatch):
+    # launch variants: default shape, single split (output written directly),
+    # 2- and 4-wavefront workgroups merged in LDS
+    if waves is not None:
+        monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
+        monkeypatch.setenv("OASIS_ATTN_SPLITS", str(splits))
     B, H = len(ctxs), 2
     T = 1 + D
     Nmax = max((c + BLK - 1) // BLK for c in ctxs)
