@@ -64,7 +64,23 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
   const int split = wid - unit * splits;
   const int n = ctx_len[unit / H];
 
-  // This wavefront's selection entries: i0 + wv, i0 + wv + 4, ... (one per lane).
+  // (issued first: independent of the selection lookups below)
+  // Query rows as the B operand of S^T = K Q^T: lane (col, grp) holds row
+  // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.
+  uint4 Qb[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      // row clamped so the load is unconditional; padded rows are zeroed below
+      Qb[rt][s] = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(unit) * GT + min(row, rows - 1)) * D +
+                                                  8 * (4 * s + grp));
+      if (row >= rows) Qb[rt][s] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // This wavefront's selection entries: i0 + wv, i0 + wv + W, ... (one per lane).
   const int i0 = split * split_len;
   const int cnt = min(split_len, kb - i0);
   const int e = wv + W * lane;
@@ -87,20 +103,6 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
   const int dst = (my_slot >= 0 ? pos : 63) * 4;
   const int c_slot = __builtin_amdgcn_ds_permute(dst, my_slot);
   const int c_ntok = __builtin_amdgcn_ds_permute(dst, my_ntok);
-
-  // Query rows as the B operand of S^T = K Q^T: lane (col, grp) holds row
-  // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.
-  uint4 Qb[RT][KS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + col;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      Qb[rt][s] = (row < rows)
-          ? *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(unit) * GT + row) * D + 8 * (4 * s + grp))
-          : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
 
   f32x4_t acc[RT][CT];
   float mrun[RT], lrun[RT];
@@ -400,11 +402,23 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   float a[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) a[j] = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float w = __shfl(w_own, s);
-    const float* src = ws_acc + ((static_cast<size_t>(unit) * splits + s) * rows + row) * D;
+  // 8 partials at a time so their loads are in flight together (split index
+  // clamped; the weight of a clamped repeat is zero)
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float v[8][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) a[j] += w * src[lane + kWave * j];
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, splits - 1);
+      const float* src = ws_acc + ((static_cast<size_t>(unit) * splits + s) * rows + row) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = src[lane + kWave * j];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = (s0 + u < splits) ? __shfl(w_own, s0 + u) : 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) a[j] += w * v[u][j];
+    }
   }
   const float inv = 1.f / L;
 #pragma unroll

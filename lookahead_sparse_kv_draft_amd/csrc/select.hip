@@ -5,31 +5,60 @@
 // top-K blocks).  Ranking is the total order (descending score, ascending block
 // index) with -0.0 ranked as +0.0.
 //
-// One 256-thread workgroup per unit.  A 4-pass, 8-bit radix select over 32-bit
-// order keys finds the key T of the m-th best candidate; one ordered pass then
-// collects every candidate with key < T (any order) and the lowest-index
-// candidates with key == T (workgroup ballot ranks), and a bitonic sort of the
-// m (key, index) pairs in LDS produces the rank order.  Scores are read from
-// global memory (L2-resident: the score kernel just wrote them).
+// One 256-thread workgroup per unit, latency-oriented (the whole launch moves
+// well under a megabyte):
+//   1. the candidates' 32-bit order keys are staged once in LDS;
+//   2. a 3-pass radix select (11, 11, 10-bit digits) finds the key T of the
+//      m-th best candidate; each pass counts digits with LDS atomics and one
+//      wavefront scans the 2048 bins, so a pass costs two barriers;
+//   3. candidates with key < T and those equal to T are collected with LDS
+//      atomics (if very many keys equal T, an ordered ballot pass takes the
+//      lowest indices instead);
+//   4. the rank of each collected (key, index) pair is the number of smaller
+//      pairs, which places it directly in the output (rank counting instead of
+//      a sorting network); equal keys rank by index, so ties go to the lower
+//      index.
+//
+// Fast path (N <= 8192 blocks, k <= 512): one 1024-thread workgroup per unit,
+// every thread holding at most 8 keys in registers (candidate c lives in slot
+// c / 1024 of thread c % 1024).  Serial chains are what cost time in a kernel
+// this small, so each step is spread over all threads:
+//   * the radix digits are 10 bits (one histogram bin per thread) taken from the
+//     highest bit where the keys differ (block min/max), so the first pass
+//     already spreads the keys; the search stops as soon as the bin holding the
+//     m-th key is taken whole (usually after one or two passes);
+//   * winners are appended with one LDS atomic per wavefront (ballot counts);
+//     ties at the threshold, when a bin is not taken whole, are ranked in index
+//     order with a workgroup scan;
+//   * each winner's output position is the number of smaller winners, counted
+//     with unrolled broadcast reads of the winner list.
 #include "block_ops.h"
 
 namespace oasis {
 namespace {
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
+constexpr int kBins = 2048;
+
+struct TopkShared {
+  int hist[2][kBins];
+  int wave_tot[kWavesPerWG];
+  int digit, rem, n_lt, n_eq;
+};
+
+__global__ __launch_bounds__(256) void topk_wg_kernel(const float* __restrict__ scores,
                                                    const int32_t* __restrict__ ctx_len,
                                                    int32_t* __restrict__ sel, int H, int Nmax,
-                                                   int kb, int P) {
-  extern __shared__ unsigned long long buf[];  // [P]
-  __shared__ int hist[256];
-  __shared__ int wave_tot[kWavesPerWG];
-  __shared__ int sh_digit, sh_rem, sh_nlt;
+                                                   int kb, int cap_list, int keys_in_lds) {
+  extern __shared__ unsigned long long dyn[];
+  unsigned long long* list = dyn;                                 // [cap_list]
+  uint32_t* keys = reinterpret_cast<uint32_t*>(list + cap_list);  // [Nmax] if keys_in_lds
+  __shared__ TopkShared sh;
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
   const int n = ctx_len[unit / H];
   const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
   const int F0 = (N == 1) ? 1 : 2;
-  const int C = max(0, N - 2);
+  const int C = max(0, N - 2);  // candidates are blocks 1 .. N-2
   const int m = min(kb - F0, C);
   int32_t* out = sel + static_cast<size_t>(unit) * kb;
   const float* sc = scores + static_cast<size_t>(unit) * Nmax;
@@ -40,69 +69,329 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   for (int i = F0 + max(m, 0) + tid; i < kb; i += kWG) out[i] = -1;
   if (m <= 0) return;
 
+  // 1. keys of candidate c = block c + 1, loaded 8 per thread at a time so the
+  //    loads are in flight together (indices clamped: no branch around a load)
+  if (keys_in_lds) {
+    for (int c0 = 0; c0 < C; c0 += 8 * kWG) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = sc[min(c0 + u * kWG + tid, C - 1) + 1];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * kWG + tid;
+        if (c < C) keys[c] = desc_key(v[u]);
+      }
+    }
+  }
+  auto key_of = [&](int c) -> uint32_t { return keys_in_lds ? keys[c] : desc_key(sc[c + 1]); };
+  for (int i = tid; i < kBins; i += kWG) sh.hist[0][i] = 0;
+  __syncthreads();
+
+  // 2. radix select over the digits (11, 11, 10 bits from the top)
   uint32_t prefix = 0u, mask = 0u;
   int rem = m;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int shift = (p == 0) ? 21 : (p == 1) ? 10 : 0;
+    const uint32_t dmask = (p == 2) ? 0x3FFu : 0x7FFu;
+    int* hist = sh.hist[p & 1];
+    int* next = sh.hist[(p + 1) & 1];
+    for (int c = tid; c < C; c += kWG) {
+      const uint32_t key = key_of(c);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+    }
+    for (int i = tid; i < kBins; i += kWG) next[i] = 0;  // cleared for the next pass
     __syncthreads();
-    for (int b = 1 + tid; b < N - 1; b += kWG) {
-      const uint32_t key = desc_key(sc[b]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    if (tid < kWave) {
+      // lane covers bins [32 * lane, 32 * lane + 32)
+      const int lane = tid;
+      int part[32];
+      int s = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        part[j] = hist[32 * lane + j];
+        s += part[j];
+      }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int excl = incl - s;
+      if (excl < rem && incl >= rem) {  // exactly one lane: the m-th key is in its bins
+        int acc = excl;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if (!found && acc + part[j] >= rem) {
+            found = true;
+            sh.digit = 32 * lane + j;
+            sh.rem = rem - acc;
+          }
+          acc += part[j];
+        }
+      }
     }
     __syncthreads();
-    const int v = hist[tid];
-    const int incl = wg_inclusive_sum(v, wave_tot);
-    const int excl = incl - v;
-    if (excl < rem && incl >= rem) {
-      sh_digit = tid;
-      sh_rem = rem - excl;
-    }
-    __syncthreads();
-    prefix |= static_cast<uint32_t>(sh_digit) << shift;
-    mask |= 255u << shift;
-    rem = sh_rem;
-    __syncthreads();
+    prefix |= static_cast<uint32_t>(sh.digit) << shift;
+    mask |= dmask << shift;
+    rem = sh.rem;
   }
   const uint32_t Tkey = prefix;
-  const int need_eq = rem;     // candidates equal to Tkey to take, lowest index first
+  const int need_eq = rem;       // candidates equal to Tkey to take, lowest index first
   const int n_lt = m - need_eq;  // candidates strictly better than Tkey
 
-  if (tid == 0) sh_nlt = 0;
+  // 3. collect: key < T into list[0 .. n_lt), key == T after them
+  if (tid == 0) {
+    sh.n_lt = 0;
+    sh.n_eq = 0;
+  }
   __syncthreads();
-  int eq_base = 0;  // uniform across the workgroup
-  for (int base = 1; base < N - 1; base += kWG) {
-    const int b = base + tid;
-    const bool valid = b < N - 1;
-    const uint32_t key = valid ? desc_key(sc[b]) : 0xFFFFFFFFu;
-    if (valid && key < Tkey) {
-      const int pos = atomicAdd(&sh_nlt, 1);
-      if (pos < P) buf[pos] = (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(b);
-    }
-    if (eq_base < need_eq) {  // uniform branch: ranks of equal keys in index order
-      const bool eq = valid && key == Tkey;
-      int tot;
-      const int rank = wg_rank_of_flag(eq, &tot, wave_tot);
-      if (eq && eq_base + rank < need_eq)
-        buf[n_lt + eq_base + rank] =
-            (static_cast<unsigned long long>(Tkey) << 32) | static_cast<uint32_t>(b);
-      eq_base += tot;
+  const int eq_room = cap_list - n_lt;
+  for (int c = tid; c < C; c += kWG) {
+    const uint32_t key = key_of(c);
+    if (key < Tkey) {
+      const int pos = atomicAdd(&sh.n_lt, 1);
+      if (pos < n_lt)
+        list[pos] = (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(c + 1);
+    } else if (key == Tkey) {
+      const int pos = atomicAdd(&sh.n_eq, 1);
+      if (pos < eq_room)
+        list[n_lt + pos] = (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(c + 1);
     }
   }
-  for (int i = m + tid; i < P; i += kWG) buf[i] = ~0ull;
   __syncthreads();
-  wg_bitonic_sort(buf, P);
-  for (int i = tid; i < m; i += kWG) out[F0 + i] = static_cast<int32_t>(buf[i] & 0xFFFFFFFFull);
+  int total = n_lt + min(sh.n_eq, eq_room);
+  if (sh.n_eq > eq_room) {
+    // Very many ties at T: take the lowest-index ones with an ordered ballot pass.
+    int base = 0;
+    for (int c0 = 0; c0 < C && base < need_eq; c0 += kWG) {
+      const int c = c0 + tid;
+      const bool eq = c < C && key_of(c) == Tkey;
+      int tot;
+      const int rank = wg_rank_of_flag(eq, &tot, sh.wave_tot);
+      if (eq && base + rank < need_eq)
+        list[n_lt + base + rank] = (static_cast<unsigned long long>(Tkey) << 32) | static_cast<uint32_t>(c + 1);
+      base += tot;
+    }
+    total = m;
+    __syncthreads();
+  }
+
+  // 4. rank counting: the output position of each pair is the number of smaller pairs
+  for (int i = tid; i < total; i += kWG) {
+    const unsigned long long v = list[i];
+    int r = 0;
+    for (int j = 0; j < total; ++j) r += (list[j] < v) ? 1 : 0;
+    if (r < m) out[F0 + r] = static_cast<int32_t>(v & 0xFFFFFFFFull);
+  }
+}
+
+
+
+constexpr int kTkThreads = 1024;
+constexpr int kTkWaves = kTkThreads / kWave;
+constexpr int kTkMaxWin = 512;
+
+struct TopkFastShared {
+  int hist[kTkThreads];
+  unsigned long long win[kTkMaxWin];
+  uint32_t wlo[kTkWaves], whi[kTkWaves];
+  int wtot[kTkWaves];
+  int bin, before, cnt, nwin;
+};
+
+// Inclusive sum over the 1024 threads and the block total (two barriers).
+__device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == kWave - 1) wtot[w] = v;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTkWaves; ++i) {
+    const int x = wtot[i];
+    off += (i < w) ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return v + off;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ ctx_len,
+                                                         int32_t* __restrict__ sel, int H, int Nmax, int kb) {
+  __shared__ TopkFastShared sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int unit = blockIdx.x;
+  const int n = ctx_len[unit / H];
+  const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
+  const int F0 = (N == 1) ? 1 : 2;
+  const int C = max(0, N - 2);  // candidates are blocks 1 .. N-2
+  const int m = min(kb - F0, C);
+  int32_t* out = sel + static_cast<size_t>(unit) * kb;
+  const float* sc = scores + static_cast<size_t>(unit) * Nmax;
+  if (tid == 0) {
+    out[0] = 0;
+    if (N > 1) out[1] = N - 1;
+  }
+  for (int i = F0 + max(m, 0) + tid; i < kb; i += kTkThreads) out[i] = -1;
+  if (m <= 0) return;
+
+  uint32_t key[KPT];
+  float v[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + tid, C - 1) + 1];  // unconditional loads
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool valid = u * kTkThreads + tid < C;
+    key[u] = valid ? desc_key(v[u]) : 0xFFFFFFFFu;
+    if (valid) {
+      lo = min(lo, key[u]);
+      hi = max(hi, key[u]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o)));
+  }
+  if (lane == 0) {
+    sh.wlo[w] = lo;
+    sh.whi[w] = hi;
+  }
+  sh.hist[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTkWaves; ++i) {
+    lo = min(lo, sh.wlo[i]);
+    hi = max(hi, sh.whi[i]);
+  }
+  // Radix select on d = key - lo in [0, hi - lo].  The selection is every key
+  // with d < base plus `rem` keys of the current bin range.
+  const uint32_t range = hi - lo;
+  const int width = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
+  int shift = max(width - 10, 0);
+  uint32_t base = 0u;
+  int rem = m;
+  bool exact = false;
+  while (true) {
+    const uint64_t span = 1ull << (shift + 10);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const uint64_t d = static_cast<uint64_t>(key[u] - lo);
+      if (u * kTkThreads + tid < C && d >= base && d - base < span)
+        atomicAdd(&sh.hist[static_cast<int>((d - base) >> shift)], 1);
+    }
+    __syncthreads();
+    const int hv = sh.hist[tid];
+    int unused_total;
+    const int incl = tk_incl_sum(hv, sh.wtot, &unused_total);
+    const int excl = incl - hv;
+    if (excl < rem && incl >= rem) {  // exactly one thread: its bin holds the m-th key
+      sh.bin = tid;
+      sh.before = excl;
+      sh.cnt = hv;
+    }
+    sh.hist[tid] = 0;  // cleared for a next pass
+    __syncthreads();
+    rem -= sh.before;
+    base += static_cast<uint32_t>(sh.bin) << shift;
+    if (sh.cnt == rem) {  // the bin is taken whole
+      base += static_cast<uint32_t>((1ull << shift) - 1ull);
+      exact = true;
+      break;
+    }
+    if (shift == 0) break;  // a single key value: ties at the threshold remain
+    shift = max(shift - 10, 0);
+  }
+  // Collect winners: d < base (d <= base when exact) with one atomic per wavefront.
+  if (tid == 0) sh.nwin = 0;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const uint32_t d = key[u] - lo;
+    const bool win = (u * kTkThreads + tid < C) && (exact ? d <= base : d < base);
+    const uint64_t bw = __ballot(win);
+    if (bw) {
+      int wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&sh.nwin, __popcll(bw));
+      wbase = __shfl(wbase, 0);
+      if (win)
+        sh.win[wbase + __popcll(bw & below)] =
+            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
+    }
+  }
+  if (!exact) {
+    // ties at d == base: the first `rem` in index order (u, then thread)
+    int taken = 0;
+    const int n_lt = m - rem;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool eq = (u * kTkThreads + tid < C) && (key[u] - lo == base);
+      int tot;
+      const int r = tk_incl_sum(eq ? 1 : 0, sh.wtot, &tot) - (eq ? 1 : 0);
+      if (eq && taken + r < rem)
+        sh.win[n_lt + taken + r] =
+            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
+      taken += tot;
+    }
+  }
+  __syncthreads();
+  // Output position = number of smaller winners (all keys distinct by index).
+  const int nw = m;
+  if (tid < nw) {
+    const unsigned long long mine = sh.win[tid];
+    int r = 0;
+    int j = 0;
+    for (; j + 8 <= nw; j += 8) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r += (sh.win[j + t] < mine) ? 1 : 0;
+    }
+    for (; j < nw; ++j) r += (sh.win[j] < mine) ? 1 : 0;
+    out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
+  }
+}
+
+template <int KPT>
+hipError_t fast_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, hipStream_t st) {
+  hipLaunchKernelGGL((topk_fast_kernel<KPT>), dim3(c.units), dim3(kTkThreads), 0, st, scores, ctx_len, sel,
+                     c.s.kv_heads, c.s.max_blocks, c.s.budget_blocks);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st) {
+  if (c.s.budget_blocks - 2 <= kTkMaxWin) {
+    const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;  // keys per thread
+    if (kpt <= 1) return fast_t<1>(c, scores, ctx_len, sel, st);
+    if (kpt <= 2) return fast_t<2>(c, scores, ctx_len, sel, st);
+    if (kpt <= 4) return fast_t<4>(c, scores, ctx_len, sel, st);
+    if (kpt <= 8) return fast_t<8>(c, scores, ctx_len, sel, st);
+  }
   int P = 1;
   while (P < c.s.budget_blocks) P <<= 1;
-  const size_t lds = static_cast<size_t>(P) * sizeof(unsigned long long);
-  hipLaunchKernelGGL(topk_kernel, dim3(c.units), dim3(kWG), lds, st, scores, ctx_len, sel,
-                     c.s.kv_heads, c.s.max_blocks, c.s.budget_blocks, P);
+  const int cap_list = 2 * P;  // the m winners plus room for ties at the threshold
+  // Stage the keys in LDS when everything fits in 60 KiB; otherwise read scores each pass.
+  const size_t fixed = sizeof(int) * (2 * 2048 + 8) + static_cast<size_t>(cap_list) * 8;
+  const int keys_in_lds = (fixed + static_cast<size_t>(c.s.max_blocks) * 4 <= 60 * 1024) ? 1 : 0;
+  const size_t lds = static_cast<size_t>(cap_list) * sizeof(unsigned long long) +
+                     (keys_in_lds ? static_cast<size_t>(c.s.max_blocks) * sizeof(uint32_t) : 0);
+  hipLaunchKernelGGL(topk_wg_kernel, dim3(c.units), dim3(kWG), lds, st, scores, ctx_len, sel,
+                     c.s.kv_heads, c.s.max_blocks, c.s.budget_blocks, cap_list, keys_in_lds);
   return hipGetLastError();
 }
 

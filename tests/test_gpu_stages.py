@@ -70,7 +70,10 @@ def test_score_parity(dtype, d, G, D, Nmax, ctxs):
     (16, [1024, 16 * 16, 16 * 17, 5], "ties"),
     (16, [1024, 999, 33, 16 * 18], "const"),
     (2, [1024, 16, 32, 48], "normal"),
-    (128, [131072, 131072 - 5, 16 * 129, 16 * 8191], "normal"),
+    (128, [131072, 131072 - 5, 16 * 129, 16 * 8191], "normal"),   # N > 4096: workgroup kernel
+    (128, [16 * 4096, 16 * 4000 + 9, 16 * 200, 16 * 130], "ties"),  # largest single-wave case
+    (512, [16 * 3000, 16 * 600, 16 * 513, 77], "normal"),          # k > 258: workgroup kernel
+    (256, [16 * 3000, 16 * 600, 16 * 257, 16 * 200], "ties"),
 ])
 def test_topk_parity(k, ctxs, kind):
     B, H = len(ctxs), 3
@@ -112,6 +115,7 @@ def _random_state(rng, N, k, n_res, kind):
     (128, 32, 2048, "normal"), (128, 16, 2048, "ties"), (128, 0, 2048, "normal"),
     (128, 128, 500, "ties"), (16, 4, 64, "normal"), (16, 1, 20, "const"), (8, 8, 8, "ties"),
     (2, 2, 1, "normal"), (128, 24, 528, "normal"), (128, 32, 8192, "ties"),
+    (512, 64, 3000, "ties"), (1024, 200, 4000, "normal"), (300, 300, 700, "const"),
 ])
 def test_diff_parity(k, cap, N, kind):
     B, H = 3, 4
