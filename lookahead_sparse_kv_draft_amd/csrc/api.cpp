@@ -48,6 +48,13 @@ int env_int(const char* name, int dflt) {
   return atoi(v);
 }
 
+// [16][d] token-major -> [d][16] channel-major.
+template <typename T>
+void transpose_block(const T* src, T* dst, int d) {
+  for (int t = 0; t < oasis::kBlock; ++t)
+    for (int ch = 0; ch < d; ++ch) dst[ch * oasis::kBlock + t] = src[t * d + ch];
+}
+
 #define CHECK_HANDLE(h) \
   if ((h) == nullptr) return fail(OASIS_EINVAL, "%s: null handle", __func__)
 #define CHECK_PTR(p) \
@@ -180,9 +187,10 @@ int oasis_pack_pages(oasis_handle h, const void* k, const void* v, const int32_t
     if (v != nullptr) {
       const char* src = static_cast<const char*>(v) + static_cast<size_t>(i) * oasis::kBlock * row_bytes;
       char* vt = pg + oasis::kBlock * row_bytes;  // V^T [d][16]
-      for (int t = 0; t < oasis::kBlock; ++t)
-        for (int ch = 0; ch < d; ++ch)
-          memcpy(vt + (static_cast<size_t>(ch) * oasis::kBlock + t) * eb, src + (static_cast<size_t>(t) * d + ch) * eb, eb);
+      if (eb == 2)
+        transpose_block(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(vt), d);
+      else
+        transpose_block(reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(vt), d);
     }
   }
   return ok();

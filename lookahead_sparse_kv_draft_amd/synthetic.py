@@ -145,10 +145,14 @@ class SyntheticRun:
             rt.wait_transfers()
         self._record(t)
 
-    def run(self, steps: int | None = None, transfer: bool = True):
+    def run(self, steps: int | None = None, transfer: bool = True, log=None):
+        """Prologue plus `steps` decode steps; `log(msg)` receives progress lines."""
         self.prologue()
-        for t in range(self.cfg.steps if steps is None else steps):
+        total = self.cfg.steps if steps is None else steps
+        for t in range(total):
             self.step(t, transfer=transfer)
+            if log is not None and (t % 8 == 7 or t == total - 1):
+                log(f"{self.cfg.name}: step {t + 1}/{total} done")
 
     # ----------------------------------------------------------------- records
     def _record_out(self, l: int, t: int):

@@ -17,9 +17,10 @@ pytestmark = pytest.mark.gpu
 
 def _run_and_compare(cfg, units, steps=None, layers=None, max_diverged_frac=0.25):
     cfg = cfg if steps is None else cfg.with_(steps=steps)
+    print(f"{cfg.name}: filling host tier and metadata", flush=True)
     run = SyntheticRun(cfg, layers=layers, record_units=units)
     try:
-        run.run()
+        run.run(log=lambda msg: print(msg, flush=True))
         results = []
         for (l, u) in units:
             st = CC.compare_unit(cfg, l, u, run.records[(l, u)], CC.oracle_unit(cfg, l, u))
@@ -62,3 +63,24 @@ def test_chain_llama8b_32k_full_size_sampled():
     cfg = CONFIGS["llama8b_32k"]
     units = [(0, u) for u in (0, 9, 22, 35, 47, 63)]
     _run_and_compare(cfg, units, steps=12)
+
+
+@pytest.mark.timeout(1100)
+def test_chain_qwen32b_32k_full_size_sampled():
+    # 8 layers, 64 query / 8 KV heads (40 attention rows, 32 scoring rows), drifting set
+    cfg = CONFIGS["qwen32b_32k"]
+    _run_and_compare(cfg, [(0, 0), (1, 37), (3, 64), (5, 101), (7, 127)])
+
+
+@pytest.mark.timeout(1100)
+def test_chain_qwen8b_reason_full_size_sampled():
+    # 64 requests, 256 appended tokens (the newest block turns over 16 times)
+    cfg = CONFIGS["qwen8b_reason"]
+    _run_and_compare(cfg, [(0, 0), (0, 77), (0, 200), (0, 333), (0, 511)])
+
+
+@pytest.mark.timeout(1100)
+def test_chain_llama8b_128k_full_size_sampled():
+    # 8192 blocks per head, 8 layers, 16 GiB host tier
+    cfg = CONFIGS["llama8b_128k"]
+    _run_and_compare(cfg, [(0, 0), (2, 13), (4, 22), (7, 31)])
