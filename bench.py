@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--mode", choices=["graph", "overlap", "eager"], default="eager",
+                   help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
+                        "second stream beside the attention, captured likewise; eager: plain launches")
     return p.parse_args()
 
 
@@ -55,8 +58,7 @@ def algorithmic_bytes(cfg, attended_blocks: int):
     attn = (attended_blocks * 2 * 16 * d * e + cfg.batch * cfg.q_heads * cfg.T * d * (e + 4)
             + units * cfg.k * 8)
     return {"lookahead_score": score, "sparse_paged_decode_attn": attn,
-            "topk_select": units * N * 4 + units * cfg.k * 4,
-            "resident_diff_cap_evict": units * cfg.k * 4 * 4 + units * cfg.fetch_cap * 12}
+            "select_and_diff": units * N * 4 + units * cfg.k * 4 * 5 + units * cfg.fetch_cap * 12}
 
 
 def attn_flops(cfg, attended_blocks: int):
@@ -121,7 +123,7 @@ def main():
     print(f"# config {cfg.name}: state {state_bytes / 2**20:.0f} MiB per replica, {replicas} replicas",
           file=sys.stderr, flush=True)
 
-    run = SyntheticRun(cfg, replicas=replicas)
+    run = SyntheticRun(cfg, replicas=replicas, overlap=args.mode == "overlap")
     rt = run.rt
     run.prologue()
     for l in range(run.L):
@@ -130,33 +132,54 @@ def main():
     torch.cuda.synchronize()
     print("# prologue done", file=sys.stderr, flush=True)
 
-    stream = torch.cuda.current_stream()
-    names = ["sparse_paged_decode_attn", "lookahead_score", "topk_select", "resident_diff_cap_evict"]
+    names = ["sparse_paged_decode_attn", "lookahead_score", "select_and_diff"]
+    ps = rt.pstream
+    ev_attn = [torch.cuda.Event() for _ in range(run.L)]
+    ev_sel = [torch.cuda.Event() for _ in range(run.L)]
 
-    def one_step(i, ev=None):
+    def chain_step(i, cs, first):
+        """One decode step over all layers with the real dependencies: the score
+        runs beside the attention (it needs only the step's drafts), the fused
+        selection/diff waits for the attention (it rewrites the selection and maps
+        the attention reads), and the next step's attention of the layer waits
+        for that selection."""
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            q = run.q[l, t + 1]
+            st = rt.state[l][rep]
+            if not first:
+                cs.wait_event(ev_sel[l])
+            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr, cs)
+            ev_attn[l].record(cs)
+            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, ps)
+            ps.wait_event(ev_attn[l])
+            L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                    st.evict, ps)
+            ev_sel[l].record(ps)
+
+    def sequential_step(i, cs, ev=None):
         rep = i % replicas
         t = i % cfg.steps
         for l in range(run.L):
             q = run.q[l, t + 1]
             st = rt.state[l][rep]
             if ev is not None:
-                ev[0].record(stream)
-            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr)
+                ev[0].record(cs)
+            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr, cs)
             if ev is not None:
-                ev[1].record(stream)
-            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores)
+                ev[1].record(cs)
+            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, cs)
             if ev is not None:
-                ev[2].record(stream)
-            L.oasis_topk_select(rt.h, st.scores, rt.ctx_len, st.sel)
+                ev[2].record(cs)
+            L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                    st.evict, cs)
             if ev is not None:
-                ev[3].record(stream)
-            L.oasis_resident_diff_cap_evict(rt.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                            st.evict)
-            if ev is not None:
-                ev[4].record(stream)
+                ev[3].record(cs)
 
+    cs0 = torch.cuda.current_stream()
     for i in range(args.warmup):
-        one_step(i)
+        sequential_step(i, cs0)
     torch.cuda.synchronize()
 
     def attended():
@@ -171,37 +194,56 @@ def main():
 
     attended_before = attended()
 
-    # timed region 1: the headline loop (no per-kernel events)
+    # Headline: G steps captured once as a HIP graph and replayed (or plain launches).
+    G = 2 * replicas
+    cs = torch.cuda.current_stream()
+    graph = None
+    if args.mode != "eager":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            gs = torch.cuda.current_stream()
+            if args.mode == "overlap":
+                ps.wait_stream(gs)
+                for j in range(G):
+                    chain_step(j, gs, first=(j == 0))
+                gs.wait_stream(ps)
+            else:
+                for j in range(G):
+                    sequential_step(j, gs)
+        for _ in range(max(1, args.warmup // G)):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    def eager_steps(n):
+        for j in range(n):
+            if args.mode == "overlap":
+                ps.wait_stream(cs)
+                chain_step(j, cs, first=(j == 0))
+                cs.wait_stream(ps)
+            else:
+                sequential_step(j, cs)
+
+    # timed region 1 (headline): K steps = K // G graph replays + an eager remainder
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(args.warmup + i)
+    if graph is not None:
+        for _ in range(args.steps // G):
+            graph.replay()
+        eager_steps(args.steps % G)
+    else:
+        eager_steps(args.steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # timed region 2: the same loop with HIP events between the kernels (per-kernel durations)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps * run.L)]
+    # timed region 2: eager launches on one stream with HIP events between the
+    # kernels (per-kernel durations for the roofline)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(args.steps):
-        rep = i % replicas
-        t = i % cfg.steps
-        for l in range(run.L):
-            ev = evs[i * run.L + l]
-            q = run.q[l, t + 1]
-            st = rt.state[l][rep]
-            ev[0].record(stream)
-            L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr)
-            ev[1].record(stream)
-            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores)
-            ev[2].record(stream)
-            L.oasis_topk_select(rt.h, st.scores, rt.ctx_len, st.sel)
-            ev[3].record(stream)
-            L.oasis_resident_diff_cap_evict(rt.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                            st.evict)
-            ev[4].record(stream)
+        sequential_step(i, cs0, evs[i])
     torch.cuda.synchronize()
-    elapsed_ev = time.perf_counter() - t1
+    elapsed_seq = time.perf_counter() - t1
     per = {n: [] for n in names}
     for ev in evs:
         for j, n in enumerate(names):
@@ -248,7 +290,10 @@ def main():
                    "attended_blocks": [attended_before, attended_after]},
         "roofline": roof,
         "kernels": kern,
-        "ms_per_step_with_events": elapsed_ev / args.steps * 1e3,
+        "ms_per_step_sequential_with_events": elapsed_seq / args.steps * 1e3,
+        "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
+                      "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
+                      "eager": "plain launches on one stream"}[args.mode],
         "hbm_bytes_per_step": sum(ab[n] for n in names) * run.L,
     }
     if not args.no_cpu_baseline:

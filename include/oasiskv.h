@@ -177,6 +177,17 @@ int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const floa
                                   int32_t* n_fetch, int32_t* evict, void* stream);
 
 /*
+ * oasis_topk_select followed by oasis_resident_diff_cap_evict on the same
+ * arguments, with identical results, in one launch when the shape allows it
+ * (max_blocks <= 8192 and budget_blocks <= 514; otherwise the two kernels run
+ * back to back).  Saves a launch and a round trip of the selection through
+ * global memory on every decode step.
+ */
+int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                          int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
+                          int32_t* n_fetch, int32_t* evict, void* stream);
+
+/*
  * Fetch issue ([EXPL] Figure 8: the transfer lands in HBM before the layer's
  * attention at the next step).  Reads a host-visible copy of fetch / n_fetch
  * (the caller must have synchronised its device-to-host copy) and enqueues one

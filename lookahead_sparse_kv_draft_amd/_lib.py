@@ -56,6 +56,7 @@ SIGNATURES = {
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "oasis_resident_diff_cap_evict": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_select_and_diff": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
@@ -195,6 +196,12 @@ def oasis_topk_select(h, scores, ctx_len, sel, stream=None):
 def oasis_resident_diff_cap_evict(h, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict,
                                   stream=None):
     _call("oasis_resident_diff_cap_evict", h, _ptr(sel), _ptr(scores), _ptr(block_to_slot),
+          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _stream(stream))
+
+
+def oasis_select_and_diff(h, scores, ctx_len, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                          stream=None):
+    _call("oasis_select_and_diff", h, _ptr(scores), _ptr(ctx_len), _ptr(sel), _ptr(block_to_slot),
           _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _stream(stream))
 
 

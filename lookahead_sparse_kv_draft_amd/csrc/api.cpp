@@ -302,6 +302,31 @@ int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const floa
                     "oasis_resident_diff_cap_evict");
 }
 
+int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                          int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch, int32_t* n_fetch,
+                          int32_t* evict, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(n_fetch);
+  if (h->c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (oasis::select_diff_fused_available(h->c))
+    return hip_status(oasis::launch_select_diff(h->c, scores, ctx_len, sel, block_to_slot, slot_to_block, fetch,
+                                                n_fetch, evict, st),
+                      "oasis_select_and_diff");
+  hipError_t e = oasis::launch_topk(h->c, scores, ctx_len, sel, st);
+  if (e == hipSuccess)
+    e = oasis::launch_diff(h->c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, st);
+  return hip_status(e, "oasis_select_and_diff");
+}
+
 int oasis_fetch_issue(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch_host,
                       const int32_t* n_fetch_host, void* stream) {
   CHECK_HANDLE(h);

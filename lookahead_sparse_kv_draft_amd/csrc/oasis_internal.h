@@ -39,6 +39,10 @@ hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int
                         float* scores, hipStream_t st);
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st);
+bool select_diff_fused_available(const Ctx& c);
+hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                              int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
+                              hipStream_t st);
 hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, int32_t* b2s,
                        int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                        hipStream_t st);

@@ -33,6 +33,7 @@
 //   * each winner's output position is the number of smaller winners, counted
 //     with unrolled broadcast reads of the winner list.
 #include "block_ops.h"
+#include "diff_body.h"
 
 namespace oasis {
 namespace {
@@ -224,11 +225,12 @@ __device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
   return v + off;
 }
 
+// The selection of one unit by a 1024-thread workgroup; also written, in rank
+// order and -1 padded, to the LDS array selL when it is not null.
 template <int KPT>
-__global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict__ scores,
-                                                         const int32_t* __restrict__ ctx_len,
-                                                         int32_t* __restrict__ sel, int H, int Nmax, int kb) {
-  __shared__ TopkFastShared sh;
+__device__ inline void topk_fast_body(const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
+                                      int32_t* __restrict__ sel, int H, int Nmax, int kb, int32_t* selL,
+                                      TopkFastShared& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
@@ -243,9 +245,16 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
   if (tid == 0) {
     out[0] = 0;
     if (N > 1) out[1] = N - 1;
+    if (selL != nullptr) {
+      selL[0] = 0;
+      if (N > 1) selL[1] = N - 1;
+    }
   }
-  for (int i = F0 + max(m, 0) + tid; i < kb; i += kTkThreads) out[i] = -1;
-  if (m <= 0) return;
+  for (int i = F0 + max(m, 0) + tid; i < kb; i += kTkThreads) {
+    out[i] = -1;
+    if (selL != nullptr) selL[i] = -1;
+  }
+  if (m <= 0) return;  // uniform: every thread leaves together
 
   uint32_t key[KPT];
   float v[KPT];
@@ -361,7 +370,39 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
     }
     for (; j < nw; ++j) r += (sh.win[j] < mine) ? 1 : 0;
     out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
+    if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
   }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict__ scores,
+                                                         const int32_t* __restrict__ ctx_len,
+                                                         int32_t* __restrict__ sel, int H, int Nmax, int kb) {
+  __shared__ TopkFastShared sh;
+  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, nullptr, sh);
+}
+
+// Fused selection + diff: the diff's slot-map and score loads are issued before
+// the selection runs, and the selection reaches the diff through LDS.
+template <int KPT>
+__global__ __launch_bounds__(1024) void select_diff_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
+    int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
+    int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int H, int Nmax, int kb, int cap) {
+  extern __shared__ unsigned long long smem_u64[];
+  int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
+  __shared__ TopkFastShared sh;
+  __shared__ DiffShared dsh;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
+  const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
+  const bool sok = sb >= 0 && sb < Nmax;
+  const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
+  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, selL, sh);
+  __syncthreads();
+  diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
+            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, smem_u64, dsh);
 }
 
 template <int KPT>
@@ -371,7 +412,31 @@ hipError_t fast_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int
   return hipGetLastError();
 }
 
+template <int KPT>
+hipError_t select_diff_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
+                         int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, hipStream_t st) {
+  const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
+  const size_t lds = diff_lds_bytes(kb, c.s.max_blocks, cap) + static_cast<size_t>(kb) * 4;
+  hipLaunchKernelGGL((select_diff_kernel<KPT>), dim3(c.units), dim3(kTkThreads), lds, st, scores, ctx_len, sel,
+                     b2s, s2b, fetch, n_fetch, evict, c.s.kv_heads, c.s.max_blocks, kb, cap);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool select_diff_fused_available(const Ctx& c) {
+  return c.s.budget_blocks - 2 <= kTkMaxWin && c.s.max_blocks <= 8 * kTkThreads;
+}
+
+hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                              int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
+                              hipStream_t st) {
+  const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
+  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
+  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
+  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
+  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
+}
 
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st) {

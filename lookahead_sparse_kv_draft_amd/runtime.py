@@ -92,7 +92,14 @@ class LayerState:
         self.host_tier = host_tier
         self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
         self.n_fetch_host = torch.empty(u, dtype=torch.int32, pin_memory=True)
-        self.fetch_done = None  # event recorded on the side stream after the last transfer
+        # events: transfer landed (side stream), attention done reading the maps
+        # (compute stream), selection/diff done (predict stream)
+        self.fetch_done = torch.cuda.Event()
+        self.fetch_wait_compute = False  # attention must wait for the last transfer
+        self.fetch_wait_predict = False  # the token append (pool page rows) must too
+        self.attn_done = torch.cuda.Event()
+        self.select_done = torch.cuda.Event()
+        self.select_pending = False
 
     def copy_from(self, other: "LayerState"):
         for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict"):
@@ -103,8 +110,13 @@ class DecodeRuntime:
     """Buffers and step chain for `layers` layers of one shape on one GPU."""
 
     def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
-                 host_tier: bool = True):
+                 host_tier: bool = True, fused_select: bool = True, overlap: bool = False):
+        """overlap: run scoring / selection on a second stream so that they overlap
+        the attention of the same step (and of other layers); the selection waits
+        only for the attention that reads the maps it rewrites."""
         self.shape = shape
+        self.fused_select = fused_select
+        self.overlap = overlap
         self.device = torch.device(device)
         self.h = shape.handle()
         s = shape
@@ -125,6 +137,7 @@ class DecodeRuntime:
         off = (-self.ws.data_ptr()) % 256
         self.ws_ptr = self.ws.data_ptr() + off
         self.side = torch.cuda.Stream(device=self.device)
+        self.pstream = torch.cuda.Stream(device=self.device) if overlap else None
 
     def close(self):
         if self.h:
@@ -179,12 +192,13 @@ class DecodeRuntime:
             return
         pb = L.oasis_page_bytes(self.h)
         tier = self.host_tier_view(layer).view(-1, pb)
+        torch.cuda.synchronize()  # after this layer's attention and every earlier selection
         staged = tier[torch.from_numpy(ids)].to(self.device)
         ids_dev = torch.from_numpy(ids.astype(np.int32)).to(self.device)
         for st in self.state[layer]:
             L.oasis_block_meta_build(self.h, staged, ids_dev, len(ids), self.ctx_len, st.meta, st.pool,
                                      st.b2s)
-        torch.cuda.current_stream().synchronize()
+        torch.cuda.synchronize()
 
     def prologue(self, layer: int, q: torch.Tensor, initial_slots):
         """Score the step -1 drafts, select S_0, install the initial residency
@@ -222,16 +236,27 @@ class DecodeRuntime:
         for st in self.state[layer]:
             L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
                                             st.evict)
-        self.transfer(layer)
+        self.transfer(layer, stream=torch.cuda.current_stream())
 
     # ------------------------------------------------------------ per-step chain
+    def _pred(self):
+        return self.pstream if self.overlap else torch.cuda.current_stream()
+
     def attention(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None):
+        """Sparse attention of step t on the current stream, after the last transfer
+        and the last selection of this layer."""
         st = self.state[layer][replica]
-        if st.fetch_done is not None:
-            torch.cuda.current_stream().wait_event(st.fetch_done)
-            st.fetch_done = None
+        cs = torch.cuda.current_stream()
+        if st.fetch_wait_compute:
+            cs.wait_event(st.fetch_done)
+            st.fetch_wait_compute = False
+        if st.select_pending:
+            cs.wait_event(st.select_done)
+            st.select_pending = False
         L.oasis_sparse_paged_decode_attn(self.h, q, st.pool, st.sel, st.b2s, self.ctx_len,
-                                         self.out if out is None else out, self.ws_ptr)
+                                         self.out if out is None else out, self.ws_ptr, cs)
+        if self.overlap:
+            st.attn_done.record(cs)
 
     def append(self, layer: int, k_new_dev, v_new_dev, k_new_host=None, v_new_host=None,
                replica: int = 0):
@@ -240,10 +265,17 @@ class DecodeRuntime:
         Every layer of a step appends at the same positions; the scoring that
         follows sees the grown context (ctx_scoring) while later layers' attention
         of the same step still sees the old one; end_step() makes it current.
+        The append may run beside this step's attention: it writes the metadata,
+        the other context buffer and page row n % 16, none of which the attention
+        reads (it sees tokens < n).
         """
         st = self.state[layer][replica]
+        ps = self._pred()
+        if st.fetch_wait_predict:
+            ps.wait_event(st.fetch_done)
+            st.fetch_wait_predict = False
         L.oasis_block_meta_update(self.h, k_new_dev, v_new_dev, self.ctx[self.ctx_cur],
-                                  self.ctx[1 - self.ctx_cur], st.meta, st.pool, st.b2s)
+                                  self.ctx[1 - self.ctx_cur], st.meta, st.pool, st.b2s, ps)
         if k_new_host is not None and replica == 0:
             L.oasis_host_tier_append(self.h, np.ascontiguousarray(k_new_host),
                                      np.ascontiguousarray(v_new_host), self.ctx_host, st.host_tier)
@@ -260,34 +292,58 @@ class DecodeRuntime:
             self._appended = False
 
     def predict_select(self, layer: int, q: torch.Tensor, replica: int = 0):
+        """Score the drafts of step t, select S_{t+1}, diff against the resident set.
+
+        With overlap the scoring runs beside the attention of step t; the
+        selection/diff waits for that attention (it rewrites the selection and
+        maps the attention reads)."""
         st = self.state[layer][replica]
         ctx = self.ctx_scoring
-        L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores)
-        L.oasis_topk_select(self.h, st.scores, ctx, st.sel)
-        L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                        st.evict)
+        ps = self._pred()
+        L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores, ps)
+        if self.overlap:
+            ps.wait_event(st.attn_done)
+        if self.fused_select:
+            L.oasis_select_and_diff(self.h, st.scores, ctx, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                    st.evict, ps)
+        else:
+            L.oasis_topk_select(self.h, st.scores, ctx, st.sel, ps)
+            L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                            st.evict, ps)
+        if self.overlap:
+            st.select_done.record(ps)
+            st.select_pending = True
 
-    def transfer(self, layer: int, replica: int = 0):
-        """Copy the fetch list to the host, then issue the page copies on the side stream."""
+    def transfer(self, layer: int, replica: int = 0, stream=None):
+        """Copy the fetch list to the host (after the diff, on its stream), then issue
+        the page copies on the side stream; later attention and appends of this
+        layer wait for them."""
         st = self.state[layer][replica]
-        cur = torch.cuda.current_stream()
-        st.fetch_host.copy_(st.fetch, non_blocking=True)
-        st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)
+        ps = self._pred() if stream is None else stream
+        with torch.cuda.stream(ps):
+            st.fetch_host.copy_(st.fetch, non_blocking=True)
+            st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)
         ready = torch.cuda.Event()
-        ready.record(cur)
+        ready.record(ps)
         ready.synchronize()
         self.side.wait_event(ready)
         L.oasis_fetch_issue(self.h, st.host_tier, st.pool, st.fetch_host, st.n_fetch_host, self.side)
-        done = torch.cuda.Event()
-        done.record(self.side)
-        st.fetch_done = done
+        st.fetch_done.record(self.side)
+        st.fetch_wait_compute = True
+        st.fetch_wait_predict = True
 
     def wait_transfers(self):
+        """Make the current stream wait for every pending transfer and selection."""
+        cs = torch.cuda.current_stream()
         for layer in self.state:
             for st in layer:
-                if st.fetch_done is not None:
-                    torch.cuda.current_stream().wait_event(st.fetch_done)
-                    st.fetch_done = None
+                if st.fetch_wait_compute or st.fetch_wait_predict:
+                    cs.wait_event(st.fetch_done)
+                    st.fetch_wait_compute = False
+                    st.fetch_wait_predict = False
+                if st.select_pending:
+                    cs.wait_event(st.select_done)
+                    st.select_pending = False
 
     # ------------------------------------------------------------ inspection
     def pool_pages(self, layer: int, replica: int = 0) -> torch.Tensor:

@@ -42,11 +42,11 @@ class SyntheticRun:
     """The decode chain of one workload configuration on cuda:0."""
 
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
-                 record_units=None, device: str = "cuda"):
+                 record_units=None, device: str = "cuda", overlap: bool = True):
         self.cfg = cfg
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
-        self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas)
+        self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap)
         self.record_units = record_units  # list of (layer, unit) to record, or None
         self.records = {}
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim

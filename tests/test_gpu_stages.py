@@ -342,3 +342,59 @@ def test_fetch_issue_copies_pages():
         for s in set(range(8)) - used:
             assert not pool[u, s].any()
     rt.close()
+
+
+@pytest.mark.parametrize("k,cap,ctxs,kind", [
+    (128, 32, [32768, 16 * 700 + 3, 16 * 130, 100], "normal"),
+    (128, 16, [32768, 32768, 16 * 129, 16 * 2], "ties"),
+    (16, 4, [1024, 999, 16 * 17, 16], "const"),
+    (128, 0, [16 * 528, 16 * 600, 16 * 300, 16 * 129], "normal"),
+    (512, 100, [16 * 3000, 16 * 600, 16 * 513, 77], "ties"),       # largest fused budget
+    (128, 32, [131072 + 16 * 10, 16 * 900, 16 * 130, 16 * 50], "normal"),  # N > 8192: two launches
+])
+def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
+    B, H = len(ctxs), 3
+    Nmax = max((c + BLK - 1) // BLK for c in ctxs)
+    units = B * H
+    sh = U.make_shape(batch=B, kv_heads=H, max_blocks=Nmax, budget_blocks=k, fetch_cap=cap)
+    h = sh.handle()
+    rng = _rng(7)
+    sc = np.stack([random_scores(rng, Nmax, kind) for _ in range(units)])
+    b2s0 = np.full((units, Nmax), -1, dtype=np.int32)
+    s2b0 = np.full((units, k), -1, dtype=np.int32)
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        n_res = [0, k // 2, k, int(rng.integers(0, k + 1))][u % 4]
+        res = rng.choice(N, size=min(n_res, N), replace=False)
+        slots = rng.choice(k, size=len(res), replace=False)
+        s2b0[u, slots] = res
+        b2s0[u, res] = slots
+    cw = max(cap, 1)
+    outs = []
+    for fused in (False, True):
+        sel = torch.full((units, k), -7, dtype=torch.int32, device="cuda")
+        b2s, s2b = U.i32(b2s0), U.i32(s2b0)
+        fetch = torch.full((units, cw, 2), -9, dtype=torch.int32, device="cuda")
+        nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+        ev = torch.full((units, cw), -9, dtype=torch.int32, device="cuda")
+        sc_d, ctx_d = torch.from_numpy(sc).cuda(), U.i32(ctxs)
+        if fused:
+            L.oasis_select_and_diff(h, sc_d, ctx_d, sel, b2s, s2b, fetch, nf, ev)
+        else:
+            L.oasis_topk_select(h, sc_d, ctx_d, sel)
+            L.oasis_resident_diff_cap_evict(h, sel, sc_d, b2s, s2b, fetch, nf, ev)
+        torch.cuda.synchronize()
+        outs.append([x.cpu().numpy() for x in (sel, b2s, s2b, fetch, nf, ev)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    sel, b2s, s2b, fetch, nf, ev = outs[1]
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        ref_sel = O.topk_select(sc[u].astype(np.float64), N, k)
+        assert list(sel[u]) == ref_sel, u
+        ref = O.resident_diff_cap_evict(ref_sel, sc[u].astype(np.float64), b2s0[u], s2b0[u], cap)
+        assert nf[u] == len(ref.fetch)
+        assert [tuple(p) for p in fetch[u][: nf[u]]] == ref.fetch, u
+        assert list(ev[u][: len(ref.evict)]) == ref.evict
+        assert np.array_equal(b2s[u], ref.block_to_slot) and np.array_equal(s2b[u], ref.slot_to_block)
+    L.oasis_destroy(h)
