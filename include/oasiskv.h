@@ -88,7 +88,7 @@ size_t oasis_page_bytes(oasis_handle h);       /* one page: 2*16*d elements */
 size_t oasis_meta_bytes(oasis_handle h);       /* B*H*max_blocks*2*d elements */
 size_t oasis_pool_bytes(oasis_handle h);       /* B*H*budget_blocks pages */
 size_t oasis_host_tier_bytes(oasis_handle h);  /* B*H*max_blocks pages */
-/* Split-K workspace of oasis_sparse_paged_decode_attn (device, 256-byte aligned). */
+/* Split partials of oasis_sparse_paged_decode_attn (device, 256-byte aligned). */
 size_t oasis_workspace_bytes(oasis_handle h);
 
 /*
@@ -204,8 +204,10 @@ int oasis_fetch_issue(oasis_handle h, const void* host_tier, void* pool, const i
  * row (g, t) and the token set J of the blocks of sel that are resident
  * (block_to_slot >= 0), tokens below ctx_len:
  *   out[r][h*G+g][t] = softmax_j(q . K[j] / sqrt(d)) . V[j]   (0 if J is empty)
- * float32 accumulation, split over the selection with a log-sum-exp merge.
- * out: [B][H*G][T][d] float32.  workspace: oasis_workspace_bytes() bytes.
+ * float32 accumulation, split over the selection with a log-sum-exp merge (a
+ * second kernel combines the splits).  out: [B][H*G][T][d] float32.
+ * workspace: oasis_workspace_bytes() bytes, not shared by calls that may run at
+ * the same time.
  */
 int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* pool,
                                    const int32_t* sel, const int32_t* block_to_slot,

@@ -111,19 +111,33 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.page_elems = static_cast<size_t>(2) * oasis::kBlock * s.head_dim;
   c.units = static_cast<int>(units);
 
-  // Attention split-K: W-wavefront workgroups per (unit, split), about 1024
-  // wavefronts in total, at least 2 selection entries per wavefront and at most
-  // one per lane.
-  int waves = env_int("OASIS_ATTN_WAVES", 1);
-  if (waves != 1 && waves != 2 && waves != 4) waves = 1;
+  // Attention: workgroups of W wavefronts, each wavefront streaming a run of
+  // consecutive selection entries (at most 64) through a ring of PF page
+  // buffers; a workgroup covers W runs (one split).  By default 2 wavefronts,
+  // a 2-page ring and about one wavefront per SIMD of the 256 compute units, so
+  // every workgroup is resident at once.
+  const int row_tiles = (rows_attn + 15) / 16;
+  const int max_waves = (row_tiles <= 2) ? 4 : 2;  // LDS of the wavefront merge
+  int waves = env_int("OASIS_ATTN_WAVES", 0);
+  if (waves != 1 && waves != 2 && waves != 4) waves = 2;
+  waves = std::min(waves, max_waves);
+  const int kbud = s.budget_blocks;
   int splits = env_int("OASIS_ATTN_SPLITS", 0);
   if (splits <= 0) splits = (1024 + c.units * waves - 1) / (c.units * waves);
-  splits = std::max(1, std::min(splits, (s.budget_blocks + 2 * waves - 1) / (2 * waves)));
-  int split_len = (s.budget_blocks + splits - 1) / splits;
-  if (split_len > waves * oasis::kWave) split_len = waves * oasis::kWave;
+  const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
+  const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
+  splits = std::max(min_splits, std::min(splits, max_splits));
+  const int run = (kbud + splits * waves - 1) / (splits * waves);
+  splits = (kbud + run * waves - 1) / (run * waves);  // no empty split
+  int pf = env_int("OASIS_ATTN_PF", 0);
+  const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
+  if (pf != 2 && pf != 4 && pf != 8) pf = 2;  // measured: a shallow ring keeps the math beside the loads
+  pf = std::min(pf, max_pf);
   c.attn_waves = waves;
-  c.attn_split_len = split_len;
-  c.attn_splits = (s.budget_blocks + split_len - 1) / split_len;
+  c.attn_pf = pf;
+  c.attn_run = run;
+  c.attn_split_len = waves * run;
+  c.attn_splits = splits;
 
   // Score kernel: 16-block tiles per wavefront, ~2048 wavefronts per launch.
   int tpw = env_int("OASIS_SCORE_TPW", 0);

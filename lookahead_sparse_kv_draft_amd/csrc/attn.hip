@@ -2,27 +2,28 @@
 // explainer, Figure 7 right: the verify query and the draft queries attend
 // together over the sparse KV working set held in HBM).
 //
-// Work unit: one (request, KV head) and one split of its selection list; the
-// splits are merged by a log-sum-exp combine kernel.  All T*G query rows of the
-// unit (verify + drafts for each grouped query head) ride in the same
-// wavefront, so every KV page is read from HBM once per step.
+// Work unit: one (request, KV head) and one split of its selection list.  All
+// T*G query rows of the unit (verify + drafts for each grouped query head) ride
+// in the same wavefront, so every KV page is read from HBM once per step.
 //
 // bf16 path, per 16-token block and per 16-row query tile, on the MFMA units:
 //   S^T[tok][row] = K[tok][:] . Q[row][:]   v_mfma_f32_16x16x32_bf16, A = the K
 //       page rows (16 contiguous bytes per lane), B = the query rows (registers);
 //       the output leaves lane (col, grp) with tokens 4grp..4grp+3 of row col;
 //   online softmax in the log2 domain, in registers: block max over the 4
-//       tokens of the lane and two cross-lane exchanges; probabilities rounded
-//       to bf16 (the running sum adds the rounded values, so weights and
-//       normaliser agree);
+//       tokens of the lane and two cross-lane exchanges, a reference max that
+//       moves only on large increases; probabilities rounded to bf16 (the running
+//       sum adds the rounded values, so weights and normaliser agree);
 //   O^T[ch][row] += V^T[ch][tok] . P^T[tok][row]  v_mfma_f32_16x16x16_bf16, A =
 //       the page's channel-major V^T (8 contiguous bytes per lane), B = the
 //       lane's own 4 probabilities: P never leaves registers.
 // The page layout (K token-major, V channel-major) is what makes both products
-// read contiguous lane-sized pieces without an LDS transpose.  The next block's
-// page loads are issued before the current block's math.
+// read contiguous lane-sized pieces without an LDS transpose.  A wavefront
+// requests all of its pages before it processes the first.
 //
 // f32 path: VALU, query rows and logits in LDS, accumulators in registers.
+// Both paths leave one partial per split; a log-sum-exp combine kernel merges
+// them.
 #include "oasis_internal.h"
 
 namespace oasis {
@@ -35,28 +36,31 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
 
-// LDS of the in-workgroup merge: per wave m and l for every row, plus the summed
-// accumulator [rows][D].
-template <int D, int RT, int W>
-struct AttnMergeLds {
-  float m[W][RT * 16];
-  float l[W][RT * 16];
-  float acc[RT * 16][D];
-};
+constexpr float kLazyRescale = 8.f;
 
-// W wavefronts per (unit, split) workgroup; W > 1 merges them in LDS.
-template <int D, int RT, int W>
+// W wavefronts per workgroup; each wavefront takes a run of `run` consecutive
+// entries of its unit's selection and streams their pages through a ring of PF
+// page buffers in registers (PF pages always in flight, every wait exact); a
+// workgroup covers W runs (one split).  The wavefronts merge in LDS; with one
+// split the workgroup writes the output, otherwise its partial (unnormalised
+// accumulator, row max, row sum) for the combine kernel.
+template <int D, int RT, int W, int PF>
 __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s,
     const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    float* __restrict__ out, int H, int GT, int rows, int Nmax, int kb, int splits, int split_len,
-    float scale_log2) {
+    float* __restrict__ out, int H, int rows, int Nmax, int kb,
+    int splits, int run, float scale_log2) {
   constexpr int KS = D / 32;  // QK k-steps of 32 channels
   constexpr int CT = D / 16;  // PV channel tiles
   constexpr int PAGE = 2 * kBlock * D;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
+  constexpr int NSLICE = (W > 1) ? W / 2 : 1;
+  __shared__ float sm_m[W][RT * 16];
+  __shared__ float sm_l[W][RT * 16];
+  __shared__ float4 sm_slice[NSLICE][RT][CT][kWave];  // wavefront accumulators in register layout
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int wid = blockIdx.x;  // unit * splits + split
@@ -64,9 +68,9 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
   const int split = wid - unit * splits;
   const int n = ctx_len[unit / H];
 
-  // (issued first: independent of the selection lookups below)
   // Query rows as the B operand of S^T = K Q^T: lane (col, grp) holds row
-  // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.
+  // rt*16+col, channels 8*(4s+grp) .. +7 for k-step s.  Issued first: they do
+  // not depend on the selection lookups below.
   uint4 Qb[RT][KS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -74,19 +78,18 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       // row clamped so the load is unconditional; padded rows are zeroed below
-      Qb[rt][s] = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(unit) * GT + min(row, rows - 1)) * D +
+      Qb[rt][s] = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(unit) * rows + min(row, rows - 1)) * D +
                                                   8 * (4 * s + grp));
       if (row >= rows) Qb[rt][s] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
-  // This wavefront's selection entries: i0 + wv, i0 + wv + W, ... (one per lane).
-  const int i0 = split * split_len;
-  const int cnt = min(split_len, kb - i0);
-  const int e = wv + W * lane;
+  // This wavefront's entries e0 .. e0+run-1 (run <= 64; lane j looks up e0 + j).
+  const int e0 = (split * W + wv) * run;
+  const int cnt = min(run, kb - e0);
   int my_slot = -1, my_ntok = 0;
-  if (e < cnt) {
-    const int b = sel[static_cast<size_t>(unit) * kb + i0 + e];
+  if (lane < cnt) {
+    const int b = sel[static_cast<size_t>(unit) * kb + e0 + lane];
     if (b >= 0 && b < Nmax) {
       const int s = b2s[static_cast<size_t>(unit) * Nmax + b];
       const int nt = min(kBlock, n - kBlock * b);
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
       }
     }
   }
-  // Compact the valid entries into lanes 0 .. nb-1 (forward lane permute).
+  // Compact the attended entries into lanes 0 .. nb-1 (forward lane permute).
   const uint64_t valid = __ballot(my_slot >= 0);
   const int nb = __popcll(valid);
   const int pos = __popcll(valid & ((1ull << lane) - 1ull));
@@ -119,16 +122,16 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
     uint4 k[KS];
     uint2 v[CT];
   };
-  // Issue the loads of compacted entry j (every call loads: no branch around the
-  // loads, so each wait below covers only the older buffer).
+  // The page base is wavefront-uniform (scalar registers); the lane offsets are
+  // the same for every page.
+  const uint16_t* kl = ubase + col * D + 8 * grp;
+  const uint16_t* vl = ubase + kBlock * D + col * kBlock + 4 * grp;
   auto load = [&](Page& pg, int j) {
-    const uint16_t* p = ubase + static_cast<size_t>(__shfl(c_slot, j)) * PAGE;
+    const size_t off = static_cast<size_t>(__builtin_amdgcn_readfirstlane(__shfl(c_slot, j))) * PAGE;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      pg.k[s] = *reinterpret_cast<const uint4*>(p + col * D + 8 * (4 * s + grp));
+    for (int s = 0; s < KS; ++s) pg.k[s] = *reinterpret_cast<const uint4*>(kl + off + 32 * s);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-      pg.v[ct] = *reinterpret_cast<const uint2*>(p + kBlock * D + (16 * ct + col) * kBlock + 4 * grp);
+    for (int ct = 0; ct < CT; ++ct) pg.v[ct] = *reinterpret_cast<const uint2*>(vl + off + 16 * kBlock * ct);
   };
   auto process = [&](const Page& pg, int ntok) {
 #pragma unroll
@@ -146,135 +149,142 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
       }
       mb = fmaxf(mb, __shfl_xor(mb, 16));
       mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float mnew = fmaxf(mrun[rt], mb);
-      const float alpha = exp2f(mrun[rt] - mnew);
-      mrun[rt] = mnew;
+      // The reference max moves only when a row's block max exceeds it by more
+      // than kLazyRescale (log2 units; the first block always moves it), so the
+      // accumulators are rescaled rarely; probabilities stay below 2^kLazyRescale.
+      if (__ballot(mb > mrun[rt] + kLazyRescale) != 0ull) {
+        const float mnew = fmaxf(mrun[rt], mb);
+        const float alpha = exp2f(mrun[rt] - mnew);
+        mrun[rt] = mnew;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] *= alpha;
+      }
       uint16_t pb[4];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pb[i] = f32_to_bf16(exp2f(x[i] - mnew));
+        pb[i] = f32_to_bf16(exp2f(x[i] - mrun[rt]));
         psum += bf16_to_f32(pb[i]);
       }
-      lrun[rt] = lrun[rt] * alpha + psum;
+      lrun[rt] += psum;
       const uint2 pw = make_uint2(static_cast<uint32_t>(pb[0]) | (static_cast<uint32_t>(pb[1]) << 16),
                                   static_cast<uint32_t>(pb[2]) | (static_cast<uint32_t>(pb[3]) << 16));
       const s16x4_t P = as_s16x4(pw);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        acc[rt][ct] *= alpha;
+      for (int ct = 0; ct < CT; ++ct)
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_s16x4(pg.v[ct]), P, acc[rt][ct], 0, 0, 0);
-      }
     }
   };
 
-  // Ping-pong over two page buffers: the next block's loads are in flight while
-  // the current block is processed.  Prefetch indices are clamped and an odd
-  // count is padded with a zero-token pass (a no-op for the online softmax once
-  // a real block has been seen), so the loop body has no branch and every wait
-  // covers only the older buffer.
+  // Ring of PF page buffers over the nb attended entries, padded to a multiple
+  // of PF: the first PF loads, then groups of PF pages where each processed
+  // buffer is refilled with the page PF entries ahead, then the last group.
+  // Every load is unconditional (indices clamped: only a padded last group
+  // repeats the last page), so each wait covers exactly the older buffers; the
+  // processing issues no loads, so skipping padded entries keeps them exact.
   if (nb > 0) {
-    Page pa, pbuf;
-    load(pa, 0);
-    for (int j = 0; j < nb; j += 2) {
-      load(pbuf, min(j + 1, nb - 1));
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-      process(pa, __shfl(c_ntok, j));
-      load(pa, min(j + 2, nb - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      process(pbuf, (j + 1 < nb) ? __shfl(c_ntok, j + 1) : 0);
-    }
-  }
-
-  if constexpr (W == 1) {
-    // Single wavefront: the registers hold the whole split.
+    Page pg[PF];
+    const int npad = (nb + PF - 1) / PF * PF;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float L = lrun[rt];
-      L += __shfl_xor(L, 16);
-      L += __shfl_xor(L, 32);
-      const int row = rt * 16 + col;
-      if (row < rows) {
-        if (splits == 1) {
-          const float inv = (mrun[rt] == -INFINITY) ? 0.f : 1.f / L;
-          float* o = out + (static_cast<size_t>(unit) * rows + row) * D;
+    for (int j = 0; j < PF; ++j) load(pg[j], min(j, nb - 1));
+    __builtin_amdgcn_sched_barrier(0);  // every page request goes out before the math
+    for (int j0 = 0; j0 < npad - PF; j0 += PF) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<float4*>(o + 16 * ct + 4 * grp) =
-                make_float4(acc[rt][ct][0] * inv, acc[rt][ct][1] * inv, acc[rt][ct][2] * inv, acc[rt][ct][3] * inv);
-        } else {
-          float* wa = ws_acc + (static_cast<size_t>(wid) * rows + row) * D;
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<float4*>(wa + 16 * ct + 4 * grp) =
-                make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
-          if (grp == 0) {
-            ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = mrun[rt];
-            ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = L;
-          }
-        }
+      for (int j = 0; j < PF; ++j) {
+        process(pg[j], __builtin_amdgcn_readfirstlane(__shfl(c_ntok, j0 + j)));
+        load(pg[j], min(j0 + j + PF, nb - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    return;
-  } else {
-  __shared__ AttnMergeLds<D, RT, W> sm;
-  // ---- merge the wavefronts of the workgroup in LDS ----
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (npad - PF + j < nb) process(pg[j], __builtin_amdgcn_readfirstlane(__shfl(c_ntok, npad - PF + j)));
+  }
+
+  // ---- merge the wavefronts: a fixed-order tree in LDS (deterministic) ----
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float L = lrun[rt];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
+    float Lw = lrun[rt];
+    Lw += __shfl_xor(Lw, 16);
+    Lw += __shfl_xor(Lw, 32);
     if (grp == 0) {
-      sm.m[wv][rt * 16 + col] = mrun[rt];
-      sm.l[wv][rt * 16 + col] = L;
+      sm_m[wv][rt * 16 + col] = mrun[rt];
+      sm_l[wv][rt * 16 + col] = Lw;
     }
   }
-  for (int i = threadIdx.x; i < RT * 16 * D; i += blockDim.x) (&sm.acc[0][0])[i] = 0.f;
   __syncthreads();
+  // workgroup row statistics for this lane's rows: M = max_w m_w,
+  // L = sum_w l_w 2^(m_w - M); every wavefront rescales to M
+  float Lwg[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = rt * 16 + col;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.m[w][row]);
-    const float f = (mrun[rt] == -INFINITY) ? 0.f : exp2f(mrun[rt] - M);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][row]);
+    float Lr = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int w = 0; w < W; ++w) Lr += (sm_m[w][row] == -INFINITY) ? 0.f : sm_l[w][row] * exp2f(sm_m[w][row] - M);
+    Lwg[rt] = Lr;
+    if (W > 1) {
+      const float f = (mrun[rt] == -INFINITY) ? 0.f : exp2f(mrun[rt] - M);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&sm.acc[row][16 * ct + 4 * grp + i], acc[rt][ct][i] * f);
+      for (int ct = 0; ct < CT; ++ct) acc[rt][ct] *= f;
+    }
+    mrun[rt] = M;
   }
-  __syncthreads();
-  // Workgroup result per row: M, L = sum_w l_w * 2^(m_w - M), and sm.acc.
-  // One split: write the normalised output; otherwise write the partial.
-  const bool final_out = (splits == 1);
-  for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
-    const int row = i / D, c = i - row * D;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, sm.m[w][row]);
-    const float a = sm.acc[row][c];
-    if (final_out) {
-      float L = 0.f;
-      if (M != -INFINITY) {
+  for (int half = W / 2; half >= 1; half >>= 1) {
+    if (wv >= half && wv < 2 * half) {
 #pragma unroll
-        for (int w = 0; w < W; ++w)
-          L += (sm.m[w][row] == -INFINITY) ? 0.f : sm.l[w][row] * exp2f(sm.m[w][row] - M);
-      }
-      out[(static_cast<size_t>(unit) * rows + row) * D + c] = (M == -INFINITY) ? 0.f : a / L;
-    } else {
-      ws_acc[(static_cast<size_t>(wid) * rows + row) * D + c] = a;
-      if (c == 0) {
-        float L = 0.f;
-        if (M != -INFINITY) {
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int w = 0; w < W; ++w)
-            L += (sm.m[w][row] == -INFINITY) ? 0.f : sm.l[w][row] * exp2f(sm.m[w][row] - M);
+        for (int ct = 0; ct < CT; ++ct)
+          sm_slice[wv - half][rt][ct][lane] = make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
+    }
+    __syncthreads();
+    if (wv < half) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float4 o = sm_slice[wv][rt][ct][lane];
+          acc[rt][ct] += f32x4_t{o.x, o.y, o.z, o.w};
         }
-        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2] = M;
-        ws_ml[(static_cast<size_t>(wid) * rows + row) * 2 + 1] = L;
+    }
+    if (half > 1) __syncthreads();
+  }
+  // wavefront 0 now holds the workgroup's accumulator
+
+  if (wv != 0) return;
+  if (splits == 1) {
+    float* ou = out + static_cast<size_t>(unit) * rows * D;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = rt * 16 + col;
+      if (row < rows) {
+        const float inv = (Lwg[rt] > 0.f) ? 1.f / Lwg[rt] : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          *reinterpret_cast<float4*>(ou + static_cast<size_t>(row) * D + 16 * ct + 4 * grp) =
+              make_float4(acc[rt][ct][0] * inv, acc[rt][ct][1] * inv, acc[rt][ct][2] * inv, acc[rt][ct][3] * inv);
       }
     }
+    return;
   }
+  float* wa = ws_acc + static_cast<size_t>(wid) * rows * D;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+    if (row < rows) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        *reinterpret_cast<float4*>(wa + static_cast<size_t>(row) * D + 16 * ct + 4 * grp) =
+            make_float4(acc[rt][ct][0], acc[rt][ct][1], acc[rt][ct][2], acc[rt][ct][3]);
+      if (grp == 0)
+        *reinterpret_cast<float2*>(ws_ml + (static_cast<size_t>(wid) * rows + row) * 2) = make_float2(mrun[rt], Lwg[rt]);
+    }
   }
 }
 
@@ -366,100 +376,105 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials; one wavefront per (unit, query row),
-// four per workgroup.  All partial loads of a row are independent of each other.
-template <int D>
+// Log-sum-exp merge of the split partials: one wavefront per (unit, query row),
+// four per workgroup.  Every split's partial row and (max, sum) are loaded in one
+// batch (split index clamped to the last split, whose repeats get weight 0),
+// then merged: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <int D, int SMAX>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml,
                                                            float* __restrict__ out, int rows,
                                                            int splits, int total) {
-  constexpr int PER = D / kWave;
+  constexpr int PER = D / kWave;  // output channels per lane (1 or 2)
   const int id = blockIdx.x * 4 + threadIdx.x / kWave;  // unit * rows + row
-  if (id >= total) return;
+  if (id >= total) return;  // wavefront-uniform
   const int unit = id / rows;
   const int row = id - unit * rows;
   const int lane = threadIdx.x & (kWave - 1);
-  // lane s < splits holds split s's (m, l)
-  float ms = -INFINITY, ls = 0.f;
-  if (lane < splits) {
-    const size_t p = (static_cast<size_t>(unit) * splits + lane) * rows + row;
-    ms = ws_ml[p * 2];
-    ls = ws_ml[p * 2 + 1];
+  float v[SMAX][PER];
+  float2 ml[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    const size_t p = (static_cast<size_t>(unit) * splits + min(s, splits - 1)) * rows + row;
+    ml[s] = *reinterpret_cast<const float2*>(ws_ml + p * 2);
+    if constexpr (PER == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(ws_acc + p * D + 2 * lane);
+      v[s][0] = t.x;
+      v[s][1] = t.y;
+    } else {
+      v[s][0] = ws_acc[p * D + lane];
+    }
   }
-  float M = ms;
+  float M = -INFINITY;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float* o = out + static_cast<size_t>(id) * D;
-  if (M == -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) o[lane + kWave * j] = 0.f;
-    return;
-  }
-  const float w_own = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-  float L = w_own * ls;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-  float a[PER];
+  for (int s = 0; s < SMAX; ++s) M = fmaxf(M, ml[s].x);  // repeats do not change the max
+  float L = 0.f, a[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) a[j] = 0.f;
-  // 8 partials at a time so their loads are in flight together (split index
-  // clamped; the weight of a clamped repeat is zero)
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    float v[8][PER];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, splits - 1);
-      const float* src = ws_acc + ((static_cast<size_t>(unit) * splits + s) * rows + row) * D;
+  for (int s = 0; s < SMAX; ++s) {
+    const float w = (s >= splits || ml[s].x == -INFINITY) ? 0.f : exp2f(ml[s].x - M);
+    L += w * ml[s].y;
 #pragma unroll
-      for (int j = 0; j < PER; ++j) v[u][j] = src[lane + kWave * j];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = (s0 + u < splits) ? __shfl(w_own, s0 + u) : 0.f;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) a[j] += w * v[u][j];
-    }
+    for (int j = 0; j < PER; ++j) a[j] += w * v[s][j];
   }
-  const float inv = 1.f / L;
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  float* o = out + static_cast<size_t>(id) * D + PER * lane;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) o[lane + kWave * j] = a[j] * inv;
+  for (int j = 0; j < PER; ++j) o[j] = a[j] * inv;
 }
 
 struct WsLayout {
-  size_t acc_floats, ml_floats;
+  size_t acc_floats, ml_floats, acc_bytes, ml_bytes;
 };
 
+// workspace: partial accumulators [units][splits][rows][D], then (max, sum)
+// [units][splits][rows][2] (each region 256-byte aligned).
 WsLayout ws_layout(const Ctx& c) {
   const size_t parts = static_cast<size_t>(c.units) * c.attn_splits * c.rows_attn;
-  return {parts * c.s.head_dim, parts * 2};
+  WsLayout w{parts * c.s.head_dim, parts * 2, 0, 0};
+  w.acc_bytes = (w.acc_floats * sizeof(float) + 255) / 256 * 256;
+  w.ml_bytes = (w.ml_floats * sizeof(float) + 255) / 256 * 256;
+  return w;
 }
 
-template <int D, int RT, int W>
-hipError_t mfma_w(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
-                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
-                  float* out, float scale_log2, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, RT, W>), dim3(c.units * c.attn_splits), dim3(W * kWave), 0,
-                     st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s,
-                     ctx_len, ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.rows_attn,
-                     c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_split_len, scale_log2);
+template <int D, int RT, int W, int PF>
+hipError_t mfma_wp(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                   const int32_t* ctx_len, float* ws_acc, float* ws_ml, float* out,
+                   float scale_log2, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, RT, W, PF>), dim3(c.units * c.attn_splits), dim3(W * kWave), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s, ctx_len,
+                     ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.s.max_blocks,
+                     c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2);
   return hipGetLastError();
 }
 
-template <int D, int RT>
-hipError_t mfma_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
-                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
-                  float* out, float scale_log2, hipStream_t st) {
-  switch (c.attn_waves) {
-    case 1: return mfma_w<D, RT, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-    case 2: return mfma_w<D, RT, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-    default: return mfma_w<D, RT, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+template <int D, int RT, int W>
+hipError_t mfma_w(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                  const int32_t* ctx_len, float* ws_acc, float* ws_ml, float* out,
+                  float scale_log2, hipStream_t st) {
+  switch (c.attn_pf) {
+    case 2: return mfma_wp<D, RT, W, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    case 4: return mfma_wp<D, RT, W, 4>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    default: return mfma_wp<D, RT, W, 8>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
   }
 }
 
+template <int D, int RT>
+hipError_t mfma_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                  const int32_t* ctx_len, float* ws_acc, float* ws_ml, float* out,
+                  float scale_log2, hipStream_t st) {
+  if (c.attn_waves == 1) return mfma_w<D, RT, 1>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+  // at most 2 wavefronts for 3 or 4 row tiles (LDS of the wavefront merge)
+  if (RT >= 3 || c.attn_waves == 2)
+    return mfma_w<D, RT, 2>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+  return mfma_w<D, RT, (RT >= 3 ? 2 : 4)>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+}
+
 template <int D>
-hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
-                  const int32_t* b2s, const int32_t* ctx_len, float* ws_acc, float* ws_ml,
-                  float* out, hipStream_t st) {
+hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                  const int32_t* ctx_len, float* ws_acc, float* ws_ml, float* out,
+                  hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   if (c.s.dtype == OASIS_BF16) {
     switch ((c.rows_attn + 15) / 16) {
@@ -478,12 +493,31 @@ hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* 
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t combine_t(const Ctx& c, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+  const int total = c.units * c.rows_attn;
+  const int grid = (total + 3) / 4;
+  const int S = c.attn_splits;
+#define OASIS_COMBINE(SM)                                                                           \
+  hipLaunchKernelGGL((attn_combine_kernel<D, SM>), dim3(grid), dim3(256), 0, st, ws_acc, ws_ml, out, \
+                     c.rows_attn, S, total)
+  if (S <= 4)
+    OASIS_COMBINE(4);
+  else if (S <= 8)
+    OASIS_COMBINE(8);
+  else if (S <= 16)
+    OASIS_COMBINE(16);
+  else
+    OASIS_COMBINE(32);
+#undef OASIS_COMBINE
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t attn_workspace_bytes(const Ctx& c) {
   const WsLayout w = ws_layout(c);
-  const size_t acc_bytes = ((w.acc_floats * sizeof(float)) + 255) / 256 * 256;
-  return acc_bytes + w.ml_floats * sizeof(float);
+  return w.acc_bytes + w.ml_bytes;
 }
 
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
@@ -491,23 +525,15 @@ hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int3
                        hipStream_t st) {
   const WsLayout w = ws_layout(c);
   float* ws_acc = static_cast<float*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                          ((w.acc_floats * sizeof(float)) + 255) / 256 * 256);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + w.acc_bytes);
   hipError_t e = (c.s.head_dim == 128)
       ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st)
       : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st);
   if (e != hipSuccess) return e;
   // The bf16 kernel writes the output itself when there is a single split.
   if (c.s.dtype == OASIS_BF16 && c.attn_splits == 1) return hipSuccess;
-  const int total = c.units * c.rows_attn;
-  const int grid = (total + 3) / 4;
-  if (c.s.head_dim == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(grid), dim3(256), 0, st, ws_acc, ws_ml,
-                       out, c.rows_attn, c.attn_splits, total);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(grid), dim3(256), 0, st, ws_acc, ws_ml,
-                       out, c.rows_attn, c.attn_splits, total);
-  return hipGetLastError();
+  return (c.s.head_dim == 128) ? combine_t<128>(c, ws_acc, ws_ml, out, st)
+                               : combine_t<64>(c, ws_acc, ws_ml, out, st);
 }
 
 }  // namespace oasis

@@ -13,6 +13,7 @@ constexpr int kBlock = 16;     // tokens per KV block
 constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kMaxRows = 64;   // query rows per unit handled by the kernels (4 MFMA row tiles)
 constexpr int kMaxBudget = 1024;
+constexpr int kAttnMaxSplits = 32;  // attention splits per unit (merge statistics kept in LDS)
 
 struct Ctx {
   oasis_shape s;
@@ -23,8 +24,10 @@ struct Ctx {
   size_t page_elems;  // 2 * 16 * d
   int units;        // batch * kv_heads
   int attn_splits;  // split-K factor of the attention
-  int attn_split_len;  // selection entries per split
+  int attn_split_len;  // selection entries per split (attn_waves * attn_run)
+  int attn_run;     // selection entries per attention wavefront (<= 64)
   int attn_waves;   // wavefronts per attention workgroup (1, 2 or 4)
+  int attn_pf;      // pages in flight per attention wavefront (2, 4 or 8)
   int score_tpw;    // 16-block tiles per wave in the score kernel
 };
 

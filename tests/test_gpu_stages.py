@@ -166,12 +166,16 @@ def test_diff_parity(k, cap, N, kind):
     ("f32", 64, 4, 3, 16, [1024, 250]),
     ("f32", 128, 2, 1, 8, [200, 33]),
 ])
-@pytest.mark.parametrize("waves,splits", [(None, None), (1, 1), (2, 3), (4, 2)])
-def test_attention_parity(dtype, d, G, D, k, ctxs, waves, splits, monkeypatch):
-    # launch variants: default shape, single split (output written directly),
-    # 2- and 4-wavefront workgroups merged in LDS
+@pytest.mark.parametrize("waves,pf,splits", [(None, None, None), (1, 2, 1), (2, 4, 3), (4, 2, 0), (4, 8, 2),
+                                             (1, 8, 5)])
+def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatch):
+    # launch variants: default shape; 1-, 2- and 4-wavefront workgroups merged in
+    # LDS; rings of 2, 4 or 8 pages over runs that are shorter than, equal to or
+    # (padded) multiples of the ring; one split or several, merged by the last
+    # workgroup of each unit
     if waves is not None:
         monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
+        monkeypatch.setenv("OASIS_ATTN_PF", str(pf))
         monkeypatch.setenv("OASIS_ATTN_SPLITS", str(splits))
     B, H = len(ctxs), 2
     T = 1 + D
@@ -216,10 +220,16 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, splits, monkeypatch):
     L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nfe, torch.cuda.current_stream())
     torch.cuda.synchronize()
     q_d = U.to_dev(dtype, q)
-    rt.out.fill_(float("nan"))
-    rt.attention(0, q_d)
-    torch.cuda.synchronize()
-    got = rt.out.cpu().numpy().astype(np.float64)
+    # three calls in a row: the split arrival counters must be back at zero
+    # after every call, so every call gives the same output
+    outs = []
+    for _ in range(3):
+        rt.out.fill_(float("nan"))
+        rt.attention(0, q_d)
+        torch.cuda.synchronize()
+        outs.append(rt.out.cpu().numpy().astype(np.float64))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    got = outs[0]
     for u in range(units):
         r, hh = divmod(u, H)
         A = O.attended_blocks(sel[u], b2s[u])
@@ -240,6 +250,69 @@ def test_attention_empty_selection_gives_zero():
     rt.attention(0, q)  # sel all -1
     torch.cuda.synchronize()
     assert torch.all(rt.out == 0)
+    rt.close()
+
+
+@pytest.mark.parametrize("waves,pf", [(None, None), (1, 8)])
+def test_attention_growing_logits(waves, pf, monkeypatch):
+    """Logits that grow along the selection order by far more than the lazy
+    rescaling threshold, so the running reference max moves many times."""
+    if waves is not None:
+        monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
+        monkeypatch.setenv("OASIS_ATTN_PF", str(pf))
+    B, H, G, D, d, k = 2, 2, 4, 4, 128, 64
+    ctxs = [2048, 1500]
+    T = 1 + D
+    Nmax = 128
+    sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k,
+                      n_draft=D, fetch_cap=k, dtype="bf16")
+    rt = DecodeRuntime(sh)
+    rng = _rng(9)
+    units = B * H
+    q = U.elem_round("bf16", rng.standard_normal((B, H * G, T, d)).astype(np.float32))
+    K = np.empty((units, Nmax * BLK, d), dtype=np.float32)
+    V = U.elem_round("bf16", rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    sel = np.full((units, k), -1, dtype=np.int32)
+    s2b = np.full((units, k), -1, dtype=np.int32)
+    b2s = np.full((units, Nmax), -1, dtype=np.int32)
+    fetch = np.full((units, k, 2), -1, dtype=np.int32)
+    nfe = np.zeros(units, dtype=np.int32)
+    for u in range(units):
+        r, hh = divmod(u, H)
+        N = (ctxs[r] + BLK - 1) // BLK
+        chosen = rng.choice(N, size=k, replace=False)
+        sel[u] = chosen
+        # keys aligned with the mean query of the unit, scaled up along the rank
+        qm = q[r, hh * G:(hh + 1) * G].reshape(-1, d).mean(axis=0)
+        qm /= np.linalg.norm(qm)
+        base = rng.standard_normal((Nmax * BLK, d)).astype(np.float32)
+        for i, b in enumerate(chosen):
+            base[b * BLK:(b + 1) * BLK] += qm * (3.0 * i)
+        K[u] = U.elem_round("bf16", base)
+        for i, b in enumerate(chosen):
+            s2b[u, i] = b
+            b2s[u, b] = i
+            fetch[u, i] = (b, i)
+        nfe[u] = k
+        rt.pack_unit(0, u, U.to_elem_np("bf16", K[u]), U.to_elem_np("bf16", V[u]))
+    rt.set_ctx(ctxs)
+    st = rt.state[0][0]
+    st.sel.copy_(torch.from_numpy(sel))
+    st.b2s.copy_(torch.from_numpy(b2s))
+    st.s2b.copy_(torch.from_numpy(s2b))
+    L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nfe, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    rt.out.fill_(float("nan"))
+    rt.attention(0, U.to_dev("bf16", q))
+    torch.cuda.synchronize()
+    got = rt.out.cpu().numpy().astype(np.float64)
+    for u in range(units):
+        r, hh = divmod(u, H)
+        A = O.attended_blocks(sel[u], b2s[u])
+        ref = O.sparse_attention(q[r, hh * G:(hh + 1) * G].astype(np.float64), K[u].astype(np.float64),
+                                 V[u].astype(np.float64), A, ctxs[r])
+        ma, rl = U.attn_errors(got[r, hh * G:(hh + 1) * G], ref)
+        assert ma <= U.ATTN_MAX_ABS and rl <= U.ATTN_REL_L2, (u, ma, rl)
     rt.close()
 
 
