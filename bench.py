@@ -30,6 +30,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
+CALIB_ELEMS = 2**28  # float32: 1 GiB
+CSRC = os.path.join(ROOT, "lookahead_sparse_kv_draft_amd", "csrc")
+# source files of each op's kernels (a traffic measurement is valid while they are unchanged)
+OP_SOURCES = {"sparse_paged_decode_attn": ["attn.hip"], "lookahead_score": ["score.hip"],
+              "select_and_diff": ["select.hip", "diff_body.h", "block_ops.h"]}
+OP_KERNELS = {"sparse_paged_decode_attn": ["attn_mfma_kernel", "attn_combine_kernel"],
+              "lookahead_score": ["score_mfma_kernel"], "select_and_diff": ["select_diff_kernel"]}
 
 
 def parse():
@@ -42,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                        "`bench.py --calib-copy` into a traffic file and exit")
     p.add_argument("--mode", choices=["graph", "overlap", "eager"], default="eager",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
                         "second stream beside the attention, captured likewise; eager: plain launches")
@@ -99,8 +109,83 @@ def cpu_baseline(cfg, target_s: float):
                       f"prologue + {steps} steps each, fp64 numpy, {t_total:.1f} s"}
 
 
+def op_source_hash(op: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in OP_SOURCES[op]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(path: str):
+    """Mean counter value (KiB per dispatch) per kernel from a rocprofv3
+    counter_collection.csv: keyed by base name for the library's kernels and by
+    full name for elementwise kernels (the calibration add)."""
+    import csv
+    import re
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        full = r["Kernel_Name"]
+        m = re.search(r"(\w+)(<[^(]*>)?\(", full)
+        name = m.group(1) if m else full
+        key = full if "elementwise" in name else name
+        acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, out: str, cmdline: str):
+    """HBM bytes per launch of each op: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what it reads for the calibration add (1 GiB in,
+    1 GiB out)."""
+    fe, wr = _counter_means(fetch_csv), _counter_means(write_csv)
+    gib_kib = CALIB_ELEMS * 4 / 1024
+    calib = [k for k in wr if "elementwise" in k and abs(wr[k] - gib_kib) < 0.05 * gib_kib and k in fe]
+    if not calib:
+        raise SystemExit("no calibration kernel in the counter files (run bench.py with --calib-copy)")
+    c = calib[0]
+    f_fac = gib_kib / fe[c]
+    w_fac = gib_kib / wr[c]
+    short = c.split("(")[0][:90]
+    lines = [f"# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, llama8b_32k",
+             "# counters: cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'oasis|elementwise' "
+             "--output-format csv -d <dir> -o f -- python <repo>/bench.py --steps 8 --warmup 2 --no-cpu-baseline "
+             "--calib-copy  (then the same with WRITE_SIZE and -o w)",
+             f"# summary: {cmdline}",
+             f"calibration {short.replace(' ', '')} fetch_kib {fe[c]:.1f} write_kib {wr[c]:.1f} "
+             f"expected_kib {gib_kib:.1f} fetch_factor {f_fac:.4f} write_factor {w_fac:.4f}"]
+    for op, kernels in OP_KERNELS.items():
+        tot = 0.0
+        for k in kernels:
+            f_kib, w_kib = fe.get(k, 0.0), wr.get(k, 0.0)
+            b = (f_kib * f_fac + w_kib * w_fac) * 1024
+            tot += b
+            lines.append(f"kernel {k} op {op} fetch_kib {f_kib:.1f} write_kib {w_kib:.1f} hbm_bytes {b:.0f}")
+        lines.append(f"op {op} source {op_source_hash(op)} hbm_bytes {tot:.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic(workload: str):
+    """op -> measured HBM bytes per launch, only for ops whose sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    res = {}
+    for ln in open(path):
+        t = ln.split()
+        if len(t) >= 6 and t[0] == "op" and t[2] == "source" and t[4] == "hbm_bytes":
+            if t[3] == op_source_hash(t[1]):
+                res[t[1]] = float(t[5])
+    return res
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, cmdline=" ".join(sys.argv))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by request or "
               f"KV head with no exchange, so N GPUs would run N independent copies of this benchmark.",
@@ -235,29 +320,39 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # timed region 2: eager launches on one stream with HIP events between the
-    # kernels (per-kernel durations for the roofline)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region 2: each op alone, K back-to-back calls over the replicas on
+    # the compute stream, HIP events around the K calls (per-op durations for
+    # the roofline; the op order inside a step does not matter for these)
+    ops = {
+        "sparse_paged_decode_attn": lambda st, q: L.oasis_sparse_paged_decode_attn(
+            rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr, cs0),
+        "lookahead_score": lambda st, q: L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, cs0),
+        "select_and_diff": lambda st, q: L.oasis_select_and_diff(
+            rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, cs0),
+    }
+    avg = {}
     t1 = time.perf_counter()
-    for i in range(args.steps):
-        sequential_step(i, cs0, evs[i])
-    torch.cuda.synchronize()
-    elapsed_seq = time.perf_counter() - t1
-    per = {n: [] for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
-    avg = {n: float(np.mean(v)) for n, v in per.items()}
+    for n in names:
+        e_beg, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e_beg.record(cs0)
+        for i in range(args.steps):
+            for l in range(run.L):
+                ops[n](rt.state[l][i % replicas], run.q[l, i % cfg.steps + 1])
+        e_end.record(cs0)
+        torch.cuda.synchronize()
+        avg[n] = e_beg.elapsed_time(e_end) * 1e-3 / (args.steps * run.L)
+    elapsed_ops = time.perf_counter() - t1
     attended_after = attended()
 
     if args.calib_copy:
-        a = torch.empty(2**30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
+        # counter calibration: an elementwise add that reads 1 GiB and writes 1 GiB
+        a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device="cuda")
         for _ in range(3):
-            b.copy_(a)
+            b = a + 1.0
+            del b
         torch.cuda.synchronize()
-        del a, b
+        del a
 
     steps_total = cfg.batch * run.L * args.steps
     value = steps_total / elapsed
@@ -267,8 +362,12 @@ def main():
         gbs = ab[n] / avg[n] / 1e9
         kern[n] = {"avg_us": avg[n] * 1e6, "bytes": ab[n], "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
     dominant = max(["sparse_paged_decode_attn", "lookahead_score"], key=lambda n: avg[n])
+    traffic = load_traffic(cfg.name)
+    for n in names:
+        kern[n]["traffic_bytes"] = traffic.get(n)
     roof = {"bound": "hbm", "achieved": kern[dominant]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": kern[dominant]["GB/s"] / HBM_PEAK_GBS, "traffic": None, "kernel": dominant,
+            "frac": kern[dominant]["GB/s"] / HBM_PEAK_GBS, "traffic": traffic.get(dominant), "kernel": dominant,
+            "kernels": OP_KERNELS[dominant],
             "bytes_per_launch": ab[dominant], "avg_launch_us": avg[dominant] * 1e6}
     res = {
         "metric": "predict+select+sparse-attn decode steps/s at 32K ctx; % of peak HBM GB/s",
@@ -290,7 +389,6 @@ def main():
                    "attended_blocks": [attended_before, attended_after]},
         "roofline": roof,
         "kernels": kern,
-        "ms_per_step_sequential_with_events": elapsed_seq / args.steps * 1e3,
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
                       "eager": "plain launches on one stream"}[args.mode],
