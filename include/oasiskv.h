@@ -214,6 +214,28 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                                    const int32_t* ctx_len, float* out, void* workspace,
                                    void* stream);
 
+/*
+ * One layer's decode step ([EXPL] Figure 8: at step t the layer's attention runs
+ * over the resident part of S_t while the draft queries predict S_{t+1}; the
+ * selection and the diff that produce the next fetch follow).  Equivalent to,
+ * and bit-identical with, the sequence
+ *   oasis_sparse_paged_decode_attn(q, pool, sel, block_to_slot, ctx_attn, out, workspace)
+ *   oasis_lookahead_score(q, meta, ctx_score, scores)
+ *   oasis_select_and_diff(scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict)
+ * with the same arguments, on `stream`; the attention's split combine rides in
+ * the scoring launch (three launches instead of four).  ctx_attn is the context
+ * the attention sees (tokens < ctx_attn); ctx_score the context of the scoring
+ * and selection (larger by one after an append of this step, which the caller
+ * enqueues before this call; the attention does not read what it writes).
+ * sel, block_to_slot and slot_to_block are read by the attention and rewritten
+ * by the selection/diff afterwards.  Errors as for the three calls; every
+ * argument is validated before any launch.
+ */
+int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
+                      const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
+                      int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
+                      int32_t* n_fetch, int32_t* evict, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,7 @@ SIGNATURES = {
     "oasis_select_and_diff": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_decode_step": (_int, [_vp] * 16),
 }
 
 _lib = None
@@ -208,3 +209,10 @@ def oasis_select_and_diff(h, scores, ctx_len, sel, block_to_slot, slot_to_block,
 def oasis_sparse_paged_decode_attn(h, q, pool, sel, block_to_slot, ctx_len, out, workspace, stream=None):
     _call("oasis_sparse_paged_decode_attn", h, _ptr(q), _ptr(pool), _ptr(sel), _ptr(block_to_slot),
           _ptr(ctx_len), _ptr(out), _ptr(workspace), _stream(stream))
+
+
+def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block, scores, out,
+                      workspace, fetch, n_fetch, evict, stream=None):
+    _call("oasis_decode_step", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score), _ptr(sel),
+          _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
+          _ptr(n_fetch), _ptr(evict), _stream(stream))

@@ -396,4 +396,53 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                     "oasis_sparse_paged_decode_attn");
 }
 
+int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
+                      const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
+                      int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
+                      int32_t* n_fetch, int32_t* evict, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(meta);
+  CHECK_PTR(ctx_attn);
+  CHECK_PTR(ctx_score);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(scores);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  CHECK_PTR(n_fetch);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  CHECK_ALIGN16(meta);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_decode_step: workspace not 256-byte aligned");
+  const oasis::Ctx& c = h->c;
+  if (c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (c.s.dtype == OASIS_BF16 && oasis::attn_needs_combine(c)) {
+    e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, ctx_attn, out, workspace, st);
+    if (e == hipSuccess) e = oasis::launch_combine_and_score(c, workspace, out, q, meta, ctx_score, scores, st);
+  } else {
+    e = oasis::launch_attn(c, q, pool, sel, block_to_slot, ctx_attn, out, workspace, st);
+    if (e == hipSuccess) e = oasis::launch_score(c, q, meta, ctx_score, scores, st);
+  }
+  if (e == hipSuccess) {
+    if (oasis::select_diff_fused_available(c)) {
+      e = oasis::launch_select_diff(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                                    st);
+    } else {
+      e = oasis::launch_topk(c, scores, ctx_score, sel, st);
+      if (e == hipSuccess)
+        e = oasis::launch_diff(c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, st);
+    }
+  }
+  return hip_status(e, "oasis_decode_step");
+}
+
 }  // extern "C"

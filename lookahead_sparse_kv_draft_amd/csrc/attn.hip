@@ -24,17 +24,10 @@
 // f32 path: VALU, query rows and logits in LDS, accumulators in registers.
 // Both paths leave one partial per split; a log-sum-exp combine kernel merges
 // them.
-#include "oasis_internal.h"
+#include "attn_combine.h"
 
 namespace oasis {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
 
 constexpr float kLazyRescale = 8.f;
 
@@ -376,66 +369,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials: one wavefront per (unit, query row),
-// four per workgroup.  Every split's partial row and (max, sum) are loaded in one
-// batch (split index clamped to the last split, whose repeats get weight 0),
-// then merged: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int D, int SMAX>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_acc,
                                                            const float* __restrict__ ws_ml,
                                                            float* __restrict__ out, int rows,
                                                            int splits, int total) {
-  constexpr int PER = D / kWave;  // output channels per lane (1 or 2)
-  const int id = blockIdx.x * 4 + threadIdx.x / kWave;  // unit * rows + row
-  if (id >= total) return;  // wavefront-uniform
-  const int unit = id / rows;
-  const int row = id - unit * rows;
-  const int lane = threadIdx.x & (kWave - 1);
-  float v[SMAX][PER];
-  float2 ml[SMAX];
-#pragma unroll
-  for (int s = 0; s < SMAX; ++s) {
-    const size_t p = (static_cast<size_t>(unit) * splits + min(s, splits - 1)) * rows + row;
-    ml[s] = *reinterpret_cast<const float2*>(ws_ml + p * 2);
-    if constexpr (PER == 2) {
-      const float2 t = *reinterpret_cast<const float2*>(ws_acc + p * D + 2 * lane);
-      v[s][0] = t.x;
-      v[s][1] = t.y;
-    } else {
-      v[s][0] = ws_acc[p * D + lane];
-    }
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < SMAX; ++s) M = fmaxf(M, ml[s].x);  // repeats do not change the max
-  float L = 0.f, a[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) a[j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < SMAX; ++s) {
-    const float w = (s >= splits || ml[s].x == -INFINITY) ? 0.f : exp2f(ml[s].x - M);
-    L += w * ml[s].y;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) a[j] += w * v[s][j];
-  }
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
-  float* o = out + static_cast<size_t>(id) * D + PER * lane;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) o[j] = a[j] * inv;
-}
-
-struct WsLayout {
-  size_t acc_floats, ml_floats, acc_bytes, ml_bytes;
-};
-
-// workspace: partial accumulators [units][splits][rows][D], then (max, sum)
-// [units][splits][rows][2] (each region 256-byte aligned).
-WsLayout ws_layout(const Ctx& c) {
-  const size_t parts = static_cast<size_t>(c.units) * c.attn_splits * c.rows_attn;
-  WsLayout w{parts * c.s.head_dim, parts * 2, 0, 0};
-  w.acc_bytes = (w.acc_floats * sizeof(float) + 255) / 256 * 256;
-  w.ml_bytes = (w.ml_floats * sizeof(float) + 255) / 256 * 256;
-  return w;
+  attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, rows, splits, total, blockIdx.x * 4 + threadIdx.x / kWave,
+                            threadIdx.x & (kWave - 1));
 }
 
 template <int D, int RT, int W, int PF>
@@ -515,23 +455,29 @@ hipError_t combine_t(const Ctx& c, const float* ws_acc, const float* ws_ml, floa
 
 }  // namespace
 
-size_t attn_workspace_bytes(const Ctx& c) {
-  const WsLayout w = ws_layout(c);
-  return w.acc_bytes + w.ml_bytes;
+size_t attn_workspace_bytes(const Ctx& c) { return attn_ws_acc_bytes(c) + attn_ws_ml_bytes(c); }
+
+bool attn_needs_combine(const Ctx& c) {
+  // the bf16 kernel writes the output itself when there is a single split
+  return !(c.s.dtype == OASIS_BF16 && c.attn_splits == 1);
+}
+
+hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                            const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
+                            hipStream_t st) {
+  float* ws_acc = static_cast<float*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
+  return (c.s.head_dim == 128) ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st)
+                               : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st);
 }
 
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
                        hipStream_t st) {
-  const WsLayout w = ws_layout(c);
+  hipError_t e = launch_attn_main(c, q, pool, sel, b2s, ctx_len, out, ws, st);
+  if (e != hipSuccess || !attn_needs_combine(c)) return e;
   float* ws_acc = static_cast<float*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + w.acc_bytes);
-  hipError_t e = (c.s.head_dim == 128)
-      ? main_t<128>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st)
-      : main_t<64>(c, q, pool, sel, b2s, ctx_len, ws_acc, ws_ml, out, st);
-  if (e != hipSuccess) return e;
-  // The bf16 kernel writes the output itself when there is a single split.
-  if (c.s.dtype == OASIS_BF16 && c.attn_splits == 1) return hipSuccess;
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
   return (c.s.head_dim == 128) ? combine_t<128>(c, ws_acc, ws_ml, out, st)
                                : combine_t<64>(c, ws_acc, ws_ml, out, st);
 }

@@ -52,9 +52,24 @@ hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, in
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
                        hipStream_t st);
+// The attention without its split combine, and whether a combine must follow.
+hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                            const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
+                            hipStream_t st);
+bool attn_needs_combine(const Ctx& c);
+// The split combine and the lookahead score in one launch (bf16 only).
+hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
+                                   const int32_t* ctx_len, float* scores, hipStream_t st);
 size_t attn_workspace_bytes(const Ctx& c);
 
 // ---- small device helpers ----
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

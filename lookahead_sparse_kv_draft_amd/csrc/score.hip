@@ -15,113 +15,18 @@
 // inside each lane and two cross-lane exchanges.
 //
 // f32 path: one thread per block, query rows staged in LDS, plain fp32 VALU.
-#include "oasis_internal.h"
+#include "score_body.h"
 
 namespace oasis {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Per-16-bit-lane mask of the negative halves of a packed bf16 pair.
-__device__ __forceinline__ uint32_t neg_mask(uint32_t w) {
-  return ((w >> 15) & 0x00010001u) * 0xFFFFu;
-}
 
 template <int D, int RT>
 __global__ __launch_bounds__(256) void score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ scores, int H, int G, int T,
     int ndraft, int rows, int Nmax, int waves_per_unit, int tpw, int total_waves) {
-  constexpr int KSTEPS = D / 16;  // 32-element k-steps over the 2d metadata elements
-  constexpr int HALF = KSTEPS / 2;  // steps on the kmin half
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (wave >= total_waves) return;
-  const int unit = wave / waves_per_unit;
-  const int chunk = wave - unit * waves_per_unit;
-  const int n = ctx_len[unit / H];
-  const int N = min((n + kBlock - 1) / kBlock, Nmax);  // context capacity bounds every index
-  const int ntiles = (N + 15) / 16;
-  const int t0 = chunk * tpw;
-  if (t0 >= ntiles) return;
-  const int t1 = min(t0 + tpw, ntiles);
-  const int col = lane & 15;  // A: query row within the row tile; B/C: block within the tile
-  const int grp = lane >> 4;  // k-group of the lane
-
-  // A operands.  Lane (col, grp) at k-step s covers metadata chunk 4s + grp (8
-  // elements): kmin channels for s < HALF (paired with q-), kmax channels after
-  // (paired with q+).  Both use query channels 8 * (4 * (s mod HALF) + grp) .. +7.
-  uint4 A[RT][KSTEPS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + col;
-    if (row < rows) {
-      const int g = row / ndraft;
-      const int t = 1 + (row - g * ndraft);
-      const uint16_t* qr = q + ((static_cast<size_t>(unit) * G + g) * T + t) * D;
-#pragma unroll
-      for (int s = 0; s < HALF; ++s) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(qr + 8 * (4 * s + grp));
-        const uint4 m = make_uint4(neg_mask(raw.x), neg_mask(raw.y), neg_mask(raw.z),
-                                   neg_mask(raw.w));
-        A[rt][s] = make_uint4(raw.x & m.x, raw.y & m.y, raw.z & m.z, raw.w & m.w);
-        A[rt][HALF + s] = make_uint4(raw.x & ~m.x, raw.y & ~m.y, raw.z & ~m.z, raw.w & ~m.w);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) A[rt][s] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  const uint4* mbase = reinterpret_cast<const uint4*>(meta + static_cast<size_t>(unit) * Nmax * 2 * D);
-  float* sbase = scores + static_cast<size_t>(unit) * Nmax;
-  constexpr int CHUNKS = 2 * D / 8;  // 16-byte chunks per block row pair
-
-  // Loads are unconditional (the block index is clamped to N-1; results of
-  // blocks >= N are discarded), so the waits below only cover the older buffer.
-  auto load = [&](uint4* Bt, int tile) {
-    const int b = min(tile * 16 + col, N - 1);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp];
-  };
-  auto compute = [&](const uint4* Bt, int tile) {
-    float best = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(A[rt][s]), as_bf16x8(Bt[s]), acc, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rt * 16 + 4 * grp + i;
-        if (row < rows) best = fmaxf(best, acc[i]);
-      }
-    }
-    best = fmaxf(best, __shfl_xor(best, 16));
-    best = fmaxf(best, __shfl_xor(best, 32));
-    const int b = tile * 16 + col;
-    if (grp == 0 && b < N) sbase[b] = best;
-  };
-  // Ping-pong over two tile buffers.  The prefetch index is clamped and the
-  // loop body has no branch (an odd count repeats the last tile, whose store is
-  // identical), so every wait covers only the older buffer.
-  const int ntl = t1 - t0;
-  uint4 Ba[KSTEPS], Bb[KSTEPS];
-  load(Ba, t0);
-  for (int j = 0; j < ntl; j += 2) {
-    load(Bb, t0 + min(j + 1, ntl - 1));
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
-    compute(Ba, t0 + j);
-    load(Ba, t0 + min(j + 2, ntl - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    compute(Bb, t0 + min(j + 1, ntl - 1));
-  }
+  score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, rows, Nmax, waves_per_unit, tpw, total_waves,
+                    blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
 }
 
 template <int D>
@@ -157,8 +62,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
 template <int D, int RT>
 hipError_t mfma_t(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
                   float* scores, hipStream_t st) {
-  const int tiles = (c.s.max_blocks + 15) / 16;
-  const int wpu = (tiles + c.score_tpw - 1) / c.score_tpw;
+  const int wpu = score_waves_per_unit(c);
   const int total = c.units * wpu;
   const int grid = (total + 3) / 4;
   hipLaunchKernelGGL((score_mfma_kernel<D, RT>), dim3(grid), dim3(256), 0, st,

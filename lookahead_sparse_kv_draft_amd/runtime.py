@@ -124,7 +124,9 @@ class DecodeRuntime:
         self.replicas = replicas
         tiers = []
         for _ in range(layers):
-            tiers.append(torch.empty(L.oasis_host_tier_bytes(self.h), dtype=torch.uint8, pin_memory=True)
+            # zero-filled: pages of blocks that appends create later are fetched
+            # with their not-yet-written rows, which then hold defined values
+            tiers.append(torch.zeros(L.oasis_host_tier_bytes(self.h), dtype=torch.uint8, pin_memory=True)
                          if host_tier else None)
         # state[layer][replica]; replicas share the layer's host tier
         self.state = [[LayerState(self, tiers[l]) for _ in range(replicas)] for l in range(layers)]
@@ -257,6 +259,23 @@ class DecodeRuntime:
                                          self.out if out is None else out, self.ws_ptr, cs)
         if self.overlap:
             st.attn_done.record(cs)
+
+    def decode_step(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None):
+        """Attention of step t, scoring of its drafts, selection of S_{t+1} and the
+        diff, in one library call (three launches) on the current stream.  An
+        append of this step is enqueued before it (the attention does not read
+        what the append writes; the scoring sees the grown context)."""
+        st = self.state[layer][replica]
+        cs = torch.cuda.current_stream()
+        if st.fetch_wait_compute or st.fetch_wait_predict:
+            cs.wait_event(st.fetch_done)
+            st.fetch_wait_compute = st.fetch_wait_predict = False
+        if st.select_pending:
+            cs.wait_event(st.select_done)
+            st.select_pending = False
+        L.oasis_decode_step(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s, st.s2b,
+                            st.scores, self.out if out is None else out, self.ws_ptr, st.fetch, st.n_fetch,
+                            st.evict, cs)
 
     def append(self, layer: int, k_new_dev, v_new_dev, k_new_host=None, v_new_host=None,
                replica: int = 0):

@@ -42,8 +42,11 @@ class SyntheticRun:
     """The decode chain of one workload configuration on cuda:0."""
 
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
-                 record_units=None, device: str = "cuda", overlap: bool = True):
+                 record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True):
+        """fused_step: without overlap and drift, run each layer's step through the
+        single decode-step call (attention, scoring, selection, diff)."""
         self.cfg = cfg
+        self.fused_step = fused_step and not overlap
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap)
@@ -127,6 +130,22 @@ class SyntheticRun:
 
     def step(self, t: int, transfer: bool = True):
         cfg, rt = self.cfg, self.rt
+        if self.fused_step and self.drift is None:
+            for l in range(self.L):
+                q = self.q[l, t + 1]
+                if cfg.append:
+                    rt.append(l, self.k_new_dev[l, t], self.v_new_dev[l, t],
+                              self.k_new_host[l, t], self.v_new_host[l, t])
+                rt.decode_step(l, q)
+                if self.record_units is not None:
+                    self._record_out(l, t)
+                if transfer:
+                    rt.transfer(l)
+            rt.end_step()
+            if transfer:
+                rt.wait_transfers()
+            self._record(t)
+            return
         for l in range(self.L):
             q = self.q[l, t + 1]
             rt.attention(l, q)

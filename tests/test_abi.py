@@ -74,6 +74,18 @@ def test_sizes_and_null_checks():
         assert lib.oasis_block_meta_update(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_build(h, None, None, 0, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_lookahead_score(None, 16, 16, 16, 16, None) == L.OASIS_EINVAL
+        assert lib.oasis_select_and_diff(h, None, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_decode_step(h, *([None] * 15)) == L.OASIS_EINVAL
+        # one missing pointer among valid-looking ones, and a misaligned workspace
+        good = [256] * 15
+        for i in range(11):  # q .. workspace, then n_fetch
+            args = list(good)
+            args[i] = None
+            assert lib.oasis_decode_step(h, *args) == L.OASIS_EINVAL, i
+        args = list(good)
+        args[10] = 272  # workspace 16- but not 256-byte aligned
+        assert lib.oasis_decode_step(h, *args) == L.OASIS_EINVAL
+        assert "workspace" in L.oasis_last_error()
         # misaligned device pointers
         assert lib.oasis_lookahead_score(h, 18, 32, 16, 16, None) == L.OASIS_EINVAL
         assert "aligned" in L.oasis_last_error()
