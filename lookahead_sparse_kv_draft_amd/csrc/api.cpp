@@ -114,8 +114,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // Attention: workgroups of W wavefronts, each wavefront streaming a run of
   // consecutive selection entries (at most 64) through a ring of PF page
   // buffers; a workgroup covers W runs (one split).  By default 2 wavefronts,
-  // a 2-page ring and about one wavefront per SIMD of the 256 compute units, so
-  // every workgroup is resident at once.
+  // a 2-page ring and about 512 wavefronts per launch (measured best on the
+  // 32K-context batch-8 step: fewer, longer-running wavefronts amortise the
+  // per-workgroup start-up and write fewer partials).
   const int row_tiles = (rows_attn + 15) / 16;
   const int max_waves = (row_tiles <= 2) ? 4 : 2;  // LDS of the wavefront merge
   int waves = env_int("OASIS_ATTN_WAVES", 0);
@@ -123,7 +124,7 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   waves = std::min(waves, max_waves);
   const int kbud = s.budget_blocks;
   int splits = env_int("OASIS_ATTN_SPLITS", 0);
-  if (splits <= 0) splits = (1024 + c.units * waves - 1) / (c.units * waves);
+  if (splits <= 0) splits = (512 + c.units * waves - 1) / (c.units * waves);
   const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
   const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
   splits = std::max(min_splits, std::min(splits, max_splits));

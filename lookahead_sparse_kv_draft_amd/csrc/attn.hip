@@ -31,14 +31,17 @@ namespace {
 
 constexpr float kLazyRescale = 8.f;
 
-// W wavefronts per workgroup; each wavefront takes a run of `run` consecutive
-// entries of its unit's selection and streams their pages through a ring of PF
-// page buffers in registers (PF pages always in flight, every wait exact); a
-// workgroup covers W runs (one split).  The wavefronts merge in LDS; with one
+// Two wavefronts per SIMD for the 2-page ring with up to three row tiles: the
+// registers then hold the accumulators too (no spills), and a second wavefront
+// hides the first one's MFMA and exchange latencies.
+// W wavefronts per workgroup, splits workgroups per unit; each wavefront takes
+// an even share (at most `run` entries) of the unit's attended list and streams
+// its pages through a ring of PF page buffers in registers (PF pages always in
+// flight, every wait exact).  The wavefronts merge in LDS; with one
 // split the workgroup writes the output, otherwise its partial (unnormalised
 // accumulator, row max, row sum) for the combine kernel.
 template <int D, int RT, int W, int PF>
-__global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((PF <= 2 && RT <= 3) ? 2 : 1))) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s,
     const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
   constexpr int KS = D / 32;  // QK k-steps of 32 channels
   constexpr int CT = D / 16;  // PV channel tiles
   constexpr int PAGE = 2 * kBlock * D;
+  constexpr int NT = 64 * W;
   constexpr int NSLICE = (W > 1) ? W / 2 : 1;
   __shared__ float sm_m[W][RT * 16];
   __shared__ float sm_l[W][RT * 16];
@@ -77,28 +81,59 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(
     }
   }
 
-  // This wavefront's entries e0 .. e0+run-1 (run <= 64; lane j looks up e0 + j).
-  const int e0 = (split * W + wv) * run;
-  const int cnt = min(run, kb - e0);
-  int my_slot = -1, my_ntok = 0;
-  if (lane < cnt) {
-    const int b = sel[static_cast<size_t>(unit) * kb + e0 + lane];
-    if (b >= 0 && b < Nmax) {
-      const int s = b2s[static_cast<size_t>(unit) * Nmax + b];
-      const int nt = min(kBlock, n - kBlock * b);
-      if (s >= 0 && s < kb && nt > 0) {
-        my_slot = s;
-        my_ntok = nt;
-      }
+  // The unit's attended entries (selected blocks that are resident and hold
+  // tokens below n), in rank order, packed slot | ntok << 16: every workgroup of
+  // the unit builds the whole list in LDS (lookups in batches of four entries
+  // per thread, all loads of a batch in flight), then takes its wavefronts'
+  // shares of an even split over all splits * W wavefronts of the unit, so every
+  // wavefront streams the same number of pages (+-1).
+  __shared__ int sm_att[kMaxBudget];
+  __shared__ int sm_wcnt[4][W];
+  const uint64_t below = (1ull << lane) - 1ull;
+  int natt = 0;
+  for (int c0 = 0; c0 < kb; c0 += 4 * NT) {
+    int bsel[4], slot[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bsel[u] = sel[static_cast<size_t>(unit) * kb + min(c0 + u * NT + tid, kb - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = bsel[u];
+      slot[u] = b2s[static_cast<size_t>(unit) * Nmax + ((b >= 0 && b < Nmax) ? b : 0)];
     }
+    int v[4];
+    uint64_t bal[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + u * NT + tid;
+      const int b = bsel[u];
+      const int nt = min(kBlock, n - kBlock * b);
+      const bool ok = i < kb && b >= 0 && b < Nmax && slot[u] >= 0 && slot[u] < kb && nt > 0;
+      v[u] = ok ? (slot[u] | (nt << 16)) : -1;
+      bal[u] = __ballot(ok);
+      if (lane == 0) sm_wcnt[u][wv] = __popcll(bal[u]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const int cw = sm_wcnt[u][w];
+        before += (w < wv) ? cw : 0;
+        tot += cw;
+      }
+      if (v[u] >= 0) sm_att[natt + before + __popcll(bal[u] & below)] = v[u];
+      natt += tot;
+    }
+    __syncthreads();  // the list is complete; sm_wcnt may be reused
   }
-  // Compact the attended entries into lanes 0 .. nb-1 (forward lane permute).
-  const uint64_t valid = __ballot(my_slot >= 0);
-  const int nb = __popcll(valid);
-  const int pos = __popcll(valid & ((1ull << lane) - 1ull));
-  const int dst = (my_slot >= 0 ? pos : 63) * 4;
-  const int c_slot = __builtin_amdgcn_ds_permute(dst, my_slot);
-  const int c_ntok = __builtin_amdgcn_ds_permute(dst, my_ntok);
+  const int nwv = splits * W;
+  const int per = (natt + nwv - 1) / nwv;  // <= run <= 64
+  const int e0 = (split * W + wv) * per;
+  const int nb = max(0, min(per, natt - e0));
+  const int mine = (lane < nb) ? sm_att[e0 + lane] : 0;
+  const int c_slot = mine & 0xFFFF;
+  const int c_ntok = mine >> 16;
 
   f32x4_t acc[RT][CT];
   float mrun[RT], lrun[RT];
