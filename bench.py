@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     p.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--no-h2", action="store_true", help="skip the end-to-end (transfer-inclusive) measurement")
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --calib-copy` into a traffic file and exit")
@@ -179,6 +180,86 @@ def load_traffic(workload: str):
             if t[3] == op_source_hash(t[1]):
                 res[t[1]] = float(t[5])
     return res
+
+
+def measure_h2(args, cfg, run, rt, replicas, sequential_step, h1_step_us):
+    """End to end: every step's fetched pages move from the pinned host tier into
+    the pool (device-driven gather on the side stream) and the next step's
+    attention of the layer waits for them, as in a single-layer decode chain.
+    Reports the step time, the exposed transfer (end-to-end minus HBM-resident
+    step time), fetched bytes per step, the gather's PCIe rate and a plain pinned
+    host-to-device copy rate for reference."""
+    import torch
+
+    from lookahead_sparse_kv_draft_amd import _lib as L
+
+    cs = torch.cuda.current_stream()
+    side = rt.side
+    ev_sel = [torch.cuda.Event() for _ in range(run.L)]
+    ev_fetch = [torch.cuda.Event() for _ in range(run.L)]
+    nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
+
+    def step(i, first, count=False):
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            st = rt.state[l][rep]
+            if not first:
+                cs.wait_event(ev_fetch[l])
+            L.oasis_decode_step(rt.h, run.q[l, t + 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, cs)
+            if count:
+                nf_tot.add_(st.n_fetch.sum())
+            ev_sel[l].record(cs)
+            side.wait_event(ev_sel[l])
+            L.oasis_fetch_gather(rt.h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+            ev_fetch[l].record(side)
+
+    K = args.steps
+    for i in range(min(args.warmup, 20)):
+        step(i, i == 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, False)
+    cs.wait_event(ev_fetch[run.L - 1])
+    torch.cuda.synchronize()
+    h2_us = (time.perf_counter() - t0) / K * 1e6
+    for i in range(K):  # untimed: fetched pages per step
+        step(i, False, count=True)
+    torch.cuda.synchronize()
+    page = L.oasis_page_bytes(rt.h)
+    fetched = float(nf_tot.item()) * page / K
+    # the gather alone, back to back on the side stream, over the last lists
+    eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb.record(side)
+    for i in range(K):
+        st = rt.state[0][i % replicas]
+        L.oasis_fetch_gather(rt.h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+    ee.record(side)
+    torch.cuda.synchronize()
+    gather_us = eb.elapsed_time(ee) * 1e3 / K
+    nf_last = sum(int(rt.state[0][r].n_fetch.sum()) for r in range(replicas)) / replicas
+    # pinned host -> device copy reference (64 MiB)
+    hbuf = torch.empty(64 * 2**20, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(64 * 2**20, dtype=torch.uint8, device="cuda")
+    dbuf.copy_(hbuf, non_blocking=True)
+    torch.cuda.synchronize()
+    eb.record(cs)
+    for _ in range(5):
+        dbuf.copy_(hbuf, non_blocking=True)
+    ee.record(cs)
+    torch.cuda.synchronize()
+    memcpy_gbs = 5 * hbuf.numel() / (eb.elapsed_time(ee) * 1e-3) / 1e9
+    return {"ms_per_step": h2_us * 1e-3,
+            "steps_per_s": cfg.batch * run.L * 1e6 / h2_us,
+            "exposed_transfer_us_per_step": h2_us - h1_step_us * run.L,
+            "fetched_bytes_per_step": fetched,
+            "gather_us": gather_us,
+            "gather_pcie_GBs": (nf_last * page) / (gather_us * 1e-6) / 1e9 if gather_us > 0 else None,
+            "h2d_pinned_memcpy_GBs": memcpy_gbs,
+            "note": "PCIe-inclusive single-layer chain: each step's fetch lands before the next attention; "
+                    "not the headline value"}
 
 
 def main():
@@ -346,6 +427,8 @@ def main():
     step_call_us = e_beg.elapsed_time(e_end) * 1e3 / (args.steps * run.L)
     attended_after = attended()
 
+    h2 = None if args.no_h2 else measure_h2(args, cfg, run, rt, replicas, sequential_step, step_call_us)
+
     if args.calib_copy:
         # counter calibration: an elementwise add that reads 1 GiB and writes 1 GiB
         a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device="cuda")
@@ -395,6 +478,7 @@ def main():
                       "eager": "one decode-step call per layer (3 launches) on one stream"}[args.mode],
         "hbm_bytes_per_step": sum(ab[n] for n in names) * run.L,
         "decode_step_call_us": step_call_us,
+        "h2": h2,
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)

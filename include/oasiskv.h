@@ -199,6 +199,21 @@ int oasis_fetch_issue(oasis_handle h, const void* host_tier, void* pool, const i
                       const int32_t* n_fetch_host, void* stream);
 
 /*
+ * Fetch gather ([EXPL] Figure 8 and "What they did" item 2: the missing
+ * predicted blocks move from the host tier into their HBM slots before the
+ * layer's attention at the next step).  Device-driven alternative to
+ * oasis_fetch_issue: one kernel reads the fetch list and n_fetch where the diff
+ * left them (device memory) and copies each page from host_tier (pinned host
+ * memory, read by the GPU over PCIe) to its pool slot, on `stream`; no host
+ * synchronisation is needed between the diff and the transfer.  host_tier must
+ * be pinned host memory mapped for the device (hipHostMalloc / torch
+ * pin_memory): checked with hipPointerGetAttributes, EINVAL otherwise.  Entries
+ * beyond n_fetch, and entries whose block or slot is out of range, are skipped.
+ */
+int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch,
+                       const int32_t* n_fetch, void* stream);
+
+/*
  * Sparse paged GQA decode attention ([EXPL] Figure 7 right: verify and draft
  * queries attend together over the sparse working set).  For every unit, query
  * row (g, t) and the token set J of the blocks of sel that are resident

@@ -60,6 +60,7 @@ SIGNATURES = {
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 16),
+    "oasis_fetch_gather": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -166,6 +167,10 @@ def oasis_pack_pages(h, k, v, blocks, n_blocks, unit, pages):
 
 def oasis_host_tier_append(h, k_new, v_new, pos, host_tier):
     _call("oasis_host_tier_append", h, _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(host_tier))
+
+
+def oasis_fetch_gather(h, host_tier, pool, fetch, n_fetch, stream=None):
+    _call("oasis_fetch_gather", h, _ptr(host_tier), _ptr(pool), _ptr(fetch), _ptr(n_fetch), _stream(stream))
 
 
 def oasis_fetch_issue(h, host_tier, pool, fetch_host, n_fetch_host, stream=None):

@@ -397,6 +397,29 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                     "oasis_sparse_paged_decode_attn");
 }
 
+int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch,
+                       const int32_t* n_fetch, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(host_tier);
+  CHECK_PTR(pool);
+  CHECK_PTR(n_fetch);
+  CHECK_ALIGN16(host_tier);
+  CHECK_ALIGN16(pool);
+  const oasis::Ctx& c = h->c;
+  if (c.s.fetch_cap > 0) CHECK_PTR(fetch);
+  // The kernel dereferences the host tier: it must be pinned host memory mapped
+  // into the device's address space (hipHostMalloc).
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_tier) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();  // clear the lookup's error state
+    return fail(OASIS_EINVAL, "oasis_fetch_gather: host_tier is not pinned host memory mapped for the device");
+  }
+  return hip_status(oasis::launch_fetch_gather(c, attr.devicePointer, pool, fetch, n_fetch,
+                                               static_cast<hipStream_t>(stream)),
+                    "oasis_fetch_gather");
+}
+
 int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
                       const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
                       int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,

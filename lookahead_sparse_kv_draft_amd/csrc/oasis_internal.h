@@ -61,6 +61,8 @@ bool attn_needs_combine(const Ctx& c);
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st);
 size_t attn_workspace_bytes(const Ctx& c);
+hipError_t launch_fetch_gather(const Ctx& c, const void* host_dev, void* pool, const int32_t* fetch,
+                               const int32_t* n_fetch, hipStream_t st);
 
 // ---- small device helpers ----
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

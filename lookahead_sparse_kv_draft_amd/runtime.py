@@ -110,13 +110,15 @@ class DecodeRuntime:
     """Buffers and step chain for `layers` layers of one shape on one GPU."""
 
     def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
-                 host_tier: bool = True, fused_select: bool = True, overlap: bool = False):
+                 host_tier: bool = True, fused_select: bool = True, overlap: bool = False,
+                 gather: bool = True):
         """overlap: run scoring / selection on a second stream so that they overlap
         the attention of the same step (and of other layers); the selection waits
         only for the attention that reads the maps it rewrites."""
         self.shape = shape
         self.fused_select = fused_select
         self.overlap = overlap
+        self.gather = gather
         self.device = torch.device(device)
         self.h = shape.handle()
         s = shape
@@ -334,11 +336,22 @@ class DecodeRuntime:
             st.select_pending = True
 
     def transfer(self, layer: int, replica: int = 0, stream=None):
-        """Copy the fetch list to the host (after the diff, on its stream), then issue
-        the page copies on the side stream; later attention and appends of this
-        layer wait for them."""
+        """Move this step's fetched pages into the pool on the side stream, after the
+        diff; later attention and appends of this layer wait for them.  Default: the
+        device-driven gather (reads the fetch list in HBM and the pages from the
+        pinned host tier, no host synchronisation); with gather=False: copy the
+        fetch list to the host, wait for it, and issue one copy per page."""
         st = self.state[layer][replica]
         ps = self._pred() if stream is None else stream
+        if self.gather:
+            ready = torch.cuda.Event()
+            ready.record(ps)
+            self.side.wait_event(ready)
+            L.oasis_fetch_gather(self.h, st.host_tier, st.pool, st.fetch, st.n_fetch, self.side)
+            st.fetch_done.record(self.side)
+            st.fetch_wait_compute = True
+            st.fetch_wait_predict = True
+            return
         with torch.cuda.stream(ps):
             st.fetch_host.copy_(st.fetch, non_blocking=True)
             st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)

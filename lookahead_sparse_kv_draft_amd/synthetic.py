@@ -42,14 +42,17 @@ class SyntheticRun:
     """The decode chain of one workload configuration on cuda:0."""
 
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
-                 record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True):
+                 record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
+                 gather: bool = True):
         """fused_step: without overlap and drift, run each layer's step through the
-        single decode-step call (attention, scoring, selection, diff)."""
+        single decode-step call (attention, scoring, selection, diff).  gather: move
+        the fetched pages with the device-driven gather (else host-issued copies)."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
-        self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap)
+        self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
+                                gather=gather)
         self.record_units = record_units  # list of (layer, unit) to record, or None
         self.records = {}
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim

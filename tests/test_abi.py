@@ -76,6 +76,10 @@ def test_sizes_and_null_checks():
         assert lib.oasis_lookahead_score(None, 16, 16, 16, 16, None) == L.OASIS_EINVAL
         assert lib.oasis_select_and_diff(h, None, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_decode_step(h, *([None] * 15)) == L.OASIS_EINVAL
+        assert lib.oasis_fetch_gather(h, None, None, None, None, None) == L.OASIS_EINVAL
+        # a host tier that is not pinned, device-mapped memory is refused before any launch
+        plain = np.zeros(4096, dtype=np.uint8)
+        assert lib.oasis_fetch_gather(h, plain.ctypes.data, 256, 256, 256, None) == L.OASIS_EINVAL
         # one missing pointer among valid-looking ones, and a misaligned workspace
         good = [256] * 15
         for i in range(11):  # q .. workspace, then n_fetch

@@ -15,10 +15,10 @@ from workload import CONFIGS
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_compare(cfg, units, steps=None, layers=None, max_diverged_frac=0.25, overlap=False):
+def _run_and_compare(cfg, units, steps=None, layers=None, max_diverged_frac=0.25, overlap=False, gather=True):
     cfg = cfg if steps is None else cfg.with_(steps=steps)
     print(f"{cfg.name}: filling host tier and metadata", flush=True)
-    run = SyntheticRun(cfg, layers=layers, record_units=units, overlap=overlap)
+    run = SyntheticRun(cfg, layers=layers, record_units=units, overlap=overlap, gather=gather)
     try:
         run.run(log=lambda msg: print(msg, flush=True))
         results = []
@@ -34,10 +34,10 @@ def _run_and_compare(cfg, units, steps=None, layers=None, max_diverged_frac=0.25
     return results
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_chain_tiny_full(overlap):
+@pytest.mark.parametrize("overlap,gather", [(False, True), (True, True), (False, False)])
+def test_chain_tiny_full(overlap, gather):
     cfg = CONFIGS["tiny"]
-    res = _run_and_compare(cfg, [(0, 0)], max_diverged_frac=0.0, overlap=overlap)
+    res = _run_and_compare(cfg, [(0, 0)], max_diverged_frac=0.0, overlap=overlap, gather=gather)
     assert res[0]["diverged_at"] is None
 
 
@@ -48,11 +48,11 @@ def test_chain_small_bf16_ragged():
     _run_and_compare(cfg, [(0, u) for u in range(cfg.batch * cfg.kv_heads)])
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_chain_small_append(overlap):
+@pytest.mark.parametrize("overlap,gather", [(False, True), (True, True), (False, False)])
+def test_chain_small_append(overlap, gather):
     cfg = CONFIGS["qwen8b_reason"].with_(batch=2, ctx=16 * 40 + 13, steps=40, recency_blocks=8,
                                          planted=4, budget_tokens=16 * 16, fetch_cap=3)
-    _run_and_compare(cfg, [(0, u) for u in range(cfg.batch * cfg.kv_heads)], overlap=overlap)
+    _run_and_compare(cfg, [(0, u) for u in range(cfg.batch * cfg.kv_heads)], overlap=overlap, gather=gather)
 
 
 def test_chain_small_drift():

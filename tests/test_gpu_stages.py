@@ -417,6 +417,65 @@ def test_fetch_issue_copies_pages():
     rt.close()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_fetch_gather_matches_fetch_issue(dtype, d):
+    """The device-driven gather copies exactly the pages the host-issued copies
+    do, skips entries beyond n_fetch and entries out of range, and touches no
+    other slot."""
+    B, H, Nmax, k, cap = 2, 2, 40, 8, 5
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=Nmax, budget_blocks=k, fetch_cap=cap,
+                      dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(16)
+    ht = rt.host_tier_view(0)
+    ht.copy_(torch.from_numpy(rng.integers(0, 255, size=ht.numel(), dtype=np.uint8)))
+    st = rt.state[0][0]
+    units = B * H
+    fetch = np.full((units, cap, 2), -1, dtype=np.int32)
+    nf = np.array([5, 0, 3, 2], dtype=np.int32)
+    for u in range(units):
+        blocks = rng.choice(Nmax, size=cap, replace=False)
+        slots = rng.choice(k, size=cap, replace=False)
+        fetch[u] = np.stack([blocks, slots], axis=1)   # entries >= n_fetch hold valid-looking pairs
+    fetch_bad = fetch.copy()
+    fetch_bad[0, 1] = (Nmax + 3, 2)   # block out of range: skipped by the gather
+    fetch_bad[2, 0] = (4, k)          # slot out of range: skipped
+    pb = L.oasis_page_bytes(rt.h)
+    host = ht.numpy().reshape(units, Nmax, pb)
+    # host-issued copies of the valid lists
+    st.pool.zero_()
+    L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nf, rt.side)
+    rt.side.synchronize()
+    ref = st.pool.cpu().numpy().reshape(units, k, pb).copy()
+    # the gather from device-resident lists
+    st.pool.zero_()
+    L.oasis_fetch_gather(rt.h, st.host_tier, st.pool, U.i32(fetch), U.i32(nf))
+    torch.cuda.synchronize()
+    got = st.pool.cpu().numpy().reshape(units, k, pb)
+    assert np.array_equal(got, ref)
+    # out-of-range entries are skipped, the rest of the list still lands
+    st.pool.zero_()
+    L.oasis_fetch_gather(rt.h, st.host_tier, st.pool, U.i32(fetch_bad), U.i32(nf))
+    torch.cuda.synchronize()
+    got = st.pool.cpu().numpy().reshape(units, k, pb)
+    for u in range(units):
+        filled = set()
+        for i in range(nf[u]):
+            b, s = fetch_bad[u, i]
+            if 0 <= b < Nmax and 0 <= s < k:
+                assert np.array_equal(got[u, s], host[u, b]), (u, i)
+                filled.add(s)
+        for s in set(range(k)) - filled:
+            assert not got[u, s].any(), (u, s)
+    # pageable host memory is refused before any launch (empty lists, so even a
+    # launch would touch nothing)
+    plain = np.zeros(ht.numel(), dtype=np.uint8)
+    with pytest.raises(L.OasisError) as e:
+        L.oasis_fetch_gather(rt.h, plain, st.pool, U.i32(fetch), U.i32(np.zeros(units, dtype=np.int32)))
+    assert e.value.code == L.OASIS_EINVAL
+    rt.close()
+
+
 @pytest.mark.parametrize("k,cap,ctxs,kind", [
     (128, 32, [32768, 16 * 700 + 3, 16 * 130, 100], "normal"),
     (128, 16, [32768, 32768, 16 * 129, 16 * 2], "ties"),
