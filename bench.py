@@ -76,38 +76,69 @@ def attn_flops(cfg, attended_blocks: int):
     return attended_blocks * 16 * cfg.group * cfg.T * cfg.head_dim * 4
 
 
-def cpu_baseline(cfg, target_s: float):
-    """The oracle timed on a bounded sample of the same workload (single thread)."""
+def _oracle_unit_job(args):
+    """Prologue + `steps` oracle steps of one unit; returns its CPU seconds."""
+    cfg_name, cfg_kw, r, h, steps = args
     from threadpoolctl import threadpool_limits
 
     from oracle import oasis_oracle as O
-    from workload import synth
+    from workload import CONFIGS, synth
+    cfg = CONFIGS[cfg_name].with_(**cfg_kw) if cfg_kw else CONFIGS[cfg_name]
+    with threadpool_limits(limits=1):
+        ud = synth.unit_data(cfg, r, 0, h)
+        K = ud.keys()
+        t0 = time.perf_counter()
+        O.run_unit(K_at=lambda t: K, V=ud.V, queries=ud.queries, drafts_prologue=ud.drafts[0],
+                   n0=cfg.ctx, k=cfg.k, cap=cfg.fetch_cap, steps=steps,
+                   initial_slots=lambda S0: synth.initial_residency(cfg, r, 0, h, S0),
+                   append=cfg.append, max_blocks=cfg.max_blocks)
+        return time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, target_s: float):
+    """The oracle (fp64 numpy, one BLAS thread per worker) timed on a bounded
+    sample of the same workload: layer-0 units, prologue + 16 steps each, over a
+    process pool of the host's cores (at most 16), after a one-worker run."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
 
     H = cfg.kv_heads
-    done_unit_steps = 0
-    units_used = 0
     steps = min(cfg.steps, 16)
-    t_total = 0.0
-    with threadpool_limits(limits=1):
-        u = 0
-        while t_total < target_s and u < cfg.batch * H:
-            r, h = divmod(u, H)
-            ud = synth.unit_data(cfg, r, 0, h)
-            K = ud.keys()
-            t0 = time.perf_counter()
-            O.run_unit(K_at=lambda t: K, V=ud.V, queries=ud.queries, drafts_prologue=ud.drafts[0],
-                       n0=cfg.ctx, k=cfg.k, cap=cfg.fetch_cap, steps=steps,
-                       initial_slots=lambda S0: synth.initial_residency(cfg, r, 0, h, S0),
-                       append=cfg.append, max_blocks=cfg.max_blocks)
-            t_total += time.perf_counter() - t0
-            done_unit_steps += steps
-            units_used += 1
-            u += 1
-    # one (request x layer) step covers kv_heads units
-    value = (done_unit_steps / H) / t_total
-    return {"value": value, "unit": "decode steps/s (request x layer)", "cores": 1, "kind": "oracle",
-            "sample": f"{units_used} of {cfg.batch * H} (request, KV head) units of layer 0, "
-                      f"prologue + {steps} steps each, fp64 numpy, {t_total:.1f} s"}
+    units = [(u // H, u % H) for u in range(cfg.batch * H)]
+    # one worker: units until the time target
+    t1, n1 = 0.0, 0
+    for (r, h) in units:
+        if t1 >= target_s / 3:
+            break
+        t1 += _oracle_unit_job((cfg.name, None, r, h, steps))
+        n1 += 1
+    one = (n1 * steps / H) / t1
+    # pool: as many units as fit the target at the measured per-unit cost
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    per_unit = t1 / n1
+    n_units = int(min(len(units) * 8, max(workers, target_s * workers / per_unit)))
+    jobs = [(cfg.name, None, units[i % len(units)][0], units[i % len(units)][1], steps) for i in range(n_units)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        list(ex.map(_oracle_unit_job, jobs))
+    wall = time.perf_counter() - t0
+    value = (n_units * steps / H) / wall
+    return {"value": value, "unit": "decode steps/s (request x layer)", "cores": workers, "kind": "oracle",
+            "sample": f"{n_units} (request, KV head) units of layer 0 (cycled over the {len(units)} units), "
+                      f"prologue + {steps} steps each, fp64 numpy, {workers} worker processes x 1 BLAS "
+                      f"thread, {wall:.1f} s wall (incl. worker start-up); CPU {_cpu_model()}",
+            "one_worker": {"value": one, "units": n1, "seconds": t1}}
 
 
 def op_source_hash(op: str) -> str:
@@ -273,13 +304,20 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from workload import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # first, before anything initialises the GPU: the worker processes start clean
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
     import torch
 
     from lookahead_sparse_kv_draft_amd import _lib as L
     from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
-    from workload import CONFIGS
 
-    cfg = CONFIGS[args.config]
     torch.cuda.set_device(0)
     # per-layer HBM state (metadata + pool) and the replica count that defeats the MALL
     shape_meta = cfg.batch * cfg.kv_heads * cfg.max_blocks * 2 * cfg.head_dim * cfg.elem_bytes
@@ -480,9 +518,8 @@ def main():
         "decode_step_call_us": step_call_us,
         "h2": h2,
     }
-    if not args.no_cpu_baseline:
-        print("# cpu baseline", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     run.close()
     print(json.dumps(res))
 
