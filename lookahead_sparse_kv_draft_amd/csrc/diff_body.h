@@ -105,17 +105,24 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
       need = nc;
       nF = nfree + nc;
     }
-    if (cnd) {
-      int r = 0, j = 0;
-      for (; j + 8 <= kb; j += 8) {
+    // Each candidate's place = number of larger keys (non-candidates hold 0),
+    // counted by P adjacent threads per slot and summed across their lanes.
+    const int P0 = static_cast<int>(blockDim.x) / kb;
+    const int P = (P0 >= 16) ? 16 : (P0 >= 8) ? 8 : (P0 >= 4) ? 4 : (P0 >= 2) ? 2 : 1;
+    const int ci = tid / P, part = tid & (P - 1);
+    const unsigned long long ck = (ci < kb) ? ckey[ci] : 0ull;
+    int r = 0;
+    for (int j = part; j < kb; j += 4 * P) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) r += (ckey[j + t] > mykey) ? 1 : 0;
+      for (int t = 0; t < 4; ++t) {
+        const int jj = j + t * P;
+        r += (jj < kb && ckey[min(jj, kb - 1)] > ck) ? 1 : 0;
       }
-      for (; j < kb; ++j) r += (ckey[j] > mykey) ? 1 : 0;
-      if (r < need) {
-        vict[r] = sb;
-        victS[r] = i;
-      }
+    }
+    for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+    if (part == 0 && ck != 0ull && r < need) {
+      vict[r] = static_cast<int32_t>(ck & 0xFFFFFFFFull) - 1;  // the block (stored + 1)
+      victS[r] = ci;
     }
   }
   __syncthreads();

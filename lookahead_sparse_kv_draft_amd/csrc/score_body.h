@@ -29,14 +29,30 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
   if (wave >= total_waves) return;
   const int unit = wave / waves_per_unit;
   const int chunk = wave - unit * waves_per_unit;
+  const int t0 = chunk * tpw;  // this wavefront's first tile (< ceil(Nmax / 16) by the grid)
+  const int t1max = min(t0 + tpw, (Nmax + 15) / 16);
+  const int col = lane & 15;  // A: query row within the row tile; B/C: block within the tile
+  const int grp = lane >> 4;  // k-group of the lane
+  const uint4* mbase = reinterpret_cast<const uint4*>(meta + static_cast<size_t>(unit) * Nmax * 2 * D);
+  float* sbase = scores + static_cast<size_t>(unit) * Nmax;
+  constexpr int CHUNKS = 2 * D / 8;  // 16-byte chunks per block row pair
+  // Loads are unconditional (block indices clamped; results of blocks past the
+  // context are discarded), so every wait below covers exactly the older buffer.
+  auto load_c = [&](uint4* Bt, int tile, int nclamp) {
+    const int b = min(tile * 16 + col, nclamp - 1);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp];
+  };
+  // The first two tiles go out before the context length arrives: every block
+  // index below Nmax is in bounds, and the context only decides what is kept.
+  uint4 Ba[KSTEPS], Bb[KSTEPS];
+  load_c(Ba, t0, Nmax);
+  load_c(Bb, min(t0 + 1, t1max - 1), Nmax);
   const int n = ctx_len[unit / H];
   const int N = min((n + kBlock - 1) / kBlock, Nmax);  // context capacity bounds every index
   const int ntiles = (N + 15) / 16;
-  const int t0 = chunk * tpw;
   if (t0 >= ntiles) return;
   const int t1 = min(t0 + tpw, ntiles);
-  const int col = lane & 15;  // A: query row within the row tile; B/C: block within the tile
-  const int grp = lane >> 4;  // k-group of the lane
 
   // A operands.  Lane (col, grp) at k-step s covers metadata chunk 4s + grp (8
   // elements): kmin channels for s < HALF (paired with q-), kmax channels after
@@ -63,17 +79,7 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
     }
   }
 
-  const uint4* mbase = reinterpret_cast<const uint4*>(meta + static_cast<size_t>(unit) * Nmax * 2 * D);
-  float* sbase = scores + static_cast<size_t>(unit) * Nmax;
-  constexpr int CHUNKS = 2 * D / 8;  // 16-byte chunks per block row pair
-
-  // Loads are unconditional (the block index is clamped to N-1; results of
-  // blocks >= N are discarded), so the waits below only cover the older buffer.
-  auto load = [&](uint4* Bt, int tile) {
-    const int b = min(tile * 16 + col, N - 1);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp];
-  };
+  auto load = [&](uint4* Bt, int tile) { load_c(Bt, tile, N); };
   auto compute = [&](const uint4* Bt, int tile) {
     float best = -INFINITY;
 #pragma unroll
@@ -93,20 +99,23 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
     const int b = tile * 16 + col;
     if (grp == 0 && b < N) sbase[b] = best;
   };
-  // Ping-pong over two tile buffers.  The prefetch index is clamped and the
-  // loop body has no branch (an odd count repeats the last tile, whose store is
-  // identical), so every wait covers only the older buffer.
+  // Ping-pong over the two tile buffers: each processed buffer is refilled with
+  // the tile two ahead, the last pair without refills.  Indices are clamped and
+  // the loop body has no branch (a repeated last tile stores identical scores),
+  // so every wait covers exactly the older buffer.
   const int ntl = t1 - t0;
-  uint4 Ba[KSTEPS], Bb[KSTEPS];
-  load(Ba, t0);
-  for (int j = 0; j < ntl; j += 2) {
-    load(Bb, t0 + min(j + 1, ntl - 1));
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+  int j = 0;
+  for (; j + 2 < ntl; j += 2) {
     compute(Ba, t0 + j);
-    load(Ba, t0 + min(j + 2, ntl - 1));
+    load(Ba, t0 + j + 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of the next math
+    compute(Bb, t0 + j + 1);
+    load(Bb, t0 + min(j + 3, ntl - 1));
     __builtin_amdgcn_sched_barrier(0);
-    compute(Bb, t0 + min(j + 1, ntl - 1));
   }
+  // last pair: no refills
+  compute(Ba, t0 + j);
+  compute(Bb, t0 + min(j + 1, ntl - 1));
 }
 
 }  // namespace oasis

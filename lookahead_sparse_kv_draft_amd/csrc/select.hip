@@ -235,13 +235,18 @@ __device__ inline void topk_fast_body(const float* __restrict__ scores, const in
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
   const int unit = blockIdx.x;
+  const float* sc = scores + static_cast<size_t>(unit) * Nmax;
+  // The score loads go out before the context length arrives (every index below
+  // Nmax is in bounds; the context decides which keys take part).
+  float v[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + tid + 1, Nmax - 1)];
   const int n = ctx_len[unit / H];
   const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
   const int F0 = (N == 1) ? 1 : 2;
   const int C = max(0, N - 2);  // candidates are blocks 1 .. N-2
   const int m = min(kb - F0, C);
   int32_t* out = sel + static_cast<size_t>(unit) * kb;
-  const float* sc = scores + static_cast<size_t>(unit) * Nmax;
   if (tid == 0) {
     out[0] = 0;
     if (N > 1) out[1] = N - 1;
@@ -257,9 +262,6 @@ __device__ inline void topk_fast_body(const float* __restrict__ scores, const in
   if (m <= 0) return;  // uniform: every thread leaves together
 
   uint32_t key[KPT];
-  float v[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + tid, C - 1) + 1];  // unconditional loads
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
@@ -358,17 +360,22 @@ __device__ inline void topk_fast_body(const float* __restrict__ scores, const in
     }
   }
   __syncthreads();
-  // Output position = number of smaller winners (all keys distinct by index).
+  // Output position = number of smaller winners (all keys distinct by index),
+  // counted by P adjacent threads per winner and summed across their lanes.
   const int nw = m;
-  if (tid < nw) {
-    const unsigned long long mine = sh.win[tid];
-    int r = 0;
-    int j = 0;
-    for (; j + 8 <= nw; j += 8) {
+  const int P = (nw <= 64) ? 16 : (nw <= 128) ? 8 : (nw <= 256) ? 4 : (nw <= 512) ? 2 : 1;
+  const int wi = tid / P, part = tid & (P - 1);
+  const unsigned long long mine = (wi < nw) ? sh.win[wi] : 0ull;
+  int r = 0;
+  for (int j = part; j < nw; j += 4 * P) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) r += (sh.win[j + t] < mine) ? 1 : 0;
+    for (int t = 0; t < 4; ++t) {
+      const int jj = j + t * P;
+      r += (jj < nw && sh.win[min(jj, nw - 1)] < mine) ? 1 : 0;
     }
-    for (; j < nw; ++j) r += (sh.win[j] < mine) ? 1 : 0;
+  }
+  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+  if (part == 0 && wi < nw) {
     out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
     if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
   }
