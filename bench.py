@@ -238,7 +238,8 @@ def measure_h2(args, cfg, run, rt, replicas, sequential_step, h1_step_us):
             if not first:
                 cs.wait_event(ev_fetch[l])
             L.oasis_decode_step(rt.h, run.q[l, t + 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
-                                st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, cs)
+                                st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                st.n_attend, stream=cs)
             if count:
                 nf_tot.add_(st.n_fetch.sum())
             ev_sel[l].record(cs)
@@ -359,7 +360,7 @@ def main():
             L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, ps)
             ps.wait_event(ev_attn[l])
             L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                    st.evict, ps)
+                                    st.evict, st.attend, st.n_attend, stream=ps)
             ev_sel[l].record(ps)
 
     def sequential_step(i, cs):
@@ -371,7 +372,8 @@ def main():
             q = run.q[l, t + 1]
             st = rt.state[l][rep]
             L.oasis_decode_step(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
-                                st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, cs)
+                                st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                st.n_attend, stream=cs)
 
     cs0 = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -435,11 +437,12 @@ def main():
     # the compute stream, HIP events around the K calls (per-op durations for
     # the roofline; the op order inside a step does not matter for these)
     ops = {
-        "sparse_paged_decode_attn": lambda st, q: L.oasis_sparse_paged_decode_attn(
-            rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr, cs0),
+        "sparse_paged_decode_attn": lambda st, q: L.oasis_sparse_paged_decode_attn_list(
+            rt.h, q, st.pool, st.attend, st.n_attend, rt.ctx_len, rt.out, rt.ws_ptr, cs0),
         "lookahead_score": lambda st, q: L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, cs0),
         "select_and_diff": lambda st, q: L.oasis_select_and_diff(
-            rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, cs0),
+            rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, st.attend,
+            st.n_attend, stream=cs0),
     }
     avg = {}
     t1 = time.perf_counter()

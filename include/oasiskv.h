@@ -171,10 +171,16 @@ int oasis_topk_select(oasis_handle h, const float* scores, const int32_t* ctx_le
  * fetch [B][H][fetch_cap][2] = (block, slot) pairs, (-1, -1) padded; n_fetch
  * [B][H]; evict [B][H][fetch_cap] victim blocks in eviction order, -1 padded.
  * scores must be the ones sel was made from.
+ * attend [B][H][budget_blocks], n_attend [B][H] (optional: both or neither,
+ * EINVAL otherwise): the attended set of the next attention, S ∩ R once this
+ * step's fetch has landed ([EXPL] Figure 7 right), i.e. the selected blocks
+ * that stay resident or are fetched now, in rank order, each entry
+ * (block << 10) | slot; entries past n_attend are not written.
  */
 int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const float* scores,
                                   int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
-                                  int32_t* n_fetch, int32_t* evict, void* stream);
+                                  int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                                  void* stream);
 
 /*
  * oasis_topk_select followed by oasis_resident_diff_cap_evict on the same
@@ -185,7 +191,8 @@ int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const floa
  */
 int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
                           int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
-                          int32_t* n_fetch, int32_t* evict, void* stream);
+                          int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                          void* stream);
 
 /*
  * Fetch issue ([EXPL] Figure 8: the transfer lands in HBM before the layer's
@@ -230,26 +237,41 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                                    void* stream);
 
 /*
+ * The same attention with S ∩ R given as the attended list a diff produced
+ * (attend / n_attend of oasis_resident_diff_cap_evict, oasis_select_and_diff
+ * or oasis_decode_step): one load per entry instead of a selection lookup and a
+ * map lookup.  Same output and workspace contract; identical results to
+ * oasis_sparse_paged_decode_attn on the maps the list was made from.
+ */
+int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const void* pool,
+                                        const int32_t* attend, const int32_t* n_attend,
+                                        const int32_t* ctx_len, float* out, void* workspace,
+                                        void* stream);
+
+/*
  * One layer's decode step ([EXPL] Figure 8: at step t the layer's attention runs
  * over the resident part of S_t while the draft queries predict S_{t+1}; the
  * selection and the diff that produce the next fetch follow).  Equivalent to,
  * and bit-identical with, the sequence
  *   oasis_sparse_paged_decode_attn(q, pool, sel, block_to_slot, ctx_attn, out, workspace)
+ *     (oasis_sparse_paged_decode_attn_list(q, pool, attend, n_attend, ...) when attend is given)
  *   oasis_lookahead_score(q, meta, ctx_score, scores)
- *   oasis_select_and_diff(scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict)
+ *   oasis_select_and_diff(scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+ *                         attend, n_attend)
  * with the same arguments, on `stream`; the attention's split combine rides in
  * the scoring launch (three launches instead of four).  ctx_attn is the context
  * the attention sees (tokens < ctx_attn); ctx_score the context of the scoring
  * and selection (larger by one after an append of this step, which the caller
  * enqueues before this call; the attention does not read what it writes).
- * sel, block_to_slot and slot_to_block are read by the attention and rewritten
- * by the selection/diff afterwards.  Errors as for the three calls; every
+ * sel, block_to_slot and slot_to_block (and attend / n_attend when given: the
+ * list the previous step's diff left, which this step's diff replaces) are read
+ * by the attention and rewritten by the selection/diff afterwards.  Errors as for the three calls; every
  * argument is validated before any launch.
  */
 int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
                       const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
                       int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
-                      int32_t* n_fetch, int32_t* evict, void* stream);
+                      int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream);
 
 #ifdef __cplusplus
 }

@@ -55,11 +55,12 @@ SIGNATURES = {
     "oasis_block_meta_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
-    "oasis_resident_diff_cap_evict": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "oasis_select_and_diff": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_resident_diff_cap_evict": (_int, [_vp] * 11),
+    "oasis_select_and_diff": (_int, [_vp] * 12),
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "oasis_decode_step": (_int, [_vp] * 16),
+    "oasis_decode_step": (_int, [_vp] * 18),
+    "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
     "oasis_fetch_gather": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
@@ -200,15 +201,17 @@ def oasis_topk_select(h, scores, ctx_len, sel, stream=None):
 
 
 def oasis_resident_diff_cap_evict(h, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict,
-                                  stream=None):
+                                  attend=None, n_attend=None, stream=None):
     _call("oasis_resident_diff_cap_evict", h, _ptr(sel), _ptr(scores), _ptr(block_to_slot),
-          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _stream(stream))
+          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend),
+          _stream(stream))
 
 
 def oasis_select_and_diff(h, scores, ctx_len, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
-                          stream=None):
+                          attend=None, n_attend=None, stream=None):
     _call("oasis_select_and_diff", h, _ptr(scores), _ptr(ctx_len), _ptr(sel), _ptr(block_to_slot),
-          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _stream(stream))
+          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend),
+          _stream(stream))
 
 
 def oasis_sparse_paged_decode_attn(h, q, pool, sel, block_to_slot, ctx_len, out, workspace, stream=None):
@@ -217,7 +220,12 @@ def oasis_sparse_paged_decode_attn(h, q, pool, sel, block_to_slot, ctx_len, out,
 
 
 def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block, scores, out,
-                      workspace, fetch, n_fetch, evict, stream=None):
+                      workspace, fetch, n_fetch, evict, attend=None, n_attend=None, stream=None):
     _call("oasis_decode_step", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score), _ptr(sel),
           _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
-          _ptr(n_fetch), _ptr(evict), _stream(stream))
+          _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), _stream(stream))
+
+
+def oasis_sparse_paged_decode_attn_list(h, q, pool, attend, n_attend, ctx_len, out, workspace, stream=None):
+    _call("oasis_sparse_paged_decode_attn_list", h, _ptr(q), _ptr(pool), _ptr(attend), _ptr(n_attend),
+          _ptr(ctx_len), _ptr(out), _ptr(workspace), _stream(stream))

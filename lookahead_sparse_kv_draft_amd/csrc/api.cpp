@@ -147,6 +147,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
     tpw = static_cast<int>(std::max(1LL, std::min(16LL, tiles / 2048)));
   }
   c.score_tpw = tpw;
+  c.step_order = env_int("OASIS_STEP_ORDER", 0);
+  if (c.step_order < 0 || c.step_order > 2) c.step_order = 0;
+  c.step_launches = (env_int("OASIS_STEP_LAUNCHES", 2) == 3) ? 3 : 2;
   *out = h;
   return ok();
 }
@@ -299,10 +302,16 @@ int oasis_topk_select(oasis_handle h, const float* scores, const int32_t* ctx_le
                     "oasis_topk_select");
 }
 
+#define CHECK_ATTEND_PAIR(fn, a, n)                                                                   \
+  if (((a) == nullptr) != ((n) == nullptr))                                                           \
+    return fail(OASIS_EINVAL, fn ": attend and n_attend must both be given or both be null");
+
 int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const float* scores,
                                   int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
-                                  int32_t* n_fetch, int32_t* evict, void* stream) {
+                                  int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                                  void* stream) {
   CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_resident_diff_cap_evict", attend, n_attend);
   CHECK_PTR(sel);
   CHECK_PTR(scores);
   CHECK_PTR(block_to_slot);
@@ -313,14 +322,15 @@ int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const floa
     CHECK_PTR(evict);
   }
   return hip_status(oasis::launch_diff(h->c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch,
-                                       evict, static_cast<hipStream_t>(stream)),
+                                       evict, attend, n_attend, static_cast<hipStream_t>(stream)),
                     "oasis_resident_diff_cap_evict");
 }
 
 int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
                           int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch, int32_t* n_fetch,
-                          int32_t* evict, void* stream) {
+                          int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream) {
   CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_select_and_diff", attend, n_attend);
   CHECK_PTR(scores);
   CHECK_PTR(ctx_len);
   CHECK_PTR(sel);
@@ -334,11 +344,12 @@ int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ct
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (oasis::select_diff_fused_available(h->c))
     return hip_status(oasis::launch_select_diff(h->c, scores, ctx_len, sel, block_to_slot, slot_to_block, fetch,
-                                                n_fetch, evict, st),
+                                                n_fetch, evict, attend, n_attend, st),
                       "oasis_select_and_diff");
   hipError_t e = oasis::launch_topk(h->c, scores, ctx_len, sel, st);
   if (e == hipSuccess)
-    e = oasis::launch_diff(h->c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, st);
+    e = oasis::launch_diff(h->c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, attend,
+                           n_attend, st);
   return hip_status(e, "oasis_select_and_diff");
 }
 
@@ -392,9 +403,29 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
   CHECK_ALIGN16(pool);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(OASIS_EINVAL, "oasis_sparse_paged_decode_attn: workspace not 256-byte aligned");
-  return hip_status(oasis::launch_attn(h->c, q, pool, sel, block_to_slot, ctx_len, out, workspace,
-                                       static_cast<hipStream_t>(stream)),
+  return hip_status(oasis::launch_attn(h->c, q, pool, sel, block_to_slot, nullptr, nullptr, ctx_len, out,
+                                       workspace, static_cast<hipStream_t>(stream)),
                     "oasis_sparse_paged_decode_attn");
+}
+
+int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const void* pool, const int32_t* attend,
+                                        const int32_t* n_attend, const int32_t* ctx_len, float* out,
+                                        void* workspace, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(attend);
+  CHECK_PTR(n_attend);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_sparse_paged_decode_attn_list: workspace not 256-byte aligned");
+  return hip_status(oasis::launch_attn(h->c, q, pool, nullptr, nullptr, attend, n_attend, ctx_len, out,
+                                       workspace, static_cast<hipStream_t>(stream)),
+                    "oasis_sparse_paged_decode_attn_list");
 }
 
 int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch,
@@ -423,8 +454,9 @@ int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const 
 int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
                       const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
                       int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
-                      int32_t* n_fetch, int32_t* evict, void* stream) {
+                      int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream) {
   CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_decode_step", attend, n_attend);
   CHECK_PTR(q);
   CHECK_PTR(pool);
   CHECK_PTR(meta);
@@ -449,21 +481,34 @@ int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const voi
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (oasis::attn_needs_combine(c) && oasis::attn_and_score_fused_available(c) &&
+      oasis::select_diff_fused_available(c) && c.step_launches == 2) {
+    // two launches: attention + scoring, then selection + diff + split combine
+    e = oasis::launch_attn_and_score(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace,
+                                     meta, ctx_score, scores, st);
+    if (e == hipSuccess)
+      e = oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
+                                            evict, attend, n_attend, workspace, out, st);
+    return hip_status(e, "oasis_decode_step");
+  }
   if (c.s.dtype == OASIS_BF16 && oasis::attn_needs_combine(c)) {
-    e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, ctx_attn, out, workspace, st);
+    e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace, st);
     if (e == hipSuccess) e = oasis::launch_combine_and_score(c, workspace, out, q, meta, ctx_score, scores, st);
   } else {
-    e = oasis::launch_attn(c, q, pool, sel, block_to_slot, ctx_attn, out, workspace, st);
+    // the fp32 reference path attends from the maps (the list splits differently)
+    e = oasis::launch_attn(c, q, pool, sel, block_to_slot, c.s.dtype == OASIS_BF16 ? attend : nullptr,
+                           c.s.dtype == OASIS_BF16 ? n_attend : nullptr, ctx_attn, out, workspace, st);
     if (e == hipSuccess) e = oasis::launch_score(c, q, meta, ctx_score, scores, st);
   }
   if (e == hipSuccess) {
     if (oasis::select_diff_fused_available(c)) {
       e = oasis::launch_select_diff(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
-                                    st);
+                                    attend, n_attend, st);
     } else {
       e = oasis::launch_topk(c, scores, ctx_score, sel, st);
       if (e == hipSuccess)
-        e = oasis::launch_diff(c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, st);
+        e = oasis::launch_diff(c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, attend, n_attend,
+                               st);
     }
   }
   return hip_status(e, "oasis_decode_step");

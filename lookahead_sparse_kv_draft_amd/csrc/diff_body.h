@@ -24,7 +24,7 @@ namespace oasis {
 constexpr int kDiffMaxWaves = kMaxBudget / kWave;
 
 struct DiffShared {
-  int miss_tot[kDiffMaxWaves], free_tot[kDiffMaxWaves], cand_tot[kDiffMaxWaves];
+  int miss_tot[kDiffMaxWaves], free_tot[kDiffMaxWaves], cand_tot[kDiffMaxWaves], att_tot[kDiffMaxWaves];
 };
 
 // Dynamic LDS bytes of diff_body (8-byte aligned start).
@@ -36,10 +36,14 @@ __host__ __device__ inline size_t diff_lds_bytes(int kb, int Nmax, int cap) {
 // selL: LDS [kb], the selection in rank order (complete and visible on entry).
 // sb: block held by slot tid (slot_to_block, -1 = free; any value for tid >= kb);
 // sv: that block's score.  bu/slu: this unit's block_to_slot / slot_to_block rows.
+// attend / n_attend (optional, both or neither): the attended list the next
+// attention needs, i.e. the selected blocks resident once this step's fetch has
+// landed, in rank order, packed block << 10 | slot, and its length.
 __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int32_t* selL, int sb, float sv,
                                  int32_t* __restrict__ bu, int32_t* __restrict__ slu,
                                  int32_t* __restrict__ fetch, int32_t* __restrict__ n_fetch,
-                                 int32_t* __restrict__ evict, unsigned long long* lds, DiffShared& sh) {
+                                 int32_t* __restrict__ evict, int32_t* __restrict__ attend,
+                                 int32_t* __restrict__ n_attend, unsigned long long* lds, DiffShared& sh) {
   unsigned long long* ckey = lds;                            // [kb] candidate key per slot (0 = none)
   const int nwords = (Nmax + 31) / 32;
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(ckey + kb);  // [nwords] selected blocks
@@ -144,6 +148,25 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
     eu[j] = (j < need) ? vict[j] : -1;
   }
   if (tid == 0) n_fetch[unit] = nF;
+
+  // 5. the attended list for the next attention: selected blocks that stay
+  // resident (a resident selected block is never a victim) or are fetched now
+  if (attend != nullptr) {
+    int slot_after = -1;
+    if (bok) slot_after = (res >= 0) ? res : ((miss && mrank < nF) ? tgt[mrank] : -1);
+    const bool att = in && slot_after >= 0 && slot_after < kb;
+    const uint64_t ba = __ballot(att);
+    if (lane == 0) sh.att_tot[w] = __popcll(ba);
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int j = 0; j < nw; ++j) {
+      const int a = sh.att_tot[j];
+      off += (j < w) ? a : 0;
+      tot += a;
+    }
+    if (att) attend[static_cast<size_t>(unit) * kb + off + __popcll(ba & below)] = (b << kAttendSlotBits) | slot_after;
+    if (tid == 0) n_attend[unit] = tot;
+  }
 }
 
 }  // namespace oasis

@@ -13,6 +13,7 @@ constexpr int kBlock = 16;     // tokens per KV block
 constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kMaxRows = 64;   // query rows per unit handled by the kernels (4 MFMA row tiles)
 constexpr int kMaxBudget = 1024;
+constexpr int kAttendSlotBits = 10;   // attended-list entry = block << 10 | slot (slot < kMaxBudget)
 constexpr int kAttnMaxSplits = 32;  // attention splits per unit (merge statistics kept in LDS)
 
 struct Ctx {
@@ -29,6 +30,8 @@ struct Ctx {
   int attn_waves;   // wavefronts per attention workgroup (1, 2 or 4)
   int attn_pf;      // pages in flight per attention wavefront (2, 4 or 8)
   int score_tpw;    // 16-block tiles per wave in the score kernel
+  int step_order;   // workgroup order of the fused attention + score launch (0, 1, 2)
+  int step_launches;  // launches per decode step: 2 (fused attention + score) or 3
 };
 
 // ---- kernel launchers (defined in the .hip files); return a hipError_t ----
@@ -45,18 +48,33 @@ hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len
 bool select_diff_fused_available(const Ctx& c);
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
-                              hipStream_t st);
+                              int32_t* attend, int32_t* n_attend, hipStream_t st);
 hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, int32_t* b2s,
                        int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
-                       hipStream_t st);
+                       int32_t* attend, int32_t* n_attend, hipStream_t st);
+// Attention over S ∩ R given either (sel, b2s) or, when attend is not null, the
+// attended list a diff produced (sel and b2s are then ignored).
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
-                       const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
-                       hipStream_t st);
+                       const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
+                       const int32_t* ctx_len, float* out, void* ws, hipStream_t st);
 // The attention without its split combine, and whether a combine must follow.
 hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
-                            const int32_t* b2s, const int32_t* ctx_len, float* out, void* ws,
-                            hipStream_t st);
+                            const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
+                            const int32_t* ctx_len, float* out, void* ws, hipStream_t st);
 bool attn_needs_combine(const Ctx& c);
+// The attention (split partials) and the lookahead score in one launch (bf16,
+// 2-wavefront 2-page attention, up to three attention row tiles).
+bool attn_and_score_fused_available(const Ctx& c);
+hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                                 const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
+                                 const int32_t* ctx_attn, float* out, void* ws, const void* meta,
+                                 const int32_t* ctx_score, float* scores, hipStream_t st);
+// The fused selection + diff and the attention's split combine in one launch
+// (where select_diff_fused_available holds).
+hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                                      int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
+                                      int32_t* attend, int32_t* n_attend, const void* ws, float* out,
+                                      hipStream_t st);
 // The split combine and the lookahead score in one launch (bf16 only).
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st);

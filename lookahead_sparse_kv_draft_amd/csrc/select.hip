@@ -33,6 +33,7 @@
 //   * each winner's output position is the number of smaller winners, counted
 //     with unrolled broadcast reads of the winner list.
 #include "block_ops.h"
+#include "attn_combine.h"
 #include "diff_body.h"
 
 namespace oasis {
@@ -395,7 +396,8 @@ template <int KPT>
 __global__ __launch_bounds__(1024) void select_diff_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
-    int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int H, int Nmax, int kb, int cap) {
+    int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap) {
   extern __shared__ unsigned long long smem_u64[];
   int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   __shared__ TopkFastShared sh;
@@ -409,7 +411,72 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
   topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, selL, sh);
   __syncthreads();
   diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
-            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, smem_u64, dsh);
+            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
+}
+
+// The fused selection + diff in workgroups [0, units), then the attention's
+// split combine, sixteen query rows per workgroup, in the rest.
+template <int KPT, int D, int SMAX>
+__global__ __launch_bounds__(1024) void select_diff_combine_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
+    int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
+    int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int units,
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, float* __restrict__ out, int arows,
+    int splits, int comb_total) {
+  if (static_cast<int>(blockIdx.x) >= units) {
+    attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, arows, splits, comb_total,
+                              (blockIdx.x - units) * kTkWaves + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
+    return;
+  }
+  extern __shared__ unsigned long long smem_u64[];
+  int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
+  __shared__ TopkFastShared sh;
+  __shared__ DiffShared dsh;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
+  const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
+  const bool sok = sb >= 0 && sb < Nmax;
+  const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
+  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, selL, sh);
+  __syncthreads();
+  diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
+            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
+}
+
+template <int KPT, int D, int SMAX>
+hipError_t sdc_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
+                 int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+  const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
+  const size_t lds = diff_lds_bytes(kb, c.s.max_blocks, cap) + static_cast<size_t>(kb) * 4;
+  const int comb_total = c.units * c.rows_attn;
+  const int ncomb = (comb_total + kTkWaves - 1) / kTkWaves;
+  hipLaunchKernelGGL((select_diff_combine_kernel<KPT, D, SMAX>), dim3(c.units + ncomb), dim3(kTkThreads), lds, st,
+                     scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads,
+                     c.s.max_blocks, kb, cap, c.units, ws_acc, ws_ml, out, c.rows_attn, c.attn_splits, comb_total);
+  return hipGetLastError();
+}
+
+template <int KPT, int D>
+hipError_t sdc_s(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
+                 int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+  const int S = c.attn_splits;
+  if (S <= 4) return sdc_t<KPT, D, 4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (S <= 8) return sdc_t<KPT, D, 8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (S <= 16) return sdc_t<KPT, D, 16>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  return sdc_t<KPT, D, 32>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+}
+
+template <int KPT>
+hipError_t sdc_d(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
+                 int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+  return c.s.head_dim == 128
+             ? sdc_s<KPT, 128>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st)
+             : sdc_s<KPT, 64>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
 }
 
 template <int KPT>
@@ -421,11 +488,12 @@ hipError_t fast_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int
 
 template <int KPT>
 hipError_t select_diff_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
-                         int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, hipStream_t st) {
+                         int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                         int32_t* n_attend, hipStream_t st) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
   const size_t lds = diff_lds_bytes(kb, c.s.max_blocks, cap) + static_cast<size_t>(kb) * 4;
   hipLaunchKernelGGL((select_diff_kernel<KPT>), dim3(c.units), dim3(kTkThreads), lds, st, scores, ctx_len, sel,
-                     b2s, s2b, fetch, n_fetch, evict, c.s.kv_heads, c.s.max_blocks, kb, cap);
+                     b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap);
   return hipGetLastError();
 }
 
@@ -437,12 +505,25 @@ bool select_diff_fused_available(const Ctx& c) {
 
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
-                              hipStream_t st) {
+                              int32_t* attend, int32_t* n_attend, hipStream_t st) {
   const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
-  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
-  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
-  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
-  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, st);
+  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+}
+
+hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                                      int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
+                                      int32_t* attend, int32_t* n_attend, const void* ws, float* out,
+                                      hipStream_t st) {
+  const float* ws_acc = static_cast<const float*>(ws);
+  const float* ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + attn_ws_acc_bytes(c));
+  const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
+  if (kpt <= 1) return sdc_d<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (kpt <= 2) return sdc_d<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (kpt <= 4) return sdc_d<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  return sdc_d<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
 }
 
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,

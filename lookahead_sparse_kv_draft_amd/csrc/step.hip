@@ -1,13 +1,17 @@
-// One layer's decode step in three launches (OasisKV explainer, Figure 8: at
-// step t the layer's attention runs over the resident part of S_t while the
-// draft queries predict S_{t+1}; selection, diff and transfer follow).
+// One layer's decode step (OasisKV explainer, Figure 8: at step t the layer's
+// attention runs over the resident part of S_t while the draft queries predict
+// S_{t+1}; selection, diff and transfer follow).  The attention and the
+// lookahead scoring need only step t's inputs and neither reads the other's
+// output, so they can share a launch; the attention's split combine is small
+// and rides with whatever launch follows the attention.
 //
-//   1. attention over the resident selected blocks (split partials),
-//   2. the attention's split combine and the lookahead scoring in ONE launch:
-//      both only need step t's inputs and neither reads the other's output, so
-//      the small combine rides in the first workgroups of the scoring grid
-//      instead of paying a launch, ramp-up and drain of its own,
-//   3. top-k selection and the resident-set diff.
+// Two launches (default shape):
+//   1. attention (split partials) and scoring in ONE grid: the scoring streams
+//      while the attention is in its latency-bound start and tail,
+//   2. top-k selection and the resident-set diff, with the split combine in
+//      the workgroups after the selection's.
+// Three launches (other shapes): attention; combine + scoring; select + diff.
+#include "attn_body.h"
 #include "attn_combine.h"
 #include "score_body.h"
 
@@ -30,6 +34,89 @@ __global__ __launch_bounds__(256) void combine_score_kernel(
   }
   score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, rows, Nmax, wpu, tpw, total_waves,
                     (blockIdx.x - ncomb_wg) * 4 + wv, lane);
+}
+
+// Attention (2 wavefronts, 2-page ring) and scoring workgroups in one grid of
+// 128-thread workgroups.  order 0: attention workgroups first; 1: scoring
+// first; 2: interleaved one for one while both last.
+template <int D, int RTA, int RTS>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 2 : 1))) void attn_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend, const int32_t* __restrict__ n_attend,
+    const int32_t* __restrict__ ctx_attn, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    float* __restrict__ out, int H, int arows, int Nmax, int kb, int splits, int run, float scale_log2,
+    const uint16_t* __restrict__ meta, const int32_t* __restrict__ ctx_score, float* __restrict__ scores, int G,
+    int T, int ndraft, int srows, int wpu, int tpw, int total_waves, int n_attn_wg, int n_score_wg, int order) {
+  const int bid = blockIdx.x;
+  bool is_attn;
+  int idx;
+  if (order == 0) {
+    is_attn = bid < n_attn_wg;
+    idx = is_attn ? bid : bid - n_attn_wg;
+  } else if (order == 1) {
+    is_attn = bid >= n_score_wg;
+    idx = is_attn ? bid - n_score_wg : bid;
+  } else {
+    const int m = min(n_attn_wg, n_score_wg);
+    if (bid < 2 * m) {
+      is_attn = (bid & 1) == 0;
+      idx = bid >> 1;
+    } else {
+      is_attn = n_attn_wg > m;
+      idx = m + (bid - 2 * m);
+    }
+  }
+  if (is_attn) {
+    attn_wg<D, RTA, 2, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
+                          splits, run, scale_log2, idx);
+  } else {
+    score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, srows, Nmax, wpu, tpw, total_waves,
+                       idx * 2 + static_cast<int>(threadIdx.x) / kWave, threadIdx.x & (kWave - 1));
+  }
+}
+
+template <int D, int RTA, int RTS>
+hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  const int n_attn_wg = c.units * c.attn_splits;
+  const int wpu = score_waves_per_unit(c);
+  const int total = c.units * wpu;
+  const int n_score_wg = (total + 1) / 2;
+  hipLaunchKernelGGL((attn_score_kernel<D, RTA, RTS>), dim3(n_attn_wg + n_score_wg), dim3(128), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s, attend,
+                     n_attend, ctx_attn, ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.s.max_blocks,
+                     c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2, static_cast<const uint16_t*>(meta),
+                     ctx_score, scores, c.s.group, c.T, c.s.n_draft, c.rows_score, wpu, c.score_tpw, total,
+                     n_attn_wg, n_score_wg, c.step_order);
+  return hipGetLastError();
+}
+
+template <int D, int RTA>
+hipError_t as_s(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                hipStream_t st) {
+  switch ((c.rows_score + 15) / 16) {
+    case 1: return as_t<D, RTA, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 2: return as_t<D, RTA, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 3: return as_t<D, RTA, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    default: return as_t<D, RTA, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+  }
+}
+
+template <int D>
+hipError_t as_d(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                hipStream_t st) {
+  switch ((c.rows_attn + 15) / 16) {
+    case 1: return as_s<D, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 2: return as_s<D, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    default: return as_s<D, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+  }
 }
 
 template <int D, int RT, int SMAX>
@@ -69,6 +156,24 @@ hipError_t cs_d(const Ctx& c, const float* ws_acc, const float* ws_ml, float* ou
 }
 
 }  // namespace
+
+bool attn_and_score_fused_available(const Ctx& c) {
+  return c.s.dtype == OASIS_BF16 && c.attn_waves == 2 && c.attn_pf == 2 && c.rows_attn <= 48;
+}
+
+hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+                                 const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
+                                 const int32_t* ctx_attn, float* out, void* ws, const void* meta,
+                                 const int32_t* ctx_score, float* scores, hipStream_t st) {
+  if (!attn_and_score_fused_available(c)) return hipErrorInvalidValue;
+  float* ws_acc = static_cast<float*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
+  return c.s.head_dim == 128
+             ? as_d<128>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score,
+                         scores, st)
+             : as_d<64>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score,
+                        scores, st);
+}
 
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st) {

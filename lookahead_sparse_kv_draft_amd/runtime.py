@@ -89,6 +89,9 @@ class LayerState:
         self.fetch = torch.full((u, max(cap, 1), 2), -1, dtype=torch.int32, device=dev)
         self.n_fetch = torch.zeros(u, dtype=torch.int32, device=dev)
         self.evict = torch.full((u, max(cap, 1)), -1, dtype=torch.int32, device=dev)
+        # attended list for the next attention (written by every diff)
+        self.attend = torch.full((u, k), -1, dtype=torch.int32, device=dev)
+        self.n_attend = torch.zeros(u, dtype=torch.int32, device=dev)
         self.host_tier = host_tier
         self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
         self.n_fetch_host = torch.empty(u, dtype=torch.int32, pin_memory=True)
@@ -102,7 +105,8 @@ class LayerState:
         self.select_pending = False
 
     def copy_from(self, other: "LayerState"):
-        for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict"):
+        for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict", "attend",
+                     "n_attend"):
             getattr(self, name).copy_(getattr(other, name))
 
 
@@ -239,7 +243,7 @@ class DecodeRuntime:
             L.oasis_destroy(h_all)
         for st in self.state[layer]:
             L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                            st.evict)
+                                            st.evict, st.attend, st.n_attend)
         self.transfer(layer, stream=torch.cuda.current_stream())
 
     # ------------------------------------------------------------ per-step chain
@@ -277,7 +281,7 @@ class DecodeRuntime:
             st.select_pending = False
         L.oasis_decode_step(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s, st.s2b,
                             st.scores, self.out if out is None else out, self.ws_ptr, st.fetch, st.n_fetch,
-                            st.evict, cs)
+                            st.evict, st.attend, st.n_attend, stream=cs)
 
     def append(self, layer: int, k_new_dev, v_new_dev, k_new_host=None, v_new_host=None,
                replica: int = 0):
@@ -326,11 +330,11 @@ class DecodeRuntime:
             ps.wait_event(st.attn_done)
         if self.fused_select:
             L.oasis_select_and_diff(self.h, st.scores, ctx, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                    st.evict, ps)
+                                    st.evict, st.attend, st.n_attend, stream=ps)
         else:
             L.oasis_topk_select(self.h, st.scores, ctx, st.sel, ps)
             L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                            st.evict, ps)
+                                            st.evict, st.attend, st.n_attend, stream=ps)
         if self.overlap:
             st.select_done.record(ps)
             st.select_pending = True

@@ -69,19 +69,24 @@ def test_sizes_and_null_checks():
         assert lib.oasis_lookahead_score(h, None, None, None, None, None) == L.OASIS_EINVAL
         assert "null" in L.oasis_last_error()
         assert lib.oasis_topk_select(h, None, None, None, None) == L.OASIS_EINVAL
-        assert lib.oasis_resident_diff_cap_evict(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_resident_diff_cap_evict(h, *([None] * 10)) == L.OASIS_EINVAL
         assert lib.oasis_sparse_paged_decode_attn(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_update(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_build(h, None, None, 0, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_lookahead_score(None, 16, 16, 16, 16, None) == L.OASIS_EINVAL
-        assert lib.oasis_select_and_diff(h, None, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
-        assert lib.oasis_decode_step(h, *([None] * 15)) == L.OASIS_EINVAL
+        assert lib.oasis_select_and_diff(h, *([None] * 11)) == L.OASIS_EINVAL
+        assert lib.oasis_decode_step(h, *([None] * 17)) == L.OASIS_EINVAL
+        assert lib.oasis_sparse_paged_decode_attn_list(h, *([None] * 8)) == L.OASIS_EINVAL
         assert lib.oasis_fetch_gather(h, None, None, None, None, None) == L.OASIS_EINVAL
+        # the attended list and its length come together or not at all
+        assert lib.oasis_select_and_diff(h, *([256] * 8), 256, None, None) == L.OASIS_EINVAL
+        assert "attend" in L.oasis_last_error()
+        assert lib.oasis_resident_diff_cap_evict(h, *([256] * 7), None, 256, None) == L.OASIS_EINVAL
         # a host tier that is not pinned, device-mapped memory is refused before any launch
         plain = np.zeros(4096, dtype=np.uint8)
         assert lib.oasis_fetch_gather(h, plain.ctypes.data, 256, 256, 256, None) == L.OASIS_EINVAL
         # one missing pointer among valid-looking ones, and a misaligned workspace
-        good = [256] * 15
+        good = [256] * 17
         for i in range(11):  # q .. workspace, then n_fetch
             args = list(good)
             args[i] = None
@@ -90,6 +95,9 @@ def test_sizes_and_null_checks():
         args[10] = 272  # workspace 16- but not 256-byte aligned
         assert lib.oasis_decode_step(h, *args) == L.OASIS_EINVAL
         assert "workspace" in L.oasis_last_error()
+        args = list(good)
+        args[15] = None  # n_attend without attend's partner
+        assert lib.oasis_decode_step(h, *args) == L.OASIS_EINVAL
         # misaligned device pointers
         assert lib.oasis_lookahead_score(h, 18, 32, 16, 16, None) == L.OASIS_EINVAL
         assert "aligned" in L.oasis_last_error()

@@ -82,10 +82,23 @@ def _state_snapshot(run):
     ("tiny", dict(steps=4)),                                              # f32
 ])
 def test_decode_step_matches_separate_calls(name, kw):
-    """The single decode-step call (attention, then the split combine and the
-    scoring in one launch, then selection and diff) leaves bit-identical outputs
-    and state to the separate entry points, step after step."""
-    cfg = CONFIGS[name].with_(**kw)
+    """The single decode-step call (attention and scoring in one launch, then
+    selection, diff and the split combine) leaves bit-identical outputs and
+    state to the separate entry points, step after step."""
+    _decode_step_vs_separate(CONFIGS[name].with_(**kw))
+
+
+@pytest.mark.parametrize("launches,order", [(2, 1), (2, 2), (3, 0)])
+def test_decode_step_launch_variants(launches, order, monkeypatch):
+    """Both workgroup orders of the fused attention + scoring launch other than
+    the default, and the three-launch step, give the same bit-identical result."""
+    monkeypatch.setenv("OASIS_STEP_LAUNCHES", str(launches))
+    monkeypatch.setenv("OASIS_STEP_ORDER", str(order))
+    _decode_step_vs_separate(CONFIGS["llama8b_32k"].with_(batch=2, ctx=16 * 300 + 7, steps=4, fetch_cap=8,
+                                                          planted=15, budget_tokens=16 * 32))
+
+
+def _decode_step_vs_separate(cfg):
     runs = [SyntheticRun(cfg, overlap=False, fused_step=f) for f in (True, False)]
     try:
         for r in runs:

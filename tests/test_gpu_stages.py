@@ -136,12 +136,19 @@ def test_diff_parity(k, cap, N, kind):
     fetch = torch.full((units, cw, 2), -9, dtype=torch.int32, device="cuda")
     nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
     ev = torch.full((units, cw), -9, dtype=torch.int32, device="cuda")
-    L.oasis_resident_diff_cap_evict(h, sel_d, sc_d, b2s_d, s2b_d, fetch, nf, ev)
+    att = torch.full((units, k), -9, dtype=torch.int32, device="cuda")
+    natt = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+    L.oasis_resident_diff_cap_evict(h, sel_d, sc_d, b2s_d, s2b_d, fetch, nf, ev, att, natt)
     torch.cuda.synchronize()
     g_b2s, g_s2b = b2s_d.cpu().numpy(), s2b_d.cpu().numpy()
     g_f, g_nf, g_ev = fetch.cpu().numpy(), nf.cpu().numpy(), ev.cpu().numpy()
+    g_att, g_natt = att.cpu().numpy(), natt.cpu().numpy()
     for u in range(units):
         ref = O.resident_diff_cap_evict(sels[u], scs[u].astype(np.float64), b2ss[u], s2bs[u], cap)
+        # attended list of the next attention: S ∩ R after this fetch, rank order
+        exp_att = [(b << 10) | int(ref.block_to_slot[b]) for b in O.attended_blocks(sels[u], ref.block_to_slot)]
+        assert g_natt[u] == len(exp_att), u
+        assert list(g_att[u][: len(exp_att)]) == exp_att, u
         assert g_nf[u] == len(ref.fetch)
         exp_f = np.full((cw, 2), -9 if cap == 0 else -1)
         for i, (b, s) in enumerate(ref.fetch):
@@ -220,8 +227,7 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatc
     L.oasis_fetch_issue(rt.h, st.host_tier, st.pool, fetch, nfe, torch.cuda.current_stream())
     torch.cuda.synchronize()
     q_d = U.to_dev(dtype, q)
-    # three calls in a row: the split arrival counters must be back at zero
-    # after every call, so every call gives the same output
+    # repeated calls give the same output (deterministic merge)
     outs = []
     for _ in range(3):
         rt.out.fill_(float("nan"))
@@ -230,6 +236,22 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatc
         outs.append(rt.out.cpu().numpy().astype(np.float64))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     got = outs[0]
+    # the attended-list entry point, on the list the maps define, is bit-identical
+    att = np.full((units, k), -1, dtype=np.int32)
+    natt = np.zeros(units, dtype=np.int32)
+    for u in range(units):
+        lst = [(int(b) << 10) | int(b2s[u, b]) for b in O.attended_blocks(sel[u], b2s[u])]
+        natt[u] = len(lst)
+        att[u, : len(lst)] = lst
+    rt.out.fill_(float("nan"))
+    L.oasis_sparse_paged_decode_attn_list(rt.h, q_d, st.pool, U.i32(att), U.i32(natt), rt.ctx_len, rt.out,
+                                          rt.ws_ptr)
+    torch.cuda.synchronize()
+    got_list = rt.out.cpu().numpy().astype(np.float64)
+    if dtype == "bf16":
+        assert np.array_equal(got_list, got)
+    else:  # the fp32 kernel splits the list, not the selection: same sums, another order
+        assert np.allclose(got_list, got, rtol=1e-5, atol=1e-6)
     for u in range(units):
         r, hh = divmod(u, H)
         A = O.attended_blocks(sel[u], b2s[u])
@@ -509,17 +531,22 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
         fetch = torch.full((units, cw, 2), -9, dtype=torch.int32, device="cuda")
         nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
         ev = torch.full((units, cw), -9, dtype=torch.int32, device="cuda")
+        att = torch.full((units, k), -9, dtype=torch.int32, device="cuda")
+        natt = torch.full((units,), -9, dtype=torch.int32, device="cuda")
         sc_d, ctx_d = torch.from_numpy(sc).cuda(), U.i32(ctxs)
         if fused:
-            L.oasis_select_and_diff(h, sc_d, ctx_d, sel, b2s, s2b, fetch, nf, ev)
+            L.oasis_select_and_diff(h, sc_d, ctx_d, sel, b2s, s2b, fetch, nf, ev, att, natt)
         else:
             L.oasis_topk_select(h, sc_d, ctx_d, sel)
-            L.oasis_resident_diff_cap_evict(h, sel, sc_d, b2s, s2b, fetch, nf, ev)
+            L.oasis_resident_diff_cap_evict(h, sel, sc_d, b2s, s2b, fetch, nf, ev, att, natt)
         torch.cuda.synchronize()
-        outs.append([x.cpu().numpy() for x in (sel, b2s, s2b, fetch, nf, ev)])
+        na = natt.cpu().numpy()
+        am = att.cpu().numpy()
+        am = [list(am[u][: na[u]]) for u in range(units)]
+        outs.append([x.cpu().numpy() for x in (sel, b2s, s2b, fetch, nf, ev, natt)] + [am])
     for a, b in zip(*outs):
-        assert np.array_equal(a, b)
-    sel, b2s, s2b, fetch, nf, ev = outs[1]
+        assert (a == b) if isinstance(a, list) else np.array_equal(a, b)
+    sel, b2s, s2b, fetch, nf, ev, natt, am = outs[1]
     for u in range(units):
         N = (ctxs[u // H] + BLK - 1) // BLK
         ref_sel = O.topk_select(sc[u].astype(np.float64), N, k)
@@ -529,4 +556,5 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
         assert [tuple(p) for p in fetch[u][: nf[u]]] == ref.fetch, u
         assert list(ev[u][: len(ref.evict)]) == ref.evict
         assert np.array_equal(b2s[u], ref.block_to_slot) and np.array_equal(s2b[u], ref.slot_to_block)
+        assert am[u] == [(b << 10) | int(ref.block_to_slot[b]) for b in O.attended_blocks(ref_sel, ref.block_to_slot)]
     L.oasis_destroy(h)
