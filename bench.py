@@ -33,10 +33,16 @@ MALL_BYTES = 256 * 2**20
 CALIB_ELEMS = 2**28  # float32: 1 GiB
 CSRC = os.path.join(ROOT, "lookahead_sparse_kv_draft_amd", "csrc")
 # source files of each op's kernels (a traffic measurement is valid while they are unchanged)
-OP_SOURCES = {"sparse_paged_decode_attn": ["attn.hip"], "lookahead_score": ["score.hip"],
+OP_SOURCES = {"attend_and_score": ["step.hip", "attn_body.h", "score_body.h"],
+              "select_diff_combine": ["select.hip", "diff_body.h", "block_ops.h", "attn_combine.h"],
+              "sparse_paged_decode_attn": ["attn.hip", "attn_body.h", "attn_combine.h"],
+              "lookahead_score": ["score.hip", "score_body.h"],
               "select_and_diff": ["select.hip", "diff_body.h", "block_ops.h"]}
-OP_KERNELS = {"sparse_paged_decode_attn": ["attn_mfma_kernel", "attn_combine_kernel"],
+OP_KERNELS = {"attend_and_score": ["attn_score_kernel"], "select_diff_combine": ["select_diff_combine_kernel"],
+              "sparse_paged_decode_attn": ["attn_mfma_kernel", "attn_combine_kernel"],
               "lookahead_score": ["score_mfma_kernel"], "select_and_diff": ["select_diff_kernel"]}
+# the two launches of the decode step, then the stages on their own
+OPS = ["attend_and_score", "select_diff_combine", "sparse_paged_decode_attn", "lookahead_score", "select_and_diff"]
 
 
 def parse():
@@ -68,8 +74,10 @@ def algorithmic_bytes(cfg, attended_blocks: int):
     score = units * N * 2 * d * e + units * N * 4 + cfg.batch * cfg.q_heads * cfg.n_draft * d * e
     attn = (attended_blocks * 2 * 16 * d * e + cfg.batch * cfg.q_heads * cfg.T * d * (e + 4)
             + units * cfg.k * 8)
-    return {"lookahead_score": score, "sparse_paged_decode_attn": attn,
-            "select_and_diff": units * N * 4 + units * cfg.k * 4 * 5 + units * cfg.fetch_cap * 12}
+    sel_diff = units * N * 4 + units * cfg.k * 4 * 5 + units * cfg.fetch_cap * 12
+    out = cfg.batch * cfg.q_heads * cfg.T * d * 4  # the attention output, written by the split combine
+    return {"lookahead_score": score, "sparse_paged_decode_attn": attn, "select_and_diff": sel_diff,
+            "attend_and_score": attn - out + score, "select_diff_combine": sel_diff + out}
 
 
 def attn_flops(cfg, attended_blocks: int):
@@ -182,7 +190,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, out: str, cmdline: str):
     lines = [f"# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, llama8b_32k",
              "# counters: cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'oasis|elementwise' "
              "--output-format csv -d <dir> -o f -- python <repo>/bench.py --steps 8 --warmup 2 --no-cpu-baseline "
-             "--calib-copy  (then the same with WRITE_SIZE and -o w)",
+             "--no-h2 --calib-copy  (then the same with WRITE_SIZE and -o w)",
              f"# summary: {cmdline}",
              f"calibration {short.replace(' ', '')} fetch_kib {fe[c]:.1f} write_kib {wr[c]:.1f} "
              f"expected_kib {gib_kib:.1f} fetch_factor {f_fac:.4f} write_factor {w_fac:.4f}"]
@@ -337,7 +345,7 @@ def main():
     torch.cuda.synchronize()
     print("# prologue done", file=sys.stderr, flush=True)
 
-    names = ["sparse_paged_decode_attn", "lookahead_score", "select_and_diff"]
+    names = OPS
     ps = rt.pstream
     ev_attn = [torch.cuda.Event() for _ in range(run.L)]
     ev_sel = [torch.cuda.Event() for _ in range(run.L)]
@@ -365,7 +373,8 @@ def main():
 
     def sequential_step(i, cs):
         """One decode step over all layers: the single decode-step call per layer
-        (attention, split combine + scoring in one launch, selection + diff)."""
+        (attention beside the scoring in one launch; selection, diff and the
+        attention's split combine in the second)."""
         rep = i % replicas
         t = i % cfg.steps
         for l in range(run.L):
@@ -437,6 +446,12 @@ def main():
     # the compute stream, HIP events around the K calls (per-op durations for
     # the roofline; the op order inside a step does not matter for these)
     ops = {
+        "attend_and_score": lambda st, q: L.oasis_attend_and_score(
+            rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.attend, st.n_attend, st.scores,
+            rt.out, rt.ws_ptr, cs0),
+        "select_diff_combine": lambda st, q: L.oasis_select_diff_combine(
+            rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, st.attend,
+            st.n_attend, rt.out, rt.ws_ptr, cs0),
         "sparse_paged_decode_attn": lambda st, q: L.oasis_sparse_paged_decode_attn_list(
             rt.h, q, st.pool, st.attend, st.n_attend, rt.ctx_len, rt.out, rt.ws_ptr, cs0),
         "lookahead_score": lambda st, q: L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, cs0),
@@ -448,6 +463,8 @@ def main():
     t1 = time.perf_counter()
     for n in names:
         e_beg, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for l in range(run.L):  # untimed first call: loads the op's code objects
+            ops[n](rt.state[l][0], run.q[l, 1])
         torch.cuda.synchronize()
         e_beg.record(cs0)
         for i in range(args.steps):
@@ -486,7 +503,7 @@ def main():
     for n in names:
         gbs = ab[n] / avg[n] / 1e9
         kern[n] = {"avg_us": avg[n] * 1e6, "bytes": ab[n], "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
-    dominant = max(["sparse_paged_decode_attn", "lookahead_score"], key=lambda n: avg[n])
+    dominant = "attend_and_score"  # the step's first launch: attention beside the scoring, ~3/4 of the step
     traffic = load_traffic(cfg.name)
     for n in names:
         kern[n]["traffic_bytes"] = traffic.get(n)
@@ -516,8 +533,8 @@ def main():
         "kernels": kern,
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
-                      "eager": "one decode-step call per layer (3 launches) on one stream"}[args.mode],
-        "hbm_bytes_per_step": sum(ab[n] for n in names) * run.L,
+                      "eager": "one decode-step call per layer (2 launches) on one stream"}[args.mode],
+        "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
         "decode_step_call_us": step_call_us,
         "h2": h2,
     }

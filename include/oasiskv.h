@@ -249,6 +249,38 @@ int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const voi
                                         void* stream);
 
 /*
+ * The first launch of a layer's decode step ([EXPL] Figure 8: at step t the
+ * attention over the resident part of S_t and the drafts' prediction of S_{t+1}
+ * need only step t's inputs): the sparse paged decode attention (as
+ * oasis_sparse_paged_decode_attn, or _list when attend is given) and the
+ * lookahead scoring (as oasis_lookahead_score with ctx_score) in ONE grid where
+ * the shape allows it (bf16, the default 2-wavefront attention, at most 48
+ * attention rows), else back to back.  The attention leaves its split partials
+ * in the workspace; `out` is complete after oasis_attn_combine or
+ * oasis_select_diff_combine on the same workspace (which do nothing when the
+ * attention has a single split and wrote `out` itself).  sel/block_to_slot may
+ * be null when attend is given.
+ */
+int oasis_attend_and_score(oasis_handle h, const void* q, const void* pool, const void* meta,
+                           const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* sel,
+                           const int32_t* block_to_slot, const int32_t* attend, const int32_t* n_attend,
+                           float* scores, float* out, void* workspace, void* stream);
+
+/* Merges the attention's split partials in `workspace` into `out` (the
+ * log-sum-exp combine; nothing to do for a single split). */
+int oasis_attn_combine(oasis_handle h, void* workspace, float* out, void* stream);
+
+/*
+ * The second launch of a layer's decode step: oasis_select_and_diff (with the
+ * attended list when given) and the attention's split combine of `workspace`
+ * into `out`, in one grid where the fused selection applies, else back to back.
+ */
+int oasis_select_diff_combine(oasis_handle h, const float* scores, const int32_t* ctx_score, int32_t* sel,
+                              int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch, int32_t* n_fetch,
+                              int32_t* evict, int32_t* attend, int32_t* n_attend, float* out, void* workspace,
+                              void* stream);
+
+/*
  * One layer's decode step ([EXPL] Figure 8: at step t the layer's attention runs
  * over the resident part of S_t while the draft queries predict S_{t+1}; the
  * selection and the diff that produce the next fetch follow).  Equivalent to,
@@ -258,8 +290,9 @@ int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const voi
  *   oasis_lookahead_score(q, meta, ctx_score, scores)
  *   oasis_select_and_diff(scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
  *                         attend, n_attend)
- * with the same arguments, on `stream`; the attention's split combine rides in
- * the scoring launch (three launches instead of four).  ctx_attn is the context
+ * with the same arguments, on `stream`: oasis_attend_and_score followed by
+ * oasis_select_diff_combine, i.e. two launches for the default shape (three
+ * otherwise).  ctx_attn is the context
  * the attention sees (tokens < ctx_attn); ctx_score the context of the scoring
  * and selection (larger by one after an append of this step, which the caller
  * enqueues before this call; the attention does not read what it writes).

@@ -61,6 +61,9 @@ SIGNATURES = {
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 18),
     "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
+    "oasis_attend_and_score": (_int, [_vp] * 14),
+    "oasis_attn_combine": (_int, [_vp] * 4),
+    "oasis_select_diff_combine": (_int, [_vp] * 14),
     "oasis_fetch_gather": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
@@ -229,3 +232,21 @@ def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot,
 def oasis_sparse_paged_decode_attn_list(h, q, pool, attend, n_attend, ctx_len, out, workspace, stream=None):
     _call("oasis_sparse_paged_decode_attn_list", h, _ptr(q), _ptr(pool), _ptr(attend), _ptr(n_attend),
           _ptr(ctx_len), _ptr(out), _ptr(workspace), _stream(stream))
+
+
+def oasis_attend_and_score(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, attend, n_attend, scores, out,
+                           workspace, stream=None):
+    _call("oasis_attend_and_score", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score), _ptr(sel),
+          _ptr(block_to_slot), _ptr(attend), _ptr(n_attend), _ptr(scores), _ptr(out), _ptr(workspace),
+          _stream(stream))
+
+
+def oasis_attn_combine(h, workspace, out, stream=None):
+    _call("oasis_attn_combine", h, _ptr(workspace), _ptr(out), _stream(stream))
+
+
+def oasis_select_diff_combine(h, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                              attend, n_attend, out, workspace, stream=None):
+    _call("oasis_select_diff_combine", h, _ptr(scores), _ptr(ctx_score), _ptr(sel), _ptr(block_to_slot),
+          _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), _ptr(out),
+          _ptr(workspace), _stream(stream))

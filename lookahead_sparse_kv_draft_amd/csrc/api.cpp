@@ -451,6 +451,99 @@ int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const 
                     "oasis_fetch_gather");
 }
 
+int oasis_attend_and_score(oasis_handle h, const void* q, const void* pool, const void* meta,
+                           const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* sel,
+                           const int32_t* block_to_slot, const int32_t* attend, const int32_t* n_attend,
+                           float* scores, float* out, void* workspace, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_attend_and_score", attend, n_attend);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(meta);
+  CHECK_PTR(ctx_attn);
+  CHECK_PTR(ctx_score);
+  CHECK_PTR(scores);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  if (attend == nullptr) {
+    CHECK_PTR(sel);
+    CHECK_PTR(block_to_slot);
+  }
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  CHECK_ALIGN16(meta);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_attend_and_score: workspace not 256-byte aligned");
+  const oasis::Ctx& c = h->c;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the fp32 reference path attends from the maps when they are given
+  const bool list = attend != nullptr && (c.s.dtype == OASIS_BF16 || sel == nullptr);
+  hipError_t e;
+  if (oasis::attn_and_score_fused_available(c) && c.step_launches == 2) {
+    e = oasis::launch_attn_and_score(c, q, pool, sel, block_to_slot, list ? attend : nullptr,
+                                     list ? n_attend : nullptr, ctx_attn, out, workspace, meta, ctx_score, scores,
+                                     st);
+  } else {
+    e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, list ? attend : nullptr, list ? n_attend : nullptr,
+                                ctx_attn, out, workspace, st);
+    if (e == hipSuccess) e = oasis::launch_score(c, q, meta, ctx_score, scores, st);
+  }
+  return hip_status(e, "oasis_attend_and_score");
+}
+
+int oasis_attn_combine(oasis_handle h, void* workspace, float* out, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(workspace);
+  CHECK_PTR(out);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_attn_combine: workspace not 256-byte aligned");
+  return hip_status(oasis::launch_attn_combine(h->c, workspace, out, static_cast<hipStream_t>(stream)),
+                    "oasis_attn_combine");
+}
+
+int oasis_select_diff_combine(oasis_handle h, const float* scores, const int32_t* ctx_score, int32_t* sel,
+                              int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch, int32_t* n_fetch,
+                              int32_t* evict, int32_t* attend, int32_t* n_attend, float* out, void* workspace,
+                              void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_select_diff_combine", attend, n_attend);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_score);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(n_fetch);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_select_diff_combine: workspace not 256-byte aligned");
+  const oasis::Ctx& c = h->c;
+  if (c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (oasis::select_diff_fused_available(c) && oasis::attn_needs_combine(c)) {
+    e = oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
+                                          evict, attend, n_attend, workspace, out, st);
+  } else {
+    e = oasis::launch_attn_combine(c, workspace, out, st);
+    if (e == hipSuccess) {
+      if (oasis::select_diff_fused_available(c)) {
+        e = oasis::launch_select_diff(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                                      attend, n_attend, st);
+      } else {
+        e = oasis::launch_topk(c, scores, ctx_score, sel, st);
+        if (e == hipSuccess)
+          e = oasis::launch_diff(c, sel, scores, block_to_slot, slot_to_block, fetch, n_fetch, evict, attend,
+                                 n_attend, st);
+      }
+    }
+  }
+  return hip_status(e, "oasis_select_diff_combine");
+}
+
 int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
                       const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
                       int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,

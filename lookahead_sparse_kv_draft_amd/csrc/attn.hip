@@ -249,6 +249,13 @@ hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const
                                : main_t<64>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, st);
 }
 
+hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t st) {
+  if (!attn_needs_combine(c)) return hipSuccess;
+  float* ws_acc = static_cast<float*>(ws);
+  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
+  return (c.s.head_dim == 128) ? combine_t<128>(c, ws_acc, ws_ml, out, st) : combine_t<64>(c, ws_acc, ws_ml, out, st);
+}
+
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
                        const int32_t* ctx_len, float* out, void* ws, hipStream_t st) {

@@ -62,6 +62,8 @@ hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const
                             const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
                             const int32_t* ctx_len, float* out, void* ws, hipStream_t st);
 bool attn_needs_combine(const Ctx& c);
+// The split combine alone (nothing to do when the attention wrote the output).
+hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t st);
 // The attention (split partials) and the lookahead score in one launch (bf16,
 // 2-wavefront 2-page attention, up to three attention row tiles).
 bool attn_and_score_fused_available(const Ctx& c);

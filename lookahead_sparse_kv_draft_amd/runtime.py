@@ -266,11 +266,14 @@ class DecodeRuntime:
         if self.overlap:
             st.attn_done.record(cs)
 
-    def decode_step(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None):
+    def decode_step(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None,
+                    two_calls: bool = False):
         """Attention of step t, scoring of its drafts, selection of S_{t+1} and the
-        diff, in one library call (three launches) on the current stream.  An
-        append of this step is enqueued before it (the attention does not read
-        what the append writes; the scoring sees the grown context)."""
+        diff, in one library call (two launches for the default shape) on the
+        current stream, or (two_calls) as its two halves: attention + scoring,
+        then selection + diff + the attention's split combine.  An append of this
+        step is enqueued before it (the attention does not read what the append
+        writes; the scoring sees the grown context)."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
         if st.fetch_wait_compute or st.fetch_wait_predict:
@@ -279,9 +282,16 @@ class DecodeRuntime:
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
+        o = self.out if out is None else out
+        if two_calls:
+            L.oasis_attend_and_score(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
+                                     st.attend, st.n_attend, st.scores, o, self.ws_ptr, cs)
+            L.oasis_select_diff_combine(self.h, st.scores, self.ctx_scoring, st.sel, st.b2s, st.s2b, st.fetch,
+                                        st.n_fetch, st.evict, st.attend, st.n_attend, o, self.ws_ptr, cs)
+            return
         L.oasis_decode_step(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s, st.s2b,
-                            st.scores, self.out if out is None else out, self.ws_ptr, st.fetch, st.n_fetch,
-                            st.evict, st.attend, st.n_attend, stream=cs)
+                            st.scores, o, self.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend, st.n_attend,
+                            stream=cs)
 
     def append(self, layer: int, k_new_dev, v_new_dev, k_new_host=None, v_new_host=None,
                replica: int = 0):

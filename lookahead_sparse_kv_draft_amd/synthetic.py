@@ -43,12 +43,14 @@ class SyntheticRun:
 
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
                  record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
-                 gather: bool = True):
+                 gather: bool = True, two_calls: bool = False):
         """fused_step: without overlap and drift, run each layer's step through the
-        single decode-step call (attention, scoring, selection, diff).  gather: move
-        the fetched pages with the device-driven gather (else host-issued copies)."""
+        single decode-step call (attention, scoring, selection, diff), or through
+        its two halves (two_calls).  gather: move the fetched pages with the
+        device-driven gather (else host-issued copies)."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
+        self.two_calls = two_calls
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
@@ -139,7 +141,7 @@ class SyntheticRun:
                 if cfg.append:
                     rt.append(l, self.k_new_dev[l, t], self.v_new_dev[l, t],
                               self.k_new_host[l, t], self.v_new_host[l, t])
-                rt.decode_step(l, q)
+                rt.decode_step(l, q, two_calls=self.two_calls)
                 if self.record_units is not None:
                     self._record_out(l, t)
                 if transfer:

@@ -78,6 +78,13 @@ def test_sizes_and_null_checks():
         assert lib.oasis_decode_step(h, *([None] * 17)) == L.OASIS_EINVAL
         assert lib.oasis_sparse_paged_decode_attn_list(h, *([None] * 8)) == L.OASIS_EINVAL
         assert lib.oasis_fetch_gather(h, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_attend_and_score(h, *([None] * 13)) == L.OASIS_EINVAL
+        assert lib.oasis_attn_combine(h, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_select_diff_combine(h, *([None] * 13)) == L.OASIS_EINVAL
+        # attention inputs: the maps are needed when no attended list is given
+        assert lib.oasis_attend_and_score(h, *([256] * 5), None, None, None, None, 256, 256, 256, None) \
+            == L.OASIS_EINVAL
+        assert lib.oasis_attn_combine(h, 272, 256, None) == L.OASIS_EINVAL  # misaligned workspace
         # the attended list and its length come together or not at all
         assert lib.oasis_select_and_diff(h, *([256] * 8), 256, None, None) == L.OASIS_EINVAL
         assert "attend" in L.oasis_last_error()

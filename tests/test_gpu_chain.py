@@ -98,8 +98,19 @@ def test_decode_step_launch_variants(launches, order, monkeypatch):
                                                           planted=15, budget_tokens=16 * 32))
 
 
-def _decode_step_vs_separate(cfg):
-    runs = [SyntheticRun(cfg, overlap=False, fused_step=f) for f in (True, False)]
+@pytest.mark.parametrize("launches", [2, 3])
+def test_decode_step_halves(launches, monkeypatch):
+    """The decode step's two halves as separate calls (attention + scoring, then
+    selection + diff + split combine) leave bit-identical outputs and state to
+    the single decode-step call."""
+    monkeypatch.setenv("OASIS_STEP_LAUNCHES", str(launches))
+    cfg = CONFIGS["llama8b_32k"].with_(batch=2, ctx=16 * 300 + 7, steps=4, fetch_cap=8, planted=15,
+                                       budget_tokens=16 * 32)
+    _decode_step_vs_separate(cfg, runs=[SyntheticRun(cfg, overlap=False, two_calls=tc) for tc in (True, False)])
+
+
+def _decode_step_vs_separate(cfg, runs=None):
+    runs = runs or [SyntheticRun(cfg, overlap=False, fused_step=f) for f in (True, False)]
     try:
         for r in runs:
             r.prologue()

@@ -252,6 +252,27 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatc
         assert np.array_equal(got_list, got)
     else:  # the fp32 kernel splits the list, not the selection: same sums, another order
         assert np.allclose(got_list, got, rtol=1e-5, atol=1e-6)
+    if waves is None:
+        # the decode step's first half (attention beside the scoring, in one grid
+        # where the shape allows) then the split combine: the same attention
+        # output and the same scores as the separate calls, bit for bit
+        rt.build_meta(0)
+        st.scores.fill_(float("nan"))  # blocks past the context are left unwritten
+        L.oasis_lookahead_score(rt.h, q_d, st.meta, rt.ctx_len, st.scores)
+        torch.cuda.synchronize()
+        ref_scores = st.scores.cpu().numpy().copy()
+        variants = [(st.sel, st.b2s, None, None)]
+        if dtype == "bf16":
+            variants += [(None, None, U.i32(att), U.i32(natt)), (st.sel, st.b2s, U.i32(att), U.i32(natt))]
+        for sel_a, b2s_a, att_a, natt_a in variants:
+            rt.out.fill_(float("nan"))
+            st.scores.fill_(float("nan"))
+            L.oasis_attend_and_score(rt.h, q_d, st.pool, st.meta, rt.ctx_len, rt.ctx_len, sel_a, b2s_a, att_a,
+                                     natt_a, st.scores, rt.out, rt.ws_ptr)
+            L.oasis_attn_combine(rt.h, rt.ws_ptr, rt.out)
+            torch.cuda.synchronize()
+            assert np.array_equal(rt.out.cpu().numpy().astype(np.float64), got)
+            assert np.array_equal(st.scores.cpu().numpy(), ref_scores, equal_nan=True)
     for u in range(units):
         r, hh = divmod(u, H)
         A = O.attended_blocks(sel[u], b2s[u])
