@@ -115,13 +115,16 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
     const int P = (P0 >= 16) ? 16 : (P0 >= 8) ? 8 : (P0 >= 4) ? 4 : (P0 >= 2) ? 2 : 1;
     const int ci = tid / P, part = tid & (P - 1);
     const unsigned long long ck = (ci < kb) ? ckey[ci] : 0ull;
+    // (the reads of a batch are unconditional, indices clamped, so they are
+    // in flight together)
+    constexpr int kBatch = 8;
     int r = 0;
-    for (int j = part; j < kb; j += 4 * P) {
+    for (int j = part; j < kb; j += kBatch * P) {
+      unsigned long long x[kBatch];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jj = j + t * P;
-        r += (jj < kb && ckey[min(jj, kb - 1)] > ck) ? 1 : 0;
-      }
+      for (int t = 0; t < kBatch; ++t) x[t] = ckey[min(j + t * P, kb - 1)];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < kb) & (x[t] > ck));
     }
     for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
     if (part == 0 && ck != 0ull && r < need) {

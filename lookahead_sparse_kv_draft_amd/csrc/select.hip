@@ -226,22 +226,46 @@ __device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
   return v + off;
 }
 
-// The selection of one unit by a 1024-thread workgroup; also written, in rank
-// order and -1 padded, to the LDS array selL when it is not null.
+// This thread's candidate scores (candidate c = block c + 1 in slot c / 1024 of
+// thread c % 1024).  Issued first by every caller: every index below Nmax is in
+// bounds, and the context length, which arrives later, decides which keys take
+// part.
 template <int KPT>
-__device__ inline void topk_fast_body(const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
+__device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores, int Nmax, float (&v)[KPT]) {
+  const float* sc = scores + static_cast<size_t>(blockIdx.x) * Nmax;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + static_cast<int>(threadIdx.x) + 1, Nmax - 1)];
+}
+
+// Number of entries of a[0 .. n) below `mine`, counted by P adjacent threads
+// (this thread is `part` of them) and summed across their lanes.  The reads of
+// a batch are unconditional (indices clamped), so they are in flight together.
+template <typename K>
+__device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int part) {
+  constexpr int kBatch = 8;
+  int r = 0;
+  for (int j = part; j < n; j += kBatch * P) {
+    K x[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) x[t] = a[min(j + t * P, n - 1)];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < n) & (x[t] < mine));
+  }
+  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+  return r;
+}
+
+// The selection of one unit by a 1024-thread workgroup from the scores
+// topk_fast_load returned; also written, in rank order and -1 padded, to the LDS
+// array selL when it is not null.
+template <int KPT>
+__device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __restrict__ ctx_len,
                                       int32_t* __restrict__ sel, int H, int Nmax, int kb, int32_t* selL,
                                       TopkFastShared& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
   const int unit = blockIdx.x;
-  const float* sc = scores + static_cast<size_t>(unit) * Nmax;
-  // The score loads go out before the context length arrives (every index below
-  // Nmax is in bounds; the context decides which keys take part).
-  float v[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + tid + 1, Nmax - 1)];
   const int n = ctx_len[unit / H];
   const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
   const int F0 = (N == 1) ? 1 : 2;
@@ -366,16 +390,8 @@ __device__ inline void topk_fast_body(const float* __restrict__ scores, const in
   const int nw = m;
   const int P = (nw <= 64) ? 16 : (nw <= 128) ? 8 : (nw <= 256) ? 4 : (nw <= 512) ? 2 : 1;
   const int wi = tid / P, part = tid & (P - 1);
-  const unsigned long long mine = (wi < nw) ? sh.win[wi] : 0ull;
-  int r = 0;
-  for (int j = part; j < nw; j += 4 * P) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int jj = j + t * P;
-      r += (jj < nw && sh.win[min(jj, nw - 1)] < mine) ? 1 : 0;
-    }
-  }
-  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+  const unsigned long long mine = sh.win[min(wi, nw - 1)];
+  const int r = rank_below(sh.win, nw, mine, P, part);
   if (part == 0 && wi < nw) {
     out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
     if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
@@ -387,7 +403,9 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
                                                          const int32_t* __restrict__ ctx_len,
                                                          int32_t* __restrict__ sel, int H, int Nmax, int kb) {
   __shared__ TopkFastShared sh;
-  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, nullptr, sh);
+  float v[KPT];
+  topk_fast_load<KPT>(scores, Nmax, v);
+  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, nullptr, sh);
 }
 
 // Fused selection + diff: the diff's slot-map and score loads are issued before
@@ -404,11 +422,15 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
   __shared__ DiffShared dsh;
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
+  // the selection's score loads first; the diff's slot-map and score loads
+  // behind them stay in flight through the selection
+  float v[KPT];
+  topk_fast_load<KPT>(scores, Nmax, v);
   const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
   const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
   const bool sok = sb >= 0 && sb < Nmax;
   const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
-  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, selL, sh);
+  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
   __syncthreads();
   diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
             s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
@@ -435,11 +457,15 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
   __shared__ DiffShared dsh;
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
+  // the selection's score loads first; the diff's slot-map and score loads
+  // behind them stay in flight through the selection
+  float v[KPT];
+  topk_fast_load<KPT>(scores, Nmax, v);
   const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
   const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
   const bool sok = sb >= 0 && sb < Nmax;
   const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
-  topk_fast_body<KPT>(scores, ctx_len, sel, H, Nmax, kb, selL, sh);
+  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
   __syncthreads();
   diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
             s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
