@@ -30,7 +30,25 @@ struct DiffShared {
 // Dynamic LDS bytes of diff_body (8-byte aligned start).
 __host__ __device__ inline size_t diff_lds_bytes(int kb, int Nmax, int cap) {
   const size_t nwords = static_cast<size_t>(Nmax + 31) / 32;
-  return static_cast<size_t>(kb) * 8 + nwords * 4 + static_cast<size_t>(kb + 4 * cap) * 4;
+  return static_cast<size_t>(kb) * 8 + nwords * 4 + static_cast<size_t>(2 * kb + 4 * cap) * 4;
+}
+
+// Number of entries of a[0 .. n) below `mine`, counted by P adjacent threads
+// (this thread is `part` of them) and summed across their lanes.  The reads of
+// a batch are unconditional (indices clamped), so they are in flight together.
+template <typename K>
+__device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int part) {
+  constexpr int kBatch = 8;
+  int r = 0;
+  for (int j = part; j < n; j += kBatch * P) {
+    K x[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) x[t] = a[min(j + t * P, n - 1)];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < n) & (x[t] < mine));
+  }
+  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
+  return r;
 }
 
 // selL: LDS [kb], the selection in rank order (complete and visible on entry).
@@ -44,42 +62,55 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
                                  int32_t* __restrict__ fetch, int32_t* __restrict__ n_fetch,
                                  int32_t* __restrict__ evict, int32_t* __restrict__ attend,
                                  int32_t* __restrict__ n_attend, unsigned long long* lds, DiffShared& sh) {
-  unsigned long long* ckey = lds;                            // [kb] candidate key per slot (0 = none)
+  unsigned long long* candK = lds;                           // [kb] complemented keys of the candidates
   const int nwords = (Nmax + 31) / 32;
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(ckey + kb);  // [nwords] selected blocks
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(candK + kb);  // [nwords] selected blocks
   int32_t* F = reinterpret_cast<int32_t*>(bitmap + nwords);  // [cap] fetched blocks
   int32_t* tgt = F + cap;                                     // [cap] their target slots
   int32_t* freeS = tgt + cap;                                 // [kb] free slots, ascending
   int32_t* vict = freeS + kb;                                 // [cap] victim blocks
   int32_t* victS = vict + cap;                                // [cap] victim slots
+  int32_t* candS = victS + cap;                               // [kb] the candidates' slots
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
-  const int nw = blockDim.x / kWave;
+  // Only the first ceil(k / 64) wavefronts hold selection entries and slots; in
+  // a larger workgroup the others skip the per-entry work (wavefront-uniform
+  // branches) and only meet the barriers, so they take no issue slots from the
+  // wavefronts on the critical path.
+  const int nwa = min(static_cast<int>(blockDim.x) / kWave, (kb + kWave - 1) / kWave);
+  const bool act = w < nwa;
   const uint64_t below = (1ull << lane) - 1ull;
   const int i = tid;
   const bool in = i < kb;
-  const int b = in ? selL[i] : -1;
   if (!in) sb = -1;
+  int b = -1, res = -1;
+  if (act) {
+    b = in ? selL[i] : -1;
+    res = bu[(b >= 0 && b < Nmax) ? b : 0];  // slot of the selected block (index clamped: no branch)
+  }
   const bool bok = b >= 0 && b < Nmax;
   const bool sok = sb >= 0 && sb < Nmax;
   for (int j = tid; j < nwords; j += blockDim.x) bitmap[j] = 0u;
-  const int res = bu[bok ? b : 0];  // slot of the selected block (index clamped: no branch)
   __syncthreads();
   if (bok) atomicOr(&bitmap[b >> 5], 1u << (b & 31));
 
   // 1 + 2: ordered ranks of "missing" (by selection entry) and "free" (by slot)
   const bool miss = bok && res < 0;
   const bool fr = in && sb < 0;
-  const uint64_t bm = __ballot(miss), bf = __ballot(fr);
-  if (lane == 0) {
-    sh.miss_tot[w] = __popcll(bm);
-    sh.free_tot[w] = __popcll(bf);
+  uint64_t bm = 0ull, bf = 0ull;
+  if (act) {
+    bm = __ballot(miss);
+    bf = __ballot(fr);
+    if (lane == 0) {
+      sh.miss_tot[w] = __popcll(bm);
+      sh.free_tot[w] = __popcll(bf);
+    }
   }
   __syncthreads();
   int moff = 0, foff = 0, nmiss = 0, nfree = 0;
-  for (int j = 0; j < nw; ++j) {
+  for (int j = 0; j < nwa; ++j) {
     const int a = sh.miss_tot[j], c = sh.free_tot[j];
     moff += (j < w) ? a : 0;
     foff += (j < w) ? c : 0;
@@ -92,44 +123,49 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
   int nF = min(cap, nmiss);
   int need = max(0, nF - nfree);  // uniform
 
-  // 3. victims (only when the free slots do not cover the fetch)
+  // 3. victims (only when the free slots do not cover the fetch): the
+  // candidates are compacted (slot order), then each one's place is the number
+  // of candidates with a larger key.  Usually few slots are candidates (about
+  // as many as blocks are missing), so this is short.
   if (need > 0) {
-    const bool cnd = sok && !((bitmap[sb >> 5] >> (sb & 31)) & 1u);
-    const unsigned long long mykey =
-        cnd ? ((static_cast<unsigned long long>(desc_key(sv)) << 32) | static_cast<uint32_t>(sb + 1)) : 0ull;
-    if (in) ckey[i] = mykey;
-    const uint64_t bc = __ballot(cnd);
-    if (lane == 0) sh.cand_tot[w] = __popcll(bc);
+    bool cnd = false;
+    unsigned long long mykey = 0ull;
+    uint64_t bc = 0ull;
+    if (act) {
+      cnd = sok && !((bitmap[sb >> 5] >> (sb & 31)) & 1u);
+      mykey = (static_cast<unsigned long long>(desc_key(sv)) << 32) | static_cast<uint32_t>(sb + 1);
+      bc = __ballot(cnd);
+      if (lane == 0) sh.cand_tot[w] = __popcll(bc);
+    }
     __syncthreads();
-    int nc = 0;
-    for (int j = 0; j < nw; ++j) nc += sh.cand_tot[j];
+    int nc = 0, coff = 0;
+    for (int j = 0; j < nwa; ++j) {
+      const int a = sh.cand_tot[j];
+      coff += (j < w) ? a : 0;
+      nc += a;
+    }
+    if (cnd) {
+      const int pos = coff + __popcll(bc & below);
+      candK[pos] = ~mykey;  // complemented: a larger key ranks first
+      candS[pos] = i;
+    }
     // Consistent maps with at most k selected blocks always leave enough
     // victims; clamp anyway so inconsistent input stays within the buffers.
     if (need > nc) {
       need = nc;
       nF = nfree + nc;
     }
-    // Each candidate's place = number of larger keys (non-candidates hold 0),
-    // counted by P adjacent threads per slot and summed across their lanes.
-    const int P0 = static_cast<int>(blockDim.x) / kb;
-    const int P = (P0 >= 16) ? 16 : (P0 >= 8) ? 8 : (P0 >= 4) ? 4 : (P0 >= 2) ? 2 : 1;
+    __syncthreads();
+    const int nthr = static_cast<int>(blockDim.x);
+    const int P = (nc * 8 <= nthr) ? 8 : (nc * 4 <= nthr) ? 4 : (nc * 2 <= nthr) ? 2 : 1;
     const int ci = tid / P, part = tid & (P - 1);
-    const unsigned long long ck = (ci < kb) ? ckey[ci] : 0ull;
-    // (the reads of a batch are unconditional, indices clamped, so they are
-    // in flight together)
-    constexpr int kBatch = 8;
-    int r = 0;
-    for (int j = part; j < kb; j += kBatch * P) {
-      unsigned long long x[kBatch];
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) x[t] = ckey[min(j + t * P, kb - 1)];
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < kb) & (x[t] > ck));
-    }
-    for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
-    if (part == 0 && ck != 0ull && r < need) {
-      vict[r] = static_cast<int32_t>(ck & 0xFFFFFFFFull) - 1;  // the block (stored + 1)
-      victS[r] = ci;
+    if (ci < nc) {  // whole groups of P adjacent lanes: the shuffles stay inside them
+      const unsigned long long ck = candK[ci];
+      const int r = rank_below(candK, nc, ck, P, part);
+      if (part == 0 && r < need) {
+        vict[r] = static_cast<int32_t>(~ck & 0xFFFFFFFFull) - 1;  // the block (stored + 1)
+        victS[r] = candS[ci];
+      }
     }
   }
   __syncthreads();
@@ -158,11 +194,14 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
     int slot_after = -1;
     if (bok) slot_after = (res >= 0) ? res : ((miss && mrank < nF) ? tgt[mrank] : -1);
     const bool att = in && slot_after >= 0 && slot_after < kb;
-    const uint64_t ba = __ballot(att);
-    if (lane == 0) sh.att_tot[w] = __popcll(ba);
+    uint64_t ba = 0ull;
+    if (act) {
+      ba = __ballot(att);
+      if (lane == 0) sh.att_tot[w] = __popcll(ba);
+    }
     __syncthreads();
     int off = 0, tot = 0;
-    for (int j = 0; j < nw; ++j) {
+    for (int j = 0; j < nwa; ++j) {
       const int a = sh.att_tot[j];
       off += (j < w) ? a : 0;
       tot += a;

@@ -237,24 +237,6 @@ __device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores,
   for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + static_cast<int>(threadIdx.x) + 1, Nmax - 1)];
 }
 
-// Number of entries of a[0 .. n) below `mine`, counted by P adjacent threads
-// (this thread is `part` of them) and summed across their lanes.  The reads of
-// a batch are unconditional (indices clamped), so they are in flight together.
-template <typename K>
-__device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int part) {
-  constexpr int kBatch = 8;
-  int r = 0;
-  for (int j = part; j < n; j += kBatch * P) {
-    K x[kBatch];
-#pragma unroll
-    for (int t = 0; t < kBatch; ++t) x[t] = a[min(j + t * P, n - 1)];
-#pragma unroll
-    for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < n) & (x[t] < mine));
-  }
-  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
-  return r;
-}
-
 // The selection of one unit by a 1024-thread workgroup from the scores
 // topk_fast_load returned; also written, in rank order and -1 padded, to the LDS
 // array selL when it is not null.
