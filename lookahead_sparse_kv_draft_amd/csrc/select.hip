@@ -26,7 +26,9 @@
 //   * the radix digits are 10 bits (one histogram bin per thread) taken from the
 //     highest bit where the keys differ (block min/max), so the first pass
 //     already spreads the keys; the search stops as soon as the bin holding the
-//     m-th key is taken whole (usually after one or two passes);
+//     m-th key can be taken whole: when its keys are exactly the ones still
+//     needed, or when they fit the winner list beside the keys above it (the
+//     ranking then keeps the first m), so one pass is the rule;
 //   * winners are appended with one LDS atomic per wavefront (ballot counts);
 //     ties at the threshold, when a bin is not taken whole, are ranked in index
 //     order with a workgroup scan;
@@ -198,13 +200,17 @@ constexpr int kTkMaxWin = 512;
 
 struct TopkFastShared {
   int hist[kTkThreads];
+  int start[kTkThreads + 1];  // first pass: keys in the bins before each bin
   unsigned long long win[kTkMaxWin];
   uint32_t wlo[kTkWaves], whi[kTkWaves];
   int wtot[kTkWaves];
   int bin, before, cnt, nwin;
 };
 
-// Inclusive sum over the 1024 threads and the block total (two barriers).
+// Inclusive sum over the 1024 threads and the block total (two barriers; with
+// TRAIL = false the second one, which protects wtot for the next call, is left
+// to the caller).
+template <bool TRAIL = true>
 __device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
 #pragma unroll
@@ -221,7 +227,7 @@ __device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
     off += (i < w) ? x : 0;
     tot += x;
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   *total = tot;
   return v + off;
 }
@@ -303,6 +309,8 @@ __device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __re
   uint32_t base = 0u;
   int rem = m;
   bool exact = false;
+  bool first = true;  // still in the first pass (bins over the whole key range)
+  int ncoll = m;      // keys the collection below gathers
   while (true) {
     const uint64_t span = 1ull << (shift + 10);
 #pragma unroll
@@ -314,8 +322,12 @@ __device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __re
     __syncthreads();
     const int hv = sh.hist[tid];
     int unused_total;
-    const int incl = tk_incl_sum(hv, sh.wtot, &unused_total);
+    const int incl = tk_incl_sum<false>(hv, sh.wtot, &unused_total);  // the barrier below protects wtot
     const int excl = incl - hv;
+    if (first) {
+      sh.start[tid] = excl;
+      if (tid == kTkThreads - 1) sh.start[kTkThreads] = incl;
+    }
     if (excl < rem && incl >= rem) {  // exactly one thread: its bin holds the m-th key
       sh.bin = tid;
       sh.before = excl;
@@ -325,18 +337,53 @@ __device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __re
     __syncthreads();
     rem -= sh.before;
     base += static_cast<uint32_t>(sh.bin) << shift;
-    if (sh.cnt == rem) {  // the bin is taken whole
+    // The bin is taken whole when its keys are exactly the ones still needed,
+    // or when the winners so far plus the whole bin fit the winner list: the
+    // rank counting below then keeps the first m of them (the bin's keys rank
+    // after every key above the bin).
+    if (sh.cnt == rem || m - rem + sh.cnt <= kTkMaxWin) {
+      ncoll = m - rem + sh.cnt;
       base += static_cast<uint32_t>((1ull << shift) - 1ull);
       exact = true;
       break;
     }
     if (shift == 0) break;  // a single key value: ties at the threshold remain
     shift = max(shift - 10, 0);
+    first = false;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (exact && first) {
+    // One pass was enough: the winners are the keys of bins 0 .. bin (the
+    // histogram bins over the whole range, the last one taken whole).  Each key
+    // goes to its bin's range of the winner list (counting-sort scatter, the
+    // cleared histogram as cursors), and its output position is the number of
+    // keys in earlier bins plus its rank inside its own bin, so only keys that
+    // share a bin are compared.
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const uint32_t d = key[u] - lo;
+      if (u * kTkThreads + tid < C && d <= base) {
+        const int bk = static_cast<int>(d >> shift);
+        sh.win[sh.start[bk] + atomicAdd(&sh.hist[bk], 1)] =
+            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
+      }
+    }
+    __syncthreads();
+    if (tid < ncoll) {
+      const unsigned long long mine = sh.win[tid];
+      const int bk = static_cast<int>((static_cast<uint32_t>(mine >> 32) - lo) >> shift);
+      const int b0 = sh.start[bk], b1 = sh.start[bk + 1];
+      const int r = b0 + rank_below(sh.win + b0, b1 - b0, mine, 1, 0);
+      if (r < m) {
+        out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
+        if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
+      }
+    }
+    return;
   }
   // Collect winners: d < base (d <= base when exact) with one atomic per wavefront.
   if (tid == 0) sh.nwin = 0;
   __syncthreads();
-  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
     const uint32_t d = key[u] - lo;
@@ -369,12 +416,12 @@ __device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __re
   __syncthreads();
   // Output position = number of smaller winners (all keys distinct by index),
   // counted by P adjacent threads per winner and summed across their lanes.
-  const int nw = m;
+  const int nw = ncoll;  // the m winners, and with a whole threshold bin the rest of its keys
   const int P = (nw <= 64) ? 16 : (nw <= 128) ? 8 : (nw <= 256) ? 4 : (nw <= 512) ? 2 : 1;
   const int wi = tid / P, part = tid & (P - 1);
   const unsigned long long mine = sh.win[min(wi, nw - 1)];
   const int r = rank_below(sh.win, nw, mine, P, part);
-  if (part == 0 && wi < nw) {
+  if (part == 0 && wi < nw && r < m) {
     out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
     if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
   }

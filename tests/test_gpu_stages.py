@@ -74,6 +74,9 @@ def test_score_parity(dtype, d, G, D, Nmax, ctxs):
     (128, [16 * 4096, 16 * 4000 + 9, 16 * 200, 16 * 130], "ties"),  # largest single-wave case
     (512, [16 * 3000, 16 * 600, 16 * 513, 77], "normal"),          # k > 258: workgroup kernel
     (256, [16 * 3000, 16 * 600, 16 * 257, 16 * 200], "ties"),
+    # all keys equal: 512 candidates fit the winner list beside the threshold
+    # bin (taken whole, trimmed by rank), 513 and more take the ordered tie pass
+    (128, [16 * 514, 16 * 515, 16 * 513, 16 * 516], "const"),
 ])
 def test_topk_parity(k, ctxs, kind):
     B, H = len(ctxs), 3
