@@ -12,7 +12,7 @@ namespace oasis {
 // batch (split index clamped to the last split, whose repeats get weight 0),
 // then merged: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int D, int SMAX>
-__device__ inline void attn_combine_row(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+__device__ __forceinline__ void attn_combine_row(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
                                         float* __restrict__ out, int rows, int splits, int total, int id,
                                         int lane) {
   constexpr int PER = D / kWave;  // output channels per lane (1 or 2)

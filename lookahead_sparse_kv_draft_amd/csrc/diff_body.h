@@ -57,7 +57,7 @@ __device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int 
 // attend / n_attend (optional, both or neither): the attended list the next
 // attention needs, i.e. the selected blocks resident once this step's fetch has
 // landed, in rank order, packed block << 10 | slot, and its length.
-__device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int32_t* selL, int sb, float sv,
+__device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, const int32_t* selL, int sb, float sv,
                                  int32_t* __restrict__ bu, int32_t* __restrict__ slu,
                                  int32_t* __restrict__ fetch, int32_t* __restrict__ n_fetch,
                                  int32_t* __restrict__ evict, int32_t* __restrict__ attend,
@@ -208,6 +208,152 @@ __device__ inline void diff_body(int unit, int kb, int Nmax, int cap, const int3
     }
     if (att) attend[static_cast<size_t>(unit) * kb + off + __popcll(ba & below)] = (b << kAttendSlotBits) | slot_after;
     if (tid == 0) n_attend[unit] = tot;
+  }
+}
+
+// The same step run by ONE wavefront for k <= 128 (the largest shape of the
+// decode step's default path): lane l handles selection entries and slots l and
+// l + 64, every rank is a ballot within the wavefront, so there is no barrier at
+// all (the wavefront's LDS accesses complete in order).  selL: LDS [kb], the
+// selection; b2sL: LDS [Nmax], this unit's block_to_slot row before the step;
+// bitmap words in `lds` already cleared; sb/sv: the slot map and its blocks'
+// scores for slots l and l + 64 (-1 / any for slots >= kb).
+constexpr int kDiffWaveMaxBudget = 2 * kWave;
+
+__device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL, const int32_t* b2sL,
+                                 const int (&sb)[2], const float (&sv)[2], int32_t* __restrict__ bu,
+                                 int32_t* __restrict__ slu, int32_t* __restrict__ fetch,
+                                 int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict,
+                                 int32_t* __restrict__ attend, int32_t* __restrict__ n_attend,
+                                 unsigned long long* lds) {
+  unsigned long long* candK = lds;
+  const int nwords = (Nmax + 31) / 32;
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(candK + kb);
+  int32_t* F = reinterpret_cast<int32_t*>(bitmap + nwords);
+  int32_t* tgt = F + cap;
+  int32_t* freeS = tgt + cap;
+  int32_t* vict = freeS + kb;
+  int32_t* victS = vict + cap;
+  int32_t* candS = victS + cap;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (1ull << lane) - 1ull;
+  int b[2], res[2], mrank[2];
+  bool in[2], bok[2], sok[2], miss[2];
+  uint64_t bm[2], bf[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = lane + e * kWave;
+    in[e] = i < kb;
+    b[e] = in[e] ? selL[i] : -1;
+    bok[e] = b[e] >= 0 && b[e] < Nmax;
+    res[e] = bok[e] ? b2sL[b[e]] : -1;
+    sok[e] = in[e] && sb[e] >= 0 && sb[e] < Nmax;
+    if (bok[e]) atomicOr(&bitmap[b[e] >> 5], 1u << (b[e] & 31));
+    miss[e] = bok[e] && res[e] < 0;
+    bm[e] = __ballot(miss[e]);
+    bf[e] = __ballot(in[e] && sb[e] < 0);
+  }
+  // 1 + 2: missing blocks in selection order, free slots in ascending order
+  const int nm0 = __popcll(bm[0]), nf0 = __popcll(bf[0]);
+  const int nmiss = nm0 + __popcll(bm[1]), nfree = nf0 + __popcll(bf[1]);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    mrank[e] = (e ? nm0 : 0) + __popcll(bm[e] & below);
+    if (miss[e] && mrank[e] < cap) F[mrank[e]] = b[e];
+    if ((bf[e] >> lane) & 1ull) freeS[(e ? nf0 : 0) + __popcll(bf[e] & below)] = lane + e * kWave;
+  }
+  int nF = min(cap, nmiss);
+  int need = max(0, nF - nfree);
+  // lanes exchange data through LDS below: order each phase's accesses
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // 3. victims: resident blocks outside the selection, compacted in slot order,
+  // then placed by the number of candidates with a larger key
+  if (need > 0) {
+    bool cnd[2];
+    unsigned long long ck[2];
+    uint64_t bc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int sbc = sok[e] ? sb[e] : 0;  // index clamped: no branch around the read
+      cnd[e] = sok[e] && !((bitmap[sbc >> 5] >> (sbc & 31)) & 1u);
+      ck[e] = ~((static_cast<unsigned long long>(desc_key(sv[e])) << 32) | static_cast<uint32_t>(sb[e] + 1));
+      bc[e] = __ballot(cnd[e]);
+    }
+    const int nc0 = __popcll(bc[0]);
+    const int nc = nc0 + __popcll(bc[1]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (cnd[e]) {
+        const int pos = (e ? nc0 : 0) + __popcll(bc[e] & below);
+        candK[pos] = ck[e];  // complemented: a larger key ranks first
+        candS[pos] = lane + e * kWave;
+      }
+    // Consistent maps with at most k selected blocks always leave enough
+    // victims; clamp anyway so inconsistent input stays within the buffers.
+    if (need > nc) {
+      need = nc;
+      nF = nfree + nc;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    constexpr int kBatch = 8;
+    int r0 = 0, r1 = 0;
+    for (int j = 0; j < nc; j += kBatch) {
+      unsigned long long x[kBatch];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) x[t] = candK[min(j + t, nc - 1)];
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        const bool ok = j + t < nc;
+        r0 += static_cast<int>(ok & (x[t] < ck[0]));
+        r1 += static_cast<int>(ok & (x[t] < ck[1]));
+      }
+    }
+    const int r[2] = {r0, r1};
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (cnd[e] && r[e] < need) {
+        vict[r[e]] = sb[e];
+        victS[r[e]] = lane + e * kWave;
+      }
+  }
+
+  // 4. targets, then the map updates and the lists
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int t = lane; t < nF; t += kWave) tgt[t] = (t < nfree) ? freeS[t] : victS[t - nfree];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int t = lane; t < need; t += kWave) bu[vict[t]] = -1;
+  for (int t = lane; t < nF; t += kWave) {
+    const int s = tgt[t];
+    slu[s] = F[t];
+    bu[F[t]] = s;
+  }
+  int32_t* fu = fetch + static_cast<size_t>(unit) * cap * 2;
+  int32_t* eu = evict + static_cast<size_t>(unit) * cap;
+  for (int j = lane; j < cap; j += kWave) {
+    fu[2 * j] = (j < nF) ? F[j] : -1;
+    fu[2 * j + 1] = (j < nF) ? tgt[j] : -1;
+    eu[j] = (j < need) ? vict[j] : -1;
+  }
+  if (lane == 0) n_fetch[unit] = nF;
+
+  // 5. the attended list for the next attention (selection order)
+  if (attend != nullptr) {
+    int sa[2];
+    uint64_t ba[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      sa[e] = -1;
+      if (bok[e]) sa[e] = (res[e] >= 0) ? res[e] : ((miss[e] && mrank[e] < nF) ? tgt[mrank[e]] : -1);
+      ba[e] = __ballot(in[e] && sa[e] >= 0 && sa[e] < kb);
+    }
+    const int na0 = __popcll(ba[0]);
+    int32_t* au = attend + static_cast<size_t>(unit) * kb;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if ((ba[e] >> lane) & 1ull) au[(e ? na0 : 0) + __popcll(ba[e] & below)] = (b[e] << kAttendSlotBits) | sa[e];
+    if (lane == 0) n_attend[unit] = na0 + __popcll(ba[1]);
   }
 }
 

@@ -247,7 +247,7 @@ __device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores,
 // topk_fast_load returned; also written, in rank order and -1 padded, to the LDS
 // array selL when it is not null.
 template <int KPT>
-__device__ inline void topk_fast_body(const float (&v)[KPT], const int32_t* __restrict__ ctx_len,
+__device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], const int32_t* __restrict__ ctx_len,
                                       int32_t* __restrict__ sel, int H, int Nmax, int kb, int32_t* selL,
                                       TopkFastShared& sh) {
   const int tid = threadIdx.x;
@@ -437,8 +437,66 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
   topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, nullptr, sh);
 }
 
-// Fused selection + diff: the diff's slot-map and score loads are issued before
-// the selection runs, and the selection reaches the diff through LDS.
+// Dynamic LDS of the fused selection + diff: the diff's arrays, the selection
+// (k ints), and for k <= 128 this unit's block_to_slot row (N_max ints).
+inline size_t select_diff_lds_bytes(int kb, int Nmax, int cap) {
+  return diff_lds_bytes(kb, Nmax, cap) + static_cast<size_t>(kb) * 4 +
+         (kb <= kDiffWaveMaxBudget ? static_cast<size_t>(Nmax) * 4 : 0);
+}
+
+// Fused selection + diff of one unit by a 1024-thread workgroup.  The
+// selection's score loads go out first, the diff's loads behind them stay in
+// flight through the selection, which reaches the diff through LDS.  For
+// k <= 128 the block_to_slot row is staged in LDS during the selection and a
+// single wavefront runs the diff with no barrier; otherwise every wavefront
+// takes part (diff_body).
+template <int KPT>
+__device__ __forceinline__ void select_diff_unit(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
+    int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
+    int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, unsigned long long* smem_u64,
+    TopkFastShared& sh, DiffShared& dsh) {
+  int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  int32_t* bu = b2s + static_cast<size_t>(unit) * Nmax;
+  int32_t* slu = s2b + static_cast<size_t>(unit) * kb;
+  const float* su = scores + static_cast<size_t>(unit) * Nmax;
+  float v[KPT];
+  topk_fast_load<KPT>(scores, Nmax, v);
+  if (kb <= kDiffWaveMaxBudget) {
+    int32_t* b2sL = selL + kb;
+    int bv[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) bv[u] = bu[min(u * kTkThreads + tid, Nmax - 1)];
+    int sbw[2];
+    float svw[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      sbw[e] = slu[min((tid & (kWave - 1)) + e * kWave, kb - 1)];  // clamped: no branch around the loads
+      svw[e] = su[(sbw[e] >= 0 && sbw[e] < Nmax) ? sbw[e] : 0];
+    }
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
+    for (int j = tid; j < (Nmax + 31) / 32; j += kTkThreads) bitmap[j] = 0u;  // ordered by the selection's barriers
+    topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
+    __syncthreads();
+    if (tid >= kWave) return;
+    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, svw, bu, slu, fetch, n_fetch, evict, attend, n_attend,
+              smem_u64);
+    return;
+  }
+  const int sb = slu[min(tid, kb - 1)];  // clamped: no branch around the loads
+  const bool sok = sb >= 0 && sb < Nmax;
+  const float sv = su[sok ? sb : 0];
+  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
+  __syncthreads();
+  diff_body(unit, kb, Nmax, cap, selL, sb, sv, bu, slu, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
+}
+
 template <int KPT>
 __global__ __launch_bounds__(1024) void select_diff_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
@@ -446,23 +504,10 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
     int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap) {
   extern __shared__ unsigned long long smem_u64[];
-  int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   __shared__ TopkFastShared sh;
   __shared__ DiffShared dsh;
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  // the selection's score loads first; the diff's slot-map and score loads
-  // behind them stay in flight through the selection
-  float v[KPT];
-  topk_fast_load<KPT>(scores, Nmax, v);
-  const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
-  const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
-  const bool sok = sb >= 0 && sb < Nmax;
-  const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
-  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
-  __syncthreads();
-  diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
-            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
+  select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
+                        smem_u64, sh, dsh);
 }
 
 // The fused selection + diff in workgroups [0, units), then the attention's
@@ -481,23 +526,10 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
     return;
   }
   extern __shared__ unsigned long long smem_u64[];
-  int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   __shared__ TopkFastShared sh;
   __shared__ DiffShared dsh;
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  // the selection's score loads first; the diff's slot-map and score loads
-  // behind them stay in flight through the selection
-  float v[KPT];
-  topk_fast_load<KPT>(scores, Nmax, v);
-  const int ic = min(tid, kb - 1);  // clamped: no branch around the loads
-  const int sb = s2b[static_cast<size_t>(unit) * kb + ic];
-  const bool sok = sb >= 0 && sb < Nmax;
-  const float sv = scores[static_cast<size_t>(unit) * Nmax + (sok ? sb : 0)];
-  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
-  __syncthreads();
-  diff_body(unit, kb, Nmax, cap, selL, sb, sv, b2s + static_cast<size_t>(unit) * Nmax,
-            s2b + static_cast<size_t>(unit) * kb, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
+  select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
+                        smem_u64, sh, dsh);
 }
 
 template <int KPT, int D, int SMAX>
@@ -505,7 +537,7 @@ hipError_t sdc_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int3
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
                  int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
-  const size_t lds = diff_lds_bytes(kb, c.s.max_blocks, cap) + static_cast<size_t>(kb) * 4;
+  const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   const int comb_total = c.units * c.rows_attn;
   const int ncomb = (comb_total + kTkWaves - 1) / kTkWaves;
   hipLaunchKernelGGL((select_diff_combine_kernel<KPT, D, SMAX>), dim3(c.units + ncomb), dim3(kTkThreads), lds, st,
@@ -546,7 +578,7 @@ hipError_t select_diff_t(const Ctx& c, const float* scores, const int32_t* ctx_l
                          int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
                          int32_t* n_attend, hipStream_t st) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
-  const size_t lds = diff_lds_bytes(kb, c.s.max_blocks, cap) + static_cast<size_t>(kb) * 4;
+  const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   hipLaunchKernelGGL((select_diff_kernel<KPT>), dim3(c.units), dim3(kTkThreads), lds, st, scores, ctx_len, sel,
                      b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap);
   return hipGetLastError();
