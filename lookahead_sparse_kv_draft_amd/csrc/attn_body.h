@@ -63,15 +63,22 @@ __device__ __forceinline__ void attn_wg(
   // This wavefront's pages: nb entries, slot and token count of entry j in lane j.
   int nb, c_slot, c_ntok;
   if (attend != nullptr) {
-    // The attended list a diff left (rank order, block << 10 | slot): one load
-    // for its length, then this wavefront's contiguous share of an even split
-    // over all splits * W wavefronts of the unit.
-    const int natt = min(max(n_attend[unit], 0), kb);
+    // The attended list a diff left (rank order, block << 10 | slot) and its
+    // length; this wavefront takes a contiguous share of an even split over all
+    // splits * W wavefronts of the unit.  The share of a full list (length k,
+    // the steady state) is loaded beside the length, so the page loads wait for
+    // one round trip, not two; a shorter list loads its own share after.
     const int nwv = splits * W;
+    const int* au = attend + static_cast<size_t>(unit) * kb;
+    const int perk = (kb + nwv - 1) / nwv;
+    const int e0k = (split * W + wv) * perk;
+    int pk = au[min(e0k + lane, kb - 1)];  // clamped: no branch around the load
+    const int natt = min(max(n_attend[unit], 0), kb);
     const int per = (natt + nwv - 1) / nwv;  // <= run <= 64
     const int e0 = (split * W + wv) * per;
     const int cnt = max(0, min(per, natt - e0));
-    const int pk = (lane < cnt) ? attend[static_cast<size_t>(unit) * kb + e0 + lane] : 0;
+    if (natt != kb) pk = au[min(e0 + lane, kb - 1)];  // wavefront-uniform
+    if (lane >= cnt) pk = 0;
     int my_slot = -1, my_ntok = 0;
     if (lane < cnt) {
       const int b = pk >> kAttendSlotBits;
