@@ -22,8 +22,12 @@
  *    the verify query, rows 1..n_draft the draft queries of the step.
  *  - Element type (OASIS_BF16 or OASIS_F32) applies to q, block metadata, K/V
  *    pages and appended tokens; scores and attention output are float32.
- *  - Block metadata "meta": [B][H][max_blocks][2][d]; row 0 = per-channel key
- *    min of the block, row 1 = per-channel key max.
+ *  - Block metadata "meta": per block a row of 2*d elements, the per-channel
+ *    key min of the block then the per-channel key max.  Stored per (request,
+ *    KV head) in ceil(max_blocks/16) tiles of 16 blocks; inside a tile the rows
+ *    are cut into 16-byte chunks stored chunk-major (chunk c of block 16t + j at
+ *    chunk position 16c + j), so that each MFMA k-step of the scoring reads one
+ *    contiguous KiB.  The buffer is opaque to callers apart from its size.
  *  - Page = one block of one unit: K rows [16][d] (token-major) followed by V
  *    transposed [d][16] (channel-major), 2*16*d elements.  The host tier is
  *    [B][H][max_blocks][page] (pinned host memory); the HBM pool is
@@ -85,7 +89,7 @@ int oasis_version(void);
 
 /* Byte sizes of the caller-allocated buffers of one layer (0 on a bad handle). */
 size_t oasis_page_bytes(oasis_handle h);       /* one page: 2*16*d elements */
-size_t oasis_meta_bytes(oasis_handle h);       /* B*H*max_blocks*2*d elements */
+size_t oasis_meta_bytes(oasis_handle h);       /* B*H*ceil(max_blocks/16)*16*2*d elements */
 size_t oasis_pool_bytes(oasis_handle h);       /* B*H*budget_blocks pages */
 size_t oasis_host_tier_bytes(oasis_handle h);  /* B*H*max_blocks pages */
 /* Split partials of oasis_sparse_paged_decode_attn (device, 256-byte aligned). */

@@ -164,7 +164,9 @@ size_t oasis_page_bytes(oasis_handle h) {
 }
 
 size_t oasis_meta_bytes(oasis_handle h) {
-  return h ? static_cast<size_t>(h->c.units) * h->c.s.max_blocks * 2 * h->c.s.head_dim * h->c.elem_bytes : 0;
+  return h ? static_cast<size_t>(h->c.units) * oasis::meta_tiles(h->c.s.max_blocks) * oasis::kMetaTile * 2 *
+                 h->c.s.head_dim * h->c.elem_bytes
+           : 0;
 }
 
 size_t oasis_pool_bytes(oasis_handle h) {

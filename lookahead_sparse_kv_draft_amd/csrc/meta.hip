@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
   if (b >= N) return;
   const int ntok = min(kBlock, n - kBlock * b);
   const E* pg = pages + static_cast<size_t>(w) * PAGE;
-  E* mrow = meta + static_cast<size_t>(id) * 2 * D;
+  constexpr int CE = 16 / static_cast<int>(sizeof(E));
   for (int c = lane; c < D; c += kWave) {
     float mn = Elem<E>::load(pg[c]);
     float mx = mn;
@@ -48,8 +48,8 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
       mn = fminf(mn, v);
       mx = fmaxf(mx, v);
     }
-    mrow[c] = Elem<E>::store(mn);
-    mrow[D + c] = Elem<E>::store(mx);
+    meta[meta_offset<D, CE>(unit, b, c, Nmax)] = Elem<E>::store(mn);
+    meta[meta_offset<D, CE>(unit, b, D + c, Nmax)] = Elem<E>::store(mx);
   }
   if (pool != nullptr && b2s != nullptr) {
     const int slot = b2s[id];
@@ -77,18 +77,20 @@ __global__ __launch_bounds__(64) void meta_update_kernel(
   const int j = p - b * kBlock;
   if (p < 0 || b >= Nmax) return;
   const size_t id = static_cast<size_t>(unit) * Nmax + b;
-  E* mrow = meta + id * 2 * D;
+  constexpr int CE = 16 / static_cast<int>(sizeof(E));
   const E* kn = k_new + static_cast<size_t>(unit) * D;
   const E* vn = v_new + static_cast<size_t>(unit) * D;
   for (int c = lane; c < D; c += kWave) {
     const E kv = kn[c];
+    E* mn = meta + meta_offset<D, CE>(unit, b, c, Nmax);
+    E* mx = meta + meta_offset<D, CE>(unit, b, D + c, Nmax);
     if (j == 0) {
-      mrow[c] = kv;
-      mrow[D + c] = kv;
+      *mn = kv;
+      *mx = kv;
     } else {
       const float kf = Elem<E>::load(kv);
-      mrow[c] = Elem<E>::store(fminf(Elem<E>::load(mrow[c]), kf));
-      mrow[D + c] = Elem<E>::store(fmaxf(Elem<E>::load(mrow[D + c]), kf));
+      *mn = Elem<E>::store(fminf(Elem<E>::load(*mn), kf));
+      *mx = Elem<E>::store(fmaxf(Elem<E>::load(*mx), kf));
     }
   }
   const int slot = b2s[id];

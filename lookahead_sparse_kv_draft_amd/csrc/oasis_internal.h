@@ -14,6 +14,24 @@ constexpr int kWave = 64;      // CDNA wavefront width
 constexpr int kMaxRows = 64;   // query rows per unit handled by the kernels (4 MFMA row tiles)
 constexpr int kMaxBudget = 1024;
 constexpr int kAttendSlotBits = 10;   // attended-list entry = block << 10 | slot (slot < kMaxBudget)
+
+// Block metadata layout.  Per unit, ceil(max_blocks / 16) tiles of 16 blocks;
+// in a tile, the 16-byte chunks of the blocks' 2d-element rows (key min, then
+// key max) are stored chunk-major: chunk c of block 16t + j at position
+// 16c + j.  A 64-lane load of 16 bytes per lane then reads chunks 4s .. 4s+3
+// of all 16 blocks, 1 KiB contiguous (the scoring's MFMA operand for k-step s).
+constexpr int kMetaTile = 16;
+__host__ __device__ inline int meta_tiles(int Nmax) { return (Nmax + kMetaTile - 1) / kMetaTile; }
+// Element offset of element e (0 <= e < 2d) of block b of unit `unit`; CE =
+// elements per 16-byte chunk (8 for bf16, 4 for fp32).
+template <int D, int CE>
+__host__ __device__ inline size_t meta_offset(int unit, int b, int e, int Nmax) {
+  constexpr int NC = 2 * D / CE;  // chunks per block row
+  const int t = b / kMetaTile, j = b - t * kMetaTile;
+  const int c = e / CE, o = e - c * CE;
+  return ((static_cast<size_t>(unit) * meta_tiles(Nmax) + t) * NC + c) * (kMetaTile * CE) +
+         static_cast<size_t>(j) * CE + o;
+}
 constexpr int kAttnMaxSplits = 32;  // attention splits per unit (merge statistics kept in LDS)
 
 struct Ctx {

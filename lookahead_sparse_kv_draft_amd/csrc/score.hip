@@ -9,7 +9,8 @@
 // (v_mfma_f32_16x16x32_bf16): q+ and q- are exact in bf16, every product is exact
 // in fp32 and the sum accumulates in fp32.  One wavefront streams 16-block tiles
 // of one (request, KV head): B operand = 16 blocks x 32 metadata elements, each
-// lane loading 16 contiguous bytes (a tile is 8 KiB contiguous), A operand = the
+// lane loading 16 bytes of one contiguous 1 KiB piece per k-step (the metadata
+// tiles are stored chunk-major for this), A operand = the
 // split query rows held in registers for the whole wavefront.  The next tile's
 // loads are issued before the current tile's MFMAs.  Rows are reduced with a max
 // inside each lane and two cross-lane exchanges.
@@ -46,13 +47,12 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
   __syncthreads();
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= N) return;
-  const float* mr = meta + (static_cast<size_t>(unit) * Nmax + b) * 2 * D;
   float best = -INFINITY;
   for (int row = 0; row < rows; ++row) {
     float s = 0.f;
     for (int c = 0; c < D; ++c) {
       const float qc = qs[row * D + c];
-      s += fmaxf(qc * mr[c], qc * mr[D + c]);
+      s += fmaxf(qc * meta[meta_offset<D, 4>(unit, b, c, Nmax)], qc * meta[meta_offset<D, 4>(unit, b, D + c, Nmax)]);
     }
     best = fmaxf(best, s);
   }

@@ -33,15 +33,18 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
   const int t1max = min(t0 + tpw, (Nmax + 15) / 16);
   const int col = lane & 15;  // A: query row within the row tile; B/C: block within the tile
   const int grp = lane >> 4;  // k-group of the lane
-  const uint4* mbase = reinterpret_cast<const uint4*>(meta + static_cast<size_t>(unit) * Nmax * 2 * D);
+  // chunk-major metadata tiles (meta_offset): 4d 16-byte chunks per tile, the
+  // chunk lane (col, grp) needs at k-step s (chunk 4s + grp of block col) is
+  // at 64s + lane, so each k-step is one contiguous 1 KiB load
+  constexpr int TILE4 = 4 * D;
+  const uint4* mbase = reinterpret_cast<const uint4*>(meta) + static_cast<size_t>(unit) * meta_tiles(Nmax) * TILE4;
   float* sbase = scores + static_cast<size_t>(unit) * Nmax;
-  constexpr int CHUNKS = 2 * D / 8;  // 16-byte chunks per block row pair
-  // Loads are unconditional (block indices clamped; results of blocks past the
+  // Loads are unconditional (tile indices clamped; results of blocks past the
   // context are discarded), so every wait below covers exactly the older buffer.
   auto load_c = [&](uint4* Bt, int tile, int nclamp) {
-    const int b = min(tile * 16 + col, nclamp - 1);
+    const int t = min(tile, (nclamp + 15) / 16 - 1);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(b) * CHUNKS + 4 * s + grp];
+    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(t) * TILE4 + 64 * s + lane];
   };
   // The first two tiles go out before the context length arrives: every block
   // index below Nmax is in bounds, and the context only decides what is kept.

@@ -73,6 +73,30 @@ class Shape:
                               self.fetch_cap if fetch_cap is None else fetch_cap, self.code)
 
 
+def untile_meta(meta: torch.Tensor, units: int, max_blocks: int, d: int, dtype: str) -> torch.Tensor:
+    """[units][max_blocks][2][d] elements (int16 bit patterns for bf16, float32
+    otherwise) of a metadata buffer in the library's chunk-major 16-block tiles."""
+    el = meta.view(torch.int16 if dtype == "bf16" else torch.float32)
+    ce = 16 // el.element_size()
+    tiles = (max_blocks + 15) // 16
+    t = el.view(units, tiles, 2 * d // ce, 16, ce).permute(0, 1, 3, 2, 4)
+    return t.reshape(units, tiles * 16, 2, d)[:, :max_blocks].contiguous()
+
+
+def tile_meta(meta: np.ndarray) -> np.ndarray:
+    """Host-side packing of logical metadata [units][max_blocks][2][d] (bf16 bit
+    patterns as uint16/int16, or float32) into the library's chunk-major tiles of
+    16 blocks; flat, zero-padded to whole tiles (the inverse of untile_meta)."""
+    units, nmax, two, d = meta.shape
+    assert two == 2
+    ce = 16 // meta.dtype.itemsize
+    tiles = (nmax + 15) // 16
+    pad = np.zeros((units, tiles * 16, 2 * d), dtype=meta.dtype)
+    pad[:, :nmax] = meta.reshape(units, nmax, 2 * d)
+    t = pad.reshape(units, tiles, 16, 2 * d // ce, ce).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
 class LayerState:
     """Device state of one layer (one replica) plus its pinned host tier."""
 
@@ -398,7 +422,9 @@ class DecodeRuntime:
         return st.pool.view(s.units, s.budget_blocks, -1)
 
     def meta_view(self, layer: int, replica: int = 0) -> torch.Tensor:
+        """The layer's block metadata as [units][max_blocks][2][d] (a copy): the
+        library stores it in chunk-major tiles of 16 blocks (16-byte chunks of
+        each block's row, chunk c of block 16t + j at position 16c + j)."""
         s = self.shape
         st = self.state[layer][replica]
-        el = st.meta.view(torch.int16 if s.dtype == "bf16" else torch.float32)
-        return el.view(s.units, s.max_blocks, 2, s.head_dim)
+        return untile_meta(st.meta, s.units, s.max_blocks, s.head_dim, s.dtype)

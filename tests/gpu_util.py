@@ -22,10 +22,17 @@ def to_elem_np(dtype: str, x: np.ndarray) -> np.ndarray:
     return to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
-def to_dev(dtype: str, x: np.ndarray) -> torch.Tensor:
-    """Element-typed float32 numpy values -> device tensor of the element type (exact)."""
+def to_dev(dtype: str, x: np.ndarray, tiled_meta: bool = False) -> torch.Tensor:
+    """Element-typed float32 numpy values -> device tensor of the element type
+    (exact).  tiled_meta: x is logical block metadata [units][N][2][d], stored in
+    the library's tile layout."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+    t = t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    if tiled_meta:
+        from lookahead_sparse_kv_draft_amd.runtime import tile_meta
+        bits = t.view(torch.int16) if dtype == "bf16" else t
+        t = torch.from_numpy(tile_meta(bits.numpy())).view(t.dtype)
+    return t.cuda()
 
 
 def from_dev_elem(dtype: str, t: torch.Tensor) -> np.ndarray:

@@ -44,7 +44,7 @@ def test_score_parity(dtype, d, G, D, Nmax, ctxs):
     kmax = U.elem_round(dtype, np.maximum(a, b) * 1.5)
     q = U.elem_round(dtype, rng.standard_normal((B, H * G, 1 + D, d)).astype(np.float32))
     meta = np.stack([kmin, kmax], axis=2)  # [units][Nmax][2][d]
-    meta_d = U.to_dev(dtype, meta)
+    meta_d = U.to_dev(dtype, meta, tiled_meta=True)
     q_d = U.to_dev(dtype, q)
     ctx_d = U.i32(ctxs)
     scores = torch.full((units, Nmax), float("nan"), device="cuda")
