@@ -60,6 +60,12 @@ def parse():
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --calib-copy` into a traffic file and exit")
+    p.add_argument("--pipeline", action="store_true",
+                   help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
+                        "(one JSON line per sweep instead of the headline)")
+    p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
+    p.add_argument("--cap-fracs", default="0,0.01,0.02,0.05,0.10,0.20,1.0",
+                   help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--mode", choices=["graph", "overlap", "eager"], default="eager",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
                         "second stream beside the attention, captured likewise; eager: plain launches")
@@ -303,8 +309,114 @@ def measure_h2(args, cfg, run, rt, replicas, sequential_step, h1_step_us):
                     "not the headline value"}
 
 
+def pipeline_sweep(args):
+    """Cross-layer pipeline: per step, every layer runs its decode step on the
+    compute stream and its fetched pages move with the device-driven gather on
+    the side stream; layer l's next attention waits only for layer l's gather, so
+    each layer's transfer runs while the later layers (and the next step's
+    earlier layers) compute.  For each fetch cap: the HBM-resident step time
+    (H1, no transfer), the end-to-end step time (H2), exposed transfer = H2 - H1,
+    bytes fetched per step and the gather's PCIe rate."""
+    import torch
+
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
+    from workload import CONFIGS
+
+    base = CONFIGS[args.config]
+    kb = base.k
+    fracs = [float(x) for x in args.cap_fracs.split(",")]
+    caps = sorted({min(kb, int(round(f * kb))) if f < 1.0 else kb for f in fracs})
+    cfg = base.with_(layers=args.layers, fetch_cap=max(caps))
+    torch.cuda.set_device(0)
+    print(f"# pipeline: {cfg.name} x {cfg.layers} layers, caps {caps}", file=sys.stderr, flush=True)
+    run = SyntheticRun(cfg, overlap=False)
+    run.prologue()
+    rt = run.rt
+    torch.cuda.synchronize()
+    cs = torch.cuda.current_stream()
+    side = rt.side
+    nl = run.L
+    page = L.oasis_page_bytes(rt.h)
+    ev_sel = [torch.cuda.Event() for _ in range(nl)]
+    ev_fetch = [torch.cuda.Event() for _ in range(nl)]
+    nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
+    points = []
+    for cap in caps:
+        h = rt.shape.handle(fetch_cap=cap)
+
+        def step(i, transfer, first=False, count=False):
+            t = i % cfg.steps
+            for l in range(nl):
+                st = rt.state[l][0]
+                if transfer and not first:
+                    cs.wait_event(ev_fetch[l])
+                L.oasis_decode_step(h, run.q[l, t + 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                    st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict,
+                                    st.attend, st.n_attend, stream=cs)
+                if count:
+                    nf_tot.add_(st.n_fetch.sum())
+                if transfer:
+                    ev_sel[l].record(cs)
+                    side.wait_event(ev_sel[l])
+                    L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+                    ev_fetch[l].record(side)
+
+        K = args.steps
+        res = {}
+        for transfer in (False, True):
+            for i in range(args.warmup):
+                step(i, transfer, first=(i == 0))
+            cs.wait_stream(side)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(K):
+                step(i, transfer)
+            cs.wait_stream(side)
+            torch.cuda.synchronize()
+            res[transfer] = (time.perf_counter() - t0) / K * 1e6
+        nf_tot.zero_()
+        for i in range(K):  # untimed: pages fetched per step
+            step(i, True, count=True)
+        cs.wait_stream(side)
+        torch.cuda.synchronize()
+        fetched = float(nf_tot.item()) * page / K
+        # the gather alone, back to back on the side stream, over the last lists of every layer
+        eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb.record(side)
+        for _ in range(4):
+            for l in range(nl):
+                st = rt.state[l][0]
+                L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+        ee.record(side)
+        torch.cuda.synchronize()
+        g_us = eb.elapsed_time(ee) * 1e3 / 4
+        last = sum(int(rt.state[l][0].n_fetch.sum()) for l in range(nl)) * page
+        points.append({"cap": cap, "cap_frac_of_k": cap / kb, "h1_us_per_step": res[False],
+                       "h2_us_per_step": res[True], "exposed_transfer_us_per_step": res[True] - res[False],
+                       "fetched_MB_per_step": fetched / 1e6, "gather_us_per_step": g_us,
+                       "gather_GBs": last / (g_us * 1e-6) / 1e9 if g_us > 0 else None,
+                       "h2_steps_per_s": cfg.batch * nl * 1e6 / res[True]})
+        print(f"# cap {cap}: H1 {res[False]:.1f} us, H2 {res[True]:.1f} us, {fetched / 1e6:.2f} MB/step",
+              file=sys.stderr, flush=True)
+        L.oasis_destroy(h)
+    run.close()
+    print(json.dumps({
+        "metric": "cross-layer pipeline: exposed transfer per decode step vs fetch cap",
+        "unit": "us per step (all layers, whole batch)",
+        "config": {"workload": f"{cfg.name} shape, {nl} layers, batch {cfg.batch}, ctx {cfg.ctx}, k {kb} blocks",
+                   "layers": nl, "steps": args.steps, "warmup": args.warmup},
+        "data": "synthetic", "points": points,
+        "note": "H1 = decode steps with inputs resident (no transfer); H2 = with every step's fetched pages "
+                "moved by the device-driven gather on a side stream, each layer's next attention waiting for "
+                "its own gather only"}))
+
+
 def main():
     args = parse()
+    if args.pipeline:
+        pipeline_sweep(args)
+        return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, cmdline=" ".join(sys.argv))
         return
