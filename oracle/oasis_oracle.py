@@ -138,6 +138,7 @@ class DiffResult:
     evict: list            # victim blocks in eviction order
     block_to_slot: np.ndarray
     slot_to_block: np.ndarray
+    last_use: np.ndarray = None  # LRU policy only: per-slot stamp after the step
 
 
 def resident_diff_cap_evict(sel, score, block_to_slot, slot_to_block, cap: int) -> DiffResult:
@@ -175,6 +176,46 @@ def resident_diff_cap_evict(sel, score, block_to_slot, slot_to_block, cap: int) 
         s2b[s] = b
         b2s[b] = s
     return DiffResult(fetch=list(zip(F, targets)), evict=V, block_to_slot=b2s, slot_to_block=s2b)
+
+
+def resident_diff_cap_evict_lru(sel, score, block_to_slot, slot_to_block, last_use, cap: int,
+                                step: int) -> DiffResult:
+    """The same step with least-recently-used eviction ([EXPL] Table 2: the
+    fetch-ratio ablation runs with LRU eviction).
+
+    Readings (the pages name the policy only): a slot is used when an attention
+    reads it, and each step stamps the slots of the next attention's blocks (the
+    selection after this step's fetch, resident) with `step`; a slot never
+    stamped holds -1.  Victims are the resident blocks outside S with the oldest
+    stamp first; among equal stamps, the lowest-score order of
+    resident_diff_cap_evict (lowest score first, then the higher block index).
+    Fetch order and target slots are as in resident_diff_cap_evict.
+    """
+    k = len(slot_to_block)
+    b2s = np.array(block_to_slot, dtype=np.int64).copy()
+    s2b = np.array(slot_to_block, dtype=np.int64).copy()
+    lu = np.array(last_use, dtype=np.int64).copy()
+    S = [int(b) for b in sel if b >= 0]
+    Sset = set(S)
+    missing = [b for b in S if b2s[b] < 0]
+    F = missing[: min(cap, len(missing))]
+    free = [s for s in range(k) if s2b[s] < 0]
+    need = max(0, len(F) - len(free))
+    outside = [int(s2b[s]) for s in range(k) if s2b[s] >= 0 and int(s2b[s]) not in Sset]
+    # oldest stamp first; then lowest score (-0.0 as +0.0), then higher index
+    ranked = sorted(outside, key=lambda b: (int(lu[b2s[b]]), float(score[b]) + 0.0, -b))
+    V = ranked[:need]
+    assert len(V) == need, "fewer victims than needed: |S| must not exceed k"
+    targets = free[: min(len(F), len(free))] + [int(b2s[v]) for v in V]
+    for v in V:
+        b2s[v] = -1
+    for b, s in zip(F, targets):
+        s2b[s] = b
+        b2s[b] = s
+    for b in S:  # the next attention reads these slots
+        if b2s[b] >= 0:
+            lu[b2s[b]] = step
+    return DiffResult(fetch=list(zip(F, targets)), evict=V, block_to_slot=b2s, slot_to_block=s2b, last_use=lu)
 
 
 # --------------------------------------------------------------------------

@@ -237,6 +237,70 @@ def check_diff_worked_example(diff):
     assert res.fetch == [] and res.evict == [] and list(res.slot_to_block) == [7, -1, 3, 5]
 
 
+def check_diff_lru(topk_select, diff, diff_lru, seed=11, trials=300):
+    """LRU eviction: with every stamp equal it is the lowest-score policy; with
+    random stamps every victim is at least as old as every resident block
+    outside S that stays (and at equal stamps ranks after it in the score
+    order); the fetch and the maps obey the same rules; the next attention's
+    slots carry the step's stamp and no other slot changes."""
+    rng = np.random.default_rng(seed)
+    for i in range(trials):
+        N = int(rng.integers(1, 50))
+        k = int(rng.integers(2, 16))
+        cap = int(rng.choice([0, 1, 3, 1000, int(rng.integers(0, k + 1))]))
+        n_res = int(rng.integers(0, k + 1))
+        score = rng.choice([0.0, -0.0, 1.0, 2.0], size=N) if i % 3 == 0 else rng.standard_normal(N)
+        b2s, s2b = random_maps(rng, N, k, n_res)
+        sel = topk_select(score, N, k)
+        step = int(rng.integers(0, 50))
+        same = np.full(k, int(rng.integers(-1, 5)))
+        a = diff(sel, score, b2s, s2b, cap)
+        b = diff_lru(sel, score, b2s, s2b, same, cap, step)
+        assert a.fetch == b.fetch and a.evict == b.evict
+        assert np.array_equal(a.block_to_slot, b.block_to_slot) and np.array_equal(a.slot_to_block, b.slot_to_block)
+        lu = rng.integers(-1, 4, size=k)
+        r = diff_lru(sel, score, b2s, s2b, lu, cap, step)
+        S = {x for x in sel if x >= 0}
+        V = list(r.evict)
+        stay = [int(x) for x in s2b if x >= 0 and int(x) not in S and int(x) not in V]
+        key = lambda x: (int(lu[b2s[x]]), float(score[x]) + 0.0, -x)
+        assert [key(v) for v in V] == sorted(key(v) for v in V)          # eviction order
+        for v in V:
+            for w in stay:
+                assert key(v) < key(w)
+        ref = diff(sel, score, b2s, s2b, cap)                            # same fetch list and count
+        assert [f for f, _ in r.fetch] == [f for f, _ in ref.fetch] and len(V) == len(ref.evict)
+        nxt = {int(r.block_to_slot[x]) for x in S if r.block_to_slot[x] >= 0}
+        for s in range(k):
+            assert r.last_use[s] == (step if s in nxt else lu[s])
+        for s in range(k):                                               # maps are inverse
+            x = r.slot_to_block[s]
+            if x >= 0:
+                assert r.block_to_slot[x] == s
+
+
+def check_diff_lru_worked_example(diff_lru):
+    # the lowest-score worked example above, with stamps: slot 0 (block 7) last read
+    # at step 5, slot 2 (block 3) at step 2, slot 3 (block 5) at step 1; slot 1 free
+    s2b = np.array([7, -1, 3, 5])
+    b2s = np.full(10, -1)
+    b2s[7], b2s[3], b2s[5] = 0, 2, 3
+    score = np.array([9.0, 1.0, 8.0, 6.0, 4.0, 0.5, 2.0, 0.5, 3.0, 5.0])
+    sel = [0, 9, 2, 3]
+    lu = np.array([5, -1, 2, 1])
+    res = diff_lru(sel, score, b2s, s2b, lu, 2, 6)
+    # cap 2: fetch 0 into free slot 1, then 9 into the slot of the least recently
+    # read resident block outside S: 5 (stamp 1), where the score policy takes 7
+    assert res.fetch == [(0, 1), (9, 3)] and res.evict == [5]
+    assert list(res.slot_to_block) == [7, 0, 3, 9]
+    assert list(res.last_use) == [5, 6, 6, 6]   # 0, 9 and 3 are read next; 7 keeps its stamp
+    res = diff_lru(sel, score, b2s, s2b, lu, 3, 6)
+    assert res.fetch == [(0, 1), (9, 3), (2, 0)] and res.evict == [5, 7]
+    assert list(res.last_use) == [6, 6, 6, 6]
+    res = diff_lru(sel, score, b2s, s2b, lu, 0, 6)
+    assert res.fetch == [] and res.evict == [] and list(res.last_use) == [5, -1, 6, 1]
+
+
 # ---------------------------------------------------------------- O6 attention
 def _sdpa(q, K, V):
     qt = torch.from_numpy(np.asarray(q, dtype=np.float64)).reshape(1, 1, -1, q.shape[-1])

@@ -118,7 +118,58 @@ def _fails(fn, *args):
     return False
 
 
+def _lru_variant(newest_first=False, index_ties=False, no_stamp=False, stamp_all=False):
+    def f(sel, score, b2s, s2b, last_use, cap, step):
+        r = O.resident_diff_cap_evict_lru(sel, score, b2s, s2b, last_use, cap, step)
+        if not (newest_first or index_ties):
+            lu = r.last_use
+        if newest_first or index_ties:
+            k = len(s2b)
+            S = {int(b) for b in sel if b >= 0}
+            outside = [int(s2b[s]) for s in range(k) if s2b[s] >= 0 and int(s2b[s]) not in S]
+            if newest_first:
+                key = lambda b: (-int(last_use[b2s[b]]), float(score[b]) + 0.0, -b)  # noqa: E731
+            else:
+                key = lambda b: (int(last_use[b2s[b]]), b)  # noqa: E731
+            V = sorted(outside, key=key)[: len(r.evict)]
+            b2 = np.array(b2s).copy()
+            s2 = np.array(s2b).copy()
+            F = [f for f, _ in r.fetch]
+            free = [s for s in range(k) if s2[s] < 0]
+            tg = free[: min(len(F), len(free))] + [int(b2[v]) for v in V]
+            for v in V:
+                b2[v] = -1
+            for b, s in zip(F, tg):
+                s2[s] = b
+                b2[b] = s
+            lu = np.array(last_use).copy()
+            for b in S:
+                if b2[b] >= 0:
+                    lu[b2[b]] = step
+            return O.DiffResult(fetch=list(zip(F, tg)), evict=V, block_to_slot=b2, slot_to_block=s2, last_use=lu)
+        if no_stamp:
+            lu = np.array(last_use).copy()
+        if stamp_all:
+            lu = np.full(len(s2b), step)
+        return O.DiffResult(fetch=r.fetch, evict=r.evict, block_to_slot=r.block_to_slot,
+                            slot_to_block=r.slot_to_block, last_use=lu)
+    return f
+
+
+def _fails_lru(variant):
+    try:
+        C.check_diff_lru(O.topk_select, O.resident_diff_cap_evict, variant)
+        C.check_diff_lru_worked_example(variant)
+    except AssertionError:
+        return True
+    return False
+
+
 MUTANTS = [
+    ("LRU evicts the newest", lambda: _fails_lru(_lru_variant(newest_first=True))),
+    ("LRU ties by block index", lambda: _fails_lru(_lru_variant(index_ties=True))),
+    ("LRU stamps nothing", lambda: _fails_lru(_lru_variant(no_stamp=True))),
+    ("LRU stamps every slot", lambda: _fails_lru(_lru_variant(stamp_all=True))),
     ("meta includes token n", lambda: _fails(C.check_meta_brute, meta_off_by_one)),
     ("meta ignores context length", lambda: _fails(C.check_meta_brute, meta_whole_block)),
     ("append does not reset a new block", lambda: _fails(C.check_meta_append, O.block_meta, append_no_reset)),

@@ -63,6 +63,14 @@ def test_diff_invariants():
     C.check_diff_invariants(O.topk_select, O.resident_diff_cap_evict)
 
 
+def test_diff_lru_pins():
+    C.check_diff_lru(O.topk_select, O.resident_diff_cap_evict, O.resident_diff_cap_evict_lru)
+
+
+def test_diff_lru_worked_example():
+    C.check_diff_lru_worked_example(O.resident_diff_cap_evict_lru)
+
+
 def test_diff_worked_example():
     C.check_diff_worked_example(O.resident_diff_cap_evict)
 
