@@ -285,6 +285,28 @@ int oasis_select_diff_combine(oasis_handle h, const float* scores, const int32_t
                               void* stream);
 
 /*
+ * Least-recently-used eviction variants ([EXPL] Table 2: the fetch-ratio
+ * ablation evicts least-recently-used blocks).  As oasis_select_and_diff and
+ * oasis_select_diff_combine, except for the victims when the free slots do not
+ * cover the fetch: the resident blocks outside the new selection whose slot
+ * was read longest ago, i.e. with the smallest stamp in slot_last_use
+ * ([B][H][budget_blocks] int32, device, caller-owned; -1 = never read, the
+ * caller's initial value), ties in the lowest-score order.  Every slot of the
+ * next attention's blocks (the selection after this step's fetch, resident)
+ * is stamped with `step` (monotone across calls, chosen by the caller).
+ * Available for budget_blocks <= 128 and max_blocks <= 8192, otherwise
+ * OASIS_EUNSUPPORTED.
+ */
+int oasis_select_and_diff_lru(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                              int32_t* block_to_slot, int32_t* slot_to_block, int32_t* slot_last_use, int32_t step,
+                              int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                              void* stream);
+int oasis_select_diff_combine_lru(oasis_handle h, const float* scores, const int32_t* ctx_score, int32_t* sel,
+                                  int32_t* block_to_slot, int32_t* slot_to_block, int32_t* slot_last_use,
+                                  int32_t step, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                                  int32_t* n_attend, float* out, void* workspace, void* stream);
+
+/*
  * One layer's decode step ([EXPL] Figure 8: at step t the layer's attention runs
  * over the resident part of S_t while the draft queries predict S_{t+1}; the
  * selection and the diff that produce the next fetch follow).  Equivalent to,

@@ -64,6 +64,8 @@ SIGNATURES = {
     "oasis_attend_and_score": (_int, [_vp] * 14),
     "oasis_attn_combine": (_int, [_vp] * 4),
     "oasis_select_diff_combine": (_int, [_vp] * 14),
+    "oasis_select_and_diff_lru": (_int, [_vp] * 7 + [_i32] + [_vp] * 6),
+    "oasis_select_diff_combine_lru": (_int, [_vp] * 7 + [_i32] + [_vp] * 8),
     "oasis_fetch_gather": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
@@ -250,3 +252,17 @@ def oasis_select_diff_combine(h, scores, ctx_score, sel, block_to_slot, slot_to_
     _call("oasis_select_diff_combine", h, _ptr(scores), _ptr(ctx_score), _ptr(sel), _ptr(block_to_slot),
           _ptr(slot_to_block), _ptr(fetch), _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), _ptr(out),
           _ptr(workspace), _stream(stream))
+
+
+def oasis_select_and_diff_lru(h, scores, ctx_len, sel, block_to_slot, slot_to_block, slot_last_use, step, fetch,
+                              n_fetch, evict, attend=None, n_attend=None, stream=None):
+    _call("oasis_select_and_diff_lru", h, _ptr(scores), _ptr(ctx_len), _ptr(sel), _ptr(block_to_slot),
+          _ptr(slot_to_block), _ptr(slot_last_use), int(step), _ptr(fetch), _ptr(n_fetch), _ptr(evict),
+          _ptr(attend), _ptr(n_attend), _stream(stream))
+
+
+def oasis_select_diff_combine_lru(h, scores, ctx_score, sel, block_to_slot, slot_to_block, slot_last_use, step,
+                                  fetch, n_fetch, evict, attend, n_attend, out, workspace, stream=None):
+    _call("oasis_select_diff_combine_lru", h, _ptr(scores), _ptr(ctx_score), _ptr(sel), _ptr(block_to_slot),
+          _ptr(slot_to_block), _ptr(slot_last_use), int(step), _ptr(fetch), _ptr(n_fetch), _ptr(evict),
+          _ptr(attend), _ptr(n_attend), _ptr(out), _ptr(workspace), _stream(stream))

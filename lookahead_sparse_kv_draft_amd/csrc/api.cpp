@@ -503,6 +503,69 @@ int oasis_attn_combine(oasis_handle h, void* workspace, float* out, void* stream
                     "oasis_attn_combine");
 }
 
+int oasis_select_and_diff_lru(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
+                              int32_t* block_to_slot, int32_t* slot_to_block, int32_t* slot_last_use, int32_t step,
+                              int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                              void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_select_and_diff_lru", attend, n_attend);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(slot_last_use);
+  CHECK_PTR(n_fetch);
+  if (h->c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  if (!oasis::select_diff_lru_available(h->c))
+    return fail(OASIS_EUNSUPPORTED, "oasis_select_and_diff_lru: needs budget_blocks <= 128 and max_blocks <= 8192");
+  return hip_status(oasis::launch_select_diff(h->c, scores, ctx_len, sel, block_to_slot, slot_to_block, fetch, n_fetch,
+                                              evict, attend, n_attend, static_cast<hipStream_t>(stream),
+                                              oasis::LruState{slot_last_use, step}),
+                    "oasis_select_and_diff_lru");
+}
+
+int oasis_select_diff_combine_lru(oasis_handle h, const float* scores, const int32_t* ctx_score, int32_t* sel,
+                                  int32_t* block_to_slot, int32_t* slot_to_block, int32_t* slot_last_use,
+                                  int32_t step, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                                  int32_t* n_attend, float* out, void* workspace, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_ATTEND_PAIR("oasis_select_diff_combine_lru", attend, n_attend);
+  CHECK_PTR(scores);
+  CHECK_PTR(ctx_score);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(slot_to_block);
+  CHECK_PTR(slot_last_use);
+  CHECK_PTR(n_fetch);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_select_diff_combine_lru: workspace not 256-byte aligned");
+  const oasis::Ctx& c = h->c;
+  if (c.s.fetch_cap > 0) {
+    CHECK_PTR(fetch);
+    CHECK_PTR(evict);
+  }
+  if (!oasis::select_diff_lru_available(c))
+    return fail(OASIS_EUNSUPPORTED,
+                "oasis_select_diff_combine_lru: needs budget_blocks <= 128 and max_blocks <= 8192");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const oasis::LruState lru{slot_last_use, step};
+  hipError_t e;
+  if (oasis::attn_needs_combine(c)) {
+    e = oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
+                                          evict, attend, n_attend, workspace, out, st, lru);
+  } else {
+    e = oasis::launch_select_diff(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                                  attend, n_attend, st, lru);
+  }
+  return hip_status(e, "oasis_select_diff_combine_lru");
+}
+
 int oasis_select_diff_combine(oasis_handle h, const float* scores, const int32_t* ctx_score, int32_t* sel,
                               int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch, int32_t* n_fetch,
                               int32_t* evict, int32_t* attend, int32_t* n_attend, float* out, void* workspace,

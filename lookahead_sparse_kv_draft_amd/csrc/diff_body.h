@@ -30,7 +30,7 @@ struct DiffShared {
 // Dynamic LDS bytes of diff_body (8-byte aligned start).
 __host__ __device__ inline size_t diff_lds_bytes(int kb, int Nmax, int cap) {
   const size_t nwords = static_cast<size_t>(Nmax + 31) / 32;
-  return static_cast<size_t>(kb) * 8 + nwords * 4 + static_cast<size_t>(2 * kb + 4 * cap) * 4;
+  return static_cast<size_t>(kb) * 8 + nwords * 4 + static_cast<size_t>(3 * kb + 4 * cap) * 4;
 }
 
 // Number of entries of a[0 .. n) below `mine`, counted by P adjacent threads
@@ -218,10 +218,16 @@ __device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, c
 // selection; b2sL: LDS [Nmax], this unit's block_to_slot row before the step;
 // bitmap words in `lds` already cleared; sb/sv: the slot map and its blocks'
 // scores for slots l and l + 64 (-1 / any for slots >= kb).
+// Least-recently-used eviction when lu (this unit's per-slot stamps) is not
+// null: luv holds the stamps of slots l and l + 64; victims are taken oldest
+// stamp first, then in the lowest-score order, and the slots the next attention
+// reads are stamped with `step` ([EXPL] Table 2 runs LRU eviction).
 constexpr int kDiffWaveMaxBudget = 2 * kWave;
 
-__device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL, const int32_t* b2sL,
-                                 const int (&sb)[2], const float (&sv)[2], int32_t* __restrict__ bu,
+__device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL,
+                                          const int32_t* b2sL, const int (&sb)[2], const float (&sv)[2],
+                                          const int (&luv)[2], int32_t* __restrict__ lu, int step,
+                                          int32_t* __restrict__ bu,
                                  int32_t* __restrict__ slu, int32_t* __restrict__ fetch,
                                  int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict,
                                  int32_t* __restrict__ attend, int32_t* __restrict__ n_attend,
@@ -235,6 +241,7 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
   int32_t* vict = freeS + kb;
   int32_t* victS = vict + cap;
   int32_t* candS = victS + cap;
+  int32_t* candA = candS + kb;  // LRU: the candidates' stamps
 
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t below = (1ull << lane) - 1ull;
@@ -289,6 +296,7 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
         const int pos = (e ? nc0 : 0) + __popcll(bc[e] & below);
         candK[pos] = ck[e];  // complemented: a larger key ranks first
         candS[pos] = lane + e * kWave;
+        if (lu != nullptr) candA[pos] = luv[e];
       }
     // Consistent maps with at most k selected blocks always leave enough
     // victims; clamp anyway so inconsistent input stays within the buffers.
@@ -299,15 +307,34 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     constexpr int kBatch = 8;
     int r0 = 0, r1 = 0;
-    for (int j = 0; j < nc; j += kBatch) {
-      unsigned long long x[kBatch];
+    if (lu == nullptr) {
+      for (int j = 0; j < nc; j += kBatch) {
+        unsigned long long x[kBatch];
 #pragma unroll
-      for (int t = 0; t < kBatch; ++t) x[t] = candK[min(j + t, nc - 1)];
+        for (int t = 0; t < kBatch; ++t) x[t] = candK[min(j + t, nc - 1)];
 #pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        const bool ok = j + t < nc;
-        r0 += static_cast<int>(ok & (x[t] < ck[0]));
-        r1 += static_cast<int>(ok & (x[t] < ck[1]));
+        for (int t = 0; t < kBatch; ++t) {
+          const bool ok = j + t < nc;
+          r0 += static_cast<int>(ok & (x[t] < ck[0]));
+          r1 += static_cast<int>(ok & (x[t] < ck[1]));
+        }
+      }
+    } else {
+      // (older stamp, then the lowest-score order) ranks first
+      for (int j = 0; j < nc; j += kBatch) {
+        unsigned long long x[kBatch];
+        int a[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          x[t] = candK[min(j + t, nc - 1)];
+          a[t] = candA[min(j + t, nc - 1)];
+        }
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) {
+          const bool ok = j + t < nc;
+          r0 += static_cast<int>(ok & ((a[t] < luv[0]) | ((a[t] == luv[0]) & (x[t] < ck[0]))));
+          r1 += static_cast<int>(ok & ((a[t] < luv[1]) | ((a[t] == luv[1]) & (x[t] < ck[1]))));
+        }
       }
     }
     const int r[2] = {r0, r1};
@@ -338,8 +365,9 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
   }
   if (lane == 0) n_fetch[unit] = nF;
 
-  // 5. the attended list for the next attention (selection order)
-  if (attend != nullptr) {
+  // 5. the attended list for the next attention (selection order); with LRU
+  // its slots take this step's stamp
+  if (attend != nullptr || lu != nullptr) {
     int sa[2];
     uint64_t ba[2];
 #pragma unroll
@@ -347,7 +375,9 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
       sa[e] = -1;
       if (bok[e]) sa[e] = (res[e] >= 0) ? res[e] : ((miss[e] && mrank[e] < nF) ? tgt[mrank[e]] : -1);
       ba[e] = __ballot(in[e] && sa[e] >= 0 && sa[e] < kb);
+      if (lu != nullptr && ((ba[e] >> lane) & 1ull)) lu[sa[e]] = step;
     }
+    if (attend == nullptr) return;
     const int na0 = __popcll(ba[0]);
     int32_t* au = attend + static_cast<size_t>(unit) * kb;
 #pragma unroll

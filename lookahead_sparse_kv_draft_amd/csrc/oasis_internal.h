@@ -64,9 +64,17 @@ hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st);
 bool select_diff_fused_available(const Ctx& c);
+// Least-recently-used eviction (null last_use: lowest-score eviction): the
+// per-slot stamps [B][H][k] and this step's stamp.  Supported by the fused
+// selection + diff for k <= 128 (select_diff_lru_available).
+struct LruState {
+  int32_t* last_use = nullptr;
+  int step = 0;
+};
+bool select_diff_lru_available(const Ctx& c);
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
-                              int32_t* attend, int32_t* n_attend, hipStream_t st);
+                              int32_t* attend, int32_t* n_attend, hipStream_t st, LruState lru = {});
 hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, int32_t* b2s,
                        int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                        int32_t* attend, int32_t* n_attend, hipStream_t st);
@@ -94,7 +102,7 @@ hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, 
 hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                                       int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                                       int32_t* attend, int32_t* n_attend, const void* ws, float* out,
-                                      hipStream_t st);
+                                      hipStream_t st, LruState lru = {});
 // The split combine and the lookahead score in one launch (bf16 only).
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st);

@@ -455,8 +455,8 @@ __device__ __forceinline__ void select_diff_unit(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
-    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, unsigned long long* smem_u64,
-    TopkFastShared& sh, DiffShared& dsh) {
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step,
+    unsigned long long* smem_u64, TopkFastShared& sh, DiffShared& dsh) {
   int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
@@ -470,11 +470,14 @@ __device__ __forceinline__ void select_diff_unit(
     int bv[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) bv[u] = bu[min(u * kTkThreads + tid, Nmax - 1)];
-    int sbw[2];
+    int sbw[2], luw[2] = {0, 0};
     float svw[2];
+    int32_t* lu = (last_use != nullptr) ? last_use + static_cast<size_t>(unit) * kb : nullptr;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      sbw[e] = slu[min((tid & (kWave - 1)) + e * kWave, kb - 1)];  // clamped: no branch around the loads
+      const int ie = min((tid & (kWave - 1)) + e * kWave, kb - 1);  // clamped: no branch around the loads
+      sbw[e] = slu[ie];
+      if (lu != nullptr) luw[e] = lu[ie];
       svw[e] = su[(sbw[e] >= 0 && sbw[e] < Nmax) ? sbw[e] : 0];
     }
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
@@ -485,8 +488,8 @@ __device__ __forceinline__ void select_diff_unit(
       if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
     __syncthreads();
     if (tid >= kWave) return;
-    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, svw, bu, slu, fetch, n_fetch, evict, attend, n_attend,
-              smem_u64);
+    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, svw, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
+              n_attend, smem_u64);
     return;
   }
   const int sb = slu[min(tid, kb - 1)];  // clamped: no branch around the loads
@@ -502,12 +505,12 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
-    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap) {
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step) {
   extern __shared__ unsigned long long smem_u64[];
   __shared__ TopkFastShared sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
-                        smem_u64, sh, dsh);
+                        last_use, step, smem_u64, sh, dsh);
 }
 
 // The fused selection + diff in workgroups [0, units), then the attention's
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
     int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int units,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, float* __restrict__ out, int arows,
-    int splits, int comb_total) {
+    int splits, int comb_total, int32_t* __restrict__ last_use, int step) {
   if (static_cast<int>(blockIdx.x) >= units) {
     attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, arows, splits, comb_total,
                               (blockIdx.x - units) * kTkWaves + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
@@ -529,41 +532,42 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
   __shared__ TopkFastShared sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
-                        smem_u64, sh, dsh);
+                        last_use, step, smem_u64, sh, dsh);
 }
 
 template <int KPT, int D, int SMAX>
 hipError_t sdc_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
   const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   const int comb_total = c.units * c.rows_attn;
   const int ncomb = (comb_total + kTkWaves - 1) / kTkWaves;
   hipLaunchKernelGGL((select_diff_combine_kernel<KPT, D, SMAX>), dim3(c.units + ncomb), dim3(kTkThreads), lds, st,
                      scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads,
-                     c.s.max_blocks, kb, cap, c.units, ws_acc, ws_ml, out, c.rows_attn, c.attn_splits, comb_total);
+                     c.s.max_blocks, kb, cap, c.units, ws_acc, ws_ml, out, c.rows_attn, c.attn_splits, comb_total,
+                     lru.last_use, lru.step);
   return hipGetLastError();
 }
 
 template <int KPT, int D>
 hipError_t sdc_s(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
   const int S = c.attn_splits;
-  if (S <= 4) return sdc_t<KPT, D, 4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  if (S <= 8) return sdc_t<KPT, D, 8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  if (S <= 16) return sdc_t<KPT, D, 16>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  return sdc_t<KPT, D, 32>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (S <= 4) return sdc_t<KPT, D, 4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (S <= 8) return sdc_t<KPT, D, 8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (S <= 16) return sdc_t<KPT, D, 16>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  return sdc_t<KPT, D, 32>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
 }
 
 template <int KPT>
 hipError_t sdc_d(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
   return c.s.head_dim == 128
-             ? sdc_s<KPT, 128>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st)
-             : sdc_s<KPT, 64>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+             ? sdc_s<KPT, 128>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru)
+             : sdc_s<KPT, 64>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
 }
 
 template <int KPT>
@@ -576,11 +580,12 @@ hipError_t fast_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int
 template <int KPT>
 hipError_t select_diff_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                          int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                         int32_t* n_attend, hipStream_t st) {
+                         int32_t* n_attend, hipStream_t st, LruState lru) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
   const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   hipLaunchKernelGGL((select_diff_kernel<KPT>), dim3(c.units), dim3(kTkThreads), lds, st, scores, ctx_len, sel,
-                     b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap);
+                     b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap,
+                     lru.last_use, lru.step);
   return hipGetLastError();
 }
 
@@ -590,27 +595,33 @@ bool select_diff_fused_available(const Ctx& c) {
   return c.s.budget_blocks - 2 <= kTkMaxWin && c.s.max_blocks <= 8 * kTkThreads;
 }
 
+bool select_diff_lru_available(const Ctx& c) {
+  return select_diff_fused_available(c) && c.s.budget_blocks <= kDiffWaveMaxBudget;
+}
+
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
-                              int32_t* attend, int32_t* n_attend, hipStream_t st) {
+                              int32_t* attend, int32_t* n_attend, hipStream_t st, LruState lru) {
+  if (lru.last_use != nullptr && !select_diff_lru_available(c)) return hipErrorInvalidValue;
   const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
-  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
-  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
-  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
-  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
+  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
+  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
+  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
 }
 
 hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                                       int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                                       int32_t* attend, int32_t* n_attend, const void* ws, float* out,
-                                      hipStream_t st) {
+                                      hipStream_t st, LruState lru) {
+  if (lru.last_use != nullptr && !select_diff_lru_available(c)) return hipErrorInvalidValue;
   const float* ws_acc = static_cast<const float*>(ws);
   const float* ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + attn_ws_acc_bytes(c));
   const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
-  if (kpt <= 1) return sdc_d<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  if (kpt <= 2) return sdc_d<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  if (kpt <= 4) return sdc_d<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
-  return sdc_d<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (kpt <= 1) return sdc_d<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (kpt <= 2) return sdc_d<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (kpt <= 4) return sdc_d<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  return sdc_d<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
 }
 
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,

@@ -81,6 +81,11 @@ def test_sizes_and_null_checks():
         assert lib.oasis_attend_and_score(h, *([None] * 13)) == L.OASIS_EINVAL
         assert lib.oasis_attn_combine(h, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_select_diff_combine(h, *([None] * 13)) == L.OASIS_EINVAL
+        assert lib.oasis_select_and_diff_lru(h, *([None] * 6), 0, *([None] * 6)) == L.OASIS_EINVAL
+        assert lib.oasis_select_diff_combine_lru(h, *([None] * 6), 0, *([None] * 8)) == L.OASIS_EINVAL
+        # LRU needs the stamps
+        assert lib.oasis_select_and_diff_lru(h, *([256] * 5), None, 3, *([256] * 3), None, None, None) \
+            == L.OASIS_EINVAL
         # attention inputs: the maps are needed when no attended list is given
         assert lib.oasis_attend_and_score(h, *([256] * 5), None, None, None, None, 256, 256, 256, None) \
             == L.OASIS_EINVAL

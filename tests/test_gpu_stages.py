@@ -582,3 +582,109 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
         assert np.array_equal(b2s[u], ref.block_to_slot) and np.array_equal(s2b[u], ref.slot_to_block)
         assert am[u] == [(b << 10) | int(ref.block_to_slot[b]) for b in O.attended_blocks(ref_sel, ref.block_to_slot)]
     L.oasis_destroy(h)
+
+
+# ------------------------------------------------------------------ LRU eviction
+@pytest.mark.parametrize("k,cap,N,kind,steps", [
+    (128, 32, 2048, "normal", 6), (128, 8, 700, "ties", 6), (16, 4, 64, "normal", 8),
+    (64, 64, 300, "normal", 5), (128, 0, 500, "normal", 3), (8, 3, 40, "const", 6), (2, 2, 9, "normal", 4),
+])
+def test_select_and_diff_lru_parity(k, cap, N, kind, steps):
+    """Several steps in a row of selection + diff with least-recently-used
+    eviction against the oracle, bit for bit: selection, fetch and eviction
+    lists, both maps, the per-slot stamps and the attended list."""
+    B, H = 2, 3
+    units = B * H
+    ctxs = [N * BLK, max(1, N * BLK - 37)]
+    sh = U.make_shape(batch=B, kv_heads=H, max_blocks=N, budget_blocks=k, fetch_cap=cap)
+    h = sh.handle()
+    rng = _rng(21)
+    b2ss, s2bs, lus = [], [], []
+    for u in range(units):
+        Nu = (ctxs[u // H] + BLK - 1) // BLK
+        _, _, b2s, s2b = _random_state(rng, Nu, k, [0, k // 2, k][u % 3], kind)
+        full = np.full(N, -1, dtype=np.int64)
+        full[:Nu] = b2s
+        b2ss.append(full), s2bs.append(s2b), lus.append(rng.integers(-1, 3, size=k))
+    b2s_d, s2b_d, lu_d = U.i32(b2ss), U.i32(s2bs), U.i32(lus)
+    ctx_d = U.i32(ctxs)
+    cw = max(cap, 1)
+    sel_d = torch.full((units, k), -9, dtype=torch.int32, device="cuda")
+    for t in range(steps):
+        scs = np.stack([random_scores(rng, N, kind) for _ in range(units)])
+        sc_d = torch.from_numpy(scs).cuda()
+        fetch = torch.full((units, cw, 2), -9, dtype=torch.int32, device="cuda")
+        nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+        ev = torch.full((units, cw), -9, dtype=torch.int32, device="cuda")
+        att = torch.full((units, k), -9, dtype=torch.int32, device="cuda")
+        natt = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+        L.oasis_select_and_diff_lru(h, sc_d, ctx_d, sel_d, b2s_d, s2b_d, lu_d, 100 + t, fetch, nf, ev, att, natt)
+        torch.cuda.synchronize()
+        g = [x.cpu().numpy() for x in (sel_d, b2s_d, s2b_d, lu_d, fetch, nf, ev, att, natt)]
+        for u in range(units):
+            Nu = (ctxs[u // H] + BLK - 1) // BLK
+            sel = O.topk_select(scs[u].astype(np.float64), Nu, k)
+            ref = O.resident_diff_cap_evict_lru(sel, scs[u].astype(np.float64), b2ss[u], s2bs[u], lus[u], cap, 100 + t)
+            assert list(g[0][u]) == sel, (t, u)
+            assert np.array_equal(g[1][u], ref.block_to_slot), (t, u)
+            assert np.array_equal(g[2][u], ref.slot_to_block), (t, u)
+            assert np.array_equal(g[3][u], ref.last_use), (t, u)
+            assert g[5][u] == len(ref.fetch), (t, u)
+            if cap > 0:
+                exp_f = np.full((cw, 2), -1)
+                for i, (b, s) in enumerate(ref.fetch):
+                    exp_f[i] = (b, s)
+                assert np.array_equal(g[4][u], exp_f), (t, u)
+                exp_e = np.full(cap, -1)
+                exp_e[: len(ref.evict)] = ref.evict
+                assert np.array_equal(g[6][u], exp_e), (t, u)
+            exp_att = [(b << 10) | int(ref.block_to_slot[b]) for b in O.attended_blocks(sel, ref.block_to_slot)]
+            assert g[8][u] == len(exp_att) and list(g[7][u][: len(exp_att)]) == exp_att, (t, u)
+            b2ss[u], s2bs[u], lus[u] = ref.block_to_slot, ref.slot_to_block, ref.last_use
+    # more than 128 blocks of budget: not supported by the LRU variant
+    h2 = U.make_shape(batch=1, kv_heads=1, max_blocks=300, budget_blocks=256, fetch_cap=4).handle()
+    z = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    with pytest.raises(L.OasisError) as e:
+        L.oasis_select_and_diff_lru(h2, z, z, z, z, z, z, 0, z, z, z)
+    assert e.value.code == L.OASIS_EUNSUPPORTED
+    L.oasis_destroy(h2)
+    L.oasis_destroy(h)
+
+
+def test_select_diff_combine_lru_matches_two_calls():
+    """The step's second launch with LRU eviction leaves the same output and
+    state as the split combine followed by the LRU selection + diff."""
+    from workload import CONFIGS
+    from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
+    cfg = CONFIGS["llama8b_32k"].with_(batch=2, ctx=16 * 300 + 7, steps=3, fetch_cap=8, planted=15,
+                                       budget_tokens=16 * 32)
+    run = SyntheticRun(cfg, overlap=False, replicas=2)
+    try:
+        run.prologue()
+        rt = run.rt
+        rt.state[0][1].copy_from(rt.state[0][0])
+        lus = [torch.full((rt.shape.units, rt.shape.budget_blocks), -1, dtype=torch.int32, device="cuda")
+               for _ in range(2)]
+        outs = [torch.zeros_like(rt.out) for _ in range(2)]
+        for t in range(cfg.steps):
+            q = run.q[0, t + 1]
+            for rep in range(2):
+                st = rt.state[0][rep]
+                L.oasis_attend_and_score(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.attend,
+                                         st.n_attend, st.scores, outs[rep], rt.ws_ptr)
+                if rep == 0:
+                    L.oasis_select_diff_combine_lru(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, lus[rep], t,
+                                                    st.fetch, st.n_fetch, st.evict, st.attend, st.n_attend,
+                                                    outs[rep], rt.ws_ptr)
+                else:
+                    L.oasis_attn_combine(rt.h, rt.ws_ptr, outs[rep])
+                    L.oasis_select_and_diff_lru(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, lus[rep], t,
+                                                st.fetch, st.n_fetch, st.evict, st.attend, st.n_attend)
+            torch.cuda.synchronize()
+            a, b = rt.state[0][0], rt.state[0][1]
+            assert torch.equal(outs[0], outs[1]), t
+            assert torch.equal(lus[0], lus[1]), t
+            for name in ("sel", "b2s", "s2b", "fetch", "n_fetch", "evict", "attend", "n_attend"):
+                assert torch.equal(getattr(a, name), getattr(b, name)), (t, name)
+    finally:
+        run.close()
