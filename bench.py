@@ -66,6 +66,8 @@ def parse():
     p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
     p.add_argument("--cap-fracs", default="0,0.01,0.02,0.05,0.10,0.20,1.0",
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
+    p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
+                   help="--pipeline eviction policies: lowest score, least recently used, or both")
     p.add_argument("--mode", choices=["graph", "overlap", "eager"], default="eager",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
                         "second stream beside the attention, captured likewise; eager: plain launches")
@@ -314,9 +316,11 @@ def pipeline_sweep(args):
     compute stream and its fetched pages move with the device-driven gather on
     the side stream; layer l's next attention waits only for layer l's gather, so
     each layer's transfer runs while the later layers (and the next step's
-    earlier layers) compute.  For each fetch cap: the HBM-resident step time
-    (H1, no transfer), the end-to-end step time (H2), exposed transfer = H2 - H1,
-    bytes fetched per step and the gather's PCIe rate."""
+    earlier layers) compute.  For each eviction policy (lowest score; least
+    recently used) and fetch cap, from the same starting state: the
+    HBM-resident step time (H1, no transfer), the end-to-end step time (H2),
+    exposed transfer = H2 - H1, bytes fetched per step and the gather's PCIe
+    rate."""
     import torch
 
     from lookahead_sparse_kv_draft_amd import _lib as L
@@ -327,89 +331,110 @@ def pipeline_sweep(args):
     kb = base.k
     fracs = [float(x) for x in args.cap_fracs.split(",")]
     caps = sorted({min(kb, int(round(f * kb))) if f < 1.0 else kb for f in fracs})
+    policies = ["score", "lru"] if args.eviction == "both" else [args.eviction]
     cfg = base.with_(layers=args.layers, fetch_cap=max(caps))
     torch.cuda.set_device(0)
-    print(f"# pipeline: {cfg.name} x {cfg.layers} layers, caps {caps}", file=sys.stderr, flush=True)
-    run = SyntheticRun(cfg, overlap=False)
+    print(f"# pipeline: {cfg.name} x {cfg.layers} layers, caps {caps}, eviction {policies}", file=sys.stderr,
+          flush=True)
+    run = SyntheticRun(cfg, overlap=False, replicas=2)  # replica 1 keeps the starting state
     run.prologue()
     rt = run.rt
+    nl = run.L
+    for l in range(nl):
+        rt.state[l][1].copy_from(rt.state[l][0])
     torch.cuda.synchronize()
     cs = torch.cuda.current_stream()
     side = rt.side
-    nl = run.L
     page = L.oasis_page_bytes(rt.h)
+    units, k = rt.shape.units, rt.shape.budget_blocks
+    lus = [torch.full((units, k), -1, dtype=torch.int32, device="cuda") for _ in range(nl)]
     ev_sel = [torch.cuda.Event() for _ in range(nl)]
     ev_fetch = [torch.cuda.Event() for _ in range(nl)]
     nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
     points = []
-    for cap in caps:
-        h = rt.shape.handle(fetch_cap=cap)
-
-        def step(i, transfer, first=False, count=False):
-            t = i % cfg.steps
+    for policy in policies:
+        for cap in caps:
+            h = rt.shape.handle(fetch_cap=cap)
             for l in range(nl):
-                st = rt.state[l][0]
-                if transfer and not first:
-                    cs.wait_event(ev_fetch[l])
-                L.oasis_decode_step(h, run.q[l, t + 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
-                                    st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict,
-                                    st.attend, st.n_attend, stream=cs)
-                if count:
-                    nf_tot.add_(st.n_fetch.sum())
-                if transfer:
-                    ev_sel[l].record(cs)
-                    side.wait_event(ev_sel[l])
+                rt.state[l][0].copy_from(rt.state[l][1])
+                lus[l].fill_(-1)
+            clock = [0]
+
+            def step(i, transfer, first=False, count=False):
+                t = i % cfg.steps
+                clock[0] += 1
+                for l in range(nl):
+                    st = rt.state[l][0]
+                    if transfer and not first:
+                        cs.wait_event(ev_fetch[l])
+                    q = run.q[l, t + 1]
+                    if policy == "score":
+                        L.oasis_decode_step(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
+                                            st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                            st.n_attend, stream=cs)
+                    else:
+                        L.oasis_attend_and_score(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                                 st.attend, st.n_attend, st.scores, rt.out, rt.ws_ptr, cs)
+                        L.oasis_select_diff_combine_lru(h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, lus[l],
+                                                        clock[0], st.fetch, st.n_fetch, st.evict, st.attend,
+                                                        st.n_attend, rt.out, rt.ws_ptr, cs)
+                    if count:
+                        nf_tot.add_(st.n_fetch.sum())
+                    if transfer:
+                        ev_sel[l].record(cs)
+                        side.wait_event(ev_sel[l])
+                        L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+                        ev_fetch[l].record(side)
+
+            K = args.steps
+            res = {}
+            for transfer in (False, True):
+                for i in range(args.warmup):
+                    step(i, transfer, first=(i == 0))
+                cs.wait_stream(side)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(K):
+                    step(i, transfer)
+                cs.wait_stream(side)
+                torch.cuda.synchronize()
+                res[transfer] = (time.perf_counter() - t0) / K * 1e6
+            nf_tot.zero_()
+            for i in range(K):  # untimed: pages fetched per step
+                step(i, True, count=True)
+            cs.wait_stream(side)
+            torch.cuda.synchronize()
+            fetched = float(nf_tot.item()) * page / K
+            # the gather alone, back to back on the side stream, over the last lists of every layer
+            eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            eb.record(side)
+            for _ in range(4):
+                for l in range(nl):
+                    st = rt.state[l][0]
                     L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
-                    ev_fetch[l].record(side)
-
-        K = args.steps
-        res = {}
-        for transfer in (False, True):
-            for i in range(args.warmup):
-                step(i, transfer, first=(i == 0))
-            cs.wait_stream(side)
+            ee.record(side)
             torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(K):
-                step(i, transfer)
-            cs.wait_stream(side)
-            torch.cuda.synchronize()
-            res[transfer] = (time.perf_counter() - t0) / K * 1e6
-        nf_tot.zero_()
-        for i in range(K):  # untimed: pages fetched per step
-            step(i, True, count=True)
-        cs.wait_stream(side)
-        torch.cuda.synchronize()
-        fetched = float(nf_tot.item()) * page / K
-        # the gather alone, back to back on the side stream, over the last lists of every layer
-        eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        eb.record(side)
-        for _ in range(4):
-            for l in range(nl):
-                st = rt.state[l][0]
-                L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
-        ee.record(side)
-        torch.cuda.synchronize()
-        g_us = eb.elapsed_time(ee) * 1e3 / 4
-        last = sum(int(rt.state[l][0].n_fetch.sum()) for l in range(nl)) * page
-        points.append({"cap": cap, "cap_frac_of_k": cap / kb, "h1_us_per_step": res[False],
-                       "h2_us_per_step": res[True], "exposed_transfer_us_per_step": res[True] - res[False],
-                       "fetched_MB_per_step": fetched / 1e6, "gather_us_per_step": g_us,
-                       "gather_GBs": last / (g_us * 1e-6) / 1e9 if g_us > 0 else None,
-                       "h2_steps_per_s": cfg.batch * nl * 1e6 / res[True]})
-        print(f"# cap {cap}: H1 {res[False]:.1f} us, H2 {res[True]:.1f} us, {fetched / 1e6:.2f} MB/step",
-              file=sys.stderr, flush=True)
-        L.oasis_destroy(h)
+            g_us = eb.elapsed_time(ee) * 1e3 / 4
+            last = sum(int(rt.state[l][0].n_fetch.sum()) for l in range(nl)) * page
+            points.append({"eviction": policy, "cap": cap, "cap_frac_of_k": cap / kb,
+                           "h1_us_per_step": res[False], "h2_us_per_step": res[True],
+                           "exposed_transfer_us_per_step": res[True] - res[False],
+                           "fetched_MB_per_step": fetched / 1e6, "gather_us_per_step": g_us,
+                           "gather_GBs": last / (g_us * 1e-6) / 1e9 if g_us > 0 else None,
+                           "h2_steps_per_s": cfg.batch * nl * 1e6 / res[True]})
+            print(f"# {policy} cap {cap}: H1 {res[False]:.1f} us, H2 {res[True]:.1f} us, "
+                  f"{fetched / 1e6:.2f} MB/step", file=sys.stderr, flush=True)
+            L.oasis_destroy(h)
     run.close()
     print(json.dumps({
-        "metric": "cross-layer pipeline: exposed transfer per decode step vs fetch cap",
+        "metric": "cross-layer pipeline: exposed transfer per decode step vs fetch cap and eviction policy",
         "unit": "us per step (all layers, whole batch)",
         "config": {"workload": f"{cfg.name} shape, {nl} layers, batch {cfg.batch}, ctx {cfg.ctx}, k {kb} blocks",
                    "layers": nl, "steps": args.steps, "warmup": args.warmup},
         "data": "synthetic", "points": points,
         "note": "H1 = decode steps with inputs resident (no transfer); H2 = with every step's fetched pages "
                 "moved by the device-driven gather on a side stream, each layer's next attention waiting for "
-                "its own gather only"}))
+                "its own gather only; every (policy, cap) run starts from the same state"}))
 
 
 def main():
