@@ -64,6 +64,9 @@ def parse():
                    help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
                         "(one JSON line per sweep instead of the headline)")
     p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
+    p.add_argument("--recall", action="store_true",
+                   help="prediction recall of the drafts' selection against the verify query's own selection, "
+                        "and the cost of a blocking corrective fetch (one JSON line)")
     p.add_argument("--cap-fracs", default="0,0.01,0.02,0.05,0.10,0.20,1.0",
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
@@ -437,8 +440,89 @@ def pipeline_sweep(args):
                 "its own gather only; every (policy, cap) run starts from the same state"}))
 
 
+def recall_measure(args):
+    """Prediction recall and corrective fetch on one layer.  At step t the drafts
+    of step t-1 predicted S_pred(t) (the selection in place before step t's decode
+    call); the verify query of step t selects S_exact(t) with the same bound and
+    top-k rule.  Reports recall |S_pred & S_exact| / |S_exact| and the recall of
+    S_exact's 20 highest-ranked blocks, the blocks of S_exact not resident after
+    the prefetch (what a corrective fetch moves), and the step time of the chain
+    without and with the blocking corrective fetch (each step's prefetch lands
+    before the next step, as in a single-layer chain)."""
+    import torch
+
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
+    from workload import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    run = SyntheticRun(cfg, overlap=False, replicas=2)
+    run.prologue()
+    rt = run.rt
+    rt.state[0][1].copy_from(rt.state[0][0])  # the starting state of every pass
+    cs = torch.cuda.current_stream()
+    page = L.oasis_page_bytes(rt.h)
+    steps = min(args.steps, cfg.steps)
+
+    def chain(corrective, stats=None):
+        st = rt.state[0][0]
+        st.copy_from(rt.state[0][1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            q = run.q[0, t + 1]
+            if stats is not None:
+                rt.exact_select(0, q)
+                pred = st.sel.cpu().numpy()
+                exact = st.vsel.cpu().numpy()
+                b2s = st.b2s.cpu().numpy()
+                for u in range(pred.shape[0]):
+                    P = {int(b) for b in pred[u] if b >= 0}
+                    E = [int(b) for b in exact[u] if b >= 0]
+                    stats["recall"].append(len(P & set(E)) / len(E))
+                    stats["recall20"].append(len(P & set(E[:20])) / min(20, len(E)))
+                    stats["missed"].append(sum(1 for b in E if b2s[u, b] < 0))
+            if corrective:
+                rt.corrective(0, q)
+            L.oasis_decode_step(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
+                                st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                st.n_attend, stream=cs)
+            L.oasis_fetch_gather(rt.h, st.host_tier, st.pool, st.fetch, st.n_fetch, cs)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    chain(False)  # warm-up
+    chain(True)
+    t_pred = chain(False)
+    t_corr = chain(True)
+    stats = {"recall": [], "recall20": [], "missed": []}
+    chain(True, stats)
+    run.close()
+    units = cfg.batch * cfg.kv_heads
+    missed = np.array(stats["missed"], dtype=np.float64).reshape(steps, units)
+    print(json.dumps({
+        "metric": "prediction recall of the draft-predicted selection vs the verify query's selection; "
+                  "corrective fetch cost",
+        "config": {"workload": f"{cfg.name}: batch {cfg.batch}, 1 layer, ctx {cfg.ctx}, k {cfg.k} blocks, "
+                               f"{cfg.n_draft} drafts, cap {cfg.fetch_cap}", "steps": steps},
+        "data": "synthetic",
+        "recall_at_k": {"mean": float(np.mean(stats["recall"])), "min": float(np.min(stats["recall"]))},
+        "recall_top20": {"mean": float(np.mean(stats["recall20"])), "min": float(np.min(stats["recall20"]))},
+        "corrective_pages_per_step": float(missed.sum(1).mean()),
+        "corrective_MB_per_step": float(missed.sum(1).mean() * page / 1e6),
+        "units_with_a_miss_frac": float((missed > 0).mean()),
+        "step_us_prefetch_only": t_pred,
+        "step_us_with_corrective_fetch": t_corr,
+        "note": "single-layer chain, every transfer on the compute stream (nothing hides it); recall per "
+                "(request, KV head) unit and step"}))
+
+
 def main():
     args = parse()
+    if args.recall:
+        recall_measure(args)
+        return
     if args.pipeline:
         pipeline_sweep(args)
         return

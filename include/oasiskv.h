@@ -153,6 +153,20 @@ int oasis_lookahead_score(oasis_handle h, const void* q, const void* meta, const
                           float* scores, void* stream);
 
 /*
+ * The same bound from the verify query rows (t = 0) instead of the drafts:
+ *   scores[u][b] = max over group heads g of
+ *                  sum_c max(q[0][g][c]*kmin[b][c], q[0][g][c]*kmax[b][c]).
+ * Selecting the top-k of these scores gives the set the true next-token query
+ * picks ([EXPL] Figure 6: the predicted top-K set against the exact set of the
+ * true next-token query); the blocks of that set that the lookahead prefetch
+ * missed are what a corrective fetch must bring in ([EXPL] "Limits and open
+ * work": prediction misses need corrective fetches).  Layout and errors as
+ * oasis_lookahead_score.
+ */
+int oasis_verify_score(oasis_handle h, const void* q, const void* meta, const int32_t* ctx_len, float* scores,
+                       void* stream);
+
+/*
  * Top-k selection.  sel [B][H][budget_blocks] int32 in rank order: the sink
  * block 0, then the newest block N-1 (if N > 1), then the other blocks by
  * descending score with ties broken by lower index (-0.0 ranks as +0.0), up to

@@ -55,6 +55,7 @@ SIGNATURES = {
     "oasis_block_meta_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
+    "oasis_verify_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_resident_diff_cap_evict": (_int, [_vp] * 11),
     "oasis_select_and_diff": (_int, [_vp] * 12),
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
@@ -266,3 +267,7 @@ def oasis_select_diff_combine_lru(h, scores, ctx_score, sel, block_to_slot, slot
     _call("oasis_select_diff_combine_lru", h, _ptr(scores), _ptr(ctx_score), _ptr(sel), _ptr(block_to_slot),
           _ptr(slot_to_block), _ptr(slot_last_use), int(step), _ptr(fetch), _ptr(n_fetch), _ptr(evict),
           _ptr(attend), _ptr(n_attend), _ptr(out), _ptr(workspace), _stream(stream))
+
+
+def oasis_verify_score(h, q, meta, ctx_len, scores, stream=None):
+    _call("oasis_verify_score", h, _ptr(q), _ptr(meta), _ptr(ctx_len), _ptr(scores), _stream(stream))

@@ -294,6 +294,19 @@ int oasis_lookahead_score(oasis_handle h, const void* q, const void* meta, const
                     "oasis_lookahead_score");
 }
 
+int oasis_verify_score(oasis_handle h, const void* q, const void* meta, const int32_t* ctx_len, float* scores,
+                       void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(meta);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(scores);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(meta);
+  return hip_status(oasis::launch_score(h->c, q, meta, ctx_len, scores, static_cast<hipStream_t>(stream), true),
+                    "oasis_verify_score");
+}
+
 int oasis_topk_select(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
                       void* stream) {
   CHECK_HANDLE(h);

@@ -59,8 +59,10 @@ hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids
 hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,
                               const int32_t* ctx_in, int32_t* ctx_out, void* meta, void* pool,
                               const int32_t* b2s, hipStream_t st);
+// The lookahead score from the draft rows, or (verify) the same bound from the
+// verify query rows.
 hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                        float* scores, hipStream_t st);
+                        float* scores, hipStream_t st, bool verify = false);
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st);
 bool select_diff_fused_available(const Ctx& c);

@@ -25,15 +25,15 @@ template <int D, int RT>
 __global__ __launch_bounds__(256) void score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
     const int32_t* __restrict__ ctx_len, float* __restrict__ scores, int H, int G, int T,
-    int ndraft, int rows, int Nmax, int waves_per_unit, int tpw, int total_waves) {
-  score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, rows, Nmax, waves_per_unit, tpw, total_waves,
+    int ndraft, int t0, int rows, int Nmax, int waves_per_unit, int tpw, int total_waves) {
+  score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, t0, rows, Nmax, waves_per_unit, tpw, total_waves,
                     blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void score_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ meta, const int32_t* __restrict__ ctx_len,
-    float* __restrict__ scores, int H, int G, int T, int ndraft, int rows, int Nmax) {
+    float* __restrict__ scores, int H, int G, int T, int ndraft, int t0, int rows, int Nmax) {
   extern __shared__ float qs[];  // [rows][D]
   const int unit = blockIdx.y;
   const int n = ctx_len[unit / H];
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
   if (static_cast<int>(blockIdx.x) * 256 >= N) return;
   for (int i = threadIdx.x; i < rows * D; i += blockDim.x) {
     const int row = i / D, c = i - (i / D) * D;
-    const int g = row / ndraft, t = 1 + (row - g * ndraft);
+    const int g = row / ndraft, t = t0 + (row - g * ndraft);
     qs[i] = q[((static_cast<size_t>(unit) * G + g) * T + t) * D + c];
   }
   __syncthreads();
@@ -59,50 +59,57 @@ __global__ __launch_bounds__(256) void score_f32_kernel(
   scores[static_cast<size_t>(unit) * Nmax + b] = best;
 }
 
+// Query rows scored: rows t0 .. t0 + nd - 1 of every group member (the drafts:
+// t0 = 1, nd = n_draft; the verify query: t0 = 0, nd = 1).
+struct ScoreRows {
+  int nd, t0, rows;
+};
+
 template <int D, int RT>
 hipError_t mfma_t(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                  float* scores, hipStream_t st) {
+                  float* scores, ScoreRows sr, hipStream_t st) {
   const int wpu = score_waves_per_unit(c);
   const int total = c.units * wpu;
   const int grid = (total + 3) / 4;
   hipLaunchKernelGGL((score_mfma_kernel<D, RT>), dim3(grid), dim3(256), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(meta), ctx_len,
-                     scores, c.s.kv_heads, c.s.group, c.T, c.s.n_draft, c.rows_score,
+                     scores, c.s.kv_heads, c.s.group, c.T, sr.nd, sr.t0, sr.rows,
                      c.s.max_blocks, wpu, c.score_tpw, total);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t f32_t(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                 float* scores, hipStream_t st) {
+                 float* scores, ScoreRows sr, hipStream_t st) {
   dim3 grid((c.s.max_blocks + 255) / 256, c.units);
-  const size_t lds = static_cast<size_t>(c.rows_score) * D * sizeof(float);
+  const size_t lds = static_cast<size_t>(sr.rows) * D * sizeof(float);
   hipLaunchKernelGGL((score_f32_kernel<D>), grid, dim3(256), lds, st,
                      static_cast<const float*>(q), static_cast<const float*>(meta), ctx_len, scores,
-                     c.s.kv_heads, c.s.group, c.T, c.s.n_draft, c.rows_score, c.s.max_blocks);
+                     c.s.kv_heads, c.s.group, c.T, sr.nd, sr.t0, sr.rows, c.s.max_blocks);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t mfma_rows(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                     float* scores, hipStream_t st) {
-  switch ((c.rows_score + 15) / 16) {
-    case 1: return mfma_t<D, 1>(c, q, meta, ctx_len, scores, st);
-    case 2: return mfma_t<D, 2>(c, q, meta, ctx_len, scores, st);
-    case 3: return mfma_t<D, 3>(c, q, meta, ctx_len, scores, st);
-    default: return mfma_t<D, 4>(c, q, meta, ctx_len, scores, st);
+                     float* scores, ScoreRows sr, hipStream_t st) {
+  switch ((sr.rows + 15) / 16) {
+    case 1: return mfma_t<D, 1>(c, q, meta, ctx_len, scores, sr, st);
+    case 2: return mfma_t<D, 2>(c, q, meta, ctx_len, scores, sr, st);
+    case 3: return mfma_t<D, 3>(c, q, meta, ctx_len, scores, sr, st);
+    default: return mfma_t<D, 4>(c, q, meta, ctx_len, scores, sr, st);
   }
 }
 
 }  // namespace
 
 hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                        float* scores, hipStream_t st) {
+                        float* scores, hipStream_t st, bool verify) {
+  const ScoreRows sr = verify ? ScoreRows{1, 0, c.s.group} : ScoreRows{c.s.n_draft, 1, c.rows_score};
   if (c.s.dtype == OASIS_BF16)
-    return c.s.head_dim == 128 ? mfma_rows<128>(c, q, meta, ctx_len, scores, st)
-                               : mfma_rows<64>(c, q, meta, ctx_len, scores, st);
-  return c.s.head_dim == 128 ? f32_t<128>(c, q, meta, ctx_len, scores, st)
-                             : f32_t<64>(c, q, meta, ctx_len, scores, st);
+    return c.s.head_dim == 128 ? mfma_rows<128>(c, q, meta, ctx_len, scores, sr, st)
+                               : mfma_rows<64>(c, q, meta, ctx_len, scores, sr, st);
+  return c.s.head_dim == 128 ? f32_t<128>(c, q, meta, ctx_len, scores, sr, st)
+                             : f32_t<64>(c, q, meta, ctx_len, scores, sr, st);
 }
 
 }  // namespace oasis

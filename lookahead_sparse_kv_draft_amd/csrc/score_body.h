@@ -22,7 +22,7 @@ inline int score_waves_per_unit(const Ctx& c) {
 template <int D, int RT>
 __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta,
                                   const int32_t* __restrict__ ctx_len, float* __restrict__ scores, int H, int G,
-                                  int T, int ndraft, int rows, int Nmax, int waves_per_unit, int tpw,
+                                  int T, int ndraft, int qt0, int rows, int Nmax, int waves_per_unit, int tpw,
                                   int total_waves, int wave, int lane) {
   constexpr int KSTEPS = D / 16;  // 32-element k-steps over the 2d metadata elements
   constexpr int HALF = KSTEPS / 2;  // steps on the kmin half
@@ -66,7 +66,7 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
     const int row = rt * 16 + col;
     if (row < rows) {
       const int g = row / ndraft;
-      const int t = 1 + (row - g * ndraft);
+      const int t = qt0 + (row - g * ndraft);  // query rows qt0 .. qt0 + ndraft - 1 of each group member
       const uint16_t* qr = q + ((static_cast<size_t>(unit) * G + g) * T + t) * D;
 #pragma unroll
       for (int s = 0; s < HALF; ++s) {

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void combine_score_kernel(
     attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, arows, splits, comb_total, blockIdx.x * 4 + wv, lane);
     return;
   }
-  score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, rows, Nmax, wpu, tpw, total_waves,
+  score_wave<D, RT>(q, meta, ctx_len, scores, H, G, T, ndraft, 1, rows, Nmax, wpu, tpw, total_waves,
                     (blockIdx.x - ncomb_wg) * 4 + wv, lane);
 }
 
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 
     attn_wg<D, RTA, 2, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
                           splits, run, scale_log2, idx);
   } else {
-    score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, srows, Nmax, wpu, tpw, total_waves,
+    score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, 1, srows, Nmax, wpu, tpw, total_waves,
                        idx * 2 + static_cast<int>(threadIdx.x) / kWave, threadIdx.x & (kWave - 1));
   }
 }

@@ -116,6 +116,7 @@ class LayerState:
         # attended list for the next attention (written by every diff)
         self.attend = torch.full((u, k), -1, dtype=torch.int32, device=dev)
         self.n_attend = torch.zeros(u, dtype=torch.int32, device=dev)
+        self.vscores = None  # corrective path buffers (allocated on first use)
         self.host_tier = host_tier
         self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
         self.n_fetch_host = torch.empty(u, dtype=torch.int32, pin_memory=True)
@@ -127,6 +128,19 @@ class LayerState:
         self.attn_done = torch.cuda.Event()
         self.select_done = torch.cuda.Event()
         self.select_pending = False
+
+    def ensure_corrective(self, rt: "DecodeRuntime"):
+        """Buffers of the corrective path: the verify query's scores and selection,
+        and an uncapped fetch / evict list."""
+        if self.vscores is not None:
+            return
+        s, dev = rt.shape, rt.device
+        u, k, N = s.units, s.budget_blocks, s.max_blocks
+        self.vscores = torch.zeros((u, N), dtype=torch.float32, device=dev)
+        self.vsel = torch.full((u, k), -1, dtype=torch.int32, device=dev)
+        self.cfetch = torch.full((u, k, 2), -1, dtype=torch.int32, device=dev)
+        self.cn_fetch = torch.zeros(u, dtype=torch.int32, device=dev)
+        self.cevict = torch.full((u, k), -1, dtype=torch.int32, device=dev)
 
     def copy_from(self, other: "LayerState"):
         for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict", "attend",
@@ -149,6 +163,7 @@ class DecodeRuntime:
         self.gather = gather
         self.device = torch.device(device)
         self.h = shape.handle()
+        self._h_full = None
         s = shape
         self.n_layers = layers
         self.replicas = replicas
@@ -175,6 +190,9 @@ class DecodeRuntime:
         if self.h:
             L.oasis_destroy(self.h)
             self.h = 0
+        if self._h_full:
+            L.oasis_destroy(self._h_full)
+            self._h_full = None
 
     # ------------------------------------------------------------ setup (untimed)
     @property
@@ -372,6 +390,43 @@ class DecodeRuntime:
         if self.overlap:
             st.select_done.record(ps)
             st.select_pending = True
+
+    def exact_select(self, layer: int, q: torch.Tensor, replica: int = 0):
+        """The set the verify query itself selects (same bound and top-k rule, from
+        the verify rows instead of the drafts) into st.vsel, with its scores in
+        st.vscores, on the current stream."""
+        st = self.state[layer][replica]
+        st.ensure_corrective(self)
+        cs = torch.cuda.current_stream()
+        L.oasis_verify_score(self.h, q, st.meta, self.ctx_len, st.vscores, cs)
+        L.oasis_topk_select(self.h, st.vscores, self.ctx_len, st.vsel, cs)
+
+    def corrective(self, layer: int, q: torch.Tensor, replica: int = 0):
+        """Blocking corrective fetch before this step's attention: the verify
+        query's own selection (exact_select), the blocks of it the prefetch missed
+        fetched without a cap on the current stream (victims: the lowest-scoring
+        resident blocks outside that set), and the attended list set to that set.
+        The next decode_step of the layer then attends over the exact set."""
+        st = self.state[layer][replica]
+        cs = torch.cuda.current_stream()
+        if st.fetch_wait_compute or st.fetch_wait_predict:  # a pending prefetch may target the same slots
+            cs.wait_event(st.fetch_done)
+            st.fetch_wait_compute = st.fetch_wait_predict = False
+        if st.select_pending:
+            cs.wait_event(st.select_done)
+            st.select_pending = False
+        self.exact_select(layer, q, replica)
+        hf = self.full_cap_handle()
+        L.oasis_resident_diff_cap_evict(hf, st.vsel, st.vscores, st.b2s, st.s2b, st.cfetch, st.cn_fetch, st.cevict,
+                                        st.attend, st.n_attend, cs)
+        L.oasis_fetch_gather(hf, st.host_tier, st.pool, st.cfetch, st.cn_fetch, cs)
+
+    def full_cap_handle(self) -> int:
+        """A handle of the same shape whose fetch cap is the whole budget (the
+        corrective fetch is not capped)."""
+        if self._h_full is None:
+            self._h_full = self.shape.handle(fetch_cap=self.shape.budget_blocks)
+        return self._h_full
 
     def transfer(self, layer: int, replica: int = 0, stream=None):
         """Move this step's fetched pages into the pool on the side stream, after the

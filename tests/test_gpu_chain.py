@@ -7,8 +7,10 @@ is independent of the others).
 """
 import numpy as np
 import pytest
+import torch
 
 from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
+from oracle import oasis_oracle as O
 from tests import chain_compare as CC
 from workload import CONFIGS
 
@@ -152,3 +154,41 @@ def test_chain_llama8b_128k_full_size_sampled():
     # 8192 blocks per head, 8 layers, 16 GiB host tier
     cfg = CONFIGS["llama8b_128k"]
     _run_and_compare(cfg, [(0, 0), (2, 13), (4, 22), (7, 31)])
+
+
+def test_corrective_fetch_makes_exact_set_resident():
+    """After a few capped prefetch steps, the corrective path selects the verify
+    query's own top-k (bit for bit the oracle's selection on the same scores),
+    fetches every block of it the prefetch missed, and leaves the attended list
+    equal to that set with the host tier's pages in its slots."""
+    cfg = CONFIGS["llama8b_32k"].with_(batch=2, ctx=16 * 300 + 7, steps=4, fetch_cap=2, planted=15,
+                                       budget_tokens=16 * 32)
+    run = SyntheticRun(cfg, overlap=False)
+    try:
+        run.prologue()
+        for t in range(2):
+            run.step(t)
+        rt = run.rt
+        st = rt.state[0][0]
+        q = run.q[0, 3]
+        rt.corrective(0, q)
+        torch.cuda.synchronize()
+        H = cfg.kv_heads
+        vs, vsel = st.vscores.cpu().numpy(), st.vsel.cpu().numpy()
+        b2s, att, natt = st.b2s.cpu().numpy(), st.attend.cpu().numpy(), st.n_attend.cpu().numpy()
+        ncf = st.cn_fetch.cpu().numpy()
+        pool = rt.pool_pages(0).cpu().numpy()
+        tier = rt.host_tier_view(0).numpy().reshape(rt.shape.units, rt.shape.max_blocks, -1)
+        assert ncf.sum() > 0, "the capped prefetch left nothing for the corrective fetch to do"
+        for u in range(rt.shape.units):
+            N = (int(rt.ctx_host[u // H]) + 15) // 16
+            ref = O.topk_select(vs[u].astype(np.float64), N, rt.shape.budget_blocks)
+            assert list(vsel[u]) == ref, u
+            S = [b for b in ref if b >= 0]
+            assert all(b2s[u, b] >= 0 for b in S), u
+            assert natt[u] == len(S) and [e >> 10 for e in att[u, :natt[u]]] == S, u
+            for e in att[u, :natt[u]]:
+                b, s = e >> 10, e & 1023
+                assert s == b2s[u, b] and np.array_equal(pool[u, s], tier[u, b]), (u, b)
+    finally:
+        run.close()

@@ -47,19 +47,22 @@ def test_score_parity(dtype, d, G, D, Nmax, ctxs):
     meta_d = U.to_dev(dtype, meta, tiled_meta=True)
     q_d = U.to_dev(dtype, q)
     ctx_d = U.i32(ctxs)
-    scores = torch.full((units, Nmax), float("nan"), device="cuda")
-    L.oasis_lookahead_score(h, q_d, meta_d, ctx_d, scores)
-    torch.cuda.synchronize()
-    got = scores.cpu().numpy().astype(np.float64)
-    for u in range(units):
-        r, hh = divmod(u, H)
-        N = (ctxs[r] + BLK - 1) // BLK
-        qd = q[r, hh * G:(hh + 1) * G, 1:, :].astype(np.float64)
-        ref = O.lookahead_score(qd, kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
-        tol = U.score_tolerance(qd.reshape(-1, d), kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
-        err = np.abs(got[u, :N] - ref)
-        assert np.all(err <= tol), (u, float(err.max()), float(tol.min()))
-        assert np.all(np.isnan(got[u, N:])), "blocks past the context must not be written"
+    # the drafts' lookahead score, then the same bound from the verify query rows
+    for fn, rows in ((L.oasis_lookahead_score, slice(1, None)), (L.oasis_verify_score, slice(0, 1))):
+        scores = torch.full((units, Nmax), float("nan"), device="cuda")
+        fn(h, q_d, meta_d, ctx_d, scores)
+        torch.cuda.synchronize()
+        got = scores.cpu().numpy().astype(np.float64)
+        for u in range(units):
+            r, hh = divmod(u, H)
+            N = (ctxs[r] + BLK - 1) // BLK
+            qd = q[r, hh * G:(hh + 1) * G, rows, :].astype(np.float64)
+            ref = O.lookahead_score(qd, kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
+            tol = U.score_tolerance(qd.reshape(-1, d), kmin[u, :N].astype(np.float64),
+                                    kmax[u, :N].astype(np.float64))
+            err = np.abs(got[u, :N] - ref)
+            assert np.all(err <= tol), (fn.__name__, u, float(err.max()), float(tol.min()))
+            assert np.all(np.isnan(got[u, N:])), "blocks past the context must not be written"
     L.oasis_destroy(h)
 
 
