@@ -33,7 +33,8 @@ MALL_BYTES = 256 * 2**20
 CALIB_ELEMS = 2**28  # float32: 1 GiB
 CSRC = os.path.join(ROOT, "lookahead_sparse_kv_draft_amd", "csrc")
 # source files of each op's kernels (a traffic measurement is valid while they are unchanged)
-OP_SOURCES = {"attend_and_score": ["step.hip", "attn_body.h", "score_body.h", "oasis_internal.h"],
+# (api.cpp holds the launch shapes)
+OP_SOURCES = {"attend_and_score": ["step.hip", "attn_body.h", "score_body.h", "oasis_internal.h", "api.cpp"],
               "select_diff_combine": ["select.hip", "diff_body.h", "block_ops.h", "attn_combine.h",
                                       "oasis_internal.h"],
               "sparse_paged_decode_attn": ["attn.hip", "attn_body.h", "attn_combine.h", "oasis_internal.h"],

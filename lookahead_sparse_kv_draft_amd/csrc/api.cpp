@@ -123,8 +123,17 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   if (waves != 1 && waves != 2 && waves != 4) waves = 2;
   waves = std::min(waves, max_waves);
   const int kbud = s.budget_blocks;
+  // The decode step's first launch (attention beside the scoring, bf16 with the
+  // default shape) is best with about twice as many attention wavefronts and
+  // runs of 2 scoring tiles (a sweep of splits x tiles per wavefront on the
+  // 32K-context batch-8 step: 36.3 us against 37.7 us for the standalone
+  // kernels' defaults).
+  const bool step_fused = s.dtype == OASIS_BF16 && waves == 2 && rows_attn <= 48;
   int splits = env_int("OASIS_ATTN_SPLITS", 0);
-  if (splits <= 0) splits = (512 + c.units * waves - 1) / (c.units * waves);
+  if (splits <= 0) {
+    const int target = step_fused ? 1024 : 512;
+    splits = (target + c.units * waves - 1) / (c.units * waves);
+  }
   const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
   const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
   splits = std::max(min_splits, std::min(splits, max_splits));
@@ -144,7 +153,7 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   int tpw = env_int("OASIS_SCORE_TPW", 0);
   if (tpw <= 0) {
     const long long tiles = units * ((s.max_blocks + 15) / 16);
-    tpw = static_cast<int>(std::max(1LL, std::min(16LL, tiles / 2048)));
+    tpw = static_cast<int>(std::max(1LL, std::min(16LL, tiles / (step_fused ? 4096 : 2048))));
   }
   c.score_tpw = tpw;
   c.step_order = env_int("OASIS_STEP_ORDER", 0);
