@@ -710,6 +710,20 @@ def main():
 
     h2 = None if args.no_h2 else measure_h2(args, cfg, run, rt, replicas, sequential_step, step_call_us)
 
+    # achievable-bandwidth reference on this machine: torch's device copy of 1 GiB
+    # (1 GiB read + 1 GiB written), HIP events around 5 copies after a warm-up
+    src = torch.empty(CALIB_ELEMS, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb.record(cs0)
+    for _ in range(5):
+        dst.copy_(src)
+    ee.record(cs0)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * CALIB_ELEMS * 4 / (eb.elapsed_time(ee) * 1e-3) / 1e9
+    del src, dst
+
     if args.calib_copy:
         # counter calibration: an elementwise add that reads 1 GiB and writes 1 GiB
         a = torch.ones(CALIB_ELEMS, dtype=torch.float32, device="cuda")
@@ -759,6 +773,8 @@ def main():
                       "eager": "one decode-step call per layer (2 launches) on one stream"}[args.mode],
         "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
         "decode_step_call_us": step_call_us,
+        "hbm_reference": {"kernel": "torch device copy, 1 GiB read + 1 GiB written", "GB/s": copy_gbs,
+                          "frac": copy_gbs / HBM_PEAK_GBS},
         "h2": h2,
     }
     if cpu is not None:

@@ -131,6 +131,22 @@ int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* pag
                            const int32_t* block_to_slot, void* stream);
 
 /*
+ * Admission of a prefill computed on the device ([EXPL] Figure 7 left: after the
+ * prefill the full KV cache lives in CPU memory and only per-block key min/max
+ * stays on the GPU).  k_rows, v_rows: the prefill's keys and values in device
+ * memory, [B][H][max_blocks*16][d] token-major (element type; k_rows 16-byte
+ * aligned).  For every block b < N(ctx_len) of every unit, one kernel writes the
+ * page (K token-major, V channel-major) into host_tier, which must be pinned
+ * host memory mapped for the device (the GPU stores it over PCIe; EINVAL
+ * otherwise), the block's metadata row (min and max over its tokens below
+ * ctx_len) into meta, and, when pool and block_to_slot are given (both or
+ * neither) and the block has a slot, the page into that pool slot.  Token rows
+ * at or past ctx_len are copied as given.  Blocks >= N are not touched.
+ */
+int oasis_admit(oasis_handle h, const void* k_rows, const void* v_rows, const int32_t* ctx_len, void* host_tier,
+                void* meta, void* pool, const int32_t* block_to_slot, void* stream);
+
+/*
  * Append one token per unit (long-output decode).  k_new, v_new: [B][H][d]
  * device.  The token goes to position p = ctx_len_in[r]: the metadata row of
  * block p/16 is initialised to the token (p % 16 == 0) or absorbs it by

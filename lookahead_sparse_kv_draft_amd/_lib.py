@@ -56,6 +56,7 @@ SIGNATURES = {
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "oasis_verify_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_admit": (_int, [_vp] * 9),
     "oasis_resident_diff_cap_evict": (_int, [_vp] * 11),
     "oasis_select_and_diff": (_int, [_vp] * 12),
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
@@ -271,3 +272,8 @@ def oasis_select_diff_combine_lru(h, scores, ctx_score, sel, block_to_slot, slot
 
 def oasis_verify_score(h, q, meta, ctx_len, scores, stream=None):
     _call("oasis_verify_score", h, _ptr(q), _ptr(meta), _ptr(ctx_len), _ptr(scores), _stream(stream))
+
+
+def oasis_admit(h, k_rows, v_rows, ctx_len, host_tier, meta, pool=None, block_to_slot=None, stream=None):
+    _call("oasis_admit", h, _ptr(k_rows), _ptr(v_rows), _ptr(ctx_len), _ptr(host_tier), _ptr(meta), _ptr(pool),
+          _ptr(block_to_slot), _stream(stream))

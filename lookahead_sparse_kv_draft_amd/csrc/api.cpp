@@ -452,6 +452,30 @@ int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const voi
                     "oasis_sparse_paged_decode_attn_list");
 }
 
+int oasis_admit(oasis_handle h, const void* k_rows, const void* v_rows, const int32_t* ctx_len, void* host_tier,
+                void* meta, void* pool, const int32_t* block_to_slot, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(k_rows);
+  CHECK_PTR(v_rows);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(host_tier);
+  CHECK_PTR(meta);
+  CHECK_ALIGN16(k_rows);
+  CHECK_ALIGN16(host_tier);
+  if ((pool == nullptr) != (block_to_slot == nullptr))
+    return fail(OASIS_EINVAL, "oasis_admit: pool and block_to_slot must both be given or both be null");
+  if (pool != nullptr) CHECK_ALIGN16(pool);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_tier) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();  // clear the lookup's error state
+    return fail(OASIS_EINVAL, "oasis_admit: host_tier is not pinned host memory mapped for the device");
+  }
+  return hip_status(oasis::launch_admit(h->c, k_rows, v_rows, ctx_len, attr.devicePointer, meta, pool, block_to_slot,
+                                        static_cast<hipStream_t>(stream)),
+                    "oasis_admit");
+}
+
 int oasis_fetch_gather(oasis_handle h, const void* host_tier, void* pool, const int32_t* fetch,
                        const int32_t* n_fetch, void* stream) {
   CHECK_HANDLE(h);

@@ -6,6 +6,9 @@
 //  meta_update - one wavefront per (request, KV head): absorbs the appended
 //                token into its block's min/max and writes it into the page if
 //                the block is resident.
+//  admit       - one wavefront per block of a prefill on the device: page into
+//                the pinned host tier (and its pool slot if resident) plus the
+//                metadata row.
 #include "oasis_internal.h"
 
 namespace oasis {
@@ -104,6 +107,73 @@ __global__ __launch_bounds__(64) void meta_update_kernel(
   if (h == 0 && lane == 0) ctx_out[r] = p + 1;
 }
 
+// Admission of a prefill: one wavefront per (unit, block) below the context.
+// Reads the block's 16 key and value rows from the device, writes the page (K
+// token-major, V channel-major) into the host tier (pinned, device-mapped: the
+// stores go over PCIe) and, if the block is resident, into its pool slot, and
+// the block's metadata row.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void admit_kernel(
+    const E* __restrict__ k_rows, const E* __restrict__ v_rows, const int32_t* __restrict__ ctx_len,
+    E* __restrict__ host, E* __restrict__ meta, E* __restrict__ pool, const int32_t* __restrict__ b2s, int units,
+    int H, int Nmax, int kb) {
+  constexpr int PAGE = 2 * kBlock * D;
+  constexpr int CE = 16 / static_cast<int>(sizeof(E));
+  constexpr int KCH = kBlock * D / CE;  // 16-byte chunks of the K half
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long w = static_cast<long long>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (w >= static_cast<long long>(units) * Nmax) return;
+  const int unit = static_cast<int>(w / Nmax);
+  const int b = static_cast<int>(w - static_cast<long long>(unit) * Nmax);
+  const int n = ctx_len[unit / H];
+  const int N = min((n + kBlock - 1) / kBlock, Nmax);
+  if (b >= N) return;
+  const int ntok = min(kBlock, n - kBlock * b);
+  const size_t row0 = (static_cast<size_t>(unit) * Nmax + b) * kBlock;
+  const E* kr = k_rows + row0 * D;
+  const E* vr = v_rows + row0 * D;
+  const int slot = (pool != nullptr && b2s != nullptr) ? b2s[static_cast<size_t>(unit) * Nmax + b] : -1;
+  E* hp = host + (static_cast<size_t>(unit) * Nmax + b) * PAGE;
+  E* pp = (slot >= 0 && slot < kb) ? pool + (static_cast<size_t>(unit) * kb + slot) * PAGE : nullptr;
+  // K half: the rows as they are
+  for (int i = lane; i < KCH; i += kWave) {
+    const uint4 x = reinterpret_cast<const uint4*>(kr)[i];
+    reinterpret_cast<uint4*>(hp)[i] = x;
+    if (pp != nullptr) reinterpret_cast<uint4*>(pp)[i] = x;
+  }
+  // V half transposed, and the metadata row
+  for (int c = lane; c < D; c += kWave) {
+    E vt[kBlock];
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) vt[t] = vr[static_cast<size_t>(t) * D + c];
+#pragma unroll
+    for (int t = 0; t < kBlock; ++t) {
+      hp[kBlock * D + c * kBlock + t] = vt[t];
+      if (pp != nullptr) pp[kBlock * D + c * kBlock + t] = vt[t];
+    }
+    float mn = Elem<E>::load(kr[c]);
+    float mx = mn;
+    for (int t = 1; t < ntok; ++t) {
+      const float x = Elem<E>::load(kr[static_cast<size_t>(t) * D + c]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    meta[meta_offset<D, CE>(unit, b, c, Nmax)] = Elem<E>::store(mn);
+    meta[meta_offset<D, CE>(unit, b, D + c, Nmax)] = Elem<E>::store(mx);
+  }
+}
+
+template <typename E, int D>
+hipError_t admit_t(const Ctx& c, const void* k_rows, const void* v_rows, const int32_t* ctx_len, void* host_dev,
+                   void* meta, void* pool, const int32_t* b2s, hipStream_t st) {
+  const long long waves = static_cast<long long>(c.units) * c.s.max_blocks;
+  const int grid = static_cast<int>((waves + 3) / 4);
+  hipLaunchKernelGGL((admit_kernel<E, D>), dim3(grid), dim3(256), 0, st, static_cast<const E*>(k_rows),
+                     static_cast<const E*>(v_rows), ctx_len, static_cast<E*>(host_dev), static_cast<E*>(meta),
+                     static_cast<E*>(pool), b2s, c.units, c.s.kv_heads, c.s.max_blocks, c.s.budget_blocks);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t build_t(const Ctx& c, const void* pages, const int32_t* ids, int32_t count,
                    const int32_t* ctx_len, void* meta, void* pool, const int32_t* b2s,
@@ -139,6 +209,16 @@ hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids
               : build_t<float, 128>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
   return bf ? build_t<uint16_t, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st)
             : build_t<float, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
+}
+
+hipError_t launch_admit(const Ctx& c, const void* k_rows, const void* v_rows, const int32_t* ctx_len,
+                        void* host_dev, void* meta, void* pool, const int32_t* b2s, hipStream_t st) {
+  const bool bf = c.s.dtype == OASIS_BF16;
+  if (c.s.head_dim == 128)
+    return bf ? admit_t<uint16_t, 128>(c, k_rows, v_rows, ctx_len, host_dev, meta, pool, b2s, st)
+              : admit_t<float, 128>(c, k_rows, v_rows, ctx_len, host_dev, meta, pool, b2s, st);
+  return bf ? admit_t<uint16_t, 64>(c, k_rows, v_rows, ctx_len, host_dev, meta, pool, b2s, st)
+            : admit_t<float, 64>(c, k_rows, v_rows, ctx_len, host_dev, meta, pool, b2s, st);
 }
 
 hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,

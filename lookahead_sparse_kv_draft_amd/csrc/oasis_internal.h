@@ -59,6 +59,10 @@ hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids
 hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,
                               const int32_t* ctx_in, int32_t* ctx_out, void* meta, void* pool,
                               const int32_t* b2s, hipStream_t st);
+// Prefill admission: pages into the host tier (device-mapped pinned memory)
+// and resident pool slots, plus the metadata rows.
+hipError_t launch_admit(const Ctx& c, const void* k_rows, const void* v_rows, const int32_t* ctx_len,
+                        void* host_dev, void* meta, void* pool, const int32_t* b2s, hipStream_t st);
 // The lookahead score from the draft rows, or (verify) the same bound from the
 // verify query rows.
 hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,

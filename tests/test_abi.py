@@ -69,6 +69,8 @@ def test_sizes_and_null_checks():
         assert lib.oasis_lookahead_score(h, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_verify_score(h, 18, 32, 16, 16, None) == L.OASIS_EINVAL  # misaligned q
         assert lib.oasis_verify_score(h, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_admit(h, *([None] * 8)) == L.OASIS_EINVAL
+        assert lib.oasis_admit(h, 16, 16, 16, 16, 16, 16, None, None) == L.OASIS_EINVAL  # pool without the map
         assert "null" in L.oasis_last_error()
         assert lib.oasis_topk_select(h, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_resident_diff_cap_evict(h, *([None] * 10)) == L.OASIS_EINVAL

@@ -691,3 +691,50 @@ def test_select_diff_combine_lru_matches_two_calls():
                 assert torch.equal(getattr(a, name), getattr(b, name)), (t, name)
     finally:
         run.close()
+
+
+# ------------------------------------------------------------------ prefill admission
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_admit_parity(dtype, d):
+    """Admission of a device-resident prefill: every page below the context in
+    the pinned host tier (K token-major, V channel-major, bytes as given), the
+    metadata rows equal to the oracle's min/max, resident blocks' pages in their
+    pool slots, and nothing past the context touched."""
+    B, H, Nmax, k = 2, 2, 13, 8
+    ctxs = [Nmax * BLK, 7 * BLK + 5]
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=Nmax, budget_blocks=k, dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rt.set_ctx(ctxs)
+    units = B * H
+    rng = _rng(31)
+    K = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    V = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    b2s = np.full((units, Nmax), -1, dtype=np.int32)
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        for s, b in enumerate(rng.choice(N, size=min(k, N, 5), replace=False)):
+            b2s[u, b] = s
+    st = rt.state[0][0]
+    L.oasis_admit(rt.h, U.to_dev(dtype, K), U.to_dev(dtype, V), rt.ctx_len, st.host_tier, st.meta, st.pool,
+                  U.i32(b2s))
+    torch.cuda.synchronize()
+    Ke, Ve = U.to_elem_np(dtype, K), U.to_elem_np(dtype, V)
+    tier = st.host_tier.numpy().view(Ke.dtype).reshape(units, Nmax, -1)
+    pool = st.pool.cpu().numpy().view(Ke.dtype).reshape(units, k, -1)
+    m = rt.meta_view(0)
+    mv = (m.view(torch.bfloat16).float() if dtype == "bf16" else m).cpu().numpy().astype(np.float64)
+    for u in range(units):
+        n = ctxs[u // H]
+        N = (n + BLK - 1) // BLK
+        kmin, kmax = O.block_meta(K[u].astype(np.float64), n)
+        assert np.array_equal(mv[u, :N, 0], kmin) and np.array_equal(mv[u, :N, 1], kmax), u
+        for b in range(Nmax):
+            if b >= N:
+                assert not tier[u, b].any(), (u, b)   # untouched (the tier starts zeroed)
+                continue
+            page = np.concatenate([Ke[u, b * BLK:(b + 1) * BLK].reshape(-1),
+                                   Ve[u, b * BLK:(b + 1) * BLK].T.reshape(-1)])
+            assert np.array_equal(tier[u, b], page), (u, b)
+            if b2s[u, b] >= 0:
+                assert np.array_equal(pool[u, b2s[u, b]], page), (u, b)
+    rt.close()
