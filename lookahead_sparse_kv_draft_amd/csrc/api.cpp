@@ -114,9 +114,10 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // Attention: workgroups of W wavefronts, each wavefront streaming a run of
   // consecutive selection entries (at most 64) through a ring of PF page
   // buffers; a workgroup covers W runs (one split).  By default 2 wavefronts,
-  // a 2-page ring and about 512 wavefronts per launch (measured best on the
-  // 32K-context batch-8 step: fewer, longer-running wavefronts amortise the
-  // per-workgroup start-up and write fewer partials).
+  // a 2-page ring and about 512 wavefronts per launch for the attention on its
+  // own (fewer, longer-running wavefronts amortise the per-workgroup start-up
+  // and write fewer partials), 1024 when it shares the decode step's launch
+  // with the scoring (below).
   const int row_tiles = (rows_attn + 15) / 16;
   const int max_waves = (row_tiles <= 2) ? 4 : 2;  // LDS of the wavefront merge
   int waves = env_int("OASIS_ATTN_WAVES", 0);
@@ -149,7 +150,8 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.attn_split_len = waves * run;
   c.attn_splits = splits;
 
-  // Score kernel: 16-block tiles per wavefront, ~2048 wavefronts per launch.
+  // Scoring: runs of 16-block tiles per wavefront, about 2048 wavefronts on its
+  // own, 4096 beside the attention.
   int tpw = env_int("OASIS_SCORE_TPW", 0);
   if (tpw <= 0) {
     const long long tiles = units * ((s.max_blocks + 15) / 16);

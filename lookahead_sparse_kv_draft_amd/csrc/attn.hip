@@ -19,7 +19,8 @@
 //       lane's own 4 probabilities: P never leaves registers.
 // The page layout (K token-major, V channel-major) is what makes both products
 // read contiguous lane-sized pieces without an LDS transpose.  A wavefront
-// requests all of its pages before it processes the first.
+// keeps a ring of PF pages in flight: each page's math runs while the next
+// pages' loads are outstanding.
 //
 // f32 path: VALU, query rows and logits in LDS, accumulators in registers.
 // Both paths leave one partial per split; a log-sum-exp combine kernel merges
