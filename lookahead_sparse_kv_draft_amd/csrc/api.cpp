@@ -129,7 +129,7 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // runs of 2 scoring tiles (a sweep of splits x tiles per wavefront on the
   // 32K-context batch-8 step: 36.3 us against 37.7 us for the standalone
   // kernels' defaults).
-  const bool step_fused = s.dtype == OASIS_BF16 && waves == 2 && rows_attn <= 48;
+  const bool step_fused = s.dtype == OASIS_BF16 && rows_attn <= 48 && (waves == 2 || (waves == 4 && row_tiles <= 2));
   int splits = env_int("OASIS_ATTN_SPLITS", 0);
   if (splits <= 0) {
     const int target = step_fused ? 1024 : 512;

@@ -36,11 +36,12 @@ __global__ __launch_bounds__(256) void combine_score_kernel(
                     (blockIdx.x - ncomb_wg) * 4 + wv, lane);
 }
 
-// Attention (2 wavefronts, 2-page ring) and scoring workgroups in one grid of
-// 128-thread workgroups.  order 0: attention workgroups first; 1: scoring
-// first; 2: interleaved one for one while both last.
-template <int D, int RTA, int RTS>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 2 : 1))) void attn_score_kernel(
+// Attention (2-page ring) and scoring workgroups in one grid of workgroups of
+// W wavefronts (W = 2, or 4 for up to two attention row tiles).
+// order 0: attention workgroups first; 1: scoring first; 2: interleaved one for
+// one while both last.
+template <int D, int RTA, int RTS, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 2 : 1))) void attn_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend, const int32_t* __restrict__ n_attend,
     const int32_t* __restrict__ ctx_attn, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
@@ -67,15 +68,15 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 
     }
   }
   if (is_attn) {
-    attn_wg<D, RTA, 2, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
+    attn_wg<D, RTA, W, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
                           splits, run, scale_log2, idx);
   } else {
     score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, 1, srows, Nmax, wpu, tpw, total_waves,
-                       idx * 2 + static_cast<int>(threadIdx.x) / kWave, threadIdx.x & (kWave - 1));
+                       idx * W + static_cast<int>(threadIdx.x) / kWave, threadIdx.x & (kWave - 1));
   }
 }
 
-template <int D, int RTA, int RTS>
+template <int D, int RTA, int RTS, int W>
 hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                 const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
                 float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
@@ -84,8 +85,8 @@ hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* se
   const int n_attn_wg = c.units * c.attn_splits;
   const int wpu = score_waves_per_unit(c);
   const int total = c.units * wpu;
-  const int n_score_wg = (total + 1) / 2;
-  hipLaunchKernelGGL((attn_score_kernel<D, RTA, RTS>), dim3(n_attn_wg + n_score_wg), dim3(128), 0, st,
+  const int n_score_wg = (total + W - 1) / W;
+  hipLaunchKernelGGL((attn_score_kernel<D, RTA, RTS, W>), dim3(n_attn_wg + n_score_wg), dim3(64 * W), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s, attend,
                      n_attend, ctx_attn, ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.s.max_blocks,
                      c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2, static_cast<const uint16_t*>(meta),
@@ -94,16 +95,16 @@ hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* se
   return hipGetLastError();
 }
 
-template <int D, int RTA>
+template <int D, int RTA, int W>
 hipError_t as_s(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                 const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
                 float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
                 hipStream_t st) {
   switch ((c.rows_score + 15) / 16) {
-    case 1: return as_t<D, RTA, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
-    case 2: return as_t<D, RTA, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
-    case 3: return as_t<D, RTA, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
-    default: return as_t<D, RTA, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 1: return as_t<D, RTA, 1, W>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 2: return as_t<D, RTA, 2, W>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 3: return as_t<D, RTA, 3, W>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    default: return as_t<D, RTA, 4, W>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
   }
 }
 
@@ -112,10 +113,13 @@ hipError_t as_d(const Ctx& c, const void* q, const void* pool, const int32_t* se
                 const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
                 float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
                 hipStream_t st) {
+  const bool w4 = c.attn_waves == 4;
   switch ((c.rows_attn + 15) / 16) {
-    case 1: return as_s<D, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
-    case 2: return as_s<D, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
-    default: return as_s<D, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 1: return w4 ? as_s<D, 1, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st)
+                      : as_s<D, 1, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    case 2: return w4 ? as_s<D, 2, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st)
+                      : as_s<D, 2, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
+    default: return as_s<D, 3, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, st);
   }
 }
 
@@ -158,7 +162,8 @@ hipError_t cs_d(const Ctx& c, const float* ws_acc, const float* ws_ml, float* ou
 }  // namespace
 
 bool attn_and_score_fused_available(const Ctx& c) {
-  return c.s.dtype == OASIS_BF16 && c.attn_waves == 2 && c.attn_pf == 2 && c.rows_attn <= 48;
+  return c.s.dtype == OASIS_BF16 && c.attn_pf == 2 && c.rows_attn <= 48 &&
+         (c.attn_waves == 2 || (c.attn_waves == 4 && c.rows_attn <= 32));
 }
 
 hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, const int32_t* sel,

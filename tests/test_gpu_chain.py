@@ -90,12 +90,14 @@ def test_decode_step_matches_separate_calls(name, kw):
     _decode_step_vs_separate(CONFIGS[name].with_(**kw))
 
 
-@pytest.mark.parametrize("launches,order", [(2, 1), (2, 2), (3, 0)])
-def test_decode_step_launch_variants(launches, order, monkeypatch):
+@pytest.mark.parametrize("launches,order,waves", [(2, 1, 2), (2, 2, 2), (3, 0, 2), (2, 0, 4), (2, 2, 4)])
+def test_decode_step_launch_variants(launches, order, waves, monkeypatch):
     """Both workgroup orders of the fused attention + scoring launch other than
-    the default, and the three-launch step, give the same bit-identical result."""
+    the default, workgroups of 4 wavefronts, and the three-launch step give the
+    same bit-identical result as the separate calls."""
     monkeypatch.setenv("OASIS_STEP_LAUNCHES", str(launches))
     monkeypatch.setenv("OASIS_STEP_ORDER", str(order))
+    monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
     _decode_step_vs_separate(CONFIGS["llama8b_32k"].with_(batch=2, ctx=16 * 300 + 7, steps=4, fetch_cap=8,
                                                           planted=15, budget_tokens=16 * 32))
 
