@@ -130,16 +130,20 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // 32K-context batch-8 step: 36.3 us against 37.7 us for the standalone
   // kernels' defaults).
   const bool step_fused = s.dtype == OASIS_BF16 && rows_attn <= 48 && (waves == 2 || (waves == 4 && row_tiles <= 2));
-  int splits = env_int("OASIS_ATTN_SPLITS", 0);
-  if (splits <= 0) {
-    const int target = step_fused ? 1024 : 512;
-    splits = (target + c.units * waves - 1) / (c.units * waves);
-  }
-  const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
-  const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
-  splits = std::max(min_splits, std::min(splits, max_splits));
-  const int run = (kbud + splits * waves - 1) / (splits * waves);
-  splits = (kbud + run * waves - 1) / (run * waves);  // no empty split
+  const int env_splits = env_int("OASIS_ATTN_SPLITS", 0);
+  // split count for about `target` wavefronts, then the run per wavefront
+  auto shape_splits = [&](int target, int* run_out) {
+    int sp = env_splits > 0 ? env_splits : (target + c.units * waves - 1) / (c.units * waves);
+    const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
+    const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
+    sp = std::max(min_splits, std::min(sp, max_splits));
+    const int r = (kbud + sp * waves - 1) / (sp * waves);
+    *run_out = r;
+    return (kbud + r * waves - 1) / (r * waves);  // no empty split
+  };
+  int run = 0, run_solo = 0;
+  const int splits = shape_splits(step_fused ? 1024 : 512, &run);
+  const int splits_solo = shape_splits(512, &run_solo);
   int pf = env_int("OASIS_ATTN_PF", 0);
   const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
   if (pf != 2 && pf != 4 && pf != 8) pf = 2;  // measured: a shallow ring keeps the math beside the loads
@@ -149,6 +153,8 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.attn_run = run;
   c.attn_split_len = waves * run;
   c.attn_splits = splits;
+  c.attn_splits_solo = splits_solo;
+  c.attn_run_solo = run_solo;
 
   // Scoring: runs of 16-block tiles per wavefront, about 2048 wavefronts on its
   // own, 4096 beside the attention.

@@ -25,6 +25,8 @@
 // f32 path: VALU, query rows and logits in LDS, accumulators in registers.
 // Both paths leave one partial per split; a log-sum-exp combine kernel merges
 // them.
+#include <algorithm>
+
 #include "attn_body.h"
 #include "attn_combine.h"
 
@@ -234,7 +236,11 @@ hipError_t combine_t(const Ctx& c, const float* ws_acc, const float* ws_ml, floa
 
 }  // namespace
 
-size_t attn_workspace_bytes(const Ctx& c) { return attn_ws_acc_bytes(c) + attn_ws_ml_bytes(c); }
+size_t attn_workspace_bytes(const Ctx& c) {
+  Ctx solo = c;
+  solo.attn_splits = c.attn_splits_solo;
+  return std::max(attn_ws_acc_bytes(c) + attn_ws_ml_bytes(c), attn_ws_acc_bytes(solo) + attn_ws_ml_bytes(solo));
+}
 
 bool attn_needs_combine(const Ctx& c) {
   // the bf16 kernel writes the output itself when there is a single split
@@ -257,9 +263,14 @@ hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t s
   return (c.s.head_dim == 128) ? combine_t<128>(c, ws_acc, ws_ml, out, st) : combine_t<64>(c, ws_acc, ws_ml, out, st);
 }
 
-hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
+hipError_t launch_attn(const Ctx& c0, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
                        const int32_t* ctx_len, float* out, void* ws, hipStream_t st) {
+  // the attention on its own: its own split shape (the workspace fits the larger one)
+  Ctx c = c0;
+  c.attn_splits = c0.attn_splits_solo;
+  c.attn_run = c0.attn_run_solo;
+  c.attn_split_len = c0.attn_waves * c0.attn_run_solo;
   hipError_t e = launch_attn_main(c, q, pool, sel, b2s, attend, n_attend, ctx_len, out, ws, st);
   if (e != hipSuccess || !attn_needs_combine(c)) return e;
   float* ws_acc = static_cast<float*>(ws);

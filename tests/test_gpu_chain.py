@@ -124,7 +124,13 @@ def _decode_step_vs_separate(cfg, runs=None):
                 r.step(t)
                 snaps.append(_state_snapshot(r))
             for i, (a, b) in enumerate(zip(*snaps)):
-                assert np.array_equal(a, b, equal_nan=True), (t, i)
+                if i == 0:
+                    # the attention output: the standalone attention may split the
+                    # attended list differently (its own split count), which only
+                    # reorders fp32 sums; every discrete output must be identical
+                    assert np.allclose(a, b, rtol=1e-5, atol=1e-6), (t, float(np.abs(a - b).max()))
+                else:
+                    assert np.array_equal(a, b, equal_nan=True), (t, i)
             print(f"{cfg.name} step {t}: identical", flush=True)
     finally:
         for r in runs:

@@ -261,7 +261,8 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatc
     if waves is None:
         # the decode step's first half (attention beside the scoring, in one grid
         # where the shape allows) then the split combine: the same attention
-        # output and the same scores as the separate calls, bit for bit
+        # output as the separate calls (to fp32 reordering) and the same scores,
+        # bit for bit
         rt.build_meta(0)
         st.scores.fill_(float("nan"))  # blocks past the context are left unwritten
         L.oasis_lookahead_score(rt.h, q_d, st.meta, rt.ctx_len, st.scores)
@@ -277,7 +278,9 @@ def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatc
                                      natt_a, st.scores, rt.out, rt.ws_ptr)
             L.oasis_attn_combine(rt.h, rt.ws_ptr, rt.out)
             torch.cuda.synchronize()
-            assert np.array_equal(rt.out.cpu().numpy().astype(np.float64), got)
+            # the step's launch may split the list differently from the attention on
+            # its own (its own split count): the same sums in another fp32 order
+            assert np.allclose(rt.out.cpu().numpy().astype(np.float64), got, rtol=1e-5, atol=1e-6)
             assert np.array_equal(st.scores.cpu().numpy(), ref_scores, equal_nan=True)
     for u in range(units):
         r, hh = divmod(u, H)
