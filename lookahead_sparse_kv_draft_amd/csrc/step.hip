@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void combine_score_kernel(
 // order 0: attention workgroups first; 1: scoring first; 2: interleaved one for
 // one while both last.
 template <int D, int RTA, int RTS, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(RTA <= 3 ? 2 : 1))) void attn_score_kernel(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((RTA <= 3 && RTS <= 2) ? 2 : 1))) void attn_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend, const int32_t* __restrict__ n_attend,
     const int32_t* __restrict__ ctx_attn, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
