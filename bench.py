@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --calib-copy` into a traffic file and exit")
+    p.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                   help="average per kernel every counter of rocprofv3 --pmc counter_collection.csv "
+                        "files, the last argument being the output text file, and exit")
     p.add_argument("--pipeline", action="store_true",
                    help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
                         "(one JSON line per sweep instead of the headline)")
@@ -216,6 +219,37 @@ def traffic_summary(fetch_csv: str, write_csv: str, out: str, cmdline: str):
             tot += b
             lines.append(f"kernel {k} op {op} fetch_kib {f_kib:.1f} write_kib {w_kib:.1f} hbm_bytes {b:.0f}")
         lines.append(f"op {op} source {op_source_hash(op)} hbm_bytes {tot:.0f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counter_summary(paths, out: str, cmdline: str):
+    """Mean of every counter per kernel (template arguments kept) over the
+    dispatches of rocprofv3 --pmc counter_collection.csv files."""
+    import csv
+    import re
+    acc, calls = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            m = re.search(r"(\w+_kernel)(<[^(]*>)?", r["Kernel_Name"])
+            k = (m.group(1) + (m.group(2) or "")) if m else r["Kernel_Name"][:60]
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in acc.values() for c in v})
+    lines = [f"# rocprofv3 --pmc counters per kernel (mean over dispatches), llama8b_32k",
+             "# counters: cd /tmp && rocprofv3 --pmc MfmaUtil VALUBusy --kernel-include-regex 'oasis' "
+             "--output-format csv -d <dir1> -o m -- python <repo>/bench.py --steps 8 --warmup 2 --no-cpu-baseline "
+             "--no-h2  (then the same with --pmc MfmaFlopsBF16 OccupancyPercent and -d <dir2>)",
+             "# MfmaUtil, VALUBusy, OccupancyPercent: percent of the kernel's active time (derived counters); "
+             "MfmaFlopsBF16: bf16 MFMA flops per dispatch",
+             f"# summary: {cmdline}",
+             "kernel " + " ".join(f"{n}(calls)" for n in names)]
+    for k in sorted(acc):
+        cells = []
+        for n in names:
+            v = acc[k].get(n)
+            cells.append("-" if v is None else f"{sum(v) / len(v):.4g}({len(v)})")
+        lines.append(f"{k.replace(' ', '')} " + " ".join(cells))
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -527,6 +561,11 @@ def main():
         return
     if args.pipeline:
         pipeline_sweep(args)
+        return
+    if args.counter_summary:
+        if len(args.counter_summary) < 2:
+            raise SystemExit("--counter-summary needs at least one CSV and the output file")
+        counter_summary(args.counter_summary[:-1], args.counter_summary[-1], " ".join(sys.argv))
         return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, cmdline=" ".join(sys.argv))
