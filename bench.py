@@ -769,13 +769,13 @@ def main():
     # Infinity Cache): the device copy (1 GiB read and 1 GiB written, whose
     # written lines the launch's reads then push out to HBM) and a read-only sum;
     # HIP events around the launch alone
-    def cold_after(flush):
+    def cold_after(flush, op="attend_and_score"):
         t = []
         for i in range(10):
             flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(cs0)
-            ops["attend_and_score"](rt.state[0][i % replicas], run.q[0, i % cfg.steps + 1])
+            ops[op](rt.state[0][i % replicas], run.q[0, i % cfg.steps + 1])
             e1.record(cs0)
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1) * 1e3)
@@ -783,7 +783,11 @@ def main():
 
     cold_us = cold_after(lambda: dst.copy_(src))
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    cold_clean_us = cold_after(lambda: torch.sum(src, dim=(0,), out=sink))
+    read_flush = lambda: torch.sum(src, dim=(0,), out=sink)  # noqa: E731
+    cold_clean_us = cold_after(read_flush)
+    # every op cold after the read-only sweep (the selection ops read the
+    # scores and maps the step left, the attention the attended list)
+    cold_ops = {n: cold_after(read_flush, n) for n in names}
     del src, dst
 
     if args.calib_copy:
@@ -801,7 +805,8 @@ def main():
     kern = {}
     for n in names:
         gbs = ab[n] / avg[n] / 1e9
-        kern[n] = {"avg_us": avg[n] * 1e6, "bytes": ab[n], "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+        kern[n] = {"avg_us": avg[n] * 1e6, "bytes": ab[n], "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                   "cold_us": cold_ops[n]}
     dominant = "attend_and_score"  # the step's first launch: attention beside the scoring, ~3/4 of the step
     traffic = load_traffic(cfg.name)
     for n in names:
