@@ -50,8 +50,10 @@ OPS = ["attend_and_score", "select_diff_combine", "sparse_paged_decode_attn", "l
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    # the warm-up runs long enough (~10 ms at the default workload) for the GPU to
+    # reach its steady state; 20 steps measured ~4 % slow in the first timed steps
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--config", default="llama8b_32k")
     p.add_argument("--replicas", type=int, default=0,
                    help="0 = enough for each op's own footprint to exceed the Infinity Cache twice")

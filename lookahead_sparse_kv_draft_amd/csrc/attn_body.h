@@ -174,9 +174,9 @@ __device__ __forceinline__ void attn_wg(
   auto load = [&](Page& pg, int j) {
     const size_t off = static_cast<size_t>(__builtin_amdgcn_readfirstlane(__shfl(c_slot, j))) * PAGE;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) pg.k[s] = *reinterpret_cast<const uint4*>(kl + off + 32 * s);
+    for (int s = 0; s < KS; ++s) pg.k[s] = load_stream(reinterpret_cast<const uint4*>(kl + off + 32 * s));
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) pg.v[ct] = *reinterpret_cast<const uint2*>(vl + off + 16 * kBlock * ct);
+    for (int ct = 0; ct < CT; ++ct) pg.v[ct] = load_stream(reinterpret_cast<const uint2*>(vl + off + 16 * kBlock * ct));
   };
   auto process = [&](const Page& pg, int ntok) {
 #pragma unroll

@@ -44,7 +44,7 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
   auto load_c = [&](uint4* Bt, int tile, int nclamp) {
     const int t = min(tile, (nclamp + 15) / 16 - 1);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) Bt[s] = mbase[static_cast<size_t>(t) * TILE4 + 64 * s + lane];
+    for (int s = 0; s < KSTEPS; ++s) Bt[s] = load_stream(mbase + static_cast<size_t>(t) * TILE4 + 64 * s + lane);
   };
   // The first two tiles go out before the context length arrives: every block
   // index below Nmax is in bounds, and the context only decides what is kept.
