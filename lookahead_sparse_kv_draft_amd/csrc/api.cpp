@@ -114,10 +114,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // Attention: workgroups of W wavefronts, each wavefront streaming a run of
   // consecutive selection entries (at most 64) through a ring of PF page
   // buffers; a workgroup covers W runs (one split).  By default 2 wavefronts,
-  // a 2-page ring and about 512 wavefronts per launch for the attention on its
-  // own (fewer, longer-running wavefronts amortise the per-workgroup start-up
-  // and write fewer partials), 1024 when it shares the decode step's launch
-  // with the scoring (below).
+  // a 2-page ring and about 512 wavefronts per launch, on its own and beside
+  // the scoring (fewer, longer-running wavefronts amortise the per-workgroup
+  // start-up and write fewer partials).
   const int row_tiles = (rows_attn + 15) / 16;
   const int max_waves = (row_tiles <= 2) ? 4 : 2;  // LDS of the wavefront merge
   int waves = env_int("OASIS_ATTN_WAVES", 0);
@@ -125,10 +124,11 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   waves = std::min(waves, max_waves);
   const int kbud = s.budget_blocks;
   // The decode step's first launch (attention beside the scoring, bf16 with the
-  // default shape) is best with about twice as many attention wavefronts and
-  // runs of 2 scoring tiles (a sweep of splits x tiles per wavefront on the
-  // 32K-context batch-8 step: 36.3 us against 37.7 us for the standalone
-  // kernels' defaults).
+  // default shape) keeps its own attention and scoring shapes.  With the
+  // non-temporal page and metadata loads, about 512 attention wavefronts (as on
+  // their own) and runs of 2 scoring tiles measured best: at the 32K-context
+  // batch-8 step 34.4 us against 35.3 us with 1024 attention wavefronts, at the
+  // 128K-context 8-layer step 40.8 against 42.8 us, within 0.5 % elsewhere.
   const bool step_fused = s.dtype == OASIS_BF16 && rows_attn <= 48 && (waves == 2 || (waves == 4 && row_tiles <= 2));
   const int env_splits = env_int("OASIS_ATTN_SPLITS", 0);
   // split count for about `target` wavefronts, then the run per wavefront
@@ -142,7 +142,7 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
     return (kbud + r * waves - 1) / (r * waves);  // no empty split
   };
   int run = 0, run_solo = 0;
-  const int splits = shape_splits(step_fused ? 1024 : 512, &run);
+  const int splits = shape_splits(512, &run);
   const int splits_solo = shape_splits(512, &run_solo);
   int pf = env_int("OASIS_ATTN_PF", 0);
   const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
@@ -156,8 +156,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.attn_splits_solo = splits_solo;
   c.attn_run_solo = run_solo;
 
-  // Scoring: runs of 16-block tiles per wavefront, about 2048 wavefronts on its
-  // own, 4096 beside the attention.
+  // Scoring: runs of 16-block tiles per wavefront, for about 4096 wavefronts
+  // where the decode step runs it beside the attention (bf16), 2048 otherwise;
+  // the scoring on its own takes the same runs.
   int tpw = env_int("OASIS_SCORE_TPW", 0);
   if (tpw <= 0) {
     const long long tiles = units * ((s.max_blocks + 15) / 16);
