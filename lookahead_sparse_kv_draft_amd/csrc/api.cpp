@@ -157,14 +157,17 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   c.attn_run_solo = run_solo;
 
   // Scoring: runs of 16-block tiles per wavefront, for about 4096 wavefronts
-  // where the decode step runs it beside the attention (bf16), 2048 otherwise;
-  // the scoring on its own takes the same runs.
-  int tpw = env_int("OASIS_SCORE_TPW", 0);
-  if (tpw <= 0) {
-    const long long tiles = units * ((s.max_blocks + 15) / 16);
-    tpw = static_cast<int>(std::max(1LL, std::min(16LL, tiles / (step_fused ? 4096 : 2048))));
-  }
-  c.score_tpw = tpw;
+  // where the decode step runs it beside the attention (bf16), 2048 in a launch
+  // of its own (at the 32K-context batch-8 workload the scoring alone takes
+  // 12.6 us with runs of 4 tiles against 13.4 us with 2, while the step's
+  // launch is 0.4 us faster with 2).
+  const long long tiles = units * ((s.max_blocks + 15) / 16);
+  auto runs_for = [&](long long waves) {
+    const int t = env_int("OASIS_SCORE_TPW", 0);
+    return t > 0 ? t : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
+  };
+  c.score_tpw = runs_for(step_fused ? 4096 : 2048);
+  c.score_tpw_solo = runs_for(2048);
   c.step_order = env_int("OASIS_STEP_ORDER", 0);
   if (c.step_order < 0 || c.step_order > 2) c.step_order = 0;
   c.step_launches = (env_int("OASIS_STEP_LAUNCHES", 2) == 3) ? 3 : 2;

@@ -50,7 +50,8 @@ struct Ctx {
   int attn_splits_solo, attn_run_solo;
   int attn_waves;   // wavefronts per attention workgroup (1, 2 or 4)
   int attn_pf;      // pages in flight per attention wavefront (2, 4 or 8)
-  int score_tpw;    // 16-block tiles per wave in the score kernel
+  int score_tpw;    // 16-block tiles per scoring wave beside the attention in the step's launch
+  int score_tpw_solo;  // the same in a scoring launch of its own
   int step_order;   // workgroup order of the fused attention + score launch (0, 1, 2)
   int step_launches;  // launches per decode step: 2 (fused attention + score) or 3
 };

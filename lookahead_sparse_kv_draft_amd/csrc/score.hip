@@ -102,8 +102,11 @@ hipError_t mfma_rows(const Ctx& c, const void* q, const void* meta, const int32_
 
 }  // namespace
 
-hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
+hipError_t launch_score(const Ctx& c0, const void* q, const void* meta, const int32_t* ctx_len,
                         float* scores, hipStream_t st, bool verify) {
+  // a scoring launch of its own: its own run of tiles per wavefront
+  Ctx c = c0;
+  c.score_tpw = c0.score_tpw_solo;
   const ScoreRows sr = verify ? ScoreRows{1, 0, c.s.group} : ScoreRows{c.s.n_draft, 1, c.rows_score};
   if (c.s.dtype == OASIS_BF16)
     return c.s.head_dim == 128 ? mfma_rows<128>(c, q, meta, ctx_len, scores, sr, st)
