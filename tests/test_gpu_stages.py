@@ -66,6 +66,53 @@ def test_score_parity(dtype, d, G, D, Nmax, ctxs):
     L.oasis_destroy(h)
 
 
+def test_score_standalone_matches_step_launch():
+    """At 64 units x 2048 blocks (8192 tiles of 16 blocks) the scoring on its own
+    runs 4 tiles per wavefront and the decode step's first launch, beside the
+    attention, 2; every block's bound is the same MFMA sequence either way, so
+    the two must agree bit for bit, and with the oracle on sampled units."""
+    B, H, G, D, d, Nmax, k = 8, 8, 4, 4, 128, 2048, 16
+    ctxs = [32768, 32768 - 5, 16 * 2000 + 3, 16 * 1500, 32768, 16 * 1024, 16 * 700 + 9, 16 * 2047]
+    sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k, n_draft=D)
+    h = sh.handle()
+    rng = _rng(11)
+    units = B * H
+    a = rng.standard_normal((units, Nmax, d), dtype=np.float32)
+    b = rng.standard_normal((units, Nmax, d), dtype=np.float32)
+    kmin = U.elem_round("bf16", np.minimum(a, b))
+    kmax = U.elem_round("bf16", np.maximum(a, b))
+    del a, b
+    q = U.elem_round("bf16", rng.standard_normal((B, H * G, 1 + D, d)).astype(np.float32))
+    meta_d = U.to_dev("bf16", np.stack([kmin, kmax], axis=2), tiled_meta=True)
+    q_d = U.to_dev("bf16", q)
+    ctx_d = U.i32(ctxs)
+    solo = torch.full((units, Nmax), float("nan"), device="cuda")
+    L.oasis_lookahead_score(h, q_d, meta_d, ctx_d, solo)
+    # the step's first launch with nothing to attend (empty attended lists)
+    pool = torch.zeros(L.oasis_pool_bytes(h), dtype=torch.uint8, device="cuda")
+    sel = torch.full((units, k), -1, dtype=torch.int32, device="cuda")
+    b2s = torch.full((units, Nmax), -1, dtype=torch.int32, device="cuda")
+    attend = torch.full((units, k), -1, dtype=torch.int32, device="cuda")
+    n_attend = torch.zeros(units, dtype=torch.int32, device="cuda")
+    out = torch.zeros((B, H * G, 1 + D, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.oasis_workspace_bytes(h) + 256, dtype=torch.uint8, device="cuda")
+    ws_ptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+    fused = torch.full((units, Nmax), float("nan"), device="cuda")
+    L.oasis_attend_and_score(h, q_d, pool, meta_d, ctx_d, ctx_d, sel, b2s, attend, n_attend, fused, out, ws_ptr)
+    torch.cuda.synchronize()
+    got_solo, got_fused = solo.cpu().numpy(), fused.cpu().numpy()
+    assert np.array_equal(got_solo, got_fused, equal_nan=True)
+    for u in (0, 9, 37, 63):
+        r, hh = divmod(u, H)
+        N = (ctxs[r] + BLK - 1) // BLK
+        qd = q[r, hh * G:(hh + 1) * G, 1:].reshape(-1, d).astype(np.float64)
+        ref = O.lookahead_score(qd, kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
+        tol = U.score_tolerance(qd, kmin[u, :N].astype(np.float64), kmax[u, :N].astype(np.float64))
+        assert np.all(np.abs(got_solo[u, :N] - ref) <= tol), u
+        assert np.all(np.isnan(got_solo[u, N:])), "blocks past the context must not be written"
+    L.oasis_destroy(h)
+
+
 # ------------------------------------------------------------------ top-k
 @pytest.mark.parametrize("k,ctxs,kind", [
     (128, [32768, 16 * 130, 16 * 128, 16 * 127 + 3], "normal"),
