@@ -244,17 +244,17 @@ __device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores,
 }
 
 // The selection of one unit by a 1024-thread workgroup from the scores
-// topk_fast_load returned; also written, in rank order and -1 padded, to the LDS
-// array selL when it is not null.
+// topk_fast_load returned and the request's context length n (read by the
+// caller before anything else, so its round trip overlaps the scores'); also
+// written, in rank order and -1 padded, to the LDS array selL when it is not
+// null.
 template <int KPT>
-__device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], const int32_t* __restrict__ ctx_len,
-                                      int32_t* __restrict__ sel, int H, int Nmax, int kb, int32_t* selL,
-                                      TopkFastShared& sh) {
+__device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int32_t* __restrict__ sel, int Nmax,
+                                      int kb, int32_t* selL, TopkFastShared& sh) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
   const int unit = blockIdx.x;
-  const int n = ctx_len[unit / H];
   const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
   const int F0 = (N == 1) ? 1 : 2;
   const int C = max(0, N - 2);  // candidates are blocks 1 .. N-2
@@ -432,9 +432,10 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
                                                          const int32_t* __restrict__ ctx_len,
                                                          int32_t* __restrict__ sel, int H, int Nmax, int kb) {
   __shared__ TopkFastShared sh;
+  const int n = ctx_len[blockIdx.x / H];
   float v[KPT];
   topk_fast_load<KPT>(scores, Nmax, v);
-  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, nullptr, sh);
+  topk_fast_body<KPT>(v, n, sel, Nmax, kb, nullptr, sh);
 }
 
 // Dynamic LDS of the fused selection + diff: the diff's arrays, the selection
@@ -463,6 +464,9 @@ __device__ __forceinline__ void select_diff_unit(
   int32_t* bu = b2s + static_cast<size_t>(unit) * Nmax;
   int32_t* slu = s2b + static_cast<size_t>(unit) * kb;
   const float* su = scores + static_cast<size_t>(unit) * Nmax;
+  // Loads in the order that keeps one round trip before the selection starts:
+  // the scores and the map rows (independent), then the context length, then
+  // the scores of the resident blocks (which need the slot map).
   float v[KPT];
   topk_fast_load<KPT>(scores, Nmax, v);
   if (kb <= kDiffWaveMaxBudget) {
@@ -478,11 +482,14 @@ __device__ __forceinline__ void select_diff_unit(
       const int ie = min((tid & (kWave - 1)) + e * kWave, kb - 1);  // clamped: no branch around the loads
       sbw[e] = slu[ie];
       if (lu != nullptr) luw[e] = lu[ie];
-      svw[e] = su[(sbw[e] >= 0 && sbw[e] < Nmax) ? sbw[e] : 0];
     }
+    const int n = ctx_len[unit / H];
+    __builtin_amdgcn_sched_barrier(0);  // the context length goes out before the wait for the slot map
+#pragma unroll
+    for (int e = 0; e < 2; ++e) svw[e] = su[(sbw[e] >= 0 && sbw[e] < Nmax) ? sbw[e] : 0];
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
     for (int j = tid; j < (Nmax + 31) / 32; j += kTkThreads) bitmap[j] = 0u;  // ordered by the selection's barriers
-    topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
+    topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh);
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
       if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
@@ -493,9 +500,11 @@ __device__ __forceinline__ void select_diff_unit(
     return;
   }
   const int sb = slu[min(tid, kb - 1)];  // clamped: no branch around the loads
+  const int n = ctx_len[unit / H];
+  __builtin_amdgcn_sched_barrier(0);
   const bool sok = sb >= 0 && sb < Nmax;
   const float sv = su[sok ? sb : 0];
-  topk_fast_body<KPT>(v, ctx_len, sel, H, Nmax, kb, selL, sh);
+  topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh);
   __syncthreads();
   diff_body(unit, kb, Nmax, cap, selL, sb, sv, bu, slu, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
 }
