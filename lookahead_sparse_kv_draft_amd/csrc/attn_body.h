@@ -73,6 +73,10 @@ __device__ __forceinline__ void attn_wg(
     const int perk = (kb + nwv - 1) / nwv;
     const int e0k = (split * W + wv) * perk;
     int pk = au[min(e0k + lane, kb - 1)];  // clamped: no branch around the load
+    // a compiler-only barrier (no instruction, no wait): the load above is issued
+    // here, not merged with the short-list load below into one that waits for
+    // the length
+    asm volatile("" ::: "memory");
     const int natt = min(max(n_attend[unit], 0), kb);
     const int per = (natt + nwv - 1) / nwv;  // <= run <= 64
     const int e0 = (split * W + wv) * per;
