@@ -196,8 +196,7 @@ __device__ __forceinline__ void attn_wg(
         x[i] = (4 * grp + i < ntok) ? st[i] * scale_log2 : -INFINITY;
         mb = fmaxf(mb, x[i]);
       }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = max_xor32(max_xor16(mb));
       // The reference max moves only when a row's block max exceeds it by more
       // than kLazyRescale (log2 units; the first block always moves it), so the
       // accumulators are rescaled rarely; probabilities stay below 2^kLazyRescale.
@@ -255,8 +254,7 @@ __device__ __forceinline__ void attn_wg(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float Lw = lrun[rt];
-    Lw += __shfl_xor(Lw, 16);
-    Lw += __shfl_xor(Lw, 32);
+    Lw = add_xor32(add_xor16(Lw));
     if (grp == 0) {
       sm_m[wv][rt * 16 + col] = mrun[rt];
       sm_l[wv][rt * 16 + col] = Lw;

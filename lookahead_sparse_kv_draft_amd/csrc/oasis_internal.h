@@ -128,6 +128,42 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
 
+// A value combined with the same value 16 (or 32) lanes away, through the
+// gfx950 lane swaps (VALU instructions, no LDS round trip as a shuffle takes):
+// swapping a register with itself leaves, in every lane, the lane's own value
+// in one result and the value of lane ^ 16 (^ 32) in the other, in an order that
+// depends on the lane, so only commutative combinations are formed from them.
+__device__ __forceinline__ void lane_pair16(uint32_t x, uint32_t& a, uint32_t& b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  a = p[0];
+  b = p[1];
+}
+__device__ __forceinline__ void lane_pair32(uint32_t x, uint32_t& a, uint32_t& b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  a = p[0];
+  b = p[1];
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  uint32_t a, b;
+  lane_pair16(__float_as_uint(x), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  uint32_t a, b;
+  lane_pair32(__float_as_uint(x), a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  uint32_t a, b;
+  lane_pair16(__float_as_uint(x), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  uint32_t a, b;
+  lane_pair32(__float_as_uint(x), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+
 // Streaming loads of data read once per launch (block metadata tiles, KV
 // pages): the non-temporal hint keeps them from displacing cached lines on the
 // way in, which measured 4-6 % faster for the bandwidth-bound launches.

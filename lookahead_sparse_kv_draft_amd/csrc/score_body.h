@@ -97,8 +97,7 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
         if (row < rows) best = fmaxf(best, acc[i]);
       }
     }
-    best = fmaxf(best, __shfl_xor(best, 16));
-    best = fmaxf(best, __shfl_xor(best, 32));
+    best = max_xor32(max_xor16(best));
     const int b = tile * 16 + col;
     if (grp == 0 && b < N) sbase[b] = best;
   };

@@ -285,8 +285,19 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
       hi = max(hi, key[u]);
     }
   }
+  {
+    uint32_t a0, a1, b0, b1;  // lanes ^ 32 and ^ 16 through the lane swaps, then shuffles
+    lane_pair32(lo, a0, a1);
+    lane_pair32(hi, b0, b1);
+    lo = min(a0, a1);
+    hi = max(b0, b1);
+    lane_pair16(lo, a0, a1);
+    lane_pair16(hi, b0, b1);
+    lo = min(a0, a1);
+    hi = max(b0, b1);
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
+  for (int o = 8; o > 0; o >>= 1) {
     lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o)));
     hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o)));
   }
