@@ -171,12 +171,13 @@ __device__ __forceinline__ void attn_wg(
     uint4 k[KS];
     uint2 v[CT];
   };
-  // The page base is wavefront-uniform (scalar registers); the lane offsets are
-  // the same for every page.
+  // The page base is wavefront-uniform (scalar registers, read from the entry's
+  // lane; entry indices stay below nb <= 64); the lane offsets are the same for
+  // every page.
   const uint16_t* kl = ubase + col * D + 8 * grp;
   const uint16_t* vl = ubase + kBlock * D + col * kBlock + 4 * grp;
   auto load = [&](Page& pg, int j) {
-    const size_t off = static_cast<size_t>(__builtin_amdgcn_readfirstlane(__shfl(c_slot, j))) * PAGE;
+    const size_t off = static_cast<size_t>(__builtin_amdgcn_readlane(c_slot, j)) * PAGE;
 #pragma unroll
     for (int s = 0; s < KS; ++s) pg.k[s] = load_stream(reinterpret_cast<const uint4*>(kl + off + 32 * s));
 #pragma unroll
@@ -240,14 +241,14 @@ __device__ __forceinline__ void attn_wg(
     for (int j0 = 0; j0 < npad - PF; j0 += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
-        process(pg[j], __builtin_amdgcn_readfirstlane(__shfl(c_ntok, j0 + j)));
+        process(pg[j], __builtin_amdgcn_readlane(c_ntok, j0 + j));
         load(pg[j], min(j0 + j + PF, nb - 1));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j)
-      if (npad - PF + j < nb) process(pg[j], __builtin_amdgcn_readfirstlane(__shfl(c_ntok, npad - PF + j)));
+      if (npad - PF + j < nb) process(pg[j], __builtin_amdgcn_readlane(c_ntok, npad - PF + j));
   }
 
   // ---- merge the wavefronts: a fixed-order tree in LDS (deterministic) ----
