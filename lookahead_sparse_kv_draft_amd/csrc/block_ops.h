@@ -33,11 +33,7 @@ __device__ __forceinline__ int wg_rank_of_flag(bool flag, int* total, int* wave_
 __device__ __forceinline__ int wg_inclusive_sum(int v, int* wave_tot) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) wave_tot[w] = v;
   __syncthreads();
   int off = 0;

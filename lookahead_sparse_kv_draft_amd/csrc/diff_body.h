@@ -34,7 +34,8 @@ __host__ __device__ inline size_t diff_lds_bytes(int kb, int Nmax, int cap) {
 }
 
 // Number of entries of a[0 .. n) below `mine`, counted by P adjacent threads
-// (this thread is `part` of them) and summed across their lanes.  The reads of
+// (this thread is `part` of them; P <= 16, the group fully active) and summed
+// across their lanes.  The reads of
 // a batch are unconditional (indices clamped), so they are in flight together.
 template <typename K>
 __device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int part) {
@@ -47,8 +48,7 @@ __device__ __forceinline__ int rank_below(const K* a, int n, K mine, int P, int 
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) r += static_cast<int>((j + t * P < n) & (x[t] < mine));
   }
-  for (int o = 1; o < P; o <<= 1) r += __shfl_xor(r, o);
-  return r;
+  return group_sum(r, P);
 }
 
 // selL: LDS [kb], the selection in rank order (complete and visible on entry).

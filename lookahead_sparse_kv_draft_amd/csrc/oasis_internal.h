@@ -164,6 +164,40 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(a) + __uint_as_float(b);
 }
 
+// DPP moves inside a 16-lane row (VALU, no LDS round trip): lane i takes the
+// value of lane ^ 1 (quad_perm [1,0,3,2], 0xB1), lane ^ 2 (quad_perm [2,3,0,1],
+// 0x4E), lane 7 - i of its 8 (row_half_mirror, 0x141), lane 15 - i of its row
+// (row_mirror, 0x140) or lane i - n of its row (row_shr:n, 0x110 + n; 0 for the
+// first n lanes).  The source lane must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_from(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+// Sum over each group of P adjacent lanes (P = 1, 2, 4, 8 or 16, groups aligned
+// to P and fully active); every lane of a group gets the group's sum.
+__device__ __forceinline__ int group_sum(int r, int P) {
+  if (P >= 2) r += dpp_from<0xB1>(r);
+  if (P >= 4) r += dpp_from<0x4E>(r);
+  if (P >= 8) r += dpp_from<0x141>(r);
+  if (P >= 16) r += dpp_from<0x140>(r);
+  return r;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active):
+// within each row by DPP shifts, then the totals of the rows below from
+// lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += dpp_from<0x111>(v);
+  v += dpp_from<0x112>(v);
+  v += dpp_from<0x114>(v);
+  v += dpp_from<0x118>(v);
+  const int row = (threadIdx.x & 63) >> 4;
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
 // Streaming loads of data read once per launch (block metadata tiles, KV
 // pages): the non-temporal hint keeps them from displacing cached lines on the
 // way in, which measured 4-6 % faster for the bandwidth-bound launches.

@@ -116,12 +116,7 @@ __global__ __launch_bounds__(256) void topk_wg_kernel(const float* __restrict__ 
         part[j] = hist[32 * lane + j];
         s += part[j];
       }
-      int incl = s;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
+      const int incl = wave_incl_sum(s);  // the whole wavefront takes part
       const int excl = incl - s;
       if (excl < rem && incl >= rem) {  // exactly one lane: the m-th key is in its bins
         int acc = excl;
@@ -213,11 +208,7 @@ struct TopkFastShared {
 template <bool TRAIL = true>
 __device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) wtot[w] = v;
   __syncthreads();
   int off = 0, tot = 0;
@@ -286,7 +277,7 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
     }
   }
   {
-    uint32_t a0, a1, b0, b1;  // lanes ^ 32 and ^ 16 through the lane swaps, then shuffles
+    uint32_t a0, a1, b0, b1;  // lanes ^ 32 and ^ 16 through the lane swaps
     lane_pair32(lo, a0, a1);
     lane_pair32(hi, b0, b1);
     lo = min(a0, a1);
@@ -296,11 +287,15 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
     lo = min(a0, a1);
     hi = max(b0, b1);
   }
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) {
-    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o)));
-    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o)));
-  }
+  // then across each row by DPP (lane ^ 1, ^ 2, the half-row and row mirrors)
+  lo = min(lo, static_cast<uint32_t>(dpp_from<0xB1>(static_cast<int>(lo))));
+  hi = max(hi, static_cast<uint32_t>(dpp_from<0xB1>(static_cast<int>(hi))));
+  lo = min(lo, static_cast<uint32_t>(dpp_from<0x4E>(static_cast<int>(lo))));
+  hi = max(hi, static_cast<uint32_t>(dpp_from<0x4E>(static_cast<int>(hi))));
+  lo = min(lo, static_cast<uint32_t>(dpp_from<0x141>(static_cast<int>(lo))));
+  hi = max(hi, static_cast<uint32_t>(dpp_from<0x141>(static_cast<int>(hi))));
+  lo = min(lo, static_cast<uint32_t>(dpp_from<0x140>(static_cast<int>(lo))));
+  hi = max(hi, static_cast<uint32_t>(dpp_from<0x140>(static_cast<int>(hi))));
   if (lane == 0) {
     sh.wlo[w] = lo;
     sh.whi[w] = hi;
@@ -403,7 +398,7 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
     if (bw) {
       int wbase = 0;
       if (lane == 0) wbase = atomicAdd(&sh.nwin, __popcll(bw));
-      wbase = __shfl(wbase, 0);
+      wbase = __builtin_amdgcn_readlane(wbase, 0);
       if (win)
         sh.win[wbase + __popcll(bw & below)] =
             (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
