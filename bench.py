@@ -335,12 +335,17 @@ def measure_h2(args, cfg, run, rt, replicas, sequential_step, h1_step_us):
     dbuf = torch.empty(64 * 2**20, dtype=torch.uint8, device="cuda")
     dbuf.copy_(hbuf, non_blocking=True)
     torch.cuda.synchronize()
-    eb.record(cs)
-    for _ in range(5):
-        dbuf.copy_(hbuf, non_blocking=True)
-    ee.record(cs)
-    torch.cuda.synchronize()
-    memcpy_gbs = 5 * hbuf.numel() / (eb.elapsed_time(ee) * 1e-3) / 1e9
+    # three rounds of 5 copies: the host link's rate varies from run to run, the
+    # best round is the achievable reference
+    memcpy_rounds = []
+    for _ in range(3):
+        eb.record(cs)
+        for _ in range(5):
+            dbuf.copy_(hbuf, non_blocking=True)
+        ee.record(cs)
+        torch.cuda.synchronize()
+        memcpy_rounds.append(5 * hbuf.numel() / (eb.elapsed_time(ee) * 1e-3) / 1e9)
+    memcpy_gbs = max(memcpy_rounds)
     return {"ms_per_step": h2_us * 1e-3,
             "steps_per_s": cfg.batch * run.L * 1e6 / h2_us,
             "exposed_transfer_us_per_step": h2_us - h1_step_us * run.L,
@@ -348,6 +353,7 @@ def measure_h2(args, cfg, run, rt, replicas, sequential_step, h1_step_us):
             "gather_us": gather_us,
             "gather_pcie_GBs": (nf_last * page) / (gather_us * 1e-6) / 1e9 if gather_us > 0 else None,
             "h2d_pinned_memcpy_GBs": memcpy_gbs,
+            "h2d_pinned_memcpy_rounds_GBs": memcpy_rounds,
             "note": "PCIe-inclusive single-layer chain: each step's fetch lands before the next attention; "
                     "not the headline value"}
 
