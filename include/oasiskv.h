@@ -288,8 +288,9 @@ int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const voi
  * need only step t's inputs): the sparse paged decode attention (as
  * oasis_sparse_paged_decode_attn, or _list when attend is given) and the
  * lookahead scoring (as oasis_lookahead_score with ctx_score) in ONE grid where
- * the shape allows it (bf16, the default 2-wavefront attention, at most 48
- * attention rows), else back to back.  The attention leaves its split partials
+ * the shape allows it (bf16, at most 48 attention rows, with the default
+ * 2-wavefront attention workgroups, or 4-wavefront ones for at most 32 rows),
+ * else back to back.  The attention leaves its split partials
  * in the workspace; `out` is complete after oasis_attn_combine or
  * oasis_select_diff_combine on the same workspace (which do nothing when the
  * attention has a single split and wrote `out` itself).  sel/block_to_slot may
