@@ -238,10 +238,12 @@ __device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores,
 // topk_fast_load returned and the request's context length n (read by the
 // caller before anything else, so its round trip overlaps the scores'); also
 // written, in rank order and -1 padded, to the LDS array selL when it is not
-// null.
+// null.  keysL (LDS, Nmax entries, or null) receives every candidate's order
+// key at index block - 1 (0xFFFFFFFF past the candidates), before any early
+// return, for a diff that ranks eviction victims by the same keys.
 template <int KPT>
 __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int32_t* __restrict__ sel, int Nmax,
-                                      int kb, int32_t* selL, TopkFastShared& sh) {
+                                      int kb, int32_t* selL, TopkFastShared& sh, uint32_t* keysL = nullptr) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
@@ -263,15 +265,19 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
     out[i] = -1;
     if (selL != nullptr) selL[i] = -1;
   }
+  uint32_t key[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int c = u * kTkThreads + tid;
+    key[u] = (c < C) ? desc_key(v[u]) : 0xFFFFFFFFu;
+    if (keysL != nullptr && c < Nmax) keysL[c] = key[u];
+  }
   if (m <= 0) return;  // uniform: every thread leaves together
 
-  uint32_t key[KPT];
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const bool valid = u * kTkThreads + tid < C;
-    key[u] = valid ? desc_key(v[u]) : 0xFFFFFFFFu;
-    if (valid) {
+    if (u * kTkThreads + tid < C) {
       lo = min(lo, key[u]);
       hi = max(hi, key[u]);
     }
@@ -445,10 +451,11 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
 }
 
 // Dynamic LDS of the fused selection + diff: the diff's arrays, the selection
-// (k ints), and for k <= 128 this unit's block_to_slot row (N_max ints).
+// (k ints), and for k <= 128 this unit's block_to_slot row and the candidates'
+// order keys (N_max ints each).
 inline size_t select_diff_lds_bytes(int kb, int Nmax, int cap) {
   return diff_lds_bytes(kb, Nmax, cap) + static_cast<size_t>(kb) * 4 +
-         (kb <= kDiffWaveMaxBudget ? static_cast<size_t>(Nmax) * 4 : 0);
+         (kb <= kDiffWaveMaxBudget ? static_cast<size_t>(Nmax) * 8 : 0);
 }
 
 // Fused selection + diff of one unit by a 1024-thread workgroup.  The
@@ -477,11 +484,11 @@ __device__ __forceinline__ void select_diff_unit(
   topk_fast_load<KPT>(scores, Nmax, v);
   if (kb <= kDiffWaveMaxBudget) {
     int32_t* b2sL = selL + kb;
+    uint32_t* keysL = reinterpret_cast<uint32_t*>(b2sL + Nmax);
     int bv[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) bv[u] = bu[min(u * kTkThreads + tid, Nmax - 1)];
     int sbw[2], luw[2] = {0, 0};
-    float svw[2];
     int32_t* lu = (last_use != nullptr) ? last_use + static_cast<size_t>(unit) * kb : nullptr;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -490,18 +497,15 @@ __device__ __forceinline__ void select_diff_unit(
       if (lu != nullptr) luw[e] = lu[ie];
     }
     const int n = ctx_len[unit / H];
-    __builtin_amdgcn_sched_barrier(0);  // the context length goes out before the wait for the slot map
-#pragma unroll
-    for (int e = 0; e < 2; ++e) svw[e] = su[(sbw[e] >= 0 && sbw[e] < Nmax) ? sbw[e] : 0];
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
     for (int j = tid; j < (Nmax + 31) / 32; j += kTkThreads) bitmap[j] = 0u;  // ordered by the selection's barriers
-    topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh);
+    topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh, keysL);
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
       if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
     __syncthreads();
     if (tid >= kWave) return;
-    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, svw, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
+    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, keysL, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
               n_attend, smem_u64);
     return;
   }
