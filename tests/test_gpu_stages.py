@@ -582,6 +582,10 @@ def test_fetch_gather_matches_fetch_issue(dtype, d):
     (128, 0, [16 * 528, 16 * 600, 16 * 300, 16 * 129], "normal"),
     (512, 100, [16 * 3000, 16 * 600, 16 * 513, 77], "ties"),       # largest fused budget
     (128, 32, [131072 + 16 * 10, 16 * 900, 16 * 130, 16 * 50], "normal"),  # N > 8192: two launches
+    # k = 2: only the sink and the newest block are selected (nothing to rank), yet
+    # resident blocks must still be ranked as victims by their order keys
+    (2, 2, [16 * 100, 16 * 37 + 5, 33, 16], "normal"),
+    (2, 1, [16 * 300, 16 * 64, 16 * 3, 100], "ties"),
 ])
 def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
     B, H = len(ctxs), 3
