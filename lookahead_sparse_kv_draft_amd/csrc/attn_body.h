@@ -209,16 +209,14 @@ __device__ __forceinline__ void attn_wg(
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) acc[rt][ct] *= alpha;
       }
-      uint16_t pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = f32_to_bf16(exp2f(x[i] - mrun[rt]));
-        psum += bf16_to_f32(pb[i]);
-      }
-      lrun[rt] += psum;
-      const uint2 pw = make_uint2(static_cast<uint32_t>(pb[0]) | (static_cast<uint32_t>(pb[1]) << 16),
-                                  static_cast<uint32_t>(pb[2]) | (static_cast<uint32_t>(pb[3]) << 16));
+      // probabilities rounded to bf16 in pairs by the hardware conversion
+      // (round to nearest even); the running sum adds the rounded values
+      const f32x2_t p01 = {exp2f(x[0] - mrun[rt]), exp2f(x[1] - mrun[rt])};
+      const f32x2_t p23 = {exp2f(x[2] - mrun[rt]), exp2f(x[3] - mrun[rt])};
+      const uint2 pw = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t)),
+                                  __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t)));
+      lrun[rt] += ((__uint_as_float(pw.x << 16) + __uint_as_float(pw.x & 0xFFFF0000u)) +
+                   __uint_as_float(pw.y << 16)) + __uint_as_float(pw.y & 0xFFFF0000u);
       const s16x4_t P = as_s16x4(pw);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)

@@ -124,6 +124,8 @@ hipError_t launch_fetch_gather(const Ctx& c, const void* host_dev, void* pool, c
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ s16x4_t as_s16x4(const uint2& v) { return __builtin_bit_cast(s16x4_t, v); }
