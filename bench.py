@@ -78,9 +78,12 @@ def parse():
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
                    help="--pipeline eviction policies: lowest score, least recently used, or both")
-    p.add_argument("--mode", choices=["graph", "overlap", "eager"], default="eager",
+    p.add_argument("--mode", choices=["graph", "overlap", "eager", "pipeline", "pipeline_graph"], default="eager",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
-                        "second stream beside the attention, captured likewise; eager: plain launches")
+                        "second stream beside the attention, captured likewise; eager: plain launches; "
+                        "pipeline: plain launches, each layer's selection and diff on a second stream "
+                        "beside the next layer's attention and scoring; pipeline_graph: the same captured "
+                        "as a HIP graph")
     return p.parse_args()
 
 
@@ -620,7 +623,9 @@ def main():
     print("# prologue done", file=sys.stderr, flush=True)
 
     names = OPS
-    ps = rt.pstream
+    # side stream (default priority) of the overlap and pipeline modes
+    ps = rt.pstream if rt.pstream is not None else (torch.cuda.Stream() if args.mode.startswith("pipeline")
+                                                    else None)
     ev_attn = [torch.cuda.Event() for _ in range(run.L)]
     ev_sel = [torch.cuda.Event() for _ in range(run.L)]
 
@@ -658,9 +663,38 @@ def main():
                                 st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
                                 st.n_attend, stream=cs)
 
+    ev_scored = torch.cuda.Event()
+    ev_state = [[torch.cuda.Event() for _ in range(replicas)] for _ in range(run.L)]
+
+    def pipelined_step(i, cs, first=False):
+        """One decode step over all layers, the cross-layer pipeline: on the
+        compute stream each layer's attention beside the scoring, then the
+        attention's split combine (the layer's output, which the next layer
+        needs); on the side stream, once the layer's first launch is done, its
+        selection and diff, which only the same layer's next step reads. A
+        state's next first launch waits for its previous selection."""
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            q = run.q[l, t + 1]
+            st = rt.state[l][rep]
+            if not first:
+                cs.wait_event(ev_state[l][rep])
+            L.oasis_attend_and_score(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.attend,
+                                     st.n_attend, st.scores, rt.out, rt.ws_ptr, cs)
+            ev_scored.record(cs)
+            ps.wait_event(ev_scored)
+            L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                    st.evict, st.attend, st.n_attend, stream=ps)
+            ev_state[l][rep].record(ps)
+            L.oasis_attn_combine(rt.h, rt.ws_ptr, rt.out, cs)
+
     cs0 = torch.cuda.current_stream()
     for i in range(args.warmup):
-        sequential_step(i, cs0)
+        if args.mode in ("pipeline", "pipeline_graph"):
+            pipelined_step(i, cs0)
+        else:
+            sequential_step(i, cs0)
     torch.cuda.synchronize()
 
     def attended():
@@ -679,11 +713,17 @@ def main():
     G = 2 * replicas
     cs = torch.cuda.current_stream()
     graph = None
-    if args.mode != "eager":
+    if args.mode != "eager" and args.mode != "pipeline":
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             gs = torch.cuda.current_stream()
-            if args.mode == "overlap":
+            if args.mode == "pipeline_graph":
+                # a state's first use in the graph follows the previous replay's join
+                ps.wait_stream(gs)
+                for j in range(G):
+                    pipelined_step(j, gs, first=(j < replicas))
+                gs.wait_stream(ps)
+            elif args.mode == "overlap":
                 ps.wait_stream(gs)
                 for j in range(G):
                     chain_step(j, gs, first=(j == 0))
@@ -701,6 +741,8 @@ def main():
                 ps.wait_stream(cs)
                 chain_step(j, cs, first=(j == 0))
                 cs.wait_stream(ps)
+            elif args.mode.startswith("pipeline"):
+                pipelined_step(j, cs)
             else:
                 sequential_step(j, cs)
 
@@ -845,7 +887,10 @@ def main():
         "kernels": kern,
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
-                      "eager": "one decode-step call per layer (2 launches) on one stream"}[args.mode],
+                      "eager": "one decode-step call per layer (2 launches) on one stream",
+                      "pipeline": "per layer: attention + scoring, then the split combine, on one stream; "
+                                  "the selection and diff on a second stream beside the next layer",
+                      "pipeline_graph": f"HIP graph of {G} steps of the pipeline mode"}[args.mode],
         "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
         "decode_step_call_us": step_call_us,
         "hbm_reference": {"kernel": "torch device copy, 1 GiB read + 1 GiB written", "GB/s": copy_gbs,
