@@ -78,11 +78,11 @@ def parse():
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
                    help="--pipeline eviction policies: lowest score, least recently used, or both")
-    p.add_argument("--mode", choices=["graph", "overlap", "eager", "pipeline", "pipeline_graph"], default="eager",
+    p.add_argument("--mode", choices=["graph", "overlap", "eager", "two_streams", "two_streams_graph"], default="eager",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
                         "second stream beside the attention, captured likewise; eager: plain launches; "
-                        "pipeline: plain launches, each layer's selection and diff on a second stream "
-                        "beside the next layer's attention and scoring; pipeline_graph: the same captured "
+                        "two_streams: plain launches, each layer's selection and diff on a second stream "
+                        "beside the next layer's attention and scoring; two_streams_graph: the same captured "
                         "as a HIP graph")
     return p.parse_args()
 
@@ -623,8 +623,8 @@ def main():
     print("# prologue done", file=sys.stderr, flush=True)
 
     names = OPS
-    # side stream (default priority) of the overlap and pipeline modes
-    ps = rt.pstream if rt.pstream is not None else (torch.cuda.Stream() if args.mode.startswith("pipeline")
+    # side stream (default priority) of the overlap and two-stream modes
+    ps = rt.pstream if rt.pstream is not None else (torch.cuda.Stream() if args.mode.startswith("two_streams")
                                                     else None)
     ev_attn = [torch.cuda.Event() for _ in range(run.L)]
     ev_sel = [torch.cuda.Event() for _ in range(run.L)]
@@ -666,7 +666,7 @@ def main():
     ev_scored = torch.cuda.Event()
     ev_state = [[torch.cuda.Event() for _ in range(replicas)] for _ in range(run.L)]
 
-    def pipelined_step(i, cs, first=False):
+    def two_stream_step(i, cs, first=False):
         """One decode step over all layers, the cross-layer pipeline: on the
         compute stream each layer's attention beside the scoring, then the
         attention's split combine (the layer's output, which the next layer
@@ -691,8 +691,8 @@ def main():
 
     cs0 = torch.cuda.current_stream()
     for i in range(args.warmup):
-        if args.mode in ("pipeline", "pipeline_graph"):
-            pipelined_step(i, cs0)
+        if args.mode.startswith("two_streams"):
+            two_stream_step(i, cs0)
         else:
             sequential_step(i, cs0)
     torch.cuda.synchronize()
@@ -713,15 +713,15 @@ def main():
     G = 2 * replicas
     cs = torch.cuda.current_stream()
     graph = None
-    if args.mode != "eager" and args.mode != "pipeline":
+    if args.mode != "eager" and args.mode != "two_streams":
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             gs = torch.cuda.current_stream()
-            if args.mode == "pipeline_graph":
+            if args.mode == "two_streams_graph":
                 # a state's first use in the graph follows the previous replay's join
                 ps.wait_stream(gs)
                 for j in range(G):
-                    pipelined_step(j, gs, first=(j < replicas))
+                    two_stream_step(j, gs, first=(j < replicas))
                 gs.wait_stream(ps)
             elif args.mode == "overlap":
                 ps.wait_stream(gs)
@@ -741,8 +741,8 @@ def main():
                 ps.wait_stream(cs)
                 chain_step(j, cs, first=(j == 0))
                 cs.wait_stream(ps)
-            elif args.mode.startswith("pipeline"):
-                pipelined_step(j, cs)
+            elif args.mode.startswith("two_streams"):
+                two_stream_step(j, cs)
             else:
                 sequential_step(j, cs)
 
@@ -888,9 +888,9 @@ def main():
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
                       "eager": "one decode-step call per layer (2 launches) on one stream",
-                      "pipeline": "per layer: attention + scoring, then the split combine, on one stream; "
+                      "two_streams": "per layer: attention + scoring, then the split combine, on one stream; "
                                   "the selection and diff on a second stream beside the next layer",
-                      "pipeline_graph": f"HIP graph of {G} steps of the pipeline mode"}[args.mode],
+                      "two_streams_graph": f"HIP graph of {G} steps of the two_streams mode"}[args.mode],
         "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
         "decode_step_call_us": step_call_us,
         "hbm_reference": {"kernel": "torch device copy, 1 GiB read + 1 GiB written", "GB/s": copy_gbs,
