@@ -102,9 +102,9 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
     if (grp == 0 && b < N) sbase[b] = best;
   };
   // Ping-pong over the two tile buffers: each processed buffer is refilled with
-  // the tile two ahead, the last pair without refills.  Indices are clamped and
-  // the loop body has no branch (a repeated last tile stores identical scores),
-  // so every wait covers exactly the older buffer.
+  // the tile two ahead, the last one or two tiles without refills.  Indices are
+  // clamped and the loop body has no branch (a repeated last tile stores
+  // identical scores), so every wait covers exactly the older buffer.
   const int ntl = t1 - t0;
   int j = 0;
   for (; j + 2 < ntl; j += 2) {
@@ -115,9 +115,11 @@ __device__ inline void score_wave(const uint16_t* __restrict__ q, const uint16_t
     load(Bb, t0 + min(j + 3, ntl - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
-  // last pair: no refills
+  // the last one or two tiles, no refills.  Bb holds tile t0 + j + 1 only when
+  // that tile is in the run: with a single tile (ntl == 1) it was preloaded
+  // from the capacity, past the context, and must not be stored.
   compute(Ba, t0 + j);
-  compute(Bb, t0 + min(j + 1, ntl - 1));
+  if (j + 1 < ntl) compute(Bb, t0 + j + 1);
 }
 
 }  // namespace oasis
