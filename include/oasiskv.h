@@ -79,8 +79,39 @@ typedef struct oasis_shape {
 
 typedef struct oasis_ctx* oasis_handle;
 
-/* Validates the shape (EINVAL / EUNSUPPORTED) and returns a handle.  No HIP call. */
+/*
+ * Launch shapes of the kernels (performance only: every choice computes the
+ * same selections, lists and maps; attention outputs differ only by the order
+ * of fp32 sums where the split of the attended list changes).  A field left 0
+ * takes the default, which the library picks from the shape.
+ */
+typedef struct oasis_launch_options {
+  int32_t attn_waves;     /* wavefronts per attention workgroup: 0, 1, 2 or 4 (default 2;
+                             at most 2 with more than 32 attention rows) */
+  int32_t attn_pf;        /* pages in flight per attention wavefront: 0, 2, 4 or 8 (default 2;
+                             capped by the registers the row count needs) */
+  int32_t attn_splits;    /* attention workgroups per unit, 0..32 (default: about 512
+                             attention wavefronts per launch; bounded so that a
+                             wavefront streams at most 64 blocks) */
+  int32_t score_tpw;      /* 16-block tiles per scoring wavefront, 0..64 (default: about
+                             4096 scoring wavefronts beside the attention, 2048 alone) */
+  int32_t step_order;     /* workgroup order of the step's first launch: 0 attention first
+                             (default), 1 scoring first, 2 interleaved */
+  int32_t step_launches;  /* launches per oasis_decode_step: 0 or 2 (attention beside the
+                             scoring; selection + diff + split combine), or 3 (attention;
+                             combine + scoring; selection + diff) */
+} oasis_launch_options;
+
+/* Validates the shape (EINVAL / EUNSUPPORTED) and returns a handle with the
+ * default launch options.  No HIP call. */
 int oasis_create(const oasis_shape* shape, oasis_handle* out);
+/* The same with explicit launch options (opts may be NULL = all defaults);
+ * EINVAL on a field outside the ranges above.  The handle stays immutable. */
+int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_options* opts,
+                              oasis_handle* out);
+/* The launch options a handle uses, defaults and caps resolved (score_tpw is
+ * the value beside the attention). */
+int oasis_get_launch_options(oasis_handle h, oasis_launch_options* out);
 int oasis_destroy(oasis_handle h);
 /* Last error message of the calling thread ("" if none). */
 const char* oasis_last_error(void);

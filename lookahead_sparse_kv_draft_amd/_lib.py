@@ -33,6 +33,13 @@ class oasis_shape(ctypes.Structure):
         "budget_blocks", "n_draft", "fetch_cap", "dtype")]
 
 
+class oasis_launch_options(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in (
+        "attn_waves", "attn_pf", "attn_splits", "score_tpw", "step_order", "step_launches")]
+
+
+LAUNCH_OPTION_FIELDS = tuple(f for f, _ in oasis_launch_options._fields_)
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _int = ctypes.c_int
@@ -41,6 +48,9 @@ _sz = ctypes.c_size_t
 # name -> (restype, argtypes); status-returning functions use c_int.
 SIGNATURES = {
     "oasis_create": (_int, [ctypes.POINTER(oasis_shape), ctypes.POINTER(_vp)]),
+    "oasis_create_with_options": (_int, [ctypes.POINTER(oasis_shape), ctypes.POINTER(oasis_launch_options),
+                                         ctypes.POINTER(_vp)]),
+    "oasis_get_launch_options": (_int, [_vp, ctypes.POINTER(oasis_launch_options)]),
     "oasis_destroy": (_int, [_vp]),
     "oasis_last_error": (ctypes.c_char_p, []),
     "oasis_version": (_int, []),
@@ -134,6 +144,29 @@ def oasis_create(batch, kv_heads, group, head_dim, max_blocks, budget_blocks, n_
     h = _vp()
     _call("oasis_create", ctypes.byref(s), ctypes.byref(h))
     return h.value
+
+
+def oasis_create_with_options(batch, kv_heads, group, head_dim, max_blocks, budget_blocks, n_draft, fetch_cap,
+                              dtype, options=None, block_size=16) -> int:
+    """options: a dict of oasis_launch_options fields (missing fields = 0, the default)."""
+    s = oasis_shape(batch=batch, kv_heads=kv_heads, group=group, head_dim=head_dim,
+                    block_size=block_size, max_blocks=max_blocks, budget_blocks=budget_blocks,
+                    n_draft=n_draft, fetch_cap=fetch_cap, dtype=dtype)
+    o = None
+    if options is not None:
+        unknown = set(options) - set(LAUNCH_OPTION_FIELDS)
+        if unknown:
+            raise ValueError(f"unknown launch options {sorted(unknown)}")
+        o = oasis_launch_options(**{k: int(v) for k, v in options.items()})
+    h = _vp()
+    _call("oasis_create_with_options", ctypes.byref(s), None if o is None else ctypes.byref(o), ctypes.byref(h))
+    return h.value
+
+
+def oasis_get_launch_options(h) -> dict:
+    o = oasis_launch_options()
+    _call("oasis_get_launch_options", h, ctypes.byref(o))
+    return {f: getattr(o, f) for f in LAUNCH_OPTION_FIELDS}
 
 
 def oasis_destroy(h):

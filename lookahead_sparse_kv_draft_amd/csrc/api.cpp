@@ -42,12 +42,6 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (v == nullptr || *v == '\0') return dflt;
-  return atoi(v);
-}
-
 // [16][d] token-major -> [d][16] channel-major.
 template <typename T>
 void transpose_block(const T* src, T* dst, int d) {
@@ -73,6 +67,10 @@ int oasis_version(void) { return 1; }
 const char* oasis_last_error(void) { return g_err.c_str(); }
 
 int oasis_create(const oasis_shape* shape, oasis_handle* out) {
+  return oasis_create_with_options(shape, nullptr, out);
+}
+
+int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_options* opts, oasis_handle* out) {
   CHECK_PTR(shape);
   CHECK_PTR(out);
   *out = nullptr;
@@ -99,6 +97,20 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   if (rows_attn > oasis::kMaxRows)
     return fail(OASIS_EUNSUPPORTED, "oasis_create: (1 + n_draft) * group = %d query rows > %d",
                 rows_attn, oasis::kMaxRows);
+  oasis_launch_options o{};
+  if (opts != nullptr) o = *opts;
+  if (o.attn_waves != 0 && o.attn_waves != 1 && o.attn_waves != 2 && o.attn_waves != 4)
+    return fail(OASIS_EINVAL, "oasis_create: attn_waves %d (0, 1, 2 or 4)", o.attn_waves);
+  if (o.attn_pf != 0 && o.attn_pf != 2 && o.attn_pf != 4 && o.attn_pf != 8)
+    return fail(OASIS_EINVAL, "oasis_create: attn_pf %d (0, 2, 4 or 8)", o.attn_pf);
+  if (o.attn_splits < 0 || o.attn_splits > oasis::kAttnMaxSplits)
+    return fail(OASIS_EINVAL, "oasis_create: attn_splits %d outside [0, %d]", o.attn_splits, oasis::kAttnMaxSplits);
+  if (o.score_tpw < 0 || o.score_tpw > 64)
+    return fail(OASIS_EINVAL, "oasis_create: score_tpw %d outside [0, 64]", o.score_tpw);
+  if (o.step_order < 0 || o.step_order > 2)
+    return fail(OASIS_EINVAL, "oasis_create: step_order %d outside [0, 2]", o.step_order);
+  if (o.step_launches != 0 && o.step_launches != 2 && o.step_launches != 3)
+    return fail(OASIS_EINVAL, "oasis_create: step_launches %d (0, 2 or 3)", o.step_launches);
 
   oasis_ctx* h = new (std::nothrow) oasis_ctx;
   if (h == nullptr) return fail(OASIS_EINVAL, "oasis_create: out of host memory");
@@ -119,9 +131,7 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // start-up and write fewer partials).
   const int row_tiles = (rows_attn + 15) / 16;
   const int max_waves = (row_tiles <= 2) ? 4 : 2;  // LDS of the wavefront merge
-  int waves = env_int("OASIS_ATTN_WAVES", 0);
-  if (waves != 1 && waves != 2 && waves != 4) waves = 2;
-  waves = std::min(waves, max_waves);
+  const int waves = std::min(o.attn_waves != 0 ? o.attn_waves : 2, max_waves);
   const int kbud = s.budget_blocks;
   // The decode step's first launch (attention beside the scoring, bf16 with the
   // default shape) keeps its own attention and scoring shapes.  With the
@@ -130,10 +140,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // batch-8 step 34.4 us against 35.3 us with 1024 attention wavefronts, at the
   // 128K-context 8-layer step 40.8 against 42.8 us, within 0.5 % elsewhere.
   const bool step_fused = s.dtype == OASIS_BF16 && rows_attn <= 48 && (waves == 2 || (waves == 4 && row_tiles <= 2));
-  const int env_splits = env_int("OASIS_ATTN_SPLITS", 0);
   // split count for about `target` wavefronts, then the run per wavefront
   auto shape_splits = [&](int target, int* run_out) {
-    int sp = env_splits > 0 ? env_splits : (target + c.units * waves - 1) / (c.units * waves);
+    int sp = o.attn_splits > 0 ? o.attn_splits : (target + c.units * waves - 1) / (c.units * waves);
     const int min_splits = (kbud + 64 * waves - 1) / (64 * waves);  // run <= 64
     const int max_splits = std::min(oasis::kAttnMaxSplits, (kbud + waves - 1) / waves);
     sp = std::max(min_splits, std::min(sp, max_splits));
@@ -144,10 +153,9 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   int run = 0, run_solo = 0;
   const int splits = shape_splits(512, &run);
   const int splits_solo = shape_splits(512, &run_solo);
-  int pf = env_int("OASIS_ATTN_PF", 0);
   const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
-  if (pf != 2 && pf != 4 && pf != 8) pf = 2;  // measured: a shallow ring keeps the math beside the loads
-  pf = std::min(pf, max_pf);
+  // measured: a shallow ring keeps the math beside the loads
+  const int pf = std::min(o.attn_pf != 0 ? o.attn_pf : 2, max_pf);
   c.attn_waves = waves;
   c.attn_pf = pf;
   c.attn_run = run;
@@ -163,15 +171,26 @@ int oasis_create(const oasis_shape* shape, oasis_handle* out) {
   // launch is 0.4 us faster with 2).
   const long long tiles = units * ((s.max_blocks + 15) / 16);
   auto runs_for = [&](long long waves) {
-    const int t = env_int("OASIS_SCORE_TPW", 0);
-    return t > 0 ? t : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
+    return o.score_tpw > 0 ? o.score_tpw : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
   };
   c.score_tpw = runs_for(step_fused ? 4096 : 2048);
   c.score_tpw_solo = runs_for(2048);
-  c.step_order = env_int("OASIS_STEP_ORDER", 0);
-  if (c.step_order < 0 || c.step_order > 2) c.step_order = 0;
-  c.step_launches = (env_int("OASIS_STEP_LAUNCHES", 2) == 3) ? 3 : 2;
+  c.step_order = o.step_order;
+  c.step_launches = o.step_launches == 3 ? 3 : 2;
   *out = h;
+  return ok();
+}
+
+int oasis_get_launch_options(oasis_handle h, oasis_launch_options* out) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(out);
+  const oasis::Ctx& c = h->c;
+  out->attn_waves = c.attn_waves;
+  out->attn_pf = c.attn_pf;
+  out->attn_splits = c.attn_splits;
+  out->score_tpw = c.score_tpw;
+  out->step_order = c.step_order;
+  out->step_launches = c.step_launches;
   return ok();
 }
 
