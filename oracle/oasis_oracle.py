@@ -141,81 +141,111 @@ class DiffResult:
     last_use: np.ndarray = None  # LRU policy only: per-slot stamp after the step
 
 
-def resident_diff_cap_evict(sel, score, block_to_slot, slot_to_block, cap: int) -> DiffResult:
-    """Fetch list, eviction list and updated head-wise resident maps.
+def plan_fetch_evict(sel, score, block_to_slot, slot_to_block, cap: int):
+    """O4 steps 1-5: the fetch list F and the victims V, both in order.
 
     [EXPL] explanatory diagram step 3 and "What they did" item 3: predicted
     blocks are compared with the resident ones, only the missing blocks are
     fetched, and a capped-eviction policy bounds the blocks fetched per step
     (Table 2 sweeps that cap).
-    [EXPL] Figure 9: a per-KV-head table maps each GPU block (slot) to a CPU
-    block; block_to_slot is its inverse.
 
-    Readings: the fetch takes the highest-ranked missing blocks first; free slots
-    are used in ascending order, then victims, which are resident blocks outside
-    S taken from the tail of the ranking order (lowest score first, and among
-    equal scores the higher block index first).
+    Readings: the fetch takes the highest-ranked missing blocks first; victims
+    are resident blocks outside S taken from the tail of the ranking order
+    (lowest score first, and among equal scores the higher block index first),
+    as many as the free slots do not cover.
     """
     k = len(slot_to_block)
-    b2s = np.array(block_to_slot, dtype=np.int64).copy()
-    s2b = np.array(slot_to_block, dtype=np.int64).copy()
+    b2s = np.asarray(block_to_slot)
+    s2b = np.asarray(slot_to_block)
     S = [int(b) for b in sel if b >= 0]
     Sset = set(S)
     missing = [b for b in S if b2s[b] < 0]
     F = missing[: min(cap, len(missing))]
-    free = [s for s in range(k) if s2b[s] < 0]
-    need = max(0, len(F) - len(free))
+    n_free = sum(1 for s in range(k) if s2b[s] < 0)
+    need = max(0, len(F) - n_free)
     outside = [int(s2b[s]) for s in range(k) if s2b[s] >= 0 and int(s2b[s]) not in Sset]
     ranked = sorted(outside, key=lambda b: order_key(score[b], b))
     V = list(reversed(ranked))[:need]
     assert len(V) == need, "fewer victims than needed: |S| must not exceed k"
+    return F, V
+
+
+def apply_fetch_evict(block_to_slot, slot_to_block, F, V) -> DiffResult:
+    """O4 steps 6-8: target slots and the updated head-wise resident maps.
+
+    [EXPL] Figure 9: a per-KV-head table maps each GPU block (slot) to a CPU
+    block; block_to_slot is its inverse.  Reading: the fetched blocks take the
+    free slots in ascending order first, then the victims' slots in victim
+    order.
+    """
+    k = len(slot_to_block)
+    b2s = np.array(block_to_slot, dtype=np.int64).copy()
+    s2b = np.array(slot_to_block, dtype=np.int64).copy()
+    free = [s for s in range(k) if s2b[s] < 0]
+    assert len(V) == max(0, len(F) - len(free)), "victims must cover exactly what the free slots do not"
+    assert all(b2s[v] >= 0 for v in V) and all(b2s[b] < 0 for b in F)
     targets = free[: min(len(F), len(free))] + [int(b2s[v]) for v in V]
     for v in V:
         b2s[v] = -1
     for b, s in zip(F, targets):
         s2b[s] = b
         b2s[b] = s
-    return DiffResult(fetch=list(zip(F, targets)), evict=V, block_to_slot=b2s, slot_to_block=s2b)
+    return DiffResult(fetch=list(zip(F, targets)), evict=list(V), block_to_slot=b2s, slot_to_block=s2b)
 
 
-def resident_diff_cap_evict_lru(sel, score, block_to_slot, slot_to_block, last_use, cap: int,
-                                step: int) -> DiffResult:
-    """The same step with least-recently-used eviction ([EXPL] Table 2: the
+def resident_diff_cap_evict(sel, score, block_to_slot, slot_to_block, cap: int) -> DiffResult:
+    """Fetch list, eviction list and updated head-wise resident maps (O4):
+    plan_fetch_evict, then apply_fetch_evict."""
+    F, V = plan_fetch_evict(sel, score, block_to_slot, slot_to_block, cap)
+    return apply_fetch_evict(block_to_slot, slot_to_block, F, V)
+
+
+def plan_fetch_evict_lru(sel, score, block_to_slot, slot_to_block, last_use, cap: int):
+    """O4 steps 1-5 with least-recently-used eviction ([EXPL] Table 2: the
     fetch-ratio ablation runs with LRU eviction).
 
-    Readings (the pages name the policy only): a slot is used when an attention
-    reads it, and each step stamps the slots of the next attention's blocks (the
-    selection after this step's fetch, resident) with `step`; a slot never
-    stamped holds -1.  Victims are the resident blocks outside S with the oldest
-    stamp first; among equal stamps, the lowest-score order of
-    resident_diff_cap_evict (lowest score first, then the higher block index).
-    Fetch order and target slots are as in resident_diff_cap_evict.
+    Readings (the pages name the policy only): victims are the resident blocks
+    outside S with the oldest stamp first (a slot never read holds -1); among
+    equal stamps, the lowest-score order of plan_fetch_evict (lowest score
+    first, then the higher block index).  The fetch list is as there.
     """
     k = len(slot_to_block)
-    b2s = np.array(block_to_slot, dtype=np.int64).copy()
-    s2b = np.array(slot_to_block, dtype=np.int64).copy()
-    lu = np.array(last_use, dtype=np.int64).copy()
+    b2s = np.asarray(block_to_slot)
+    s2b = np.asarray(slot_to_block)
+    lu = np.asarray(last_use)
     S = [int(b) for b in sel if b >= 0]
     Sset = set(S)
     missing = [b for b in S if b2s[b] < 0]
     F = missing[: min(cap, len(missing))]
-    free = [s for s in range(k) if s2b[s] < 0]
-    need = max(0, len(F) - len(free))
+    n_free = sum(1 for s in range(k) if s2b[s] < 0)
+    need = max(0, len(F) - n_free)
     outside = [int(s2b[s]) for s in range(k) if s2b[s] >= 0 and int(s2b[s]) not in Sset]
     # oldest stamp first; then lowest score (-0.0 as +0.0), then higher index
     ranked = sorted(outside, key=lambda b: (int(lu[b2s[b]]), float(score[b]) + 0.0, -b))
     V = ranked[:need]
     assert len(V) == need, "fewer victims than needed: |S| must not exceed k"
-    targets = free[: min(len(F), len(free))] + [int(b2s[v]) for v in V]
-    for v in V:
-        b2s[v] = -1
-    for b, s in zip(F, targets):
-        s2b[s] = b
-        b2s[b] = s
-    for b in S:  # the next attention reads these slots
-        if b2s[b] >= 0:
-            lu[b2s[b]] = step
-    return DiffResult(fetch=list(zip(F, targets)), evict=V, block_to_slot=b2s, slot_to_block=s2b, last_use=lu)
+    return F, V
+
+
+def stamp_last_use(sel, block_to_slot, last_use, step: int) -> np.ndarray:
+    """LRU stamps after a step's diff.  Reading: a slot is used when an
+    attention reads it, so the slots of the next attention's blocks (the
+    selection that is resident after this step's fetch) get `step`."""
+    lu = np.array(last_use, dtype=np.int64).copy()
+    for b in sel:
+        if b >= 0 and block_to_slot[b] >= 0:
+            lu[block_to_slot[b]] = step
+    return lu
+
+
+def resident_diff_cap_evict_lru(sel, score, block_to_slot, slot_to_block, last_use, cap: int,
+                                step: int) -> DiffResult:
+    """The O4 step with LRU eviction: plan_fetch_evict_lru, apply_fetch_evict,
+    then stamp_last_use with `step`."""
+    F, V = plan_fetch_evict_lru(sel, score, block_to_slot, slot_to_block, last_use, cap)
+    res = apply_fetch_evict(block_to_slot, slot_to_block, F, V)
+    res.last_use = stamp_last_use(sel, res.block_to_slot, last_use, step)
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -266,12 +296,12 @@ class StepRecord:
     block_to_slot: np.ndarray | None = None  # after this step's update
     slot_to_block: np.ndarray | None = None
     slot_to_block_before: np.ndarray | None = None  # before this step's update
+    block_to_slot_before: np.ndarray | None = None
+    last_use: np.ndarray | None = None  # LRU stamps after this step (LRU eviction only)
     n_missing: int = 0
 
 
-def run_unit(*, K_at, V, queries, drafts_prologue, n0: int, k: int, cap: int, steps: int,
-             initial_slots, append: bool = False, max_blocks: int | None = None,
-             with_attention: bool = True) -> list:
+class UnitChain:
     """Multi-step chain of one unit ([EXPL] Figure 8).
 
     The draft queries of step t drive scoring, selection and transfer, and the
@@ -282,56 +312,104 @@ def run_unit(*, K_at, V, queries, drafts_prologue, n0: int, k: int, cap: int, st
     the initial residency initial_slots(S_0) and runs one diff/cap/evict.
 
     K_at(t) gives the key truth valid after step t's drift (t = -1 for the
-    prologue); V is fixed; queries(t) is [G][T][d] (row 0 verify, rows 1..D the
-    drafts); drafts_prologue is [D][G][d] or [G][D][d] (only its rows matter).
-    In this oracle the HBM pool is a view of the host truth, so a fetched or
-    patched page always holds the current keys and values.
+    prologue; the same array object when nothing changed); V is fixed;
+    queries(t) is [G][T][d] (row 0 verify, rows 1..D the drafts).  In this
+    oracle the HBM pool is a view of the host truth, so a fetched or patched
+    page always holds the current keys and values.
+
+    eviction: "score" (lowest-score victims) or "lru" (least recently used;
+    the diff that prepares the attention of step t stamps its slots with t, the
+    prologue's with 0).
+
+    Two choices have more than one correct result when scores tie within the
+    comparison's tolerance: the selection of a step and the victims of its
+    diff.  They pass through choose_selection and choose_victims, which return
+    the oracle's own choice; a comparison may override them to continue from
+    another implementation's choice after checking that it is valid.
     """
-    n = n0
-    Nmax = max_blocks if max_blocks is not None else (n0 + BLOCK - 1) // BLOCK + (steps if append else 0)
-    recs = []
 
-    K = K_at(-1)
-    kmin, kmax = block_meta(K, n)
-    rec = StepRecord(t=-1, n_score=n)
-    rec.score = lookahead_score(drafts_prologue, kmin, kmax)
-    rec.sel = topk_select(rec.score, kmin.shape[0], k)
-    s2b = np.asarray(initial_slots(rec.sel), dtype=np.int64).copy()
-    b2s = np.full(Nmax, -1, dtype=np.int64)
-    for s, b in enumerate(s2b):
-        if b >= 0:
-            b2s[b] = s
-    rec.slot_to_block_before = s2b.copy()
-    res = resident_diff_cap_evict(rec.sel, rec.score, b2s, s2b, cap)
-    rec.n_missing = sum(1 for b in rec.sel if b >= 0 and b2s[b] < 0)
-    b2s, s2b = res.block_to_slot, res.slot_to_block
-    rec.fetch, rec.evict = res.fetch, res.evict
-    rec.block_to_slot, rec.slot_to_block = b2s.copy(), s2b.copy()
-    recs.append(rec)
-    sel = rec.sel
+    def __init__(self, *, K_at, V, queries, n0: int, k: int, cap: int, steps: int, append: bool = False,
+                 max_blocks: int | None = None, with_attention: bool = True, eviction: str = "score"):
+        assert eviction in ("score", "lru")
+        self.K_at, self.V, self.queries = K_at, V, queries
+        self.n = n0
+        self.k, self.cap = k, cap
+        self.append, self.with_attention, self.eviction = append, with_attention, eviction
+        self.Nmax = max_blocks if max_blocks is not None else (n0 + BLOCK - 1) // BLOCK + (steps if append else 0)
+        self.K = K_at(-1)
+        self.kmin, self.kmax = block_meta(self.K, self.n)
+        self.sel = None
+        self.b2s = self.s2b = self.last_use = None
 
-    for t in range(steps):
-        rec = StepRecord(t=t, n_attn=n)
-        q = queries(t)
-        rec.attended = attended_blocks(sel, b2s)
-        if with_attention:
-            rec.out = sparse_attention(q, K, V, rec.attended, n)
-        if append:
-            kmin, kmax = block_meta_append(kmin, kmax, n, K[n])
-            n += 1
-        K_new = K_at(t)
-        if K_new is not K:
-            K = K_new
-            kmin, kmax = block_meta(K, n)
-        rec.n_score = n
-        rec.score = lookahead_score(q[:, 1:, :], kmin, kmax)
-        rec.sel = topk_select(rec.score, kmin.shape[0], k)
-        rec.n_missing = sum(1 for b in rec.sel if b >= 0 and b2s[b] < 0)
-        rec.slot_to_block_before = s2b.copy()
-        res = resident_diff_cap_evict(rec.sel, rec.score, b2s, s2b, cap)
-        b2s, s2b = res.block_to_slot, res.slot_to_block
+    # ---- decision points (near ties) ----
+    def choose_selection(self, rec: StepRecord, sel: list) -> list:
+        return sel
+
+    def choose_victims(self, rec: StepRecord, F: list, V: list) -> list:
+        return V
+
+    # ---- stages ----
+    def _predict(self, rec: StepRecord, drafts):
+        rec.n_score = self.n
+        rec.score = lookahead_score(drafts, self.kmin, self.kmax)
+        rec.sel = self.choose_selection(rec, topk_select(rec.score, self.kmin.shape[0], self.k))
+
+    def _diff(self, rec: StepRecord, stamp: int):
+        rec.n_missing = sum(1 for b in rec.sel if b >= 0 and self.b2s[b] < 0)
+        rec.slot_to_block_before = self.s2b.copy()
+        rec.block_to_slot_before = self.b2s.copy()
+        if self.eviction == "lru":
+            F, V = plan_fetch_evict_lru(rec.sel, rec.score, self.b2s, self.s2b, self.last_use, self.cap)
+        else:
+            F, V = plan_fetch_evict(rec.sel, rec.score, self.b2s, self.s2b, self.cap)
+        V = self.choose_victims(rec, F, V)
+        res = apply_fetch_evict(self.b2s, self.s2b, F, V)
+        if self.eviction == "lru":
+            self.last_use = stamp_last_use(rec.sel, res.block_to_slot, self.last_use, stamp)
+            rec.last_use = self.last_use.copy()
+        self.b2s, self.s2b = res.block_to_slot, res.slot_to_block
         rec.fetch, rec.evict = res.fetch, res.evict
-        rec.block_to_slot, rec.slot_to_block = b2s.copy(), s2b.copy()
-        recs.append(rec)
-        sel = rec.sel
+        rec.block_to_slot, rec.slot_to_block = self.b2s.copy(), self.s2b.copy()
+        self.sel = rec.sel
+
+    def prologue(self, drafts_prologue, initial_slots) -> StepRecord:
+        """drafts_prologue is [D][G][d] or [G][D][d] (only its rows matter)."""
+        rec = StepRecord(t=-1)
+        self._predict(rec, drafts_prologue)
+        self.s2b = np.asarray(initial_slots(rec.sel), dtype=np.int64).copy()
+        self.b2s = np.full(self.Nmax, -1, dtype=np.int64)
+        for s, b in enumerate(self.s2b):
+            if b >= 0:
+                self.b2s[b] = s
+        self.last_use = np.full(self.k, -1, dtype=np.int64)
+        self._diff(rec, stamp=0)
+        return rec
+
+    def step(self, t: int) -> StepRecord:
+        rec = StepRecord(t=t, n_attn=self.n)
+        q = self.queries(t)
+        rec.attended = attended_blocks(self.sel, self.b2s)
+        if self.with_attention:
+            rec.out = sparse_attention(q, self.K, self.V, rec.attended, self.n)
+        if self.append:
+            self.kmin, self.kmax = block_meta_append(self.kmin, self.kmax, self.n, self.K[self.n])
+            self.n += 1
+        K_new = self.K_at(t)
+        if K_new is not self.K:
+            self.K = K_new
+            self.kmin, self.kmax = block_meta(self.K, self.n)
+        self._predict(rec, q[:, 1:, :])
+        self._diff(rec, stamp=t + 1)
+        return rec
+
+
+def run_unit(*, K_at, V, queries, drafts_prologue, n0: int, k: int, cap: int, steps: int,
+             initial_slots, append: bool = False, max_blocks: int | None = None,
+             with_attention: bool = True, eviction: str = "score") -> list:
+    """The prologue and `steps` steps of one unit's chain (UnitChain), as records."""
+    chain = UnitChain(K_at=K_at, V=V, queries=queries, n0=n0, k=k, cap=cap, steps=steps, append=append,
+                      max_blocks=max_blocks, with_attention=with_attention, eviction=eviction)
+    recs = [chain.prologue(drafts_prologue, initial_slots)]
+    for t in range(steps):
+        recs.append(chain.step(t))
     return recs

@@ -84,14 +84,14 @@ def test_attention_closed_forms():
 
 
 # ------------------------------------------------------------- chain pins
-def _chain(cfg, r=0, l=0, h=0, with_attention=True):
+def _chain(cfg, r=0, l=0, h=0, with_attention=True, eviction="score"):
     ud = synth.unit_data(cfg, r, l, h)
     K = ud.keys()
     return ud, K, O.run_unit(
         K_at=lambda t: K, V=ud.V, queries=ud.queries, drafts_prologue=ud.drafts[0],
-        n0=cfg.ctx, k=cfg.k, cap=cfg.fetch_cap, steps=cfg.steps,
+        n0=cfg.ctx_of(r), k=cfg.k, cap=cfg.fetch_cap, steps=cfg.steps,
         initial_slots=lambda S0: synth.initial_residency(cfg, r, l, h, S0),
-        append=cfg.append, max_blocks=cfg.max_blocks, with_attention=with_attention)
+        append=cfg.append, max_blocks=cfg.max_blocks, with_attention=with_attention, eviction=eviction)
 
 
 def _check_chain_invariants(cfg, recs):
@@ -150,3 +150,39 @@ def test_chain_small_cap(cap):
     if cap == 0:
         for rec in recs:
             assert rec.fetch == [] and rec.evict == []
+
+
+@pytest.mark.parametrize("cap", [1, 3, 16])
+def test_chain_lru_stamps_are_last_reads(cap):
+    """LRU chain: after every step a slot's stamp is the index of the last
+    attention that read it (-1 if none has), recomputed here from the attended
+    sets alone; every victim is at least as old as every resident block outside
+    the selection that stays; the chain invariants hold."""
+    cfg = CONFIGS["tiny"].with_(fetch_cap=cap, steps=8, append=True, ctx=1000)
+    ud, K, recs = _chain(cfg, with_attention=False, eviction="lru")
+    _check_chain_invariants(cfg, recs)
+    last = {}
+    for a, rec in enumerate(recs):
+        # attention a (of step a) reads the selected resident blocks this record leaves
+        for b in O.attended_blocks(rec.sel, rec.block_to_slot):
+            last[int(rec.block_to_slot[b])] = a
+        assert [last.get(s, -1) for s in range(cfg.k)] == [int(x) for x in rec.last_use], a
+        if a > 0:
+            prev = recs[a - 1].last_use
+            S = {b for b in rec.sel if b >= 0}
+            before = rec.slot_to_block_before
+            stay = [int(x) for x in before if x >= 0 and int(x) not in S and int(x) not in rec.evict]
+            slot_of = {int(x): s for s, x in enumerate(before) if x >= 0}
+            for v in rec.evict:
+                assert all(prev[slot_of[v]] <= prev[slot_of[w]] for w in stay), (a, v)
+
+
+def test_chain_lru_equals_score_policy_without_eviction_pressure():
+    """With a cap that never needs a victim beyond the free slots (cap 0) the
+    two eviction policies leave identical chains."""
+    cfg = CONFIGS["tiny"].with_(fetch_cap=0, steps=4)
+    _, _, a = _chain(cfg, with_attention=False)
+    _, _, b = _chain(cfg, with_attention=False, eviction="lru")
+    for x, y in zip(a, b):
+        assert x.sel == y.sel and x.fetch == y.fetch and x.evict == y.evict
+        assert np.array_equal(x.block_to_slot, y.block_to_slot)
