@@ -67,10 +67,13 @@ class Shape:
     def np_elem(self):
         return np.uint16 if self.dtype == "bf16" else np.float32
 
-    def handle(self, fetch_cap: int | None = None) -> int:
-        return L.oasis_create(self.batch, self.kv_heads, self.group, self.head_dim, self.max_blocks,
-                              self.budget_blocks, self.n_draft,
-                              self.fetch_cap if fetch_cap is None else fetch_cap, self.code)
+    def handle(self, fetch_cap: int | None = None, options: dict | None = None) -> int:
+        """A library handle of this shape (options: launch options, see
+        oasis_launch_options; None = the library's defaults)."""
+        return L.oasis_create_with_options(self.batch, self.kv_heads, self.group, self.head_dim, self.max_blocks,
+                                           self.budget_blocks, self.n_draft,
+                                           self.fetch_cap if fetch_cap is None else fetch_cap, self.code,
+                                           options=options)
 
 
 def untile_meta(meta: torch.Tensor, units: int, max_blocks: int, d: int, dtype: str) -> torch.Tensor:
@@ -116,6 +119,9 @@ class LayerState:
         # attended list for the next attention (written by every diff)
         self.attend = torch.full((u, k), -1, dtype=torch.int32, device=dev)
         self.n_attend = torch.zeros(u, dtype=torch.int32, device=dev)
+        # least-recently-used eviction: per-slot stamp of the last attention that read it
+        self.last_use = (torch.full((u, k), -1, dtype=torch.int32, device=dev) if rt.eviction == "lru"
+                         else None)
         self.vscores = None  # corrective path buffers (allocated on first use)
         self.host_tier = host_tier
         self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
@@ -146,6 +152,8 @@ class LayerState:
         for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict", "attend",
                      "n_attend"):
             getattr(self, name).copy_(getattr(other, name))
+        if self.last_use is not None:
+            self.last_use.copy_(other.last_use)
 
 
 class DecodeRuntime:
@@ -153,16 +161,23 @@ class DecodeRuntime:
 
     def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
                  host_tier: bool = True, fused_select: bool = True, overlap: bool = False,
-                 gather: bool = True):
+                 gather: bool = True, options: dict | None = None, eviction: str = "score"):
         """overlap: run scoring / selection on a second stream so that they overlap
         the attention of the same step (and of other layers); the selection waits
-        only for the attention that reads the maps it rewrites."""
+        only for the attention that reads the maps it rewrites.  options: launch
+        options of the library handle (None = defaults).  eviction: "score"
+        (lowest-score victims) or "lru" (least recently read slot first; the diff
+        that prepares attention t stamps that attention's slots with t)."""
+        if eviction not in ("score", "lru"):
+            raise ValueError(eviction)
         self.shape = shape
+        self.options = options
+        self.eviction = eviction
         self.fused_select = fused_select
         self.overlap = overlap
         self.gather = gather
         self.device = torch.device(device)
-        self.h = shape.handle()
+        self.h = shape.handle(options=options)
         self._h_full = None
         s = shape
         self.n_layers = layers
@@ -284,8 +299,14 @@ class DecodeRuntime:
         finally:
             L.oasis_destroy(h_all)
         for st in self.state[layer]:
-            L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
-                                            st.evict, st.attend, st.n_attend)
+            if self.eviction == "lru":
+                # the selection again (same scores, same result) with the diff
+                # that stamps the slots attention 0 reads
+                L.oasis_select_and_diff_lru(self.h, st.scores, self.ctx_len, st.sel, st.b2s, st.s2b, st.last_use, 0,
+                                            st.fetch, st.n_fetch, st.evict, st.attend, st.n_attend)
+            else:
+                L.oasis_resident_diff_cap_evict(self.h, st.sel, st.scores, st.b2s, st.s2b, st.fetch, st.n_fetch,
+                                                st.evict, st.attend, st.n_attend)
         self.transfer(layer, stream=torch.cuda.current_stream())
 
     # ------------------------------------------------------------ per-step chain
@@ -309,13 +330,14 @@ class DecodeRuntime:
             st.attn_done.record(cs)
 
     def decode_step(self, layer: int, q: torch.Tensor, replica: int = 0, out: torch.Tensor | None = None,
-                    two_calls: bool = False):
+                    two_calls: bool = False, stamp: int = 0):
         """Attention of step t, scoring of its drafts, selection of S_{t+1} and the
         diff, in one library call (two launches for the default shape) on the
         current stream, or (two_calls) as its two halves: attention + scoring,
         then selection + diff + the attention's split combine.  An append of this
         step is enqueued before it (the attention does not read what the append
-        writes; the scoring sees the grown context)."""
+        writes; the scoring sees the grown context).  stamp: with LRU eviction,
+        the index of the next attention (step t + 1), whose slots the diff stamps."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
         if st.fetch_wait_compute or st.fetch_wait_predict:
@@ -325,6 +347,13 @@ class DecodeRuntime:
             cs.wait_event(st.select_done)
             st.select_pending = False
         o = self.out if out is None else out
+        if self.eviction == "lru":
+            L.oasis_attend_and_score(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
+                                     st.attend, st.n_attend, st.scores, o, self.ws_ptr, cs)
+            L.oasis_select_diff_combine_lru(self.h, st.scores, self.ctx_scoring, st.sel, st.b2s, st.s2b, st.last_use,
+                                            stamp, st.fetch, st.n_fetch, st.evict, st.attend, st.n_attend, o,
+                                            self.ws_ptr, cs)
+            return
         if two_calls:
             L.oasis_attend_and_score(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
                                      st.attend, st.n_attend, st.scores, o, self.ws_ptr, cs)
@@ -368,7 +397,7 @@ class DecodeRuntime:
             self.ctx_host = self.ctx_host + 1
             self._appended = False
 
-    def predict_select(self, layer: int, q: torch.Tensor, replica: int = 0):
+    def predict_select(self, layer: int, q: torch.Tensor, replica: int = 0, stamp: int = 0):
         """Score the drafts of step t, select S_{t+1}, diff against the resident set.
 
         With overlap the scoring runs beside the attention of step t; the
@@ -380,7 +409,10 @@ class DecodeRuntime:
         L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores, ps)
         if self.overlap:
             ps.wait_event(st.attn_done)
-        if self.fused_select:
+        if self.eviction == "lru":
+            L.oasis_select_and_diff_lru(self.h, st.scores, ctx, st.sel, st.b2s, st.s2b, st.last_use, stamp, st.fetch,
+                                        st.n_fetch, st.evict, st.attend, st.n_attend, stream=ps)
+        elif self.fused_select:
             L.oasis_select_and_diff(self.h, st.scores, ctx, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
                                     st.evict, st.attend, st.n_attend, stream=ps)
         else:
@@ -425,7 +457,7 @@ class DecodeRuntime:
         """A handle of the same shape whose fetch cap is the whole budget (the
         corrective fetch is not capped)."""
         if self._h_full is None:
-            self._h_full = self.shape.handle(fetch_cap=self.shape.budget_blocks)
+            self._h_full = self.shape.handle(fetch_cap=self.shape.budget_blocks, options=self.options)
         return self._h_full
 
     def transfer(self, layer: int, replica: int = 0, stream=None):

@@ -43,18 +43,20 @@ class SyntheticRun:
 
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
                  record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
-                 gather: bool = True, two_calls: bool = False):
+                 gather: bool = True, two_calls: bool = False, options: dict | None = None,
+                 eviction: str = "score"):
         """fused_step: without overlap and drift, run each layer's step through the
         single decode-step call (attention, scoring, selection, diff), or through
         its two halves (two_calls).  gather: move the fetched pages with the
-        device-driven gather (else host-issued copies)."""
+        device-driven gather (else host-issued copies).  options: the library's
+        launch options (None = defaults).  eviction: "score" or "lru"."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
         self.two_calls = two_calls
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
-                                gather=gather)
+                                gather=gather, options=options, eviction=eviction)
         self.record_units = record_units  # list of (layer, unit) to record, or None
         self.records = {}
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
@@ -72,7 +74,6 @@ class SyntheticRun:
     def _fill(self):
         cfg, rt = self.cfg, self.rt
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
-        N0 = cfg.n_blocks0
         qh = np.empty((cfg.steps + 1, B, H * G, T, d), dtype=np.float32)
         if cfg.drift_blocks:
             self.drift = {}  # (l, u) -> (unit data, schedule)
@@ -81,6 +82,7 @@ class SyntheticRun:
                 r, h = divmod(u, H)
                 ud = synth.unit_data(cfg, r, l, h)
                 K = ud.keys()
+                N0 = cfg.n_blocks0_of(r)
                 rt.pack_unit(l, u, _elem(cfg, K[: N0 * BLOCK]), _elem(cfg, ud.V[: N0 * BLOCK]))
                 for t in range(-1, cfg.steps):
                     qq = ud.queries(t)  # [G][T][d]
@@ -89,7 +91,7 @@ class SyntheticRun:
                         qq[:, 0, :] = 0.0  # the prologue scores drafts only
                     qh[t + 1, r, h * G:(h + 1) * G] = qq
                 if cfg.append:
-                    pos = cfg.ctx + np.arange(cfg.steps)
+                    pos = cfg.ctx_of(r) + np.arange(cfg.steps)
                     self.k_new_host[l, :, r, h] = _elem(cfg, K[pos])
                     self.v_new_host[l, :, r, h] = _elem(cfg, ud.V[pos])
                 if self.drift is not None:
@@ -102,7 +104,7 @@ class SyntheticRun:
                                               else self.k_new_host).to(self.rt.device)
             self.v_new_dev = torch.from_numpy(self.v_new_host.view(np.int16) if cfg.dtype == "bf16"
                                               else self.v_new_host).to(self.rt.device)
-        rt.set_ctx(np.full(cfg.batch, cfg.ctx, dtype=np.int32))
+        rt.set_ctx(np.array([cfg.ctx_of(r) for r in range(cfg.batch)], dtype=np.int32))
         for l in range(self.L):
             rt.build_meta(l)
 
@@ -141,7 +143,7 @@ class SyntheticRun:
                 if cfg.append:
                     rt.append(l, self.k_new_dev[l, t], self.v_new_dev[l, t],
                               self.k_new_host[l, t], self.v_new_host[l, t])
-                rt.decode_step(l, q, two_calls=self.two_calls)
+                rt.decode_step(l, q, two_calls=self.two_calls, stamp=t + 1)
                 if self.record_units is not None:
                     self._record_out(l, t)
                 if transfer:
@@ -161,7 +163,7 @@ class SyntheticRun:
                           self.k_new_host[l, t], self.v_new_host[l, t])
             if self.drift is not None:
                 self._apply_drift(l, t)
-            rt.predict_select(l, q)
+            rt.predict_select(l, q, stamp=t + 1)
             if transfer:
                 rt.transfer(l)
         rt.end_step()
@@ -199,6 +201,8 @@ class SyntheticRun:
                 st = self.rt.state[l][0]
                 cache[l] = {k: getattr(st, k).cpu().numpy() for k in
                             ("sel", "scores", "fetch", "n_fetch", "evict", "s2b", "b2s")}
+                if st.last_use is not None:
+                    cache[l]["last_use"] = st.last_use.cpu().numpy()
             c = cache[l]
             rec = self.records.setdefault((l, u), {}).setdefault(t, {})
             nf = int(c["n_fetch"][u])
@@ -207,6 +211,8 @@ class SyntheticRun:
                        evict=[int(v) for v in c["evict"][u][:nf] if v >= 0],
                        s2b=c["s2b"][u].copy(), b2s=c["b2s"][u].copy(),
                        n_scoring=int(self.rt.ctx_len.cpu().numpy()[u // self.cfg.kv_heads]))
+            if "last_use" in c:
+                rec["last_use"] = c["last_use"][u].copy()
 
     def close(self):
         self.rt.close()

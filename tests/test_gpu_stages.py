@@ -31,11 +31,17 @@ def _rng(seed):
     ("bf16", 128, 16, 3, 300, [4800, 3333]),   # 48 rows, several tiles per wave
     ("f32", 64, 4, 3, 64, [1024, 999]),
     ("f32", 128, 2, 2, 20, [300, 20]),
+    # every tile count mod 2, 3 and 4 below the capacity of 19 tiles, so that the
+    # last run of some wavefront holds a single in-context tile with capacity past it
+    ("bf16", 128, 4, 4, 300, [16 * 16 * 4 + 5, 16 * 16 * 3 + 1, 16 * 16 * 9 + 16, 16 * 16 * 6 + 9, 16 * 16 * 18]),
 ])
-def test_score_parity(dtype, d, G, D, Nmax, ctxs):
+@pytest.mark.parametrize("tpw", [None, 2, 3, 4])
+def test_score_parity(dtype, d, G, D, Nmax, ctxs, tpw):
+    # tpw: 16-block tiles per scoring wavefront (None: the default for the shape,
+    # one tile here)
     B, H = len(ctxs), 2
     sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, n_draft=D, dtype=dtype)
-    h = sh.handle()
+    h = sh.handle(options=None if tpw is None else dict(score_tpw=tpw))
     rng = _rng(1)
     units = B * H
     a = rng.standard_normal((units, Nmax, d)).astype(np.float32)
@@ -70,9 +76,11 @@ def test_score_standalone_matches_step_launch():
     """At 64 units x 2048 blocks (8192 tiles of 16 blocks) the scoring on its own
     runs 4 tiles per wavefront and the decode step's first launch, beside the
     attention, 2; every block's bound is the same MFMA sequence either way, so
-    the two must agree bit for bit, and with the oracle on sampled units."""
+    the two must agree bit for bit, and with the oracle on every unit.  Several
+    contexts end on a tile count of 1 mod 4 (and odd) below the capacity: the
+    last wavefront of those units holds one in-context tile."""
     B, H, G, D, d, Nmax, k = 8, 8, 4, 4, 128, 2048, 16
-    ctxs = [32768, 32768 - 5, 16 * 2000 + 3, 16 * 1500, 32768, 16 * 1024, 16 * 700 + 9, 16 * 2047]
+    ctxs = [32768, 32768 - 5, 16 * 2000 + 3, 16 * 16 * 65, 16 * 65, 16 * 1024, 16 * (16 * 96 + 1) + 9, 16 * 2047]
     sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k, n_draft=D)
     h = sh.handle()
     rng = _rng(11)
@@ -102,7 +110,7 @@ def test_score_standalone_matches_step_launch():
     torch.cuda.synchronize()
     got_solo, got_fused = solo.cpu().numpy(), fused.cpu().numpy()
     assert np.array_equal(got_solo, got_fused, equal_nan=True)
-    for u in (0, 9, 37, 63):
+    for u in range(units):
         r, hh = divmod(u, H)
         N = (ctxs[r] + BLK - 1) // BLK
         qd = q[r, hh * G:(hh + 1) * G, 1:].reshape(-1, d).astype(np.float64)
@@ -120,13 +128,22 @@ def test_score_standalone_matches_step_launch():
     (16, [1024, 16 * 16, 16 * 17, 5], "ties"),
     (16, [1024, 999, 33, 16 * 18], "const"),
     (2, [1024, 16, 32, 48], "normal"),
-    (128, [131072, 131072 - 5, 16 * 129, 16 * 8191], "normal"),   # N > 4096: workgroup kernel
-    (128, [16 * 4096, 16 * 4000 + 9, 16 * 200, 16 * 130], "ties"),  # largest single-wave case
-    (512, [16 * 3000, 16 * 600, 16 * 513, 77], "normal"),          # k > 258: workgroup kernel
+    (128, [131072, 131072 - 5, 16 * 129, 16 * 8191], "normal"),   # N = 8192: largest fast-path case
+    (128, [16 * 4096, 16 * 4000 + 9, 16 * 200, 16 * 130], "ties"),
+    (512, [16 * 3000, 16 * 600, 16 * 513, 77], "normal"),          # k = 512: largest fast-path budget
     (256, [16 * 3000, 16 * 600, 16 * 257, 16 * 200], "ties"),
     # all keys equal: 512 candidates fit the winner list beside the threshold
     # bin (taken whole, trimmed by rank), 513 and more take the ordered tie pass
     (128, [16 * 514, 16 * 515, 16 * 513, 16 * 516], "const"),
+    # the workgroup kernel (N > 8192 or k > 514): normal scores, few distinct
+    # values and all equal; with ties the threshold's equal keys overflow its
+    # list (2 * 128 or 2 * 1024 entries) and take the ordered lowest-index pass
+    (128, [16 * 9000, 16 * 8200 + 3, 16 * 8193 + 1, 16 * 300], "normal"),
+    (128, [16 * 9000, 16 * 8200 + 3, 16 * 8193 + 1, 16 * 300], "ties"),
+    (128, [16 * 9000, 16 * 8200 + 3, 16 * 8193 + 1, 16 * 300], "const"),
+    (1024, [16 * 4000, 16 * 3000 + 9, 16 * 2051, 16 * 1030], "normal"),
+    (1024, [16 * 9000, 16 * 4000 + 9, 16 * 2051, 16 * 1030], "ties"),
+    (1024, [16 * 9000, 16 * 4000 + 9, 16 * 2051, 16 * 100], "const"),
 ])
 def test_topk_parity(k, ctxs, kind):
     B, H = len(ctxs), 3
@@ -228,21 +245,17 @@ def test_diff_parity(k, cap, N, kind):
 ])
 @pytest.mark.parametrize("waves,pf,splits", [(None, None, None), (1, 2, 1), (2, 4, 3), (4, 2, 0), (4, 8, 2),
                                              (1, 8, 5)])
-def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits, monkeypatch):
+def test_attention_parity(dtype, d, G, D, k, ctxs, waves, pf, splits):
     # launch variants: default shape; 1-, 2- and 4-wavefront workgroups merged in
     # LDS; rings of 2, 4 or 8 pages over runs that are shorter than, equal to or
-    # (padded) multiples of the ring; one split or several, merged by the last
-    # workgroup of each unit
-    if waves is not None:
-        monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
-        monkeypatch.setenv("OASIS_ATTN_PF", str(pf))
-        monkeypatch.setenv("OASIS_ATTN_SPLITS", str(splits))
+    # (padded) multiples of the ring; one split or several
+    opts = None if waves is None else dict(attn_waves=waves, attn_pf=pf, attn_splits=splits)
     B, H = len(ctxs), 2
     T = 1 + D
     Nmax = max((c + BLK - 1) // BLK for c in ctxs)
     sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k,
                       n_draft=D, fetch_cap=k, dtype=dtype)
-    rt = DecodeRuntime(sh)
+    rt = DecodeRuntime(sh, options=opts)
     rng = _rng(4)
     units = B * H
     K = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32) * 1.5)
@@ -353,19 +366,17 @@ def test_attention_empty_selection_gives_zero():
 
 
 @pytest.mark.parametrize("waves,pf", [(None, None), (1, 8)])
-def test_attention_growing_logits(waves, pf, monkeypatch):
+def test_attention_growing_logits(waves, pf):
     """Logits that grow along the selection order by far more than the lazy
     rescaling threshold, so the running reference max moves many times."""
-    if waves is not None:
-        monkeypatch.setenv("OASIS_ATTN_WAVES", str(waves))
-        monkeypatch.setenv("OASIS_ATTN_PF", str(pf))
+    opts = None if waves is None else dict(attn_waves=waves, attn_pf=pf)
     B, H, G, D, d, k = 2, 2, 4, 4, 128, 64
     ctxs = [2048, 1500]
     T = 1 + D
     Nmax = 128
     sh = U.make_shape(batch=B, kv_heads=H, group=G, head_dim=d, max_blocks=Nmax, budget_blocks=k,
                       n_draft=D, fetch_cap=k, dtype="bf16")
-    rt = DecodeRuntime(sh)
+    rt = DecodeRuntime(sh, options=opts)
     rng = _rng(9)
     units = B * H
     q = U.elem_round("bf16", rng.standard_normal((B, H * G, T, d)).astype(np.float32))

@@ -41,6 +41,7 @@ class Config:
     init_resident: str = "half"  # "random": k random blocks; "half": half of S0 + random others
     draft_sigma: float = 0.1
     seed: int = 20260807
+    ctx_list: tuple = ()  # per-request prompt lengths (empty: every request has `ctx`)
 
     # ---- derived sizes ----
     @property
@@ -51,9 +52,17 @@ class Config:
     def n_blocks0(self) -> int:
         return (self.ctx + BLOCK - 1) // BLOCK
 
+    def ctx_of(self, r: int) -> int:
+        """Prompt length of request r."""
+        return int(self.ctx_list[r]) if self.ctx_list else self.ctx
+
+    def n_blocks0_of(self, r: int) -> int:
+        return (self.ctx_of(r) + BLOCK - 1) // BLOCK
+
     @property
     def ctx_max(self) -> int:
-        return self.ctx + (self.steps if self.append else 0)
+        top = max(self.ctx_list) if self.ctx_list else self.ctx
+        return top + (self.steps if self.append else 0)
 
     @property
     def max_blocks(self) -> int:

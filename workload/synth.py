@@ -12,7 +12,7 @@ check sampled units of a full-size run):
 * stream (r, l, h, 0), fixed draw order:
   K_raw [max_blocks*16][d] ~ N(0, 1), V_raw [max_blocks*16][d] ~ N(0, 1),
   q_base [G][d] ~ N(0, 1), the planted block set (uniform without replacement
-  over the prompt blocks), draft noise [steps + 1][D][G][d] ~ N(0, 0.1^2).
+  over the request's prompt blocks), draft noise [steps + 1][D][G][d] ~ N(0, 0.1^2).
 * u = normalize(sum_g q_base[g]), the unit mean query direction of the group.
 * K = round(round(K_raw) + s * u) per token, s = planted_shift if the token's
   block is planted, plus recency_shift if the token lies in the last
@@ -83,7 +83,7 @@ class UnitData:
             blk = np.arange(cfg.max_blocks * BLOCK) // BLOCK
             s += cfg.planted_shift * np.isin(blk, planted).astype(np.float32)
         if cfg.recency_blocks:
-            start = max(0, (cfg.n_blocks0 - cfg.recency_blocks) * BLOCK)
+            start = max(0, (cfg.n_blocks0_of(self.r) - cfg.recency_blocks) * BLOCK)
             s[start:] += cfg.recency_shift  # last prompt blocks and every appended token
         return s
 
@@ -115,7 +115,8 @@ def unit_data(cfg: Config, r: int, l: int, h: int) -> UnitData:
     K_raw = rng.standard_normal((n, d), dtype=np.float32)
     V_raw = rng.standard_normal((n, d), dtype=np.float32)
     q_raw = rng.standard_normal((G, d), dtype=np.float32)
-    planted = np.sort(rng.choice(cfg.n_blocks0, size=min(cfg.planted, cfg.n_blocks0), replace=False))
+    nb0 = cfg.n_blocks0_of(r)
+    planted = np.sort(rng.choice(nb0, size=min(cfg.planted, nb0), replace=False))
     noise = rng.standard_normal((cfg.steps + 1, D, G, d), dtype=np.float32)
     noise *= np.float32(cfg.draft_sigma)
     su = q_raw.sum(axis=0)
@@ -140,7 +141,7 @@ def initial_residency(cfg: Config, r: int, l: int, h: int, S0) -> np.ndarray:
     S0 is the selection the caller computed for the prologue (entries < 0 ignored).
     """
     rng = _rng(cfg, r, l, h, 1)
-    k, N = cfg.k, cfg.n_blocks0
+    k, N = cfg.k, cfg.n_blocks0_of(r)
     if cfg.init_resident == "random":
         blocks = rng.choice(N, size=min(k, N), replace=False)
     elif cfg.init_resident == "half":
@@ -169,7 +170,7 @@ def drift_schedule(cfg: Config, r: int, l: int, h: int, planted0: np.ndarray):
     for _ in range(cfg.steps):
         m = min(cfg.drift_blocks, len(cur))
         unplant = np.sort(rng.choice(cur, size=m, replace=False)) if m else cur[:0]
-        pool = np.setdiff1d(np.arange(cfg.n_blocks0), cur)
+        pool = np.setdiff1d(np.arange(cfg.n_blocks0_of(r)), cur)
         m2 = min(cfg.drift_blocks, len(pool))
         plant = np.sort(rng.choice(pool, size=m2, replace=False)) if m2 else pool[:0]
         cur = np.sort(np.concatenate([np.setdiff1d(cur, unplant), plant]))
