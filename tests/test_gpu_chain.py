@@ -17,7 +17,7 @@ import torch
 from lookahead_sparse_kv_draft_amd.synthetic import SyntheticRun
 from oracle import oasis_oracle as O
 from tests import chain_compare as CC
-from workload import CONFIGS
+from workload import CONFIGS, synth
 
 pytestmark = pytest.mark.gpu
 
@@ -95,11 +95,32 @@ def test_chain_small_drift():
 
 @pytest.mark.parametrize("overlap", [False, True])
 def test_chain_small_lru(overlap):
-    """Least-recently-used eviction over a chain with appends and a binding cap
-    (victims needed at most steps), stamps compared at every step."""
+    """Least-recently-used eviction over a drifting chain with a binding cap,
+    stamps compared at every step.  The drift makes the LRU victims differ
+    from the lowest-score ones at most steps (checked on the oracle)."""
+    cfg = CONFIGS["qwen32b_32k"].with_(batch=1, layers=2, ctx=16 * 200, steps=8, planted=10, drift_blocks=4,
+                                       budget_tokens=16 * 24, fetch_cap=4)
+    units = [(l, u) for l in range(2) for u in range(cfg.kv_heads)]
+    _run_and_compare(cfg, units, overlap=overlap, eviction="lru")
+    differ = 0
+    for (l, u) in units[:3]:
+        r, h = divmod(u, cfg.kv_heads)
+        ud, K_at = CC.unit_inputs(cfg, l, u)
+        recs = {ev: O.run_unit(K_at=K_at, V=ud.V, queries=ud.queries, drafts_prologue=ud.drafts[0], n0=cfg.ctx, k=cfg.k,
+                               cap=cfg.fetch_cap, steps=cfg.steps,
+                               initial_slots=lambda S0: synth.initial_residency(cfg, r, l, h, S0),
+                               max_blocks=cfg.max_blocks, with_attention=False, eviction=ev)
+                for ev in ("score", "lru")}
+        differ += sum(a.evict != b.evict for a, b in zip(recs["score"], recs["lru"]))
+    assert differ >= 3, differ
+
+
+def test_chain_small_lru_append():
+    """Least-recently-used eviction over a chain with appends (the newest block
+    turns over), stamps compared at every step."""
     cfg = CONFIGS["qwen8b_reason"].with_(batch=2, ctx=16 * 40 + 13, steps=30, recency_blocks=8,
                                          planted=4, budget_tokens=16 * 16, fetch_cap=3)
-    _run_and_compare(cfg, _all_units(cfg), overlap=overlap, eviction="lru")
+    _run_and_compare(cfg, _all_units(cfg), eviction="lru")
 
 
 def _state_snapshot(run):
