@@ -302,6 +302,23 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                                    void* stream);
 
 /*
+ * oasis_sparse_paged_decode_attn for callers that cannot allocate memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same kernels and
+ * the same output.  The split partials live in a scratch array of 16 MiB that
+ * the library holds on each GPU it runs on until the process ends; its address
+ * is looked up once per device (hipGetSymbolAddress, on the calling thread's
+ * current device, which `stream` must belong to).  Nothing is allocated and
+ * nothing needs clearing.  EINVAL if the shape needs more workspace than the
+ * scratch holds (oasis_workspace_bytes() > 16 MiB).  Every call on a GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+int oasis_sparse_paged_decode_attn_noalloc(oasis_handle h, const void* q, const void* pool,
+                                           const int32_t* sel, const int32_t* block_to_slot,
+                                           const int32_t* ctx_len, float* out, void* stream);
+
+/*
  * The same attention with S ∩ R given as the attended list a diff produced
  * (attend / n_attend of oasis_resident_diff_cap_evict, oasis_select_and_diff
  * or oasis_decode_step): one load per entry instead of a selection lookup and a

@@ -73,6 +73,7 @@ SIGNATURES = {
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 18),
     "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
+    "oasis_sparse_paged_decode_attn_noalloc": (_int, [_vp] * 8),
     "oasis_attend_and_score": (_int, [_vp] * 14),
     "oasis_attn_combine": (_int, [_vp] * 4),
     "oasis_select_diff_combine": (_int, [_vp] * 14),
@@ -264,6 +265,11 @@ def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot,
     _call("oasis_decode_step", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score), _ptr(sel),
           _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
           _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), _stream(stream))
+
+
+def oasis_sparse_paged_decode_attn_noalloc(h, q, pool, sel, block_to_slot, ctx_len, out, stream=None):
+    _call("oasis_sparse_paged_decode_attn_noalloc", h, _ptr(q), _ptr(pool), _ptr(sel), _ptr(block_to_slot),
+          _ptr(ctx_len), _ptr(out), _stream(stream))
 
 
 def oasis_sparse_paged_decode_attn_list(h, q, pool, attend, n_attend, ctx_len, out, workspace, stream=None):

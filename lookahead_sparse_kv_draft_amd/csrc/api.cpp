@@ -463,6 +463,29 @@ int oasis_sparse_paged_decode_attn(oasis_handle h, const void* q, const void* po
                     "oasis_sparse_paged_decode_attn");
 }
 
+int oasis_sparse_paged_decode_attn_noalloc(oasis_handle h, const void* q, const void* pool, const int32_t* sel,
+                                           const int32_t* block_to_slot, const int32_t* ctx_len, float* out,
+                                           void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(sel);
+  CHECK_PTR(block_to_slot);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(out);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  const size_t need = oasis::attn_workspace_bytes(h->c);
+  if (need > oasis::attn_scratch_bytes())
+    return fail(OASIS_EINVAL,
+                "oasis_sparse_paged_decode_attn_noalloc: the shape needs %zu bytes of workspace, more than the "
+                "%zu-byte scratch (use oasis_sparse_paged_decode_attn with a workspace)",
+                need, oasis::attn_scratch_bytes());
+  return hip_status(oasis::launch_attn_noalloc(h->c, q, pool, sel, block_to_slot, ctx_len, out,
+                                               static_cast<hipStream_t>(stream)),
+                    "oasis_sparse_paged_decode_attn_noalloc");
+}
+
 int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const void* pool, const int32_t* attend,
                                         const int32_t* n_attend, const int32_t* ctx_len, float* out,
                                         void* workspace, void* stream) {

@@ -26,6 +26,7 @@
 // Both paths leave one partial per split; a log-sum-exp combine kernel merges
 // them.
 #include <algorithm>
+#include <mutex>
 
 #include "attn_body.h"
 #include "attn_combine.h"
@@ -277,6 +278,44 @@ hipError_t launch_attn(const Ctx& c0, const void* q, const void* pool, const int
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
   return (c.s.head_dim == 128) ? combine_t<128>(c, ws_acc, ws_ml, out, st)
                                : combine_t<64>(c, ws_acc, ws_ml, out, st);
+}
+
+// ---- the attention without a caller workspace ----
+// Its split partials live in this file-scope device array: one copy per GPU,
+// held until the process ends, shared by every such call on that GPU (calls
+// that overlap on one GPU race on it).  Nothing in it must start at zero: every
+// split writes its whole partial before the combine reads it.  In host code the
+// array's name is only a stand-in; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t attn_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_attn_noalloc(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                               const int32_t* ctx_len, float* out, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return launch_attn(c, q, pool, sel, b2s, nullptr, nullptr, ctx_len, out, ws, st);
 }
 
 }  // namespace oasis

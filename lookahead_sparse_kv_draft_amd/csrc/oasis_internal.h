@@ -117,6 +117,11 @@ hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const i
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st);
 size_t attn_workspace_bytes(const Ctx& c);
+// The attention with its workspace in the library's per-GPU scratch array (no
+// allocation); attn_scratch_bytes() is that array's size.
+size_t attn_scratch_bytes();
+hipError_t launch_attn_noalloc(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                               const int32_t* ctx_len, float* out, hipStream_t st);
 hipError_t launch_fetch_gather(const Ctx& c, const void* host_dev, void* pool, const int32_t* fetch,
                                const int32_t* n_fetch, hipStream_t st);
 

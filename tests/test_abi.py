@@ -179,3 +179,17 @@ def test_pack_pages_layout(dtype):
         assert np.array_equal(pages[1, 0, : 16 * d].reshape(16, d)[0], kn[0, 1])
     finally:
         L.oasis_destroy(h)
+
+
+def test_noalloc_attention_rejects_a_workspace_beyond_its_scratch():
+    # 512 units x 64 rows x 4 splits of k = 256 need 64 MiB of partials: more than
+    # the 16 MiB scratch; rejected on the host, before any device work
+    h = L.oasis_create(**_shape(batch=64, kv_heads=8, group=16, n_draft=3, max_blocks=4096, budget_blocks=256))
+    try:
+        assert L.oasis_workspace_bytes(h) > 16 << 20
+        lib = L.load()
+        assert lib.oasis_sparse_paged_decode_attn_noalloc(h, 16, 16, 16, 16, 16, 16, None) == L.OASIS_EINVAL
+        assert "scratch" in L.oasis_last_error()
+        assert lib.oasis_sparse_paged_decode_attn_noalloc(h, None, 16, 16, 16, 16, 16, None) == L.OASIS_EINVAL
+    finally:
+        L.oasis_destroy(h)
