@@ -72,6 +72,8 @@ def parse():
                    help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
                         "(one JSON line per sweep instead of the headline)")
     p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
+    p.add_argument("--groups", default="1,2,4",
+                   help="--pipeline: layers per transfer batch (one side-stream hand-off and one event each)")
     p.add_argument("--recall", action="store_true",
                    help="prediction recall of the drafts' selection against the verify query's own selection, "
                         "and the cost of a blocking corrective fetch (one JSON line)")
@@ -421,79 +423,83 @@ def pipeline_sweep(args):
     ev_fetch = [torch.cuda.Event() for _ in range(nl)]
     nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
     points = []
-    for policy in policies:
-        for cap in caps:
-            h = rt.shape.handle(fetch_cap=cap)
+    groups = [int(x) for x in args.groups.split(",")]
+    runs = [(p, c, g) for p in policies for c in caps for g in (groups if p == policies[0] else groups[-1:])]
+    for policy, cap, group in runs:
+        h = rt.shape.handle(fetch_cap=cap)
+        for l in range(nl):
+            rt.state[l][0].copy_from(rt.state[l][1])
+            lus[l].fill_(-1)
+        clock = [0]
+
+        def step(i, transfer, first=False, count=False):
+            t = i % cfg.steps
+            clock[0] += 1
             for l in range(nl):
-                rt.state[l][0].copy_from(rt.state[l][1])
-                lus[l].fill_(-1)
-            clock = [0]
+                st = rt.state[l][0]
+                gi = l // group  # layers [gi * group, ...) hand their transfers over as one batch
+                if transfer and not first and l % group == 0:
+                    cs.wait_event(ev_fetch[gi])
+                q = run.q[l, t + 1]
+                if policy == "score":
+                    L.oasis_decode_step(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
+                                        st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                        st.n_attend, stream=cs)
+                else:
+                    L.oasis_attend_and_score(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                             st.attend, st.n_attend, st.scores, rt.out, rt.ws_ptr, cs)
+                    L.oasis_select_diff_combine_lru(h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, lus[l],
+                                                    clock[0], st.fetch, st.n_fetch, st.evict, st.attend,
+                                                    st.n_attend, rt.out, rt.ws_ptr, cs)
+                if count:
+                    nf_tot.add_(st.n_fetch.sum())
+                if transfer and ((l + 1) % group == 0 or l == nl - 1):
+                    ev_sel[gi].record(cs)
+                    side.wait_event(ev_sel[gi])
+                    for ll in range(gi * group, l + 1):
+                        sl = rt.state[ll][0]
+                        L.oasis_fetch_gather(h, sl.host_tier, sl.pool, sl.fetch, sl.n_fetch, side)
+                    ev_fetch[gi].record(side)
 
-            def step(i, transfer, first=False, count=False):
-                t = i % cfg.steps
-                clock[0] += 1
-                for l in range(nl):
-                    st = rt.state[l][0]
-                    if transfer and not first:
-                        cs.wait_event(ev_fetch[l])
-                    q = run.q[l, t + 1]
-                    if policy == "score":
-                        L.oasis_decode_step(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
-                                            st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
-                                            st.n_attend, stream=cs)
-                    else:
-                        L.oasis_attend_and_score(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
-                                                 st.attend, st.n_attend, st.scores, rt.out, rt.ws_ptr, cs)
-                        L.oasis_select_diff_combine_lru(h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, lus[l],
-                                                        clock[0], st.fetch, st.n_fetch, st.evict, st.attend,
-                                                        st.n_attend, rt.out, rt.ws_ptr, cs)
-                    if count:
-                        nf_tot.add_(st.n_fetch.sum())
-                    if transfer:
-                        ev_sel[l].record(cs)
-                        side.wait_event(ev_sel[l])
-                        L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
-                        ev_fetch[l].record(side)
-
-            K = args.steps
-            res = {}
-            for transfer in (False, True):
-                for i in range(args.warmup):
-                    step(i, transfer, first=(i == 0))
-                cs.wait_stream(side)
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for i in range(K):
-                    step(i, transfer)
-                cs.wait_stream(side)
-                torch.cuda.synchronize()
-                res[transfer] = (time.perf_counter() - t0) / K * 1e6
-            nf_tot.zero_()
-            for i in range(K):  # untimed: pages fetched per step
-                step(i, True, count=True)
+        K = args.steps
+        res = {}
+        for transfer in (False, True):
+            for i in range(args.warmup):
+                step(i, transfer, first=(i == 0))
             cs.wait_stream(side)
             torch.cuda.synchronize()
-            fetched = float(nf_tot.item()) * page / K
-            # the gather alone, back to back on the side stream, over the last lists of every layer
-            eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            eb.record(side)
-            for _ in range(4):
-                for l in range(nl):
-                    st = rt.state[l][0]
-                    L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
-            ee.record(side)
+            t0 = time.perf_counter()
+            for i in range(K):
+                step(i, transfer)
+            cs.wait_stream(side)
             torch.cuda.synchronize()
-            g_us = eb.elapsed_time(ee) * 1e3 / 4
-            last = sum(int(rt.state[l][0].n_fetch.sum()) for l in range(nl)) * page
-            points.append({"eviction": policy, "cap": cap, "cap_frac_of_k": cap / kb,
-                           "h1_us_per_step": res[False], "h2_us_per_step": res[True],
-                           "exposed_transfer_us_per_step": res[True] - res[False],
-                           "fetched_MB_per_step": fetched / 1e6, "gather_us_per_step": g_us,
-                           "gather_GBs": last / (g_us * 1e-6) / 1e9 if g_us > 0 else None,
-                           "h2_steps_per_s": cfg.batch * nl * 1e6 / res[True]})
-            print(f"# {policy} cap {cap}: H1 {res[False]:.1f} us, H2 {res[True]:.1f} us, "
-                  f"{fetched / 1e6:.2f} MB/step", file=sys.stderr, flush=True)
-            L.oasis_destroy(h)
+            res[transfer] = (time.perf_counter() - t0) / K * 1e6
+        nf_tot.zero_()
+        for i in range(K):  # untimed: pages fetched per step
+            step(i, True, count=True)
+        cs.wait_stream(side)
+        torch.cuda.synchronize()
+        fetched = float(nf_tot.item()) * page / K
+        # the gather alone, back to back on the side stream, over the last lists of every layer
+        eb, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eb.record(side)
+        for _ in range(4):
+            for l in range(nl):
+                st = rt.state[l][0]
+                L.oasis_fetch_gather(h, st.host_tier, st.pool, st.fetch, st.n_fetch, side)
+        ee.record(side)
+        torch.cuda.synchronize()
+        g_us = eb.elapsed_time(ee) * 1e3 / 4
+        last = sum(int(rt.state[l][0].n_fetch.sum()) for l in range(nl)) * page
+        points.append({"eviction": policy, "cap": cap, "cap_frac_of_k": cap / kb, "layers_per_transfer": group,
+                       "h1_us_per_step": res[False], "h2_us_per_step": res[True],
+                       "exposed_transfer_us_per_step": res[True] - res[False],
+                       "fetched_MB_per_step": fetched / 1e6, "gather_us_per_step": g_us,
+                       "gather_GBs": last / (g_us * 1e-6) / 1e9 if g_us > 0 else None,
+                       "h2_steps_per_s": cfg.batch * nl * 1e6 / res[True]})
+        print(f"# {policy} cap {cap} group {group}: H1 {res[False]:.1f} us, H2 {res[True]:.1f} us, "
+              f"{fetched / 1e6:.2f} MB/step", file=sys.stderr, flush=True)
+        L.oasis_destroy(h)
     run.close()
     print(json.dumps({
         "metric": "cross-layer pipeline: exposed transfer per decode step vs fetch cap and eviction policy",
@@ -502,8 +508,9 @@ def pipeline_sweep(args):
                    "layers": nl, "steps": args.steps, "warmup": args.warmup},
         "data": "synthetic", "points": points,
         "note": "H1 = decode steps with inputs resident (no transfer); H2 = with every step's fetched pages "
-                "moved by the device-driven gather on a side stream, each layer's next attention waiting for "
-                "its own gather only; every (policy, cap) run starts from the same state"}))
+                "moved by the device-driven gather on a side stream, layers_per_transfer layers handing their "
+                "gathers over as one batch behind one event, and each batch's layers waiting at the next step "
+                "for that batch only; every (policy, cap, batch) run starts from the same state"}))
 
 
 def recall_measure(args):

@@ -100,6 +100,23 @@ def tile_meta(meta: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(t).reshape(-1)
 
 
+class PendingTransfer:
+    """One batch of page transfers on the side stream (the gathers or copies of
+    one or more layers): its completion event and the streams that have already
+    waited for it, so that each stream waits once per batch however many of the
+    batch's layers it then touches."""
+
+    def __init__(self, event):
+        self.event = event
+        self.waited = set()
+
+    def wait(self, stream):
+        key = stream.cuda_stream
+        if key not in self.waited:
+            stream.wait_event(self.event)
+            self.waited.add(key)
+
+
 class LayerState:
     """Device state of one layer (one replica) plus its pinned host tier."""
 
@@ -126,11 +143,10 @@ class LayerState:
         self.host_tier = host_tier
         self.fetch_host = torch.empty((u, max(cap, 1), 2), dtype=torch.int32, pin_memory=True)
         self.n_fetch_host = torch.empty(u, dtype=torch.int32, pin_memory=True)
-        # events: transfer landed (side stream), attention done reading the maps
-        # (compute stream), selection/diff done (predict stream)
-        self.fetch_done = torch.cuda.Event()
-        self.fetch_wait_compute = False  # attention must wait for the last transfer
-        self.fetch_wait_predict = False  # the token append (pool page rows) must too
+        # the last transfer into this layer's pool (a PendingTransfer): the next
+        # attention and the next token append wait for it; events: attention done
+        # reading the maps (compute stream), selection/diff done (predict stream)
+        self.pending = None
         self.attn_done = torch.cuda.Event()
         self.select_done = torch.cuda.Event()
         self.select_pending = False
@@ -318,9 +334,8 @@ class DecodeRuntime:
         and the last selection of this layer."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
-        if st.fetch_wait_compute:
-            cs.wait_event(st.fetch_done)
-            st.fetch_wait_compute = False
+        if st.pending is not None:
+            st.pending.wait(cs)
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
@@ -340,9 +355,8 @@ class DecodeRuntime:
         the index of the next attention (step t + 1), whose slots the diff stamps."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
-        if st.fetch_wait_compute or st.fetch_wait_predict:
-            cs.wait_event(st.fetch_done)
-            st.fetch_wait_compute = st.fetch_wait_predict = False
+        if st.pending is not None:
+            st.pending.wait(cs)
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
@@ -377,9 +391,8 @@ class DecodeRuntime:
         """
         st = self.state[layer][replica]
         ps = self._pred()
-        if st.fetch_wait_predict:
-            ps.wait_event(st.fetch_done)
-            st.fetch_wait_predict = False
+        if st.pending is not None:
+            st.pending.wait(ps)
         L.oasis_block_meta_update(self.h, k_new_dev, v_new_dev, self.ctx[self.ctx_cur],
                                   self.ctx[1 - self.ctx_cur], st.meta, st.pool, st.b2s, ps)
         if k_new_host is not None and replica == 0:
@@ -441,9 +454,8 @@ class DecodeRuntime:
         The next decode_step of the layer then attends over the exact set."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
-        if st.fetch_wait_compute or st.fetch_wait_predict:  # a pending prefetch may target the same slots
-            cs.wait_event(st.fetch_done)
-            st.fetch_wait_compute = st.fetch_wait_predict = False
+        if st.pending is not None:  # a pending prefetch may target the same slots
+            st.pending.wait(cs)
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
@@ -461,43 +473,51 @@ class DecodeRuntime:
         return self._h_full
 
     def transfer(self, layer: int, replica: int = 0, stream=None):
-        """Move this step's fetched pages into the pool on the side stream, after the
-        diff; later attention and appends of this layer wait for them.  Default: the
-        device-driven gather (reads the fetch list in HBM and the pages from the
-        pinned host tier, no host synchronisation); with gather=False: copy the
-        fetch list to the host, wait for it, and issue one copy per page."""
-        st = self.state[layer][replica]
+        """Move this step's fetched pages of one layer into its pool on the side
+        stream, after the diff (transfer_group of that layer alone)."""
+        self.transfer_group([layer], replica, stream)
+
+    def transfer_group(self, layers, replica: int = 0, stream=None):
+        """Move this step's fetched pages of several layers into their pools on the
+        side stream, after their diffs, as one batch: the side stream waits once
+        (for the work enqueued so far on the stream that ran the diffs), then
+        transfers every layer of the batch; later attention and appends of those
+        layers wait for the batch's one event.  Default: the device-driven gather
+        (reads the fetch list in HBM and the pages from the pinned host tier, no
+        host synchronisation); with gather=False: copy the fetch lists to the
+        host, wait for them once, and issue one copy per page."""
         ps = self._pred() if stream is None else stream
+        states = [self.state[l][replica] for l in layers]
         if self.gather:
             ready = torch.cuda.Event()
             ready.record(ps)
             self.side.wait_event(ready)
-            L.oasis_fetch_gather(self.h, st.host_tier, st.pool, st.fetch, st.n_fetch, self.side)
-            st.fetch_done.record(self.side)
-            st.fetch_wait_compute = True
-            st.fetch_wait_predict = True
-            return
-        with torch.cuda.stream(ps):
-            st.fetch_host.copy_(st.fetch, non_blocking=True)
-            st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)
-        ready = torch.cuda.Event()
-        ready.record(ps)
-        ready.synchronize()
-        self.side.wait_event(ready)
-        L.oasis_fetch_issue(self.h, st.host_tier, st.pool, st.fetch_host, st.n_fetch_host, self.side)
-        st.fetch_done.record(self.side)
-        st.fetch_wait_compute = True
-        st.fetch_wait_predict = True
+            for st in states:
+                L.oasis_fetch_gather(self.h, st.host_tier, st.pool, st.fetch, st.n_fetch, self.side)
+        else:
+            with torch.cuda.stream(ps):
+                for st in states:
+                    st.fetch_host.copy_(st.fetch, non_blocking=True)
+                    st.n_fetch_host.copy_(st.n_fetch, non_blocking=True)
+            ready = torch.cuda.Event()
+            ready.record(ps)
+            ready.synchronize()
+            self.side.wait_event(ready)
+            for st in states:
+                L.oasis_fetch_issue(self.h, st.host_tier, st.pool, st.fetch_host, st.n_fetch_host, self.side)
+        done = torch.cuda.Event()
+        done.record(self.side)
+        batch = PendingTransfer(done)
+        for st in states:
+            st.pending = batch
 
     def wait_transfers(self):
         """Make the current stream wait for every pending transfer and selection."""
         cs = torch.cuda.current_stream()
         for layer in self.state:
             for st in layer:
-                if st.fetch_wait_compute or st.fetch_wait_predict:
-                    cs.wait_event(st.fetch_done)
-                    st.fetch_wait_compute = False
-                    st.fetch_wait_predict = False
+                if st.pending is not None:
+                    st.pending.wait(cs)
                 if st.select_pending:
                     cs.wait_event(st.select_done)
                     st.select_pending = False

@@ -44,15 +44,18 @@ class SyntheticRun:
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
                  record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
                  gather: bool = True, two_calls: bool = False, options: dict | None = None,
-                 eviction: str = "score"):
+                 eviction: str = "score", transfer_group: int = 1):
         """fused_step: without overlap and drift, run each layer's step through the
         single decode-step call (attention, scoring, selection, diff), or through
         its two halves (two_calls).  gather: move the fetched pages with the
         device-driven gather (else host-issued copies).  options: the library's
-        launch options (None = defaults).  eviction: "score" or "lru"."""
+        launch options (None = defaults).  eviction: "score" or "lru".
+        transfer_group: layers whose transfers go to the side stream as one
+        batch (one cross-stream hand-off and one completion event per batch)."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
         self.two_calls = two_calls
+        self.group = max(1, int(transfer_group))
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
@@ -147,7 +150,7 @@ class SyntheticRun:
                 if self.record_units is not None:
                     self._record_out(l, t)
                 if transfer:
-                    rt.transfer(l)
+                    self._transfer_after(l)
             rt.end_step()
             if transfer:
                 rt.wait_transfers()
@@ -165,11 +168,17 @@ class SyntheticRun:
                 self._apply_drift(l, t)
             rt.predict_select(l, q, stamp=t + 1)
             if transfer:
-                rt.transfer(l)
+                self._transfer_after(l)
         rt.end_step()
         if transfer:
             rt.wait_transfers()
         self._record(t)
+
+    def _transfer_after(self, l: int):
+        """After layer l's diff: hand the batch that ends at layer l to the side stream."""
+        if (l + 1) % self.group == 0 or l == self.L - 1:
+            first = l - (l % self.group)
+            self.rt.transfer_group(range(first, l + 1))
 
     def run(self, steps: int | None = None, transfer: bool = True, log=None):
         """Prologue plus `steps` decode steps; `log(msg)` receives progress lines."""

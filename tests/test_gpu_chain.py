@@ -23,13 +23,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_and_compare(cfg, units, steps=None, layers=None, overlap=False, gather=True, options=None,
-                     eviction="score"):
+                     eviction="score", transfer_group=1):
     """Runs the chain on the GPU recording `units`, then compares every recorded
     unit with the oracle over every step (near ties adopted and counted)."""
     cfg = cfg if steps is None else cfg.with_(steps=steps)
     print(f"{cfg.name}: filling host tier and metadata ({len(units)} units recorded)", flush=True)
     run = SyntheticRun(cfg, layers=layers, record_units=units, overlap=overlap, gather=gather, options=options,
-                       eviction=eviction)
+                       eviction=eviction, transfer_group=transfer_group)
     try:
         run.run(log=lambda msg: print(msg, flush=True))
         records = run.records
@@ -91,6 +91,18 @@ def test_chain_small_drift():
     cfg = CONFIGS["qwen32b_32k"].with_(batch=1, layers=2, ctx=16 * 200, steps=5, planted=10,
                                        drift_blocks=4, budget_tokens=16 * 24, fetch_cap=4)
     _run_and_compare(cfg, [(l, u) for l in range(2) for u in range(cfg.kv_heads)])
+
+
+@pytest.mark.parametrize("overlap,gather,group", [(False, True, 2), (False, True, 3), (True, True, 4),
+                                                  (False, False, 4)])
+def test_chain_layer_batched_transfers(overlap, gather, group):
+    """Several layers' transfers handed to the side stream as one batch behind one
+    event (groups of 2, 3 and 4 over 5 layers, the last group short): every
+    layer's next attention still sees its fetched pages."""
+    cfg = CONFIGS["llama8b_32k"].with_(batch=1, layers=5, ctx=16 * 150 + 3, steps=5, planted=8,
+                                       budget_tokens=16 * 16, fetch_cap=4)
+    _run_and_compare(cfg, [(l, u) for l in range(5) for u in (0, 3, 6)], overlap=overlap, gather=gather,
+                     transfer_group=group)
 
 
 @pytest.mark.parametrize("overlap", [False, True])
