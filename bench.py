@@ -72,8 +72,9 @@ def parse():
                    help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
                         "(one JSON line per sweep instead of the headline)")
     p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
-    p.add_argument("--groups", default="1,2,4",
-                   help="--pipeline: layers per transfer batch (one side-stream hand-off and one event each)")
+    p.add_argument("--groups", default="inline,1,4",
+                   help="--pipeline: layers per side-stream transfer batch (one hand-off and one event each), "
+                        "or 'inline' (each layer's pages ride in the next decode step's first launch)")
     p.add_argument("--recall", action="store_true",
                    help="prediction recall of the drafts' selection against the verify query's own selection, "
                         "and the cost of a blocking corrective fetch (one JSON line)")
@@ -423,8 +424,11 @@ def pipeline_sweep(args):
     ev_fetch = [torch.cuda.Event() for _ in range(nl)]
     nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
     points = []
-    groups = [int(x) for x in args.groups.split(",")]
-    runs = [(p, c, g) for p in policies for c in caps for g in (groups if p == policies[0] else groups[-1:])]
+    # layers per side-stream batch; 0 ("inline"): each layer's pages ride in the next
+    # decode step's first launch on the compute stream (oasis_decode_step_gather)
+    groups = [0 if x.strip() == "inline" else int(x) for x in args.groups.split(",")]
+    runs = [(p, c, g) for p in policies for c in caps
+            for g in (groups if p == policies[0] else [x for x in groups if x > 0][-1:])]
     for policy, cap, group in runs:
         h = rt.shape.handle(fetch_cap=cap)
         for l in range(nl):
@@ -432,15 +436,33 @@ def pipeline_sweep(args):
             lus[l].fill_(-1)
         clock = [0]
 
+        pending = [None]  # inline: the layer whose fetched pages await the next launch
+
         def step(i, transfer, first=False, count=False):
             t = i % cfg.steps
             clock[0] += 1
             for l in range(nl):
                 st = rt.state[l][0]
+                q = run.q[l, t + 1]
+                if group == 0:
+                    pl = pending[0]
+                    carry = None
+                    if transfer and pl is not None:
+                        ps_ = rt.state[pl][0]
+                        if pl == l:
+                            L.oasis_fetch_gather(h, ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch, cs)
+                        else:
+                            carry = (ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch)
+                    L.oasis_decode_step_gather(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                               st.s2b, st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict,
+                                               st.attend, st.n_attend, transfer=carry, stream=cs)
+                    pending[0] = l if transfer else None
+                    if count:
+                        nf_tot.add_(st.n_fetch.sum())
+                    continue
                 gi = l // group  # layers [gi * group, ...) hand their transfers over as one batch
                 if transfer and not first and l % group == 0:
                     cs.wait_event(ev_fetch[gi])
-                q = run.q[l, t + 1]
                 if policy == "score":
                     L.oasis_decode_step(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
                                         st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
@@ -461,6 +483,12 @@ def pipeline_sweep(args):
                         L.oasis_fetch_gather(h, sl.host_tier, sl.pool, sl.fetch, sl.n_fetch, side)
                     ev_fetch[gi].record(side)
 
+        def flush():
+            if pending[0] is not None:
+                ps_ = rt.state[pending[0]][0]
+                L.oasis_fetch_gather(h, ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch, cs)
+                pending[0] = None
+
         K = args.steps
         res = {}
         for transfer in (False, True):
@@ -471,12 +499,14 @@ def pipeline_sweep(args):
             t0 = time.perf_counter()
             for i in range(K):
                 step(i, transfer)
+            flush()
             cs.wait_stream(side)
             torch.cuda.synchronize()
             res[transfer] = (time.perf_counter() - t0) / K * 1e6
         nf_tot.zero_()
         for i in range(K):  # untimed: pages fetched per step
             step(i, True, count=True)
+        flush()
         cs.wait_stream(side)
         torch.cuda.synchronize()
         fetched = float(nf_tot.item()) * page / K
@@ -508,9 +538,11 @@ def pipeline_sweep(args):
                    "layers": nl, "steps": args.steps, "warmup": args.warmup},
         "data": "synthetic", "points": points,
         "note": "H1 = decode steps with inputs resident (no transfer); H2 = with every step's fetched pages "
-                "moved by the device-driven gather on a side stream, layers_per_transfer layers handing their "
-                "gathers over as one batch behind one event, and each batch's layers waiting at the next step "
-                "for that batch only; every (policy, cap, batch) run starts from the same state"}))
+                "moved: layers_per_transfer > 0: by the device-driven gather on a side stream, that many layers "
+                "handing their gathers over as one batch behind one event, each batch's layers waiting at the "
+                "next step for that batch only; 0: inline, each layer's gather carried by the next decode "
+                "step's first launch on the compute stream (no second stream, no event); every (policy, cap, "
+                "batch) run starts from the same state"}))
 
 
 def recall_measure(args):

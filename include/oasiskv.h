@@ -411,6 +411,38 @@ int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const voi
                       int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
                       int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream);
 
+/* The pages a diff chose to fetch for one layer: that layer's pinned host tier
+ * (host memory mapped for the device, checked with hipPointerGetAttributes),
+ * its HBM pool, and its fetch list and counts (device, as the diff left them). */
+typedef struct oasis_transfer {
+  const void* host_tier;
+  void* pool;
+  const int32_t* fetch;    /* [B][H][fetch_cap][2] */
+  const int32_t* n_fetch;  /* [B][H] */
+} oasis_transfer;
+
+/*
+ * oasis_decode_step carrying another layer's transfer inside its first launch
+ * ([EXPL] Figure 8: each layer's selection and transfer overlap the compute of
+ * the layers after it, and land before that layer's next attention).
+ * `transfer` is a layer of the same shape whose diff already ran on this
+ * stream; its fetched pages move from its host tier into its pool in workgroups
+ * that lead this call's first launch, beside this layer's attention and
+ * scoring (the host-link reads overlap the HBM-bound work).  Stream order is
+ * the only synchronisation: the move needs no second stream and no event, and
+ * everything enqueued later on `stream` sees the pages.  The transfer's pool
+ * must not be this call's pool (EINVAL): the attention reads one while the move
+ * writes the other.  NULL transfer, or fetch_cap 0: oasis_decode_step.  Where
+ * the step's first launch cannot carry it (f32, the three-launch shape) the
+ * gather runs as its own launch first.  Results as oasis_decode_step followed by
+ * oasis_fetch_gather of the transfer.
+ */
+int oasis_decode_step_gather(oasis_handle h, const void* q, const void* pool, const void* meta,
+                             const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel,
+                             int32_t* block_to_slot, int32_t* slot_to_block, float* scores, float* out,
+                             void* workspace, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
+                             int32_t* n_attend, const oasis_transfer* transfer, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,11 @@ class oasis_launch_options(ctypes.Structure):
 
 LAUNCH_OPTION_FIELDS = tuple(f for f, _ in oasis_launch_options._fields_)
 
+
+class oasis_transfer(ctypes.Structure):
+    _fields_ = [("host_tier", ctypes.c_void_p), ("pool", ctypes.c_void_p), ("fetch", ctypes.c_void_p),
+                ("n_fetch", ctypes.c_void_p)]
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _int = ctypes.c_int
@@ -72,6 +77,7 @@ SIGNATURES = {
     "oasis_fetch_issue": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 18),
+    "oasis_decode_step_gather": (_int, [_vp] * 17 + [ctypes.POINTER(oasis_transfer), _vp]),
     "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
     "oasis_sparse_paged_decode_attn_noalloc": (_int, [_vp] * 8),
     "oasis_attend_and_score": (_int, [_vp] * 14),
@@ -270,6 +276,19 @@ def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot,
 def oasis_sparse_paged_decode_attn_noalloc(h, q, pool, sel, block_to_slot, ctx_len, out, stream=None):
     _call("oasis_sparse_paged_decode_attn_noalloc", h, _ptr(q), _ptr(pool), _ptr(sel), _ptr(block_to_slot),
           _ptr(ctx_len), _ptr(out), _stream(stream))
+
+
+def oasis_decode_step_gather(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block, scores, out,
+                             workspace, fetch, n_fetch, evict, attend=None, n_attend=None, transfer=None,
+                             stream=None):
+    """transfer: (host_tier, pool, fetch, n_fetch) of another layer, or None."""
+    tr = None
+    if transfer is not None:
+        tr = oasis_transfer(*(_ptr(x) for x in transfer))
+    _call("oasis_decode_step_gather", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score), _ptr(sel),
+          _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
+          _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), None if tr is None else ctypes.byref(tr),
+          _stream(stream))
 
 
 def oasis_sparse_paged_decode_attn_list(h, q, pool, attend, n_attend, ctx_len, out, workspace, stream=None):

@@ -709,45 +709,32 @@ int oasis_select_diff_combine(oasis_handle h, const float* scores, const int32_t
   return hip_status(e, "oasis_select_diff_combine");
 }
 
-int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
-                      const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
-                      int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
-                      int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream) {
-  CHECK_HANDLE(h);
-  CHECK_ATTEND_PAIR("oasis_decode_step", attend, n_attend);
-  CHECK_PTR(q);
-  CHECK_PTR(pool);
-  CHECK_PTR(meta);
-  CHECK_PTR(ctx_attn);
-  CHECK_PTR(ctx_score);
-  CHECK_PTR(sel);
-  CHECK_PTR(block_to_slot);
-  CHECK_PTR(slot_to_block);
-  CHECK_PTR(scores);
-  CHECK_PTR(out);
-  CHECK_PTR(workspace);
-  CHECK_PTR(n_fetch);
-  CHECK_ALIGN16(q);
-  CHECK_ALIGN16(pool);
-  CHECK_ALIGN16(meta);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(OASIS_EINVAL, "oasis_decode_step: workspace not 256-byte aligned");
-  const oasis::Ctx& c = h->c;
-  if (c.s.fetch_cap > 0) {
-    CHECK_PTR(fetch);
-    CHECK_PTR(evict);
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The decode step of one layer, optionally carrying another layer's transfer
+// (g.host != nullptr) in its first launch; arguments already validated.
+hipError_t decode_step_impl(const oasis::Ctx& c, const void* q, const void* pool, const void* meta,
+                            const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
+                            int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
+                            int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                            const oasis::StepGather& g, hipStream_t st) {
   hipError_t e;
   if (oasis::attn_needs_combine(c) && oasis::attn_and_score_fused_available(c) &&
       oasis::select_diff_fused_available(c) && c.step_launches == 2) {
-    // two launches: attention + scoring, then selection + diff + split combine
+    // two launches: (the carried transfer,) attention + scoring, then selection + diff + split combine
     e = oasis::launch_attn_and_score(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace,
-                                     meta, ctx_score, scores, st);
+                                     meta, ctx_score, scores, st, g);
     if (e == hipSuccess)
       e = oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
                                             evict, attend, n_attend, workspace, out, st);
-    return hip_status(e, "oasis_decode_step");
+    return e;
+  }
+  // other shapes: the carried transfer as its own launch first
+  if (g.host != nullptr) {
+    e = oasis::launch_fetch_gather(c, g.host, g.pool, g.fetch, g.n_fetch, st);
+    if (e != hipSuccess) return e;
   }
   if (c.s.dtype == OASIS_BF16 && oasis::attn_needs_combine(c)) {
     e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace, st);
@@ -769,7 +756,82 @@ int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const voi
                                st);
     }
   }
-  return hip_status(e, "oasis_decode_step");
+  return e;
+}
+
+#define CHECK_DECODE_STEP_ARGS(fn)                                                              \
+  CHECK_HANDLE(h);                                                                              \
+  CHECK_ATTEND_PAIR(fn, attend, n_attend);                                                      \
+  CHECK_PTR(q);                                                                                 \
+  CHECK_PTR(pool);                                                                              \
+  CHECK_PTR(meta);                                                                              \
+  CHECK_PTR(ctx_attn);                                                                          \
+  CHECK_PTR(ctx_score);                                                                         \
+  CHECK_PTR(sel);                                                                               \
+  CHECK_PTR(block_to_slot);                                                                     \
+  CHECK_PTR(slot_to_block);                                                                     \
+  CHECK_PTR(scores);                                                                            \
+  CHECK_PTR(out);                                                                               \
+  CHECK_PTR(workspace);                                                                         \
+  CHECK_PTR(n_fetch);                                                                           \
+  CHECK_ALIGN16(q);                                                                             \
+  CHECK_ALIGN16(pool);                                                                          \
+  CHECK_ALIGN16(meta);                                                                          \
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)                                        \
+    return fail(OASIS_EINVAL, fn ": workspace not 256-byte aligned");                           \
+  if (h->c.s.fetch_cap > 0) {                                                                   \
+    CHECK_PTR(fetch);                                                                           \
+    CHECK_PTR(evict);                                                                           \
+  }
+
+}  // namespace
+
+extern "C" {
+
+int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
+                      const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
+                      int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
+                      int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend, void* stream) {
+  CHECK_DECODE_STEP_ARGS("oasis_decode_step");
+  return hip_status(decode_step_impl(h->c, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block,
+                                     scores, out, workspace, fetch, n_fetch, evict, attend, n_attend,
+                                     oasis::StepGather(), static_cast<hipStream_t>(stream)),
+                    "oasis_decode_step");
+}
+
+int oasis_decode_step_gather(oasis_handle h, const void* q, const void* pool, const void* meta,
+                             const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
+                             int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
+                             int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                             const oasis_transfer* transfer, void* stream) {
+  CHECK_DECODE_STEP_ARGS("oasis_decode_step_gather");
+  oasis::StepGather g;
+  if (transfer != nullptr && h->c.s.fetch_cap > 0) {
+    CHECK_PTR(transfer->host_tier);
+    CHECK_PTR(transfer->pool);
+    CHECK_PTR(transfer->fetch);
+    CHECK_PTR(transfer->n_fetch);
+    CHECK_ALIGN16(transfer->host_tier);
+    CHECK_ALIGN16(transfer->pool);
+    if (transfer->pool == pool)
+      return fail(OASIS_EINVAL, "oasis_decode_step_gather: the transfer's pool is this step's pool");
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, transfer->host_tier) != hipSuccess || attr.type != hipMemoryTypeHost ||
+        attr.devicePointer == nullptr) {
+      (void)hipGetLastError();  // clear the lookup's error state
+      return fail(OASIS_EINVAL,
+                  "oasis_decode_step_gather: host_tier is not pinned host memory mapped for the device");
+    }
+    g.host = static_cast<const uint4*>(attr.devicePointer);
+    g.pool = static_cast<uint4*>(transfer->pool);
+    g.fetch = transfer->fetch;
+    g.n_fetch = transfer->n_fetch;
+    g.cap = h->c.s.fetch_cap;
+  }
+  return hip_status(decode_step_impl(h->c, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block,
+                                     scores, out, workspace, fetch, n_fetch, evict, attend, n_attend, g,
+                                     static_cast<hipStream_t>(stream)),
+                    "oasis_decode_step_gather");
 }
 
 }  // extern "C"

@@ -100,13 +100,25 @@ hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const
 bool attn_needs_combine(const Ctx& c);
 // The split combine alone (nothing to do when the attention wrote the output).
 hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t st);
+// Another layer's page transfer carried by the step's first launch: its host
+// tier (device address of the pinned mapping), pool, fetch list and counts
+// (host == nullptr: none).
+struct StepGather {
+  const uint4* host = nullptr;
+  uint4* pool = nullptr;
+  const int32_t* fetch = nullptr;
+  const int32_t* n_fetch = nullptr;
+  int cap = 0;
+};
 // The attention (split partials) and the lookahead score in one launch (bf16,
-// 2-wavefront 2-page attention, up to three attention row tiles).
+// 2-wavefront 2-page attention, up to three attention row tiles), optionally
+// led by workgroups that carry another layer's transfer.
 bool attn_and_score_fused_available(const Ctx& c);
 hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                                  const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
                                  const int32_t* ctx_attn, float* out, void* ws, const void* meta,
-                                 const int32_t* ctx_score, float* scores, hipStream_t st);
+                                 const int32_t* ctx_score, float* scores, hipStream_t st,
+                                 const StepGather& g = StepGather());
 // The fused selection + diff and the attention's split combine in one launch
 // (where select_diff_fused_available holds).
 hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,

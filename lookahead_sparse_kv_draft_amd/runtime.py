@@ -177,15 +177,26 @@ class DecodeRuntime:
 
     def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
                  host_tier: bool = True, fused_select: bool = True, overlap: bool = False,
-                 gather: bool = True, options: dict | None = None, eviction: str = "score"):
+                 gather: bool = True, options: dict | None = None, eviction: str = "score",
+                 transfer_mode: str = "side"):
         """overlap: run scoring / selection on a second stream so that they overlap
         the attention of the same step (and of other layers); the selection waits
         only for the attention that reads the maps it rewrites.  options: launch
         options of the library handle (None = defaults).  eviction: "score"
         (lowest-score victims) or "lru" (least recently read slot first; the diff
-        that prepares attention t stamps that attention's slots with t)."""
+        that prepares attention t stamps that attention's slots with t).
+        transfer_mode: "side" (each layer's transfer on the side stream,
+        transfer_group) or "inline" (a layer's fetched pages ride in the first
+        launch of the next decode step enqueued on the compute stream,
+        oasis_decode_step_gather: no second stream, no event; defer_transfer)."""
         if eviction not in ("score", "lru"):
             raise ValueError(eviction)
+        if transfer_mode not in ("side", "inline"):
+            raise ValueError(transfer_mode)
+        if transfer_mode == "inline" and (overlap or not gather):
+            raise ValueError("inline transfers run on the compute stream with the device gather")
+        self.transfer_mode = transfer_mode
+        self.inline_pending = None  # (layer, replica) whose fetched pages await their transfer
         self.shape = shape
         self.options = options
         self.eviction = eviction
@@ -336,6 +347,8 @@ class DecodeRuntime:
         cs = torch.cuda.current_stream()
         if st.pending is not None:
             st.pending.wait(cs)
+        if self.inline_pending == (layer, replica):
+            self.flush_inline(cs)
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
@@ -361,6 +374,19 @@ class DecodeRuntime:
             cs.wait_event(st.select_done)
             st.select_pending = False
         o = self.out if out is None else out
+        carry = None
+        if self.inline_pending is not None:
+            if self.inline_pending != (layer, replica) and self.eviction == "score" and not two_calls:
+                pst = self.state[self.inline_pending[0]][self.inline_pending[1]]
+                carry = (pst.host_tier, pst.pool, pst.fetch, pst.n_fetch)
+                self.inline_pending = None
+            else:
+                self.flush_inline(cs)
+        if carry is not None:
+            L.oasis_decode_step_gather(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
+                                       st.s2b, st.scores, o, self.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
+                                       st.n_attend, transfer=carry, stream=cs)
+            return
         if self.eviction == "lru":
             L.oasis_attend_and_score(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
                                      st.attend, st.n_attend, st.scores, o, self.ws_ptr, cs)
@@ -393,6 +419,8 @@ class DecodeRuntime:
         ps = self._pred()
         if st.pending is not None:
             st.pending.wait(ps)
+        if self.inline_pending == (layer, replica):
+            self.flush_inline(ps)
         L.oasis_block_meta_update(self.h, k_new_dev, v_new_dev, self.ctx[self.ctx_cur],
                                   self.ctx[1 - self.ctx_cur], st.meta, st.pool, st.b2s, ps)
         if k_new_host is not None and replica == 0:
@@ -419,6 +447,8 @@ class DecodeRuntime:
         st = self.state[layer][replica]
         ctx = self.ctx_scoring
         ps = self._pred()
+        if self.inline_pending == (layer, replica):  # its fetch list is about to be rewritten
+            self.flush_inline(ps)
         L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores, ps)
         if self.overlap:
             ps.wait_event(st.attn_done)
@@ -456,6 +486,8 @@ class DecodeRuntime:
         cs = torch.cuda.current_stream()
         if st.pending is not None:  # a pending prefetch may target the same slots
             st.pending.wait(cs)
+        if self.inline_pending == (layer, replica):
+            self.flush_inline(cs)
         if st.select_pending:
             cs.wait_event(st.select_done)
             st.select_pending = False
@@ -511,9 +543,25 @@ class DecodeRuntime:
         for st in states:
             st.pending = batch
 
+    def defer_transfer(self, layer: int, replica: int = 0):
+        """Inline mode: the layer's fetched pages move in the first launch of the
+        next decode step enqueued on the compute stream (or in flush_inline)."""
+        if self.inline_pending is not None:
+            self.flush_inline(torch.cuda.current_stream())
+        self.inline_pending = (layer, replica)
+
+    def flush_inline(self, stream):
+        """The pending inline transfer as a gather launch of its own on `stream`."""
+        if self.inline_pending is None:
+            return
+        st = self.state[self.inline_pending[0]][self.inline_pending[1]]
+        L.oasis_fetch_gather(self.h, st.host_tier, st.pool, st.fetch, st.n_fetch, stream)
+        self.inline_pending = None
+
     def wait_transfers(self):
         """Make the current stream wait for every pending transfer and selection."""
         cs = torch.cuda.current_stream()
+        self.flush_inline(cs)
         for layer in self.state:
             for st in layer:
                 if st.pending is not None:

@@ -44,14 +44,16 @@ class SyntheticRun:
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
                  record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
                  gather: bool = True, two_calls: bool = False, options: dict | None = None,
-                 eviction: str = "score", transfer_group: int = 1):
+                 eviction: str = "score", transfer_group: int = 1, transfer_mode: str = "side"):
         """fused_step: without overlap and drift, run each layer's step through the
         single decode-step call (attention, scoring, selection, diff), or through
         its two halves (two_calls).  gather: move the fetched pages with the
         device-driven gather (else host-issued copies).  options: the library's
         launch options (None = defaults).  eviction: "score" or "lru".
         transfer_group: layers whose transfers go to the side stream as one
-        batch (one cross-stream hand-off and one completion event per batch)."""
+        batch (one cross-stream hand-off and one completion event per batch).
+        transfer_mode: "side" or "inline" (each layer's pages ride in the next
+        decode step's first launch on the compute stream)."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
         self.two_calls = two_calls
@@ -59,7 +61,9 @@ class SyntheticRun:
         self.L = cfg.layers if layers is None else layers
         self.shape = shape_of(cfg)
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
-                                gather=gather, options=options, eviction=eviction)
+                                gather=gather, options=options, eviction=eviction,
+                                transfer_mode=(transfer_mode if self.fused_step and not cfg.drift_blocks
+                                               else "side"))
         self.record_units = record_units  # list of (layer, unit) to record, or None
         self.records = {}
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
@@ -175,7 +179,11 @@ class SyntheticRun:
         self._record(t)
 
     def _transfer_after(self, l: int):
-        """After layer l's diff: hand the batch that ends at layer l to the side stream."""
+        """After layer l's diff: hand the batch that ends at layer l to the side
+        stream (or, inline, leave the pages to the next decode step's launch)."""
+        if self.rt.transfer_mode == "inline":
+            self.rt.defer_transfer(l)
+            return
         if (l + 1) % self.group == 0 or l == self.L - 1:
             first = l - (l % self.group)
             self.rt.transfer_group(range(first, l + 1))

@@ -193,3 +193,17 @@ def test_noalloc_attention_rejects_a_workspace_beyond_its_scratch():
         assert lib.oasis_sparse_paged_decode_attn_noalloc(h, None, 16, 16, 16, 16, 16, None) == L.OASIS_EINVAL
     finally:
         L.oasis_destroy(h)
+
+
+def test_decode_step_gather_rejects_its_own_pool():
+    # the transfer's pool is the step's pool: the attention would read what the
+    # move writes; rejected before anything is enqueued
+    h = L.oasis_create(**_shape())
+    try:
+        lib = L.load()
+        tr = L.oasis_transfer(host_tier=256, pool=512, fetch=768, n_fetch=1024)
+        args = [h, 256, 512, 256] + [256] * 13
+        assert lib.oasis_decode_step_gather(*args, ctypes.byref(tr), None) == L.OASIS_EINVAL
+        assert "pool" in L.oasis_last_error()
+    finally:
+        L.oasis_destroy(h)

@@ -23,13 +23,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_and_compare(cfg, units, steps=None, layers=None, overlap=False, gather=True, options=None,
-                     eviction="score", transfer_group=1):
+                     eviction="score", transfer_group=1, transfer_mode="side"):
     """Runs the chain on the GPU recording `units`, then compares every recorded
     unit with the oracle over every step (near ties adopted and counted)."""
     cfg = cfg if steps is None else cfg.with_(steps=steps)
     print(f"{cfg.name}: filling host tier and metadata ({len(units)} units recorded)", flush=True)
     run = SyntheticRun(cfg, layers=layers, record_units=units, overlap=overlap, gather=gather, options=options,
-                       eviction=eviction, transfer_group=transfer_group)
+                       eviction=eviction, transfer_group=transfer_group, transfer_mode=transfer_mode)
     try:
         run.run(log=lambda msg: print(msg, flush=True))
         records = run.records
@@ -103,6 +103,26 @@ def test_chain_layer_batched_transfers(overlap, gather, group):
                                        budget_tokens=16 * 16, fetch_cap=4)
     _run_and_compare(cfg, [(l, u) for l in range(5) for u in (0, 3, 6)], overlap=overlap, gather=gather,
                      transfer_group=group)
+
+
+@pytest.mark.parametrize("layers", [1, 2, 5])
+def test_chain_inline_transfers(layers):
+    """Each layer's fetched pages carried in the first launch of the next decode
+    step on the compute stream (no second stream): over five layers, two, and one
+    (where a layer's own pending transfer moves as a gather before its step)."""
+    cfg = CONFIGS["llama8b_32k"].with_(batch=1, layers=layers, ctx=16 * 150 + 3, steps=5, planted=8,
+                                       budget_tokens=16 * 16, fetch_cap=4)
+    _run_and_compare(cfg, [(l, u) for l in range(layers) for u in (0, 3, 6)], transfer_mode="inline")
+
+
+@pytest.mark.parametrize("layers", [1, 3])
+def test_chain_inline_transfers_append(layers):
+    """Inline transfers with a token appended per step (a new newest block is
+    fetched first and then written by the next append)."""
+    cfg = CONFIGS["qwen8b_reason"].with_(batch=2, ctx=16 * 40 + 13, steps=24, recency_blocks=8, planted=4,
+                                         budget_tokens=16 * 16, fetch_cap=3)
+    _run_and_compare(cfg, [(l, u) for l in range(layers) for u in range(cfg.batch * cfg.kv_heads)],
+                     layers=layers, transfer_mode="inline")
 
 
 @pytest.mark.parametrize("overlap", [False, True])
