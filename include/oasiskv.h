@@ -27,7 +27,8 @@
  *    KV head) in ceil(max_blocks/16) tiles of 16 blocks; inside a tile the rows
  *    are cut into 16-byte chunks stored chunk-major (chunk c of block 16t + j at
  *    chunk position 16c + j), so that each MFMA k-step of the scoring reads one
- *    contiguous KiB.  The buffer is opaque to callers apart from its size.
+ *    contiguous KiB.  oasis_block_meta_export / _import convert it to and from
+ *    the logical layout [B][H][max_blocks][2][d].
  *  - Page = one block of one unit: K rows [16][d] (token-major) followed by V
  *    transposed [d][16] (channel-major), 2*16*d elements.  The host tier is
  *    [B][H][max_blocks][page] (pinned host memory); the HBM pool is
@@ -160,6 +161,17 @@ int oasis_host_tier_append(oasis_handle h, const void* k_new, const void* v_new,
 int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* page_ids,
                            int32_t count, const int32_t* ctx_len, void* meta, void* pool,
                            const int32_t* block_to_slot, void* stream);
+
+/*
+ * The block metadata in its logical layout ([EXPL] Figure 7 left: per-block,
+ * per-channel key min and max): meta_logical is [B][H][max_blocks][2][d]
+ * elements (device, 16-byte aligned, oasis_meta_bytes() covers it), block b's
+ * key min row then its key max row.  export copies the library's tiles into
+ * it; import writes such rows (computed elsewhere) into the tiles.  Blocks at
+ * or past a request's context are copied as they are.  Not in place.
+ */
+int oasis_block_meta_export(oasis_handle h, const void* meta, void* meta_logical, void* stream);
+int oasis_block_meta_import(oasis_handle h, const void* meta_logical, void* meta, void* stream);
 
 /*
  * Admission of a prefill computed on the device ([EXPL] Figure 7 left: after the

@@ -68,6 +68,8 @@ SIGNATURES = {
     "oasis_host_tier_append": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "oasis_block_meta_build": (_int, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "oasis_block_meta_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_block_meta_export": (_int, [_vp, _vp, _vp, _vp]),
+    "oasis_block_meta_import": (_int, [_vp, _vp, _vp, _vp]),
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_topk_select": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "oasis_verify_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
@@ -231,6 +233,14 @@ def oasis_block_meta_build(h, pages, page_ids, count, ctx_len, meta, pool=None, 
                            stream=None):
     _call("oasis_block_meta_build", h, _ptr(pages), _ptr(page_ids), count, _ptr(ctx_len), _ptr(meta),
           _ptr(pool), _ptr(block_to_slot), _stream(stream))
+
+
+def oasis_block_meta_export(h, meta, meta_logical, stream=None):
+    _call("oasis_block_meta_export", h, _ptr(meta), _ptr(meta_logical), _stream(stream))
+
+
+def oasis_block_meta_import(h, meta_logical, meta, stream=None):
+    _call("oasis_block_meta_import", h, _ptr(meta_logical), _ptr(meta), _stream(stream))
 
 
 def oasis_block_meta_update(h, k_new, v_new, ctx_len_in, ctx_len_out, meta, pool, block_to_slot,

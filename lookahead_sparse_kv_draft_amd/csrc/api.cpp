@@ -303,6 +303,28 @@ int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* pag
                     "oasis_block_meta_build");
 }
 
+int oasis_block_meta_export(oasis_handle h, const void* meta, void* meta_logical, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(meta);
+  CHECK_PTR(meta_logical);
+  CHECK_ALIGN16(meta);
+  CHECK_ALIGN16(meta_logical);
+  if (meta == meta_logical) return fail(OASIS_EINVAL, "oasis_block_meta_export: in place is not supported");
+  return hip_status(oasis::launch_meta_relayout(h->c, meta, meta_logical, true, static_cast<hipStream_t>(stream)),
+                    "oasis_block_meta_export");
+}
+
+int oasis_block_meta_import(oasis_handle h, const void* meta_logical, void* meta, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(meta_logical);
+  CHECK_PTR(meta);
+  CHECK_ALIGN16(meta);
+  CHECK_ALIGN16(meta_logical);
+  if (meta == meta_logical) return fail(OASIS_EINVAL, "oasis_block_meta_import: in place is not supported");
+  return hip_status(oasis::launch_meta_relayout(h->c, meta_logical, meta, false, static_cast<hipStream_t>(stream)),
+                    "oasis_block_meta_import");
+}
+
 int oasis_block_meta_update(oasis_handle h, const void* k_new, const void* v_new, const int32_t* ctx_len_in,
                             int32_t* ctx_len_out, void* meta, void* pool, const int32_t* block_to_slot,
                             void* stream) {

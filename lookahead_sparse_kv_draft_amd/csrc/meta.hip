@@ -65,6 +65,25 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
   }
 }
 
+// The metadata between the library's chunk-major tiles and the logical layout
+// [units][Nmax][2][d] (the key min row, then the key max row, per block): one
+// thread per 16-byte chunk of a block row; tile padding is neither read nor written.
+template <int NC>
+__global__ __launch_bounds__(256) void meta_relayout_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                            long long total, int Nmax, int to_logical) {
+  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long per_unit = static_cast<long long>(Nmax) * NC;
+  const long long unit = i / per_unit;
+  const int rem = static_cast<int>(i - unit * per_unit);
+  const int b = rem / NC, c = rem - (rem / NC) * NC;
+  const long long tiled = ((unit * meta_tiles(Nmax) + b / kMetaTile) * NC + c) * kMetaTile + (b % kMetaTile);
+  if (to_logical)
+    dst[i] = src[tiled];
+  else
+    dst[tiled] = src[i];
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(64) void meta_update_kernel(
     const E* __restrict__ k_new, const E* __restrict__ v_new, const int32_t* __restrict__ ctx_in,
@@ -230,6 +249,22 @@ hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new
               : update_t<float, 128>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st);
   return bf ? update_t<uint16_t, 64>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st)
             : update_t<float, 64>(c, k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, st);
+}
+
+hipError_t launch_meta_relayout(const Ctx& c, const void* src, void* dst, bool to_logical, hipStream_t st) {
+  const int nc = 2 * c.s.head_dim * c.elem_bytes / 16;  // 16-byte chunks per block row
+  const long long total = static_cast<long long>(c.units) * c.s.max_blocks * nc;
+  if (total == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256)), block(256);
+  const uint4* s4 = static_cast<const uint4*>(src);
+  uint4* d4 = static_cast<uint4*>(dst);
+  switch (nc) {
+    case 16: hipLaunchKernelGGL((meta_relayout_kernel<16>), grid, block, 0, st, s4, d4, total, c.s.max_blocks, to_logical); break;
+    case 32: hipLaunchKernelGGL((meta_relayout_kernel<32>), grid, block, 0, st, s4, d4, total, c.s.max_blocks, to_logical); break;
+    case 64: hipLaunchKernelGGL((meta_relayout_kernel<64>), grid, block, 0, st, s4, d4, total, c.s.max_blocks, to_logical); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace oasis

@@ -577,9 +577,21 @@ class DecodeRuntime:
         return st.pool.view(s.units, s.budget_blocks, -1)
 
     def meta_view(self, layer: int, replica: int = 0) -> torch.Tensor:
-        """The layer's block metadata as [units][max_blocks][2][d] (a copy): the
-        library stores it in chunk-major tiles of 16 blocks (16-byte chunks of
-        each block's row, chunk c of block 16t + j at position 16c + j)."""
+        """The layer's block metadata as [units][max_blocks][2][d] (a copy on the
+        device, int16 bit patterns for bf16): the library's export of its
+        chunk-major tiles into the logical layout."""
         s = self.shape
         st = self.state[layer][replica]
-        return untile_meta(st.meta, s.units, s.max_blocks, s.head_dim, s.dtype)
+        out = torch.empty((s.units, s.max_blocks, 2, s.head_dim),
+                          dtype=torch.int16 if s.dtype == "bf16" else torch.float32, device=self.device)
+        L.oasis_block_meta_export(self.h, st.meta, out)
+        return out
+
+    def load_meta(self, layer: int, meta: torch.Tensor, replica: int = 0):
+        """Write logical metadata [units][max_blocks][2][d] (device, element
+        type or its bit patterns) into the layer's tiles."""
+        s = self.shape
+        assert meta.is_cuda and meta.is_contiguous()
+        assert tuple(meta.shape) == (s.units, s.max_blocks, 2, s.head_dim)
+        assert meta.element_size() == s.elem_bytes
+        L.oasis_block_meta_import(self.h, meta, self.state[layer][replica].meta)

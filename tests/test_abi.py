@@ -77,6 +77,10 @@ def test_sizes_and_null_checks():
         assert lib.oasis_sparse_paged_decode_attn(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_update(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_build(h, None, None, 0, None, None, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_block_meta_export(h, None, 256, None) == L.OASIS_EINVAL
+        assert lib.oasis_block_meta_import(h, 256, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_block_meta_export(h, 256, 256, None) == L.OASIS_EINVAL  # not in place
+        assert lib.oasis_block_meta_import(h, 256, 264, None) == L.OASIS_EINVAL  # misaligned
         assert lib.oasis_lookahead_score(None, 16, 16, 16, 16, None) == L.OASIS_EINVAL
         assert lib.oasis_select_and_diff(h, *([None] * 11)) == L.OASIS_EINVAL
         assert lib.oasis_decode_step(h, *([None] * 17)) == L.OASIS_EINVAL

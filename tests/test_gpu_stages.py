@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from lookahead_sparse_kv_draft_amd import _lib as L
-from lookahead_sparse_kv_draft_amd.runtime import DecodeRuntime
+from lookahead_sparse_kv_draft_amd.runtime import DecodeRuntime, tile_meta
 from oracle import oasis_oracle as O
 from tests import gpu_util as U
 from workload.synth import random_scores
@@ -494,6 +494,47 @@ def test_meta_build_and_append(dtype, d):
         hp = ht[u, b]
         for j in range(first - b * BLK, last - b * BLK):
             assert np.array_equal(hp[: BLK * d].reshape(BLK, d)[j], U.to_elem_np(dtype, K[u, b * BLK + j]))
+    rt.close()
+
+
+@pytest.mark.parametrize("dtype,d,nmax", [("bf16", 128, 37), ("f32", 64, 16), ("bf16", 64, 5)])
+def test_meta_export_and_import(dtype, d, nmax):
+    """The tiles built from pages, read back through the export, equal the
+    oracle's per-block min/max; the import of those logical rows rebuilds the
+    very same tile bytes, and the host packing agrees with both."""
+    B, H = 2, 3
+    ctxs = [nmax * BLK, nmax * BLK - 7]
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=nmax, budget_blocks=4, fetch_cap=4,
+                      dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(11)
+    units = B * H
+    K = U.elem_round(dtype, rng.standard_normal((units, nmax * BLK, d)).astype(np.float32))
+    for u in range(units):
+        rt.pack_unit(0, u, U.to_elem_np(dtype, K[u]), U.to_elem_np(dtype, K[u]))
+    rt.set_ctx(ctxs)
+    rt.build_meta(0)
+    torch.cuda.synchronize()
+    exported = rt.meta_view(0)
+    torch.cuda.synchronize()
+    ev = exported.view(torch.bfloat16).float() if dtype == "bf16" else exported
+    ev = ev.cpu().numpy().astype(np.float64)
+    for u in range(units):
+        kmin, kmax = O.block_meta(K[u].astype(np.float64), ctxs[u // H])
+        N = kmin.shape[0]
+        assert np.array_equal(ev[u, :N, 0], kmin) and np.array_equal(ev[u, :N, 1], kmax), u
+    built = rt.state[0][0].meta.clone()
+    fresh = torch.zeros_like(built)
+    L.oasis_block_meta_import(rt.h, exported, fresh)
+    torch.cuda.synchronize()
+    n_valid = units * ((nmax + 15) // 16) * 16 * 2 * d * sh.elem_bytes
+    assert torch.equal(fresh[:n_valid], built[:n_valid])
+    host = tile_meta(exported.cpu().numpy())
+    assert np.array_equal(fresh[:n_valid].cpu().numpy(), host.view(np.uint8))
+    rt.state[0][0].meta.zero_()
+    rt.load_meta(0, exported)
+    torch.cuda.synchronize()
+    assert torch.equal(rt.state[0][0].meta[:n_valid], built[:n_valid])
     rt.close()
 
 
