@@ -455,6 +455,50 @@ int oasis_decode_step_gather(oasis_handle h, const void* q, const void* pool, co
                              void* workspace, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
                              int32_t* n_attend, const oasis_transfer* transfer, void* stream);
 
+/* One state's top-k selection and resident-set diff, as oasis_select_and_diff
+ * takes it: the state's scores (complete: written by an earlier launch), the
+ * context length its scoring saw, and the selection, maps, fetch / evict lists
+ * and attended list the diff updates (layouts as there; all device). */
+typedef struct oasis_select_job {
+  const float* scores;
+  const int32_t* ctx_len;
+  int32_t* sel;
+  int32_t* block_to_slot;
+  int32_t* slot_to_block;
+  int32_t* fetch;
+  int32_t* n_fetch;
+  int32_t* evict;
+  int32_t* attend;
+  int32_t* n_attend;
+} oasis_select_job;
+
+/*
+ * A layer's decode step whose first launch carries another state's selection
+ * ([EXPL] Figure 8: a layer's prediction, selection and transfer proceed while
+ * later layers compute; only that layer's next attention needs them).  Two
+ * launches:
+ *   1. `job`'s selection and diff (one workgroup per (request, KV head), ahead
+ *      of the rest; none when job is NULL), then this layer's attention over
+ *      attend / n_attend and the lookahead score of its drafts into `scores`,
+ *      led by `transfer`'s page gather when given (as oasis_decode_step_gather);
+ *   2. the attention's split combine into `out`.
+ * This layer's own selection is not run: the caller carries it, as a job, in
+ * a later call (typically the next layer's, the last layer's in the next
+ * step's first layer's) or runs it with oasis_select_and_diff; that layer's
+ * next attention must follow.  The job's results are identical, bit for bit,
+ * to oasis_select_and_diff on the same state.  The job must be another state
+ * than this step's: its scores, attended list and fetch list must not be
+ * `scores`, `attend` or the transfer's fetch list (EINVAL).  The block map is
+ * read only as the inverse of the slot map, as every diff leaves them.
+ * EUNSUPPORTED unless bf16, head_dim 128, 2 attention wavefronts per
+ * workgroup, budget_blocks <= 128, fetch_cap <= budget_blocks and
+ * max_blocks <= 8192 (score eviction).
+ */
+int oasis_decode_step_carry(oasis_handle h, const void* q, const void* pool, const void* meta,
+                            const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* attend,
+                            const int32_t* n_attend, float* scores, float* out, void* workspace,
+                            const oasis_select_job* job, const oasis_transfer* transfer, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,12 @@ class oasis_transfer(ctypes.Structure):
     _fields_ = [("host_tier", ctypes.c_void_p), ("pool", ctypes.c_void_p), ("fetch", ctypes.c_void_p),
                 ("n_fetch", ctypes.c_void_p)]
 
+
+class oasis_select_job(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("scores", "ctx_len", "sel", "block_to_slot", "slot_to_block", "fetch",
+                                               "n_fetch", "evict", "attend", "n_attend")]
+
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _int = ctypes.c_int
@@ -80,6 +86,8 @@ SIGNATURES = {
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 18),
     "oasis_decode_step_gather": (_int, [_vp] * 17 + [ctypes.POINTER(oasis_transfer), _vp]),
+    "oasis_decode_step_carry": (_int, [_vp] * 11 + [ctypes.POINTER(oasis_select_job),
+                                                     ctypes.POINTER(oasis_transfer), _vp]),
     "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
     "oasis_sparse_paged_decode_attn_noalloc": (_int, [_vp] * 8),
     "oasis_attend_and_score": (_int, [_vp] * 14),
@@ -299,6 +307,17 @@ def oasis_decode_step_gather(h, q, pool, meta, ctx_attn, ctx_score, sel, block_t
           _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
           _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), None if tr is None else ctypes.byref(tr),
           _stream(stream))
+
+
+def oasis_decode_step_carry(h, q, pool, meta, ctx_attn, ctx_score, attend, n_attend, scores, out, workspace,
+                            job=None, transfer=None, stream=None):
+    """job: (scores, ctx_len, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict, attend, n_attend) of
+    another state, or None; transfer: (host_tier, pool, fetch, n_fetch) of another layer, or None."""
+    jb = None if job is None else oasis_select_job(*(_ptr(x) for x in job))
+    tr = None if transfer is None else oasis_transfer(*(_ptr(x) for x in transfer))
+    _call("oasis_decode_step_carry", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_attn), _ptr(ctx_score),
+          _ptr(attend), _ptr(n_attend), _ptr(scores), _ptr(out), _ptr(workspace),
+          None if jb is None else ctypes.byref(jb), None if tr is None else ctypes.byref(tr), _stream(stream))
 
 
 def oasis_sparse_paged_decode_attn_list(h, q, pool, attend, n_attend, ctx_len, out, workspace, stream=None):

@@ -806,9 +806,99 @@ hipError_t decode_step_impl(const oasis::Ctx& c, const void* q, const void* pool
     CHECK_PTR(evict);                                                                           \
   }
 
+// Another layer's transfer for a step's first launch (none when transfer is
+// NULL or the cap is 0): checks and resolves the host tier's device mapping.
+int resolve_transfer(oasis_handle h, const void* pool, const oasis_transfer* transfer, oasis::StepGather* g,
+                     const char* fn) {
+  if (transfer == nullptr || h->c.s.fetch_cap == 0) return OASIS_OK;
+  CHECK_PTR(transfer->host_tier);
+  CHECK_PTR(transfer->pool);
+  CHECK_PTR(transfer->fetch);
+  CHECK_PTR(transfer->n_fetch);
+  CHECK_ALIGN16(transfer->host_tier);
+  CHECK_ALIGN16(transfer->pool);
+  if (transfer->pool == pool) return fail(OASIS_EINVAL, "%s: the transfer's pool is this step's pool", fn);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, transfer->host_tier) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();  // clear the lookup's error state
+    return fail(OASIS_EINVAL, "%s: host_tier is not pinned host memory mapped for the device", fn);
+  }
+  g->host = static_cast<const uint4*>(attr.devicePointer);
+  g->pool = static_cast<uint4*>(transfer->pool);
+  g->fetch = transfer->fetch;
+  g->n_fetch = transfer->n_fetch;
+  g->cap = h->c.s.fetch_cap;
+  return OASIS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int oasis_decode_step_carry(oasis_handle h, const void* q, const void* pool, const void* meta,
+                            const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* attend,
+                            const int32_t* n_attend, float* scores, float* out, void* workspace,
+                            const oasis_select_job* job, const oasis_transfer* transfer, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(q);
+  CHECK_PTR(pool);
+  CHECK_PTR(meta);
+  CHECK_PTR(ctx_attn);
+  CHECK_PTR(ctx_score);
+  CHECK_PTR(attend);
+  CHECK_PTR(n_attend);
+  CHECK_PTR(scores);
+  CHECK_PTR(out);
+  CHECK_PTR(workspace);
+  CHECK_ALIGN16(q);
+  CHECK_ALIGN16(pool);
+  CHECK_ALIGN16(meta);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(OASIS_EINVAL, "oasis_decode_step_carry: workspace not 256-byte aligned");
+  if (!oasis::attn_score_select_available(h->c))
+    return fail(OASIS_EUNSUPPORTED,
+                "oasis_decode_step_carry: needs bf16, head_dim 128, 2 attention wavefronts, k <= 128, "
+                "fetch_cap <= k and max_blocks <= 8192");
+  oasis::SelectJob sj;
+  if (job != nullptr) {
+    CHECK_PTR(job->scores);
+    CHECK_PTR(job->ctx_len);
+    CHECK_PTR(job->sel);
+    CHECK_PTR(job->block_to_slot);
+    CHECK_PTR(job->slot_to_block);
+    CHECK_PTR(job->n_fetch);
+    CHECK_PTR(job->attend);
+    CHECK_PTR(job->n_attend);
+    if (h->c.s.fetch_cap > 0) {
+      CHECK_PTR(job->fetch);
+      CHECK_PTR(job->evict);
+    }
+    // the carried diff must not touch what this launch reads or writes
+    if (job->scores == scores || job->attend == attend || job->n_attend == n_attend)
+      return fail(OASIS_EINVAL, "oasis_decode_step_carry: the carried selection is this step's own state");
+    sj.scores = job->scores;
+    sj.ctx_len = job->ctx_len;
+    sj.sel = job->sel;
+    sj.b2s = job->block_to_slot;
+    sj.s2b = job->slot_to_block;
+    sj.fetch = job->fetch;
+    sj.n_fetch = job->n_fetch;
+    sj.evict = job->evict;
+    sj.attend = job->attend;
+    sj.n_attend = job->n_attend;
+  }
+  oasis::StepGather g;
+  const int rc = resolve_transfer(h, pool, transfer, &g, "oasis_decode_step_carry");
+  if (rc != OASIS_OK) return rc;
+  if (job != nullptr && g.host != nullptr && (job->fetch == g.fetch || job->n_fetch == g.n_fetch))
+    return fail(OASIS_EINVAL, "oasis_decode_step_carry: the transfer reads the fetch list the carried diff writes");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = oasis::launch_attn_score_select(h->c, q, pool, attend, n_attend, ctx_attn, out, workspace, meta,
+                                                 ctx_score, scores, job != nullptr ? &sj : nullptr, st, g);
+  if (e == hipSuccess) e = oasis::launch_attn_combine(h->c, workspace, out, st);
+  return hip_status(e, "oasis_decode_step_carry");
+}
 
 int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const void* meta,
                       const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
@@ -828,28 +918,8 @@ int oasis_decode_step_gather(oasis_handle h, const void* q, const void* pool, co
                              const oasis_transfer* transfer, void* stream) {
   CHECK_DECODE_STEP_ARGS("oasis_decode_step_gather");
   oasis::StepGather g;
-  if (transfer != nullptr && h->c.s.fetch_cap > 0) {
-    CHECK_PTR(transfer->host_tier);
-    CHECK_PTR(transfer->pool);
-    CHECK_PTR(transfer->fetch);
-    CHECK_PTR(transfer->n_fetch);
-    CHECK_ALIGN16(transfer->host_tier);
-    CHECK_ALIGN16(transfer->pool);
-    if (transfer->pool == pool)
-      return fail(OASIS_EINVAL, "oasis_decode_step_gather: the transfer's pool is this step's pool");
-    hipPointerAttribute_t attr;
-    if (hipPointerGetAttributes(&attr, transfer->host_tier) != hipSuccess || attr.type != hipMemoryTypeHost ||
-        attr.devicePointer == nullptr) {
-      (void)hipGetLastError();  // clear the lookup's error state
-      return fail(OASIS_EINVAL,
-                  "oasis_decode_step_gather: host_tier is not pinned host memory mapped for the device");
-    }
-    g.host = static_cast<const uint4*>(attr.devicePointer);
-    g.pool = static_cast<uint4*>(transfer->pool);
-    g.fetch = transfer->fetch;
-    g.n_fetch = transfer->n_fetch;
-    g.cap = h->c.s.fetch_cap;
-  }
+  const int rc = resolve_transfer(h, pool, transfer, &g, "oasis_decode_step_gather");
+  if (rc != OASIS_OK) return rc;
   return hip_status(decode_step_impl(h->c, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block,
                                      scores, out, workspace, fetch, n_fetch, evict, attend, n_attend, g,
                                      static_cast<hipStream_t>(stream)),

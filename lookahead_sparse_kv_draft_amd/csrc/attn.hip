@@ -41,8 +41,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((PF <= 2
     const int32_t* __restrict__ n_attend, const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, float* __restrict__ out, int H, int rows, int Nmax, int kb,
     int splits, int run, float scale_log2) {
+  __shared__ AttnLds<D, RT, W> lds;
   attn_wg<D, RT, W, PF>(q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, H, rows, Nmax, kb, splits,
-                        run, scale_log2, blockIdx.x);
+                        run, scale_log2, blockIdx.x, lds);
 }
 
 // fp32 path: workgroup of 256 threads per (unit, split).

@@ -19,21 +19,34 @@ constexpr float kLazyRescale = 8.f;
 // flight, every wait exact).  The wavefronts merge in LDS; with one
 // split the workgroup writes the output, otherwise its partial (unnormalised
 // accumulator, row max, row sum) for the combine kernel.
+// The LDS of one attention workgroup: the wavefronts' row statistics and
+// accumulator slices for the merge, and the unit's attended list when the
+// workgroup builds it from the selection and the block map.  A kernel that also
+// runs other kinds of workgroups can overlay this with their LDS.
+template <int D, int RT, int W>
+struct AttnLds {
+  static constexpr int NSLICE = (W > 1) ? W / 2 : 1;
+  float m[W][RT * 16];
+  float l[W][RT * 16];
+  float4 slice[NSLICE][RT][D / 16][kWave];  // wavefront accumulators in register layout
+  int att[kMaxBudget];
+  int wcnt[4][W];
+};
+
 template <int D, int RT, int W, int PF>
 __device__ __forceinline__ void attn_wg(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend,
     const int32_t* __restrict__ n_attend, const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, float* __restrict__ out, int H, int rows, int Nmax, int kb,
-    int splits, int run, float scale_log2, int wid) {
+    int splits, int run, float scale_log2, int wid, AttnLds<D, RT, W>& lds) {
   constexpr int KS = D / 32;  // QK k-steps of 32 channels
   constexpr int CT = D / 16;  // PV channel tiles
   constexpr int PAGE = 2 * kBlock * D;
   constexpr int NT = 64 * W;
-  constexpr int NSLICE = (W > 1) ? W / 2 : 1;
-  __shared__ float sm_m[W][RT * 16];
-  __shared__ float sm_l[W][RT * 16];
-  __shared__ float4 sm_slice[NSLICE][RT][CT][kWave];  // wavefront accumulators in register layout
+  auto& sm_m = lds.m;
+  auto& sm_l = lds.l;
+  auto& sm_slice = lds.slice;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -106,8 +119,8 @@ __device__ __forceinline__ void attn_wg(
     // per thread, all loads of a batch in flight), then takes its wavefronts'
     // shares of an even split over all splits * W wavefronts of the unit, so every
     // wavefront streams the same number of pages (+-1).
-    __shared__ int sm_att[kMaxBudget];
-    __shared__ int sm_wcnt[4][W];
+    auto& sm_att = lds.att;
+    auto& sm_wcnt = lds.wcnt;
     const uint64_t below = (1ull << lane) - 1ull;
     int natt = 0;
     for (int c0 = 0; c0 < kb; c0 += 4 * NT) {

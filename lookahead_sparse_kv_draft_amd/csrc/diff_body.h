@@ -215,19 +215,21 @@ __device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, c
 // decode step's default path): lane l handles selection entries and slots l and
 // l + 64, every rank is a ballot within the wavefront, so there is no barrier at
 // all (the wavefront's LDS accesses complete in order).  selL: LDS [kb], the
-// selection; b2sL: LDS [Nmax], this unit's block_to_slot row before the step;
-// bitmap words in `lds` already cleared; sb: the slot map for slots l and
-// l + 64 (-1 / any for slots >= kb); keysL: LDS [Nmax], the selection's order
-// key of every candidate block b at index b - 1 (the diff ranks victims by the
-// same keys, without loading their scores again).
+// selection; b2sL: LDS [Nmax], this unit's block_to_slot row before the step
+// (int32 or int8 entries, -1 = not resident); bitmap words in `lds` already
+// cleared; sb: the slot map for slots l and l + 64 (-1 / any for slots >= kb);
+// kd: the selection's order keys (desc_key of the score) of the blocks in
+// those two slots, read only for resident blocks outside the selection (the
+// diff ranks victims by the same keys as the selection).
 // Least-recently-used eviction when lu (this unit's per-slot stamps) is not
 // null: luv holds the stamps of slots l and l + 64; victims are taken oldest
 // stamp first, then in the lowest-score order, and the slots the next attention
 // reads are stamped with `step` ([EXPL] Table 2 runs LRU eviction).
 constexpr int kDiffWaveMaxBudget = 2 * kWave;
 
+template <typename SlotT>
 __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL,
-                                          const int32_t* b2sL, const int (&sb)[2], const uint32_t* keysL,
+                                          const SlotT* b2sL, const int (&sb)[2], const uint32_t (&kd)[2],
                                           const int (&luv)[2], int32_t* __restrict__ lu, int step,
                                           int32_t* __restrict__ bu,
                                  int32_t* __restrict__ slu, int32_t* __restrict__ fetch,
@@ -256,7 +258,7 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
     in[e] = i < kb;
     b[e] = in[e] ? selL[i] : -1;
     bok[e] = b[e] >= 0 && b[e] < Nmax;
-    res[e] = bok[e] ? b2sL[b[e]] : -1;
+    res[e] = bok[e] ? static_cast<int>(b2sL[b[e]]) : -1;
     sok[e] = in[e] && sb[e] >= 0 && sb[e] < Nmax;
     if (bok[e]) atomicOr(&bitmap[b[e] >> 5], 1u << (b[e] & 31));
     miss[e] = bok[e] && res[e] < 0;
@@ -287,9 +289,7 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
     for (int e = 0; e < 2; ++e) {
       const int sbc = sok[e] ? sb[e] : 0;  // index clamped: no branch around the read
       cnd[e] = sok[e] && !((bitmap[sbc >> 5] >> (sbc & 31)) & 1u);
-      // the block's order key as the selection computed it (candidate sbc - 1)
-      const uint32_t kd = keysL[min(max(sbc - 1, 0), Nmax - 1)];
-      ck[e] = ~((static_cast<unsigned long long>(kd) << 32) | static_cast<uint32_t>(sb[e] + 1));
+      ck[e] = ~((static_cast<unsigned long long>(kd[e]) << 32) | static_cast<uint32_t>(sb[e] + 1));
       bc[e] = __ballot(cnd[e]);
     }
     const int nc0 = __popcll(bc[0]);

@@ -121,6 +121,32 @@ hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, 
                                  const int32_t* ctx_attn, float* out, void* ws, const void* meta,
                                  const int32_t* ctx_score, float* scores, hipStream_t st,
                                  const StepGather& g = StepGather());
+// Another state's top-k selection and resident-set diff carried by the step's
+// first launch (one workgroup per unit ahead of the attention and scoring):
+// that state's scores, written by an earlier launch, the context length its
+// scoring saw, and the state the diff updates.  None of it may be memory the
+// launch's own attention or scoring reads or writes.  Score eviction,
+// k <= 128, cap <= k, N_max <= 8192, bf16, head_dim 128, 2 attention wavefronts.
+struct SelectJob {
+  const float* scores = nullptr;
+  const int32_t* ctx_len = nullptr;
+  int32_t* sel = nullptr;
+  int32_t* b2s = nullptr;
+  int32_t* s2b = nullptr;
+  int32_t* fetch = nullptr;
+  int32_t* n_fetch = nullptr;
+  int32_t* evict = nullptr;
+  int32_t* attend = nullptr;
+  int32_t* n_attend = nullptr;
+};
+bool attn_score_select_available(const Ctx& c);
+// The attention (from the attended list) and the lookahead score in one launch
+// (as launch_attn_and_score), led by the transfer's workgroups and, when job is
+// not null, by the carried selection's.
+hipError_t launch_attn_score_select(const Ctx& c, const void* q, const void* pool, const int32_t* attend,
+                                    const int32_t* n_attend, const int32_t* ctx_attn, float* out, void* ws,
+                                    const void* meta, const int32_t* ctx_score, float* scores, const SelectJob* job,
+                                    hipStream_t st, const StepGather& g = StepGather());
 // The fused selection + diff and the attention's split combine in one launch
 // (where select_diff_fused_available holds).
 hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,

@@ -37,6 +37,7 @@
 #include "block_ops.h"
 #include "attn_combine.h"
 #include "diff_body.h"
+#include "topk_body.h"
 
 namespace oasis {
 namespace {
@@ -189,265 +190,15 @@ __global__ __launch_bounds__(256) void topk_wg_kernel(const float* __restrict__ 
 
 
 
-constexpr int kTkThreads = 1024;
-constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kTkMaxWin = 512;
-
-struct TopkFastShared {
-  int hist[kTkThreads];
-  int start[kTkThreads + 1];  // first pass: keys in the bins before each bin
-  unsigned long long win[kTkMaxWin];
-  uint32_t wlo[kTkWaves], whi[kTkWaves];
-  int wtot[kTkWaves];
-  int bin, before, cnt, nwin;
-};
-
-// Inclusive sum over the 1024 threads and the block total (two barriers; with
-// TRAIL = false the second one, which protects wtot for the next call, is left
-// to the caller).
-template <bool TRAIL = true>
-__device__ __forceinline__ int tk_incl_sum(int v, int* wtot, int* total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  v = wave_incl_sum(v);
-  if (lane == kWave - 1) wtot[w] = v;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kTkWaves; ++i) {
-    const int x = wtot[i];
-    off += (i < w) ? x : 0;
-    tot += x;
-  }
-  if (TRAIL) __syncthreads();
-  *total = tot;
-  return v + off;
-}
-
-// This thread's candidate scores (candidate c = block c + 1 in slot c / 1024 of
-// thread c % 1024).  Issued first by every caller: every index below Nmax is in
-// bounds, and the context length, which arrives later, decides which keys take
-// part.
-template <int KPT>
-__device__ __forceinline__ void topk_fast_load(const float* __restrict__ scores, int Nmax, float (&v)[KPT]) {
-  const float* sc = scores + static_cast<size_t>(blockIdx.x) * Nmax;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) v[u] = sc[min(u * kTkThreads + static_cast<int>(threadIdx.x) + 1, Nmax - 1)];
-}
-
-// The selection of one unit by a 1024-thread workgroup from the scores
-// topk_fast_load returned and the request's context length n (read by the
-// caller before anything else, so its round trip overlaps the scores'); also
-// written, in rank order and -1 padded, to the LDS array selL when it is not
-// null.  keysL (LDS, Nmax entries, or null) receives every candidate's order
-// key at index block - 1 (0xFFFFFFFF past the candidates), before any early
-// return, for a diff that ranks eviction victims by the same keys.
-template <int KPT>
-__device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int32_t* __restrict__ sel, int Nmax,
-                                      int kb, int32_t* selL, TopkFastShared& sh, uint32_t* keysL = nullptr) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
-  const int unit = blockIdx.x;
-  const int N = max(1, min((n + kBlock - 1) / kBlock, Nmax));
-  const int F0 = (N == 1) ? 1 : 2;
-  const int C = max(0, N - 2);  // candidates are blocks 1 .. N-2
-  const int m = min(kb - F0, C);
-  int32_t* out = sel + static_cast<size_t>(unit) * kb;
-  if (tid == 0) {
-    out[0] = 0;
-    if (N > 1) out[1] = N - 1;
-    if (selL != nullptr) {
-      selL[0] = 0;
-      if (N > 1) selL[1] = N - 1;
-    }
-  }
-  for (int i = F0 + max(m, 0) + tid; i < kb; i += kTkThreads) {
-    out[i] = -1;
-    if (selL != nullptr) selL[i] = -1;
-  }
-  uint32_t key[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int c = u * kTkThreads + tid;
-    key[u] = (c < C) ? desc_key(v[u]) : 0xFFFFFFFFu;
-    if (keysL != nullptr && c < Nmax) keysL[c] = key[u];
-  }
-  if (m <= 0) return;  // uniform: every thread leaves together
-
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    if (u * kTkThreads + tid < C) {
-      lo = min(lo, key[u]);
-      hi = max(hi, key[u]);
-    }
-  }
-  {
-    uint32_t a0, a1, b0, b1;  // lanes ^ 32 and ^ 16 through the lane swaps
-    lane_pair32(lo, a0, a1);
-    lane_pair32(hi, b0, b1);
-    lo = min(a0, a1);
-    hi = max(b0, b1);
-    lane_pair16(lo, a0, a1);
-    lane_pair16(hi, b0, b1);
-    lo = min(a0, a1);
-    hi = max(b0, b1);
-  }
-  // then across each row by DPP (lane ^ 1, ^ 2, the half-row and row mirrors)
-  lo = min(lo, static_cast<uint32_t>(dpp_from<0xB1>(static_cast<int>(lo))));
-  hi = max(hi, static_cast<uint32_t>(dpp_from<0xB1>(static_cast<int>(hi))));
-  lo = min(lo, static_cast<uint32_t>(dpp_from<0x4E>(static_cast<int>(lo))));
-  hi = max(hi, static_cast<uint32_t>(dpp_from<0x4E>(static_cast<int>(hi))));
-  lo = min(lo, static_cast<uint32_t>(dpp_from<0x141>(static_cast<int>(lo))));
-  hi = max(hi, static_cast<uint32_t>(dpp_from<0x141>(static_cast<int>(hi))));
-  lo = min(lo, static_cast<uint32_t>(dpp_from<0x140>(static_cast<int>(lo))));
-  hi = max(hi, static_cast<uint32_t>(dpp_from<0x140>(static_cast<int>(hi))));
-  if (lane == 0) {
-    sh.wlo[w] = lo;
-    sh.whi[w] = hi;
-  }
-  sh.hist[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kTkWaves; ++i) {
-    lo = min(lo, sh.wlo[i]);
-    hi = max(hi, sh.whi[i]);
-  }
-  // Radix select on d = key - lo in [0, hi - lo].  The selection is every key
-  // with d < base plus `rem` keys of the current bin range.
-  const uint32_t range = hi - lo;
-  const int width = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
-  int shift = max(width - 10, 0);
-  uint32_t base = 0u;
-  int rem = m;
-  bool exact = false;
-  bool first = true;  // still in the first pass (bins over the whole key range)
-  int ncoll = m;      // keys the collection below gathers
-  while (true) {
-    const uint64_t span = 1ull << (shift + 10);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const uint64_t d = static_cast<uint64_t>(key[u] - lo);
-      if (u * kTkThreads + tid < C && d >= base && d - base < span)
-        atomicAdd(&sh.hist[static_cast<int>((d - base) >> shift)], 1);
-    }
-    __syncthreads();
-    const int hv = sh.hist[tid];
-    int unused_total;
-    const int incl = tk_incl_sum<false>(hv, sh.wtot, &unused_total);  // the barrier below protects wtot
-    const int excl = incl - hv;
-    if (first) {
-      sh.start[tid] = excl;
-      if (tid == kTkThreads - 1) sh.start[kTkThreads] = incl;
-    }
-    if (excl < rem && incl >= rem) {  // exactly one thread: its bin holds the m-th key
-      sh.bin = tid;
-      sh.before = excl;
-      sh.cnt = hv;
-    }
-    sh.hist[tid] = 0;  // cleared for a next pass
-    __syncthreads();
-    rem -= sh.before;
-    base += static_cast<uint32_t>(sh.bin) << shift;
-    // The bin is taken whole when its keys are exactly the ones still needed,
-    // or when the winners so far plus the whole bin fit the winner list: the
-    // rank counting below then keeps the first m of them (the bin's keys rank
-    // after every key above the bin).
-    if (sh.cnt == rem || m - rem + sh.cnt <= kTkMaxWin) {
-      ncoll = m - rem + sh.cnt;
-      base += static_cast<uint32_t>((1ull << shift) - 1ull);
-      exact = true;
-      break;
-    }
-    if (shift == 0) break;  // a single key value: ties at the threshold remain
-    shift = max(shift - 10, 0);
-    first = false;
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
-  if (exact && first) {
-    // One pass was enough: the winners are the keys of bins 0 .. bin (the
-    // histogram bins over the whole range, the last one taken whole).  Each key
-    // goes to its bin's range of the winner list (counting-sort scatter, the
-    // cleared histogram as cursors), and its output position is the number of
-    // keys in earlier bins plus its rank inside its own bin, so only keys that
-    // share a bin are compared.
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const uint32_t d = key[u] - lo;
-      if (u * kTkThreads + tid < C && d <= base) {
-        const int bk = static_cast<int>(d >> shift);
-        sh.win[sh.start[bk] + atomicAdd(&sh.hist[bk], 1)] =
-            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
-      }
-    }
-    __syncthreads();
-    if (tid < ncoll) {
-      const unsigned long long mine = sh.win[tid];
-      const int bk = static_cast<int>((static_cast<uint32_t>(mine >> 32) - lo) >> shift);
-      const int b0 = sh.start[bk], b1 = sh.start[bk + 1];
-      const int r = b0 + rank_below(sh.win + b0, b1 - b0, mine, 1, 0);
-      if (r < m) {
-        out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
-        if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
-      }
-    }
-    return;
-  }
-  // Collect winners: d < base (d <= base when exact) with one atomic per wavefront.
-  if (tid == 0) sh.nwin = 0;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const uint32_t d = key[u] - lo;
-    const bool win = (u * kTkThreads + tid < C) && (exact ? d <= base : d < base);
-    const uint64_t bw = __ballot(win);
-    if (bw) {
-      int wbase = 0;
-      if (lane == 0) wbase = atomicAdd(&sh.nwin, __popcll(bw));
-      wbase = __builtin_amdgcn_readlane(wbase, 0);
-      if (win)
-        sh.win[wbase + __popcll(bw & below)] =
-            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
-    }
-  }
-  if (!exact) {
-    // ties at d == base: the first `rem` in index order (u, then thread)
-    int taken = 0;
-    const int n_lt = m - rem;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const bool eq = (u * kTkThreads + tid < C) && (key[u] - lo == base);
-      int tot;
-      const int r = tk_incl_sum(eq ? 1 : 0, sh.wtot, &tot) - (eq ? 1 : 0);
-      if (eq && taken + r < rem)
-        sh.win[n_lt + taken + r] =
-            (static_cast<unsigned long long>(key[u]) << 32) | static_cast<uint32_t>(u * kTkThreads + tid + 1);
-      taken += tot;
-    }
-  }
-  __syncthreads();
-  // Output position = number of smaller winners (all keys distinct by index),
-  // counted by P adjacent threads per winner and summed across their lanes.
-  const int nw = ncoll;  // the m winners, and with a whole threshold bin the rest of its keys
-  const int P = (nw <= 64) ? 16 : (nw <= 128) ? 8 : (nw <= 256) ? 4 : (nw <= 512) ? 2 : 1;
-  const int wi = tid / P, part = tid & (P - 1);
-  const unsigned long long mine = sh.win[min(wi, nw - 1)];
-  const int r = rank_below(sh.win, nw, mine, P, part);
-  if (part == 0 && wi < nw && r < m) {
-    out[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);  // block index = candidate + 1
-    if (selL != nullptr) selL[F0 + r] = static_cast<int32_t>(mine & 0xFFFFFFFFull);
-  }
-}
-
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict__ scores,
                                                          const int32_t* __restrict__ ctx_len,
                                                          int32_t* __restrict__ sel, int H, int Nmax, int kb) {
-  __shared__ TopkFastShared sh;
+  __shared__ TopkFastShared<kTkThreads> sh;
   const int n = ctx_len[blockIdx.x / H];
   float v[KPT];
-  topk_fast_load<KPT>(scores, Nmax, v);
-  topk_fast_body<KPT>(v, n, sel, Nmax, kb, nullptr, sh);
+  topk_fast_load<kTkThreads, KPT>(scores + static_cast<size_t>(blockIdx.x) * Nmax, Nmax, v);
+  topk_fast_body<kTkThreads, KPT>(v, n, blockIdx.x, sel, Nmax, kb, nullptr, sh);
 }
 
 // Dynamic LDS of the fused selection + diff: the diff's arrays, the selection
@@ -470,7 +221,7 @@ __device__ __forceinline__ void select_diff_unit(
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
     int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step,
-    unsigned long long* smem_u64, TopkFastShared& sh, DiffShared& dsh) {
+    unsigned long long* smem_u64, TopkFastShared<kTkThreads>& sh, DiffShared& dsh) {
   int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
@@ -481,7 +232,7 @@ __device__ __forceinline__ void select_diff_unit(
   // the scores and the map rows (independent), then the context length, then
   // the scores of the resident blocks (which need the slot map).
   float v[KPT];
-  topk_fast_load<KPT>(scores, Nmax, v);
+  topk_fast_load<kTkThreads, KPT>(su, Nmax, v);
   if (kb <= kDiffWaveMaxBudget) {
     int32_t* b2sL = selL + kb;
     uint32_t* keysL = reinterpret_cast<uint32_t*>(b2sL + Nmax);
@@ -499,13 +250,17 @@ __device__ __forceinline__ void select_diff_unit(
     const int n = ctx_len[unit / H];
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
     for (int j = tid; j < (Nmax + 31) / 32; j += kTkThreads) bitmap[j] = 0u;  // ordered by the selection's barriers
-    topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh, keysL);
+    topk_fast_body<kTkThreads, KPT>(v, n, unit, sel, Nmax, kb, selL, sh, keysL);
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
       if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
     __syncthreads();
     if (tid >= kWave) return;
-    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, keysL, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
+    // the candidates' order keys as the selection computed them (block b at b - 1)
+    uint32_t kd[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kd[e] = keysL[min(max(sbw[e] - 1, 0), Nmax - 1)];
+    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, kd, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
               n_attend, smem_u64);
     return;
   }
@@ -514,7 +269,7 @@ __device__ __forceinline__ void select_diff_unit(
   __builtin_amdgcn_sched_barrier(0);
   const bool sok = sb >= 0 && sb < Nmax;
   const float sv = su[sok ? sb : 0];
-  topk_fast_body<KPT>(v, n, sel, Nmax, kb, selL, sh);
+  topk_fast_body<kTkThreads, KPT>(v, n, unit, sel, Nmax, kb, selL, sh);
   __syncthreads();
   diff_body(unit, kb, Nmax, cap, selL, sb, sv, bu, slu, fetch, n_fetch, evict, attend, n_attend, smem_u64, dsh);
 }
@@ -526,7 +281,7 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
     int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step) {
   extern __shared__ unsigned long long smem_u64[];
-  __shared__ TopkFastShared sh;
+  __shared__ TopkFastShared<kTkThreads> sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
                         last_use, step, smem_u64, sh, dsh);
@@ -548,7 +303,7 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
     return;
   }
   extern __shared__ unsigned long long smem_u64[];
-  __shared__ TopkFastShared sh;
+  __shared__ TopkFastShared<kTkThreads> sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
                         last_use, step, smem_u64, sh, dsh);

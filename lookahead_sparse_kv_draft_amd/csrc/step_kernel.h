@@ -1,0 +1,238 @@
+// The decode step's first launch (OasisKV explainer, Figure 8: at step t the
+// layer's attention runs over the resident part of S_t while the draft queries
+// predict S_{t+1}; prediction, selection and transfer of one layer proceed
+// while later layers compute): attention workgroups (split partials) and
+// lookahead-scoring workgroups in one grid, optionally led by workgroups that
+// move another layer's fetched pages and (KPT > 0: keys per selecting thread)
+// by workgroups that run another state's top-k selection and resident-set diff
+// from scores an earlier launch wrote.  Nothing in the grid waits for anything
+// else in it: the carried selection reads and writes only the other state.
+#pragma once
+
+#include "attn_body.h"
+#include "score_body.h"
+#include "topk_body.h"
+
+namespace oasis {
+namespace {
+
+// One page of another layer's fetch list, copied from the device-mapped pinned
+// host tier into that layer's pool by one workgroup of NT threads: all reads of
+// a batch issued before its writes.  Entries beyond n_fetch and entries out of
+// range are skipped, as in the standalone gather.
+template <int NT>
+__device__ __forceinline__ void gather_page(const StepGather& g, int Nmax, int kb, int page16, int entry, int unit) {
+  constexpr int kBatch = 4;
+  const int nf = g.n_fetch[unit];
+  if (entry >= nf || entry >= g.cap) return;
+  const int b = g.fetch[(static_cast<size_t>(unit) * g.cap + entry) * 2];
+  const int s = g.fetch[(static_cast<size_t>(unit) * g.cap + entry) * 2 + 1];
+  if (b < 0 || b >= Nmax || s < 0 || s >= kb) return;
+  const uint4* src = g.host + (static_cast<size_t>(unit) * Nmax + b) * page16;
+  uint4* dst = g.pool + (static_cast<size_t>(unit) * kb + s) * page16;
+  for (int c0 = 0; c0 < page16; c0 += NT * kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      if (c < page16) v[u] = src[c];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      if (c < page16) dst[c] = v[u];
+    }
+  }
+}
+
+// Largest block count and diff LDS of a carried selection (k <= 128,
+// cap <= k): candidate keys, selection bitmap, fetch/target/victim lists, free
+// slots, candidate slots and stamps (the layout diff_wave carves).
+constexpr int kCarryMaxBlocks = 8 * 1024;
+constexpr int kCarryDiffBytes =
+    kDiffWaveMaxBudget * 8 + (kCarryMaxBlocks / 32) * 4 + (3 * kDiffWaveMaxBudget + 4 * kDiffWaveMaxBudget) * 4;
+
+template <int NT>
+struct SelectLds {
+  TopkFastShared<NT> tk;
+  int32_t selL[kDiffWaveMaxBudget];                   // the selection in rank order
+  uint32_t slot_keys[kDiffWaveMaxBudget];             // order key of the block in each slot
+  unsigned long long diff[kCarryDiffBytes / 8];        // diff_wave's arrays
+  int8_t slot_of[kCarryMaxBlocks];                     // block -> slot before the step (-1: none)
+};
+
+// The LDS of a first-launch workgroup: an attention workgroup's, overlaid with
+// a selecting workgroup's when the launch carries a selection.
+template <int D, int RT, int W, bool SEL>
+struct StepLds {
+  AttnLds<D, RT, W> attn;
+};
+template <int D, int RT, int W>
+struct StepLds<D, RT, W, true> {
+  union {
+    AttnLds<D, RT, W> attn;
+    SelectLds<64 * W> sel;
+  };
+};
+
+// The top-k selection and resident-set diff of one unit of the carried state
+// by one workgroup of NT threads: the unit's scores, slot map and context
+// length in one round trip of loads; the block -> slot table is built in LDS
+// as the inverse of the slot map (every diff keeps block_to_slot its inverse,
+// so the block map row itself is not read); then topk_body.h and diff_wave,
+// exactly as the separate selection launch computes them.
+template <int NT, int KPT>
+__device__ __forceinline__ void select_diff_wg(const SelectJob& job, int unit, int H, int Nmax, int kb, int cap,
+                                               SelectLds<NT>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  int32_t* bu = job.b2s + static_cast<size_t>(unit) * Nmax;
+  int32_t* slu = job.s2b + static_cast<size_t>(unit) * kb;
+  float v[KPT];
+  topk_fast_load<NT, KPT>(job.scores + static_cast<size_t>(unit) * Nmax, Nmax, v);
+  int sbw[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) sbw[e] = slu[min(lane + e * kWave, kb - 1)];  // clamped: no branch around the loads
+  const int sb_own = slu[min(tid, kb - 1)];  // slot tid's block, for the table
+  const int n = job.ctx_len[unit / H];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(sh.slot_of);
+  for (int j = tid; j < (Nmax + 3) / 4; j += NT) tab[j] = 0xFFFFFFFFu;  // every entry -1
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sh.diff + kb);
+  for (int j = tid; j < (Nmax + 31) / 32; j += NT) bitmap[j] = 0u;
+  __syncthreads();
+  if (tid < kb && sb_own >= 0 && sb_own < Nmax) sh.slot_of[sb_own] = static_cast<int8_t>(tid);
+  __syncthreads();
+  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, nullptr, sh.slot_of, sh.slot_keys);
+  __syncthreads();
+  if (tid >= kWave) return;
+  uint32_t kd[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) kd[e] = sh.slot_keys[min(lane + e * kWave, kb - 1)];
+  const int luw[2] = {0, 0};
+  diff_wave<int8_t>(unit, kb, Nmax, cap, sh.selL, sh.slot_of, sbw, kd, luw, nullptr, 0, bu, slu, job.fetch,
+                    job.n_fetch, job.evict, job.attend, job.n_attend, sh.diff);
+}
+
+// Attention (2-page ring) and scoring workgroups in one grid of workgroups of
+// W wavefronts (W = 2, or 4 for up to two attention row tiles), led by
+// n_gather_wg workgroups that move another layer's fetched pages (one per
+// fetch entry and unit; none without a transfer): the host-link reads start
+// with the launch and overlap its HBM-bound work.
+// order 0: attention workgroups first; 1: scoring first; 2: interleaved one for
+// one while both last.  With KPT > 0, n_select_wg workgroups (one per unit of
+// the carried state) follow the transfer's and select.
+template <int D, int RTA, int RTS, int W, int KPT>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((RTA <= 3 && RTS <= 2) ? 2 : 1))) void attn_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend, const int32_t* __restrict__ n_attend,
+    const int32_t* __restrict__ ctx_attn, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    float* __restrict__ out, int H, int arows, int Nmax, int kb, int splits, int run, float scale_log2,
+    const uint16_t* __restrict__ meta, const int32_t* __restrict__ ctx_score, float* __restrict__ scores, int G,
+    int T, int ndraft, int srows, int wpu, int tpw, int total_waves, int n_attn_wg, int n_score_wg, int order,
+    StepGather gather, int n_gather_wg, int page16, SelectJob job, int n_select_wg, int cap) {
+  constexpr bool SEL = KPT > 0;
+  __shared__ StepLds<D, RTA, W, SEL> lds;
+  if (static_cast<int>(blockIdx.x) < n_gather_wg) {
+    const int units = n_gather_wg / gather.cap;
+    gather_page<64 * W>(gather, Nmax, kb, page16, blockIdx.x / units, blockIdx.x % units);
+    return;
+  }
+  if constexpr (SEL) {
+    if (static_cast<int>(blockIdx.x) < n_gather_wg + n_select_wg) {
+      select_diff_wg<64 * W, KPT>(job, blockIdx.x - n_gather_wg, H, Nmax, kb, cap, lds.sel);
+      return;
+    }
+  }
+  const int bid = blockIdx.x - n_gather_wg - n_select_wg;
+  bool is_attn;
+  int idx;
+  if (order == 0) {
+    is_attn = bid < n_attn_wg;
+    idx = is_attn ? bid : bid - n_attn_wg;
+  } else if (order == 1) {
+    is_attn = bid >= n_score_wg;
+    idx = is_attn ? bid - n_score_wg : bid;
+  } else {
+    const int m = min(n_attn_wg, n_score_wg);
+    if (bid < 2 * m) {
+      is_attn = (bid & 1) == 0;
+      idx = bid >> 1;
+    } else {
+      is_attn = n_attn_wg > m;
+      idx = m + (bid - 2 * m);
+    }
+  }
+  if (is_attn) {
+    attn_wg<D, RTA, W, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
+                          splits, run, scale_log2, idx, lds.attn);
+    return;
+  }
+  score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, 1, srows, Nmax, wpu, tpw, total_waves,
+                     idx * W + static_cast<int>(threadIdx.x) / kWave, threadIdx.x & (kWave - 1));
+}
+
+template <int D, int RTA, int RTS, int W, int KPT>
+hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                const StepGather& g, const SelectJob* job, hipStream_t st) {
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
+  const int n_attn_wg = c.units * c.attn_splits;
+  const int wpu = score_waves_per_unit(c);
+  const int total = c.units * wpu;
+  const int n_score_wg = (total + W - 1) / W;
+  const int n_gather_wg = (g.host != nullptr && g.cap > 0) ? g.cap * c.units : 0;
+  const int page16 = static_cast<int>(c.page_elems * c.elem_bytes / 16);
+  const int n_select_wg = (KPT > 0 && job != nullptr) ? c.units : 0;
+  hipLaunchKernelGGL((attn_score_kernel<D, RTA, RTS, W, KPT>),
+                     dim3(n_gather_wg + n_select_wg + n_attn_wg + n_score_wg),
+                     dim3(64 * W), 0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel,
+                     b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn,
+                     c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2,
+                     static_cast<const uint16_t*>(meta), ctx_score, scores, c.s.group, c.T, c.s.n_draft,
+                     c.rows_score, wpu, c.score_tpw, total, n_attn_wg, n_score_wg, c.step_order, g, n_gather_wg,
+                     page16, job != nullptr ? *job : SelectJob(), n_select_wg, c.s.fetch_cap);
+  return hipGetLastError();
+}
+
+template <int D, int RTA, int W, int KPT>
+hipError_t as_s(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                const StepGather& g, const SelectJob* job, hipStream_t st) {
+  switch ((c.rows_score + 15) / 16) {
+    case 1: return as_t<D, RTA, 1, W, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+    case 2: return as_t<D, RTA, 2, W, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+    case 3: return as_t<D, RTA, 3, W, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+    default: return as_t<D, RTA, 4, W, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+  }
+}
+
+// The first launch for one head dimension: row tiles and wavefronts per
+// workgroup from the shape (a carried selection is built for W = 2 only).
+template <int D, int KPT>
+hipError_t as_d(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
+                const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_attn, float* ws_acc,
+                float* ws_ml, float* out, const void* meta, const int32_t* ctx_score, float* scores,
+                const StepGather& g, const SelectJob* job, hipStream_t st) {
+  const bool w4 = c.attn_waves == 4;
+  if constexpr (KPT > 0) {
+    if (w4) return hipErrorInvalidValue;
+    switch ((c.rows_attn + 15) / 16) {
+      case 1: return as_s<D, 1, 2, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+      case 2: return as_s<D, 2, 2, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+      default: return as_s<D, 3, 2, KPT>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+    }
+  } else {
+    switch ((c.rows_attn + 15) / 16) {
+      case 1: return w4 ? as_s<D, 1, 4, 0>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st)
+                        : as_s<D, 1, 2, 0>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+      case 2: return w4 ? as_s<D, 2, 4, 0>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st)
+                        : as_s<D, 2, 2, 0>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+      default: return as_s<D, 3, 2, 0>(c, q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, meta, ctx_score, scores, g, job, st);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace oasis

@@ -178,7 +178,7 @@ class DecodeRuntime:
     def __init__(self, shape: Shape, layers: int = 1, device: str = "cuda", replicas: int = 1,
                  host_tier: bool = True, fused_select: bool = True, overlap: bool = False,
                  gather: bool = True, options: dict | None = None, eviction: str = "score",
-                 transfer_mode: str = "side"):
+                 transfer_mode: str = "side", carry_select: bool = False):
         """overlap: run scoring / selection on a second stream so that they overlap
         the attention of the same step (and of other layers); the selection waits
         only for the attention that reads the maps it rewrites.  options: launch
@@ -188,13 +188,22 @@ class DecodeRuntime:
         transfer_mode: "side" (each layer's transfer on the side stream,
         transfer_group) or "inline" (a layer's fetched pages ride in the first
         launch of the next decode step enqueued on the compute stream,
-        oasis_decode_step_gather: no second stream, no event; defer_transfer)."""
+        oasis_decode_step_gather: no second stream, no event; defer_transfer).
+        carry_select: decode_step leaves the layer's selection and diff pending
+        and runs them as leading workgroups of the next decode step's first
+        launch (another layer's, or the next step's first layer's;
+        oasis_decode_step_carry: the second launch is the split combine alone),
+        then hands that layer's transfer on; score eviction."""
         if eviction not in ("score", "lru"):
             raise ValueError(eviction)
         if transfer_mode not in ("side", "inline"):
             raise ValueError(transfer_mode)
         if transfer_mode == "inline" and (overlap or not gather):
             raise ValueError("inline transfers run on the compute stream with the device gather")
+        if carry_select and (eviction != "score" or overlap):
+            raise ValueError("a carried selection evicts by score, on the compute stream")
+        self.carry_select = carry_select
+        self.pending_select = None  # (layer, replica, ctx tensor) whose selection and diff have not run
         self.transfer_mode = transfer_mode
         self.inline_pending = None  # (layer, replica) whose fetched pages await their transfer
         self.shape = shape
@@ -345,6 +354,7 @@ class DecodeRuntime:
         and the last selection of this layer."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
+        self._flush_select_of(layer, replica, cs)
         if st.pending is not None:
             st.pending.wait(cs)
         if self.inline_pending == (layer, replica):
@@ -368,6 +378,7 @@ class DecodeRuntime:
         the index of the next attention (step t + 1), whose slots the diff stamps."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
+        self._flush_select_of(layer, replica, cs)  # its own attention needs it
         if st.pending is not None:
             st.pending.wait(cs)
         if st.select_pending:
@@ -382,6 +393,19 @@ class DecodeRuntime:
                 self.inline_pending = None
             else:
                 self.flush_inline(cs)
+        if self.carry_select and not two_calls:
+            job = None
+            pend = self.pending_select
+            if pend is not None:
+                pst = self.state[pend[0]][pend[1]]
+                job = (pst.scores, pend[2], pst.sel, pst.b2s, pst.s2b, pst.fetch, pst.n_fetch, pst.evict,
+                       pst.attend, pst.n_attend)
+            L.oasis_decode_step_carry(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.attend,
+                                      st.n_attend, st.scores, o, self.ws_ptr, job=job, transfer=carry, stream=cs)
+            self.pending_select = (layer, replica, self.ctx_scoring)
+            if pend is not None:
+                self._selected(pend[0], pend[1], cs)
+            return
         if carry is not None:
             L.oasis_decode_step_gather(self.h, q, st.pool, st.meta, self.ctx_len, self.ctx_scoring, st.sel, st.b2s,
                                        st.s2b, st.scores, o, self.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
@@ -417,6 +441,7 @@ class DecodeRuntime:
         """
         st = self.state[layer][replica]
         ps = self._pred()
+        self._flush_select_of(layer, replica, ps)
         if st.pending is not None:
             st.pending.wait(ps)
         if self.inline_pending == (layer, replica):
@@ -447,6 +472,7 @@ class DecodeRuntime:
         st = self.state[layer][replica]
         ctx = self.ctx_scoring
         ps = self._pred()
+        self._flush_select_of(layer, replica, ps)
         if self.inline_pending == (layer, replica):  # its fetch list is about to be rewritten
             self.flush_inline(ps)
         L.oasis_lookahead_score(self.h, q, st.meta, ctx, st.scores, ps)
@@ -484,6 +510,7 @@ class DecodeRuntime:
         The next decode_step of the layer then attends over the exact set."""
         st = self.state[layer][replica]
         cs = torch.cuda.current_stream()
+        self._flush_select_of(layer, replica, cs)
         if st.pending is not None:  # a pending prefetch may target the same slots
             st.pending.wait(cs)
         if self.inline_pending == (layer, replica):
@@ -543,6 +570,31 @@ class DecodeRuntime:
         for st in states:
             st.pending = batch
 
+    def _selected(self, layer: int, replica: int, stream):
+        """The layer's carried selection and diff are enqueued on `stream`: hand
+        its transfer on (inline: to the next decode step's first launch; else
+        the side stream, behind `stream`)."""
+        if self.transfer_mode == "inline":
+            self.defer_transfer(layer, replica)
+        else:
+            self.transfer_group([layer], replica, stream)
+
+    def flush_select(self, stream):
+        """The pending carried selection and diff as a launch of their own on
+        `stream` (oasis_select_and_diff: the same results), then its transfer."""
+        if self.pending_select is None:
+            return
+        layer, replica, ctx = self.pending_select
+        self.pending_select = None
+        st = self.state[layer][replica]
+        L.oasis_select_and_diff(self.h, st.scores, ctx, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict,
+                                st.attend, st.n_attend, stream=stream)
+        self._selected(layer, replica, stream)
+
+    def _flush_select_of(self, layer: int, replica: int, stream):
+        if self.pending_select is not None and self.pending_select[:2] == (layer, replica):
+            self.flush_select(stream)
+
     def defer_transfer(self, layer: int, replica: int = 0):
         """Inline mode: the layer's fetched pages move in the first launch of the
         next decode step enqueued on the compute stream (or in flush_inline)."""
@@ -561,6 +613,7 @@ class DecodeRuntime:
     def wait_transfers(self):
         """Make the current stream wait for every pending transfer and selection."""
         cs = torch.cuda.current_stream()
+        self.flush_select(cs)
         self.flush_inline(cs)
         for layer in self.state:
             for st in layer:

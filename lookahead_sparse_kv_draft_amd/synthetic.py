@@ -44,7 +44,8 @@ class SyntheticRun:
     def __init__(self, cfg: Config, layers: int | None = None, replicas: int = 1,
                  record_units=None, device: str = "cuda", overlap: bool = True, fused_step: bool = True,
                  gather: bool = True, two_calls: bool = False, options: dict | None = None,
-                 eviction: str = "score", transfer_group: int = 1, transfer_mode: str = "side"):
+                 eviction: str = "score", transfer_group: int = 1, transfer_mode: str = "side",
+                 carry_select: bool = False):
         """fused_step: without overlap and drift, run each layer's step through the
         single decode-step call (attention, scoring, selection, diff), or through
         its two halves (two_calls).  gather: move the fetched pages with the
@@ -53,7 +54,10 @@ class SyntheticRun:
         transfer_group: layers whose transfers go to the side stream as one
         batch (one cross-stream hand-off and one completion event per batch).
         transfer_mode: "side" or "inline" (each layer's pages ride in the next
-        decode step's first launch on the compute stream)."""
+        decode step's first launch on the compute stream).
+        carry_select: each layer's selection and diff run in the next decode
+        step's first launch (oasis_decode_step_carry), which also hands that
+        layer's transfer on; used where the fused step runs."""
         self.cfg = cfg
         self.fused_step = fused_step and not overlap
         self.two_calls = two_calls
@@ -63,7 +67,9 @@ class SyntheticRun:
         self.rt = DecodeRuntime(self.shape, layers=self.L, device=device, replicas=replicas, overlap=overlap,
                                 gather=gather, options=options, eviction=eviction,
                                 transfer_mode=(transfer_mode if self.fused_step and not cfg.drift_blocks
-                                               else "side"))
+                                               else "side"),
+                                carry_select=(carry_select and self.fused_step and not cfg.drift_blocks
+                                              and not two_calls))
         self.record_units = record_units  # list of (layer, unit) to record, or None
         self.records = {}
         B, H, G, T, d = cfg.batch, cfg.kv_heads, cfg.group, cfg.T, cfg.head_dim
@@ -142,7 +148,10 @@ class SyntheticRun:
         if ids:
             rt.rebuild_blocks(l, np.concatenate(ids))
 
-    def step(self, t: int, transfer: bool = True):
+    def step(self, t: int, transfer: bool = True, sync: bool = True):
+        """One decode step over the layers; sync: end it with every selection and
+        transfer enqueued and waited for (else carried selections and inline
+        transfers stay pending into the next step)."""
         cfg, rt = self.cfg, self.rt
         if self.fused_step and self.drift is None:
             for l in range(self.L):
@@ -156,9 +165,10 @@ class SyntheticRun:
                 if transfer:
                     self._transfer_after(l)
             rt.end_step()
-            if transfer:
+            if transfer and sync:
                 rt.wait_transfers()
-            self._record(t)
+            if sync:
+                self._record(t)
             return
         for l in range(self.L):
             q = self.q[l, t + 1]
@@ -180,7 +190,10 @@ class SyntheticRun:
 
     def _transfer_after(self, l: int):
         """After layer l's diff: hand the batch that ends at layer l to the side
-        stream (or, inline, leave the pages to the next decode step's launch)."""
+        stream (or, inline, leave the pages to the next decode step's launch).
+        A carried selection hands its transfer on itself."""
+        if self.rt.carry_select:
+            return
         if self.rt.transfer_mode == "inline":
             self.rt.defer_transfer(l)
             return

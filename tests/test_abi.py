@@ -211,3 +211,44 @@ def test_decode_step_gather_rejects_its_own_pool():
         assert "pool" in L.oasis_last_error()
     finally:
         L.oasis_destroy(h)
+
+
+def test_decode_step_carry_rejects_before_any_launch():
+    """The step that carries another state's selection: missing pointers, a job
+    that is this step's own state, and a transfer reading the fetch list the
+    job writes are EINVAL; shapes outside its kernels EUNSUPPORTED; all on the
+    host, before any launch."""
+    lib = L.load()
+    # q, pool, meta, ctx_attn, ctx_score, attend, n_attend, scores, out, workspace
+    args = list(range(256, 256 * 11, 256))
+    job_fields = list(range(256 * 20, 256 * 30, 256))  # scores .. n_attend of another state
+
+    def job(**kw):
+        j = L.oasis_select_job(*job_fields)
+        for k, v in kw.items():
+            setattr(j, k, v)
+        return ctypes.byref(j)
+
+    h = L.oasis_create(**_shape())
+    try:
+        for i in (0, 5, 6, 7, 9):
+            a = list(args)
+            a[i] = None
+            assert lib.oasis_decode_step_carry(h, *a, None, None, None) == L.OASIS_EINVAL, i
+        a = list(args)
+        a[9] = 272  # workspace not 256-byte aligned
+        assert lib.oasis_decode_step_carry(h, *a, None, None, None) == L.OASIS_EINVAL
+        assert lib.oasis_decode_step_carry(h, *args, job(scores=None), None, None) == L.OASIS_EINVAL
+        assert lib.oasis_decode_step_carry(h, *args, job(scores=args[7]), None, None) == L.OASIS_EINVAL
+        assert "own state" in L.oasis_last_error()
+        assert lib.oasis_decode_step_carry(h, *args, job(attend=args[5]), None, None) == L.OASIS_EINVAL
+        assert lib.oasis_decode_step_carry(h, *args, job(n_attend=args[6]), None, None) == L.OASIS_EINVAL
+    finally:
+        L.oasis_destroy(h)
+    for kw in (dict(budget_blocks=256, fetch_cap=4), dict(head_dim=64), dict(dtype=L.OASIS_F32),
+               dict(fetch_cap=32, budget_blocks=16), dict(max_blocks=9000)):
+        h = L.oasis_create(**_shape(**kw))
+        try:
+            assert lib.oasis_decode_step_carry(h, *args, job(), None, None) == L.OASIS_EUNSUPPORTED, kw
+        finally:
+            L.oasis_destroy(h)

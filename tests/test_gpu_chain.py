@@ -23,13 +23,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_and_compare(cfg, units, steps=None, layers=None, overlap=False, gather=True, options=None,
-                     eviction="score", transfer_group=1, transfer_mode="side"):
+                     eviction="score", transfer_group=1, transfer_mode="side", carry_select=False):
     """Runs the chain on the GPU recording `units`, then compares every recorded
     unit with the oracle over every step (near ties adopted and counted)."""
     cfg = cfg if steps is None else cfg.with_(steps=steps)
     print(f"{cfg.name}: filling host tier and metadata ({len(units)} units recorded)", flush=True)
     run = SyntheticRun(cfg, layers=layers, record_units=units, overlap=overlap, gather=gather, options=options,
-                       eviction=eviction, transfer_group=transfer_group, transfer_mode=transfer_mode)
+                       eviction=eviction, transfer_group=transfer_group, transfer_mode=transfer_mode,
+                       carry_select=carry_select)
     try:
         run.run(log=lambda msg: print(msg, flush=True))
         records = run.records
@@ -38,7 +39,9 @@ def _run_and_compare(cfg, units, steps=None, layers=None, overlap=False, gather=
     del run
     results = CC.compare_units(cfg, units, records, eviction=eviction, log=lambda m: print(m, flush=True))
     print(CC.summarize(f"{cfg.name} [{eviction}{', overlap' if overlap else ''}"
-                       f"{', host copies' if not gather else ''}]", results), flush=True)
+                       f"{', host copies' if not gather else ''}"
+                       f"{', carried selection' if carry_select else ''}]", results),
+          flush=True)
     for key, st in results.items():
         assert st["compared_steps"] == cfg.steps + 1, (key, st)
     return results
@@ -162,6 +165,9 @@ def _state_snapshot(run):
         st = rt.state[l][0]
         snap += [x.cpu().numpy().copy() for x in (st.scores, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
                                                    st.evict, st.meta, st.pool)]
+        na = st.n_attend.cpu().numpy().copy()
+        att = st.attend.cpu().numpy()
+        snap += [na, np.stack([np.where(np.arange(att.shape[1]) < n, a, -1) for a, n in zip(att, na)])]
     return snap
 
 
@@ -226,6 +232,116 @@ def _decode_step_vs_separate(cfg, runs=None, options=None):
     finally:
         for r in runs:
             r.close()
+
+
+CARRY_SHAPES = [
+    # (config, overrides): three layers, a ragged context of 301 blocks (keys per
+    # selecting thread 4), cap binding
+    ("llama8b_32k", dict(batch=2, layers=3, ctx=16 * 300 + 7, steps=5, fetch_cap=8, planted=15,
+                         budget_tokens=16 * 32)),
+    # two layers of one request with 2048 blocks, the full budget (128 blocks) and cap (16 keys per thread)
+    ("llama8b_32k", dict(batch=1, layers=2, steps=4)),
+    # 8192 blocks over two KV heads (64 keys per thread)
+    ("llama8b_128k", dict(batch=1, kv_heads=2, layers=2, steps=3)),
+    # a prompt length per request
+    ("llama8b_32k", dict(batch=5, layers=2, steps=4, fetch_cap=8, planted=6, budget_tokens=16 * 32,
+                         ctx_list=(16 * 16 * 4 + 5, 16 * 16 * 3 + 1, 16 * 16 * 9 + 16, 16 * 16 * 6 + 9,
+                                   16 * 16 * 12 - 5))),
+    # appends (the newest block turns over) with two layers
+    ("qwen8b_reason", dict(batch=2, layers=2, ctx=16 * 40 + 13, steps=20, recency_blocks=8, planted=4,
+                           budget_tokens=16 * 16, fetch_cap=3)),
+    # 40 attention rows and 32 scoring rows, three layers
+    ("qwen32b_32k", dict(batch=1, layers=3, ctx=16 * 200, steps=4, planted=10, budget_tokens=16 * 24,
+                         fetch_cap=4, drift_blocks=0)),
+    # k = 2 (no candidates to rank, one attention split), cap = k, no cap, one layer
+    ("llama8b_32k", dict(batch=2, layers=2, ctx=16 * 40, steps=3, fetch_cap=2, planted=1, budget_tokens=32)),
+    ("llama8b_32k", dict(batch=2, layers=2, ctx=16 * 90 + 1, steps=4, fetch_cap=16, planted=6,
+                         budget_tokens=16 * 16)),
+    ("llama8b_32k", dict(batch=2, layers=2, ctx=16 * 90 + 1, steps=3, fetch_cap=0, planted=6,
+                         budget_tokens=16 * 16)),
+    ("llama8b_32k", dict(batch=2, layers=1, ctx=16 * 300 + 7, steps=4, fetch_cap=8, planted=15,
+                         budget_tokens=16 * 32)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CARRY_SHAPES)
+def test_carry_step_matches_decode_step(name, kw):
+    """Each layer's selection and diff carried by the next layer's first launch
+    (the last layer's run on its own at the end of each step) leave
+    bit-identical outputs and state, attended list included, to the decode step
+    that selects in its own second launch, step after step."""
+    cfg = CONFIGS[name].with_(**kw)
+    print(f"{name} {kw}", flush=True)
+    _decode_step_vs_separate(cfg, runs=[SyntheticRun(cfg, overlap=False, carry_select=c) for c in (True, False)])
+
+
+def _outputs_without_step_syncs(cfg, **kw):
+    """All steps enqueued back to back (carried selections and inline transfers
+    cross step boundaries); every layer's output copied on the stream; the
+    final state after one flush."""
+    run = SyntheticRun(cfg, overlap=False, **kw)
+    try:
+        run.prologue()
+        torch.cuda.synchronize()
+        rt = run.rt
+        outs = torch.empty((cfg.steps, run.L) + tuple(rt.out.shape), dtype=rt.out.dtype, device="cuda")
+        for t in range(cfg.steps):
+            for l in range(run.L):
+                q = run.q[l, t + 1]
+                if cfg.append:
+                    rt.append(l, run.k_new_dev[l, t], run.v_new_dev[l, t], run.k_new_host[l, t],
+                              run.v_new_host[l, t])
+                rt.decode_step(l, q, stamp=t + 1)
+                outs[t, l].copy_(rt.out)
+                run._transfer_after(l)
+            rt.end_step()
+        rt.wait_transfers()
+        torch.cuda.synchronize()
+        return outs.cpu().numpy(), _state_snapshot(run)[1:]
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("layers,mode", [(3, "side"), (3, "inline"), (5, "inline"), (2, "inline"), (1, "side")])
+def test_carry_across_steps(layers, mode):
+    """Carried selections and transfers pending across step boundaries (the last
+    layer's selection rides in the next step's first layer): every output and
+    the final state bit-identical to the decode step that selects itself."""
+    cfg = CONFIGS["llama8b_32k"].with_(batch=1, layers=layers, ctx=16 * 150 + 3, steps=6, planted=8,
+                                       budget_tokens=16 * 16, fetch_cap=4)
+    ref_out, ref_state = _outputs_without_step_syncs(cfg, transfer_mode=mode)
+    out, state = _outputs_without_step_syncs(cfg, transfer_mode=mode, carry_select=True)
+    for t in range(cfg.steps):
+        for l in range(layers):
+            assert np.array_equal(out[t, l], ref_out[t, l]), (t, l)
+    for i, (a, b) in enumerate(zip(state, ref_state)):
+        assert np.array_equal(a, b), i
+
+
+@pytest.mark.parametrize("layers,mode", [(3, "side"), (3, "inline")])
+def test_chain_carry_small(layers, mode):
+    """Carried selections against the oracle over a chain, every unit of every layer."""
+    cfg = CONFIGS["llama8b_32k"].with_(batch=2, layers=layers, ctx=16 * 300 + 7, steps=6, fetch_cap=8,
+                                       planted=15, budget_tokens=16 * 32)
+    _run_and_compare(cfg, [(l, u) for l in range(layers) for u in range(cfg.batch * cfg.kv_heads)],
+                     transfer_mode=mode, carry_select=True)
+
+
+@pytest.mark.timeout(1100)
+def test_chain_llama8b_128k_full_layer_carry():
+    """The 128K workload with every layer's selection carried by the next
+    layer's first launch: every unit of layer 2, two sampled units of the rest."""
+    cfg = CONFIGS["llama8b_128k"]
+    _run_and_compare(cfg, _layer_plus_samples(cfg, 2, 2, seed=129), carry_select=True)
+
+
+@pytest.mark.timeout(1100)
+def test_chain_qwen32b_32k_full_layer_carry():
+    """The Qwen3-32B-shaped workload (without the drift, which rebuilds metadata
+    mid-step) with carried selections: every unit of layer 6, two sampled units
+    of the rest."""
+    cfg = CONFIGS["qwen32b_32k"].with_(drift_blocks=0)
+    _run_and_compare(cfg, _layer_plus_samples(cfg, 6, 2, seed=33), carry_select=True)
 
 
 @pytest.mark.timeout(1100)
