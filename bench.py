@@ -72,9 +72,10 @@ def parse():
                    help="cross-layer transfer pipeline: exposed transfer per step against the fetch cap "
                         "(one JSON line per sweep instead of the headline)")
     p.add_argument("--layers", type=int, default=8, help="layers of the --pipeline run")
-    p.add_argument("--groups", default="inline,1,4",
+    p.add_argument("--groups", default="carry,inline,1,4",
                    help="--pipeline: layers per side-stream transfer batch (one hand-off and one event each), "
-                        "or 'inline' (each layer's pages ride in the next decode step's first launch)")
+                        "'inline' (each layer's pages ride in the next decode step's first launch), or 'carry' "
+                        "(as inline, with each layer's selection also carried by the next layer's first launch)")
     p.add_argument("--recall", action="store_true",
                    help="prediction recall of the drafts' selection against the verify query's own selection, "
                         "and the cost of a blocking corrective fetch (one JSON line)")
@@ -82,12 +83,15 @@ def parse():
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
                    help="--pipeline eviction policies: lowest score, least recently used, or both")
-    p.add_argument("--mode", choices=["graph", "overlap", "eager", "two_streams", "two_streams_graph"], default="eager",
+    p.add_argument("--mode", choices=["auto", "graph", "overlap", "eager", "carry", "two_streams",
+                                      "two_streams_graph"], default="auto",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
                         "second stream beside the attention, captured likewise; eager: plain launches; "
-                        "two_streams: plain launches, each layer's selection and diff on a second stream "
-                        "beside the next layer's attention and scoring; two_streams_graph: the same captured "
-                        "as a HIP graph")
+                        "carry: plain launches, each layer's selection and diff carried by the next layer's "
+                        "first launch (several layers only); two_streams: plain launches, each layer's "
+                        "selection and diff on a second stream beside the next layer's attention and scoring; "
+                        "two_streams_graph: the same captured as a HIP graph; auto: carry for several layers, "
+                        "else eager")
     return p.parse_args()
 
 
@@ -425,8 +429,11 @@ def pipeline_sweep(args):
     nf_tot = torch.zeros((), dtype=torch.int64, device="cuda")
     points = []
     # layers per side-stream batch; 0 ("inline"): each layer's pages ride in the next
-    # decode step's first launch on the compute stream (oasis_decode_step_gather)
-    groups = [0 if x.strip() == "inline" else int(x) for x in args.groups.split(",")]
+    # decode step's first launch on the compute stream (oasis_decode_step_gather);
+    # -1 ("carry"): the same, each layer's selection carried by the next layer's
+    # first launch too (oasis_decode_step_carry), its pages by the one after
+    groups = [{"inline": 0, "carry": -1}.get(x.strip()) if x.strip() in ("inline", "carry") else int(x)
+              for x in args.groups.split(",")]
     runs = [(p, c, g) for p in policies for c in caps
             for g in (groups if p == policies[0] else [x for x in groups if x > 0][-1:])]
     for policy, cap, group in runs:
@@ -437,6 +444,12 @@ def pipeline_sweep(args):
         clock = [0]
 
         pending = [None]  # inline: the layer whose fetched pages await the next launch
+        pending_sel = [None]  # carry: the layer whose selection awaits the next launch
+
+        def job_of(l):
+            sj = rt.state[l][0]
+            return (sj.scores, rt.ctx_len, sj.sel, sj.b2s, sj.s2b, sj.fetch, sj.n_fetch, sj.evict, sj.attend,
+                    sj.n_attend)
 
         def step(i, transfer, first=False, count=False):
             t = i % cfg.steps
@@ -444,6 +457,28 @@ def pipeline_sweep(args):
             for l in range(nl):
                 st = rt.state[l][0]
                 q = run.q[l, t + 1]
+                if group == -1:
+                    if pending_sel[0] == l:  # one layer: its own next attention needs the selection
+                        L.oasis_select_and_diff(h, *job_of(l), stream=cs)
+                        pending_sel[0] = None
+                        pending[0] = l if transfer else None
+                    carry = None
+                    if transfer and pending[0] is not None:
+                        ps_ = rt.state[pending[0]][0]
+                        if pending[0] == l:
+                            L.oasis_fetch_gather(h, ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch, cs)
+                        else:
+                            carry = (ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch)
+                        pending[0] = None
+                    js = pending_sel[0]
+                    L.oasis_decode_step_carry(h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.attend,
+                                              st.n_attend, st.scores, rt.out, rt.ws_ptr,
+                                              job=None if js is None else job_of(js), transfer=carry, stream=cs)
+                    if count and js is not None:
+                        nf_tot.add_(rt.state[js][0].n_fetch.sum())
+                    pending[0] = js if transfer else None
+                    pending_sel[0] = l
+                    continue
                 if group == 0:
                     pl = pending[0]
                     carry = None
@@ -483,7 +518,15 @@ def pipeline_sweep(args):
                         L.oasis_fetch_gather(h, sl.host_tier, sl.pool, sl.fetch, sl.n_fetch, side)
                     ev_fetch[gi].record(side)
 
-        def flush():
+        def flush(transfer=True):
+            if pending_sel[0] is not None:
+                js = pending_sel[0]
+                L.oasis_select_and_diff(h, *job_of(js), stream=cs)
+                pending_sel[0] = None
+                if transfer and pending[0] is not None:
+                    ps_ = rt.state[pending[0]][0]
+                    L.oasis_fetch_gather(h, ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch, cs)
+                pending[0] = js if transfer else None
             if pending[0] is not None:
                 ps_ = rt.state[pending[0]][0]
                 L.oasis_fetch_gather(h, ps_.host_tier, ps_.pool, ps_.fetch, ps_.n_fetch, cs)
@@ -494,12 +537,13 @@ def pipeline_sweep(args):
         for transfer in (False, True):
             for i in range(args.warmup):
                 step(i, transfer, first=(i == 0))
+            flush(transfer)
             cs.wait_stream(side)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for i in range(K):
                 step(i, transfer)
-            flush()
+            flush(transfer)
             cs.wait_stream(side)
             torch.cuda.synchronize()
             res[transfer] = (time.perf_counter() - t0) / K * 1e6
@@ -541,8 +585,10 @@ def pipeline_sweep(args):
                 "moved: layers_per_transfer > 0: by the device-driven gather on a side stream, that many layers "
                 "handing their gathers over as one batch behind one event, each batch's layers waiting at the "
                 "next step for that batch only; 0: inline, each layer's gather carried by the next decode "
-                "step's first launch on the compute stream (no second stream, no event); every (policy, cap, "
-                "batch) run starts from the same state"}))
+                "step's first launch on the compute stream (no second stream, no event); -1: carry, each "
+                "layer's selection and diff carried by the next layer's first launch and its gather by the one "
+                "after (H1 is then the carried step's own time); every (policy, cap, batch) run starts from "
+                "the same state"}))
 
 
 def recall_measure(args):
@@ -648,6 +694,11 @@ def main():
     from workload import CONFIGS
 
     cfg = CONFIGS[args.config]
+    if args.mode == "auto":
+        args.mode = "carry" if cfg.layers > 1 else "eager"
+    if args.mode == "carry" and cfg.layers < 2:
+        raise SystemExit("--mode carry needs several layers: with one layer the next step's attention needs the "
+                         "selection that would be carried")
     cpu = None
     if not args.no_cpu_baseline:
         # first, before anything initialises the GPU: the worker processes start clean
@@ -721,6 +772,30 @@ def main():
                                 st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
                                 st.n_attend, stream=cs)
 
+    pending = [None]
+
+    def carry_step(i, cs):
+        """One decode step over all layers with each layer's selection and diff
+        carried by the next call's first launch (the last layer's by the next
+        step's first layer): per layer, one call of two launches, the second
+        being the split combine alone."""
+        rep = i % replicas
+        t = i % cfg.steps
+        for l in range(run.L):
+            q = run.q[l, t + 1]
+            st = rt.state[l][rep]
+            L.oasis_decode_step_carry(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.attend, st.n_attend,
+                                      st.scores, rt.out, rt.ws_ptr, job=pending[0], stream=cs)
+            pending[0] = (st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, st.attend,
+                          st.n_attend)
+
+    def carry_flush(cs):
+        """The selection still pending after the last step, as a launch of its own."""
+        if pending[0] is not None:
+            j = pending[0]
+            L.oasis_select_and_diff(rt.h, j[0], j[1], j[2], j[3], j[4], j[5], j[6], j[7], j[8], j[9], stream=cs)
+            pending[0] = None
+
     ev_scored = torch.cuda.Event()
     ev_state = [[torch.cuda.Event() for _ in range(replicas)] for _ in range(run.L)]
 
@@ -751,8 +826,11 @@ def main():
     for i in range(args.warmup):
         if args.mode.startswith("two_streams"):
             two_stream_step(i, cs0)
+        elif args.mode == "carry":
+            carry_step(i, cs0)
         else:
             sequential_step(i, cs0)
+    carry_flush(cs0)
     torch.cuda.synchronize()
 
     def attended():
@@ -771,7 +849,7 @@ def main():
     G = 2 * replicas
     cs = torch.cuda.current_stream()
     graph = None
-    if args.mode != "eager" and args.mode != "two_streams":
+    if args.mode not in ("eager", "two_streams", "carry"):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             gs = torch.cuda.current_stream()
@@ -801,8 +879,12 @@ def main():
                 cs.wait_stream(ps)
             elif args.mode.startswith("two_streams"):
                 two_stream_step(j, cs)
+            elif args.mode == "carry":
+                carry_step(j, cs)
             else:
                 sequential_step(j, cs)
+        if args.mode == "carry":
+            carry_flush(cs)  # every step's selection inside the timed region
 
     # Every event-timed region starts with a short spin kernel ahead of its begin
     # event: the GPU stays busy while the host enqueues the first calls, so the
@@ -884,6 +966,18 @@ def main():
     e_end.record(cs0)
     torch.cuda.synchronize()
     step_call_us = e_beg.elapsed_time(e_end) * 1e3 / (args.steps * run.L)
+    # the same with each layer's selection carried by the next call (several layers)
+    carry_call_us = None
+    if run.L > 1:
+        torch.cuda.synchronize()
+        lead()
+        e_beg.record(cs0)
+        for i in range(args.steps):
+            carry_step(i, cs0)
+        carry_flush(cs0)
+        e_end.record(cs0)
+        torch.cuda.synchronize()
+        carry_call_us = e_beg.elapsed_time(e_end) * 1e3 / (args.steps * run.L)
     attended_after = attended()
 
     h2 = None if args.no_h2 else measure_h2(args, cfg, run, rt, replicas, sequential_step, step_call_us)
@@ -973,11 +1067,15 @@ def main():
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
                       "eager": "one decode-step call per layer (2 launches) on one stream",
+                      "carry": "one call per layer (2 launches) on one stream whose first launch carries the "
+                               "previous layer's selection and diff (the last layer's in the next step's first "
+                               "layer; the last step's run on its own) and whose second is the split combine",
                       "two_streams": "per layer: attention + scoring, then the split combine, on one stream; "
                                   "the selection and diff on a second stream beside the next layer",
                       "two_streams_graph": f"HIP graph of {G} steps of the two_streams mode"}[args.mode],
         "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
         "decode_step_call_us": step_call_us,
+        "decode_step_carry_call_us": carry_call_us,
         "headline_timing": {"clock": "HIP events on the compute stream around the K timed steps, after a "
                                      f"{LEAD_US:g} us spin kernel that keeps the GPU busy while the host enqueues "
                                      "the first steps",
