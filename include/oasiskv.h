@@ -264,7 +264,11 @@ int oasis_resident_diff_cap_evict(oasis_handle h, const int32_t* sel, const floa
  * arguments, with identical results, in one launch when the shape allows it
  * (max_blocks <= 8192 and budget_blocks <= 514; otherwise the two kernels run
  * back to back).  Saves a launch and a round trip of the selection through
- * global memory on every decode step.
+ * global memory on every decode step.  For budget_blocks <= 128 each (request,
+ * KV head) is selected and diffed by one workgroup that reads residency from
+ * slot_to_block alone: block_to_slot must be its inverse, as every diff,
+ * fetch and admission here leaves it (the decode-step calls read it the same
+ * way).
  */
 int oasis_select_and_diff(oasis_handle h, const float* scores, const int32_t* ctx_len, int32_t* sel,
                           int32_t* block_to_slot, int32_t* slot_to_block, int32_t* fetch,
@@ -491,8 +495,7 @@ typedef struct oasis_select_job {
  * `scores`, `attend` or the transfer's fetch list (EINVAL).  The block map is
  * read only as the inverse of the slot map, as every diff leaves them.
  * EUNSUPPORTED unless bf16, head_dim 128, 2 attention wavefronts per
- * workgroup, budget_blocks <= 128, fetch_cap <= budget_blocks and
- * max_blocks <= 8192 (score eviction).
+ * workgroup, budget_blocks <= 128 and max_blocks <= 8192 (score eviction).
  */
 int oasis_decode_step_carry(oasis_handle h, const void* q, const void* pool, const void* meta,
                             const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* attend,

@@ -858,8 +858,8 @@ int oasis_decode_step_carry(oasis_handle h, const void* q, const void* pool, con
     return fail(OASIS_EINVAL, "oasis_decode_step_carry: workspace not 256-byte aligned");
   if (!oasis::attn_score_select_available(h->c))
     return fail(OASIS_EUNSUPPORTED,
-                "oasis_decode_step_carry: needs bf16, head_dim 128, 2 attention wavefronts, k <= 128, "
-                "fetch_cap <= k and max_blocks <= 8192");
+                "oasis_decode_step_carry: needs bf16, head_dim 128, 2 attention wavefronts, k <= 128 "
+                "and max_blocks <= 8192");
   oasis::SelectJob sj;
   if (job != nullptr) {
     CHECK_PTR(job->scores);

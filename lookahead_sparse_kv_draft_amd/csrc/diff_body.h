@@ -236,15 +236,18 @@ __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, c
                                  int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict,
                                  int32_t* __restrict__ attend, int32_t* __restrict__ n_attend,
                                  unsigned long long* lds) {
+  // at most k blocks are fetched or evicted per step: the lists in LDS need
+  // min(cap, k) entries (the fetch / evict lists in memory are cap long)
+  const int capL = min(cap, kb);
   unsigned long long* candK = lds;
   const int nwords = (Nmax + 31) / 32;
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(candK + kb);
   int32_t* F = reinterpret_cast<int32_t*>(bitmap + nwords);
-  int32_t* tgt = F + cap;
-  int32_t* freeS = tgt + cap;
+  int32_t* tgt = F + capL;
+  int32_t* freeS = tgt + capL;
   int32_t* vict = freeS + kb;
-  int32_t* victS = vict + cap;
-  int32_t* candS = victS + cap;
+  int32_t* victS = vict + capL;
+  int32_t* candS = victS + capL;
   int32_t* candA = candS + kb;  // LRU: the candidates' stamps
 
   const int lane = threadIdx.x & (kWave - 1);

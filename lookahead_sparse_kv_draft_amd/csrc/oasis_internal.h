@@ -84,6 +84,9 @@ struct LruState {
   int step = 0;
 };
 bool select_diff_lru_available(const Ctx& c);
+// Budgets of at most 128 blocks and N_max <= 8192: the selection and diff of a
+// unit run in one workgroup (select_wg.h) in every launch that selects.
+bool select_wg_available(const Ctx& c);
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                               int32_t* attend, int32_t* n_attend, hipStream_t st, LruState lru = {});
@@ -121,12 +124,13 @@ hipError_t launch_attn_and_score(const Ctx& c, const void* q, const void* pool, 
                                  const int32_t* ctx_attn, float* out, void* ws, const void* meta,
                                  const int32_t* ctx_score, float* scores, hipStream_t st,
                                  const StepGather& g = StepGather());
-// Another state's top-k selection and resident-set diff carried by the step's
-// first launch (one workgroup per unit ahead of the attention and scoring):
-// that state's scores, written by an earlier launch, the context length its
-// scoring saw, and the state the diff updates.  None of it may be memory the
-// launch's own attention or scoring reads or writes.  Score eviction,
-// k <= 128, cap <= k, N_max <= 8192, bf16, head_dim 128, 2 attention wavefronts.
+// One state's top-k selection and resident-set diff run by one workgroup per
+// unit (select_wg.h): its scores (complete: written by an earlier launch), the
+// context length its scoring saw, the state the diff updates, and for
+// least-recently-used eviction the per-slot stamps and the step number the diff
+// stamps.  Carried by the step's first launch, none of it may be memory that
+// launch's own attention or scoring reads or writes (score eviction, k <= 128,
+// N_max <= 8192, bf16, head_dim 128, 2 attention wavefronts).
 struct SelectJob {
   const float* scores = nullptr;
   const int32_t* ctx_len = nullptr;
@@ -138,6 +142,8 @@ struct SelectJob {
   int32_t* evict = nullptr;
   int32_t* attend = nullptr;
   int32_t* n_attend = nullptr;
+  int32_t* last_use = nullptr;
+  int step = 0;
 };
 bool attn_score_select_available(const Ctx& c);
 // The attention (from the attended list) and the lookahead score in one launch

@@ -37,6 +37,7 @@
 #include "block_ops.h"
 #include "attn_combine.h"
 #include "diff_body.h"
+#include "select_wg.h"
 #include "topk_body.h"
 
 namespace oasis {
@@ -201,27 +202,24 @@ __global__ __launch_bounds__(1024) void topk_fast_kernel(const float* __restrict
   topk_fast_body<kTkThreads, KPT>(v, n, blockIdx.x, sel, Nmax, kb, nullptr, sh);
 }
 
-// Dynamic LDS of the fused selection + diff: the diff's arrays, the selection
-// (k ints), and for k <= 128 this unit's block_to_slot row and the candidates'
-// order keys (N_max ints each).
+// Dynamic LDS of the fused selection + diff for budgets above 128 blocks: the
+// diff's arrays and the selection (k ints).
 inline size_t select_diff_lds_bytes(int kb, int Nmax, int cap) {
-  return diff_lds_bytes(kb, Nmax, cap) + static_cast<size_t>(kb) * 4 +
-         (kb <= kDiffWaveMaxBudget ? static_cast<size_t>(Nmax) * 8 : 0);
+  return diff_lds_bytes(kb, Nmax, cap) + static_cast<size_t>(kb) * 4;
 }
 
-// Fused selection + diff of one unit by a 1024-thread workgroup.  The
-// selection's score loads go out first, the diff's loads behind them stay in
-// flight through the selection, which reaches the diff through LDS.  For
-// k <= 128 the block_to_slot row is staged in LDS during the selection and a
-// single wavefront runs the diff with no barrier; otherwise every wavefront
-// takes part (diff_body).
+// Fused selection + diff of one unit by a 1024-thread workgroup, for budgets
+// above 128 blocks (select_wg.h covers the rest): the selection's score loads
+// go out first, the diff's loads behind them stay in flight through the
+// selection, which reaches the diff through LDS; every wavefront takes part in
+// the diff (diff_body).
 template <int KPT>
 __device__ __forceinline__ void select_diff_unit(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
-    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step,
-    unsigned long long* smem_u64, TopkFastShared<kTkThreads>& sh, DiffShared& dsh) {
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, unsigned long long* smem_u64,
+    TopkFastShared<kTkThreads>& sh, DiffShared& dsh) {
   int32_t* selL = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(smem_u64) + diff_lds_bytes(kb, Nmax, cap));
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
@@ -229,41 +227,10 @@ __device__ __forceinline__ void select_diff_unit(
   int32_t* slu = s2b + static_cast<size_t>(unit) * kb;
   const float* su = scores + static_cast<size_t>(unit) * Nmax;
   // Loads in the order that keeps one round trip before the selection starts:
-  // the scores and the map rows (independent), then the context length, then
+  // the scores and the slot map (independent), then the context length, then
   // the scores of the resident blocks (which need the slot map).
   float v[KPT];
   topk_fast_load<kTkThreads, KPT>(su, Nmax, v);
-  if (kb <= kDiffWaveMaxBudget) {
-    int32_t* b2sL = selL + kb;
-    uint32_t* keysL = reinterpret_cast<uint32_t*>(b2sL + Nmax);
-    int bv[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) bv[u] = bu[min(u * kTkThreads + tid, Nmax - 1)];
-    int sbw[2], luw[2] = {0, 0};
-    int32_t* lu = (last_use != nullptr) ? last_use + static_cast<size_t>(unit) * kb : nullptr;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int ie = min((tid & (kWave - 1)) + e * kWave, kb - 1);  // clamped: no branch around the loads
-      sbw[e] = slu[ie];
-      if (lu != nullptr) luw[e] = lu[ie];
-    }
-    const int n = ctx_len[unit / H];
-    uint32_t* bitmap = reinterpret_cast<uint32_t*>(smem_u64 + kb);
-    for (int j = tid; j < (Nmax + 31) / 32; j += kTkThreads) bitmap[j] = 0u;  // ordered by the selection's barriers
-    topk_fast_body<kTkThreads, KPT>(v, n, unit, sel, Nmax, kb, selL, sh, keysL);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      if (u * kTkThreads + tid < Nmax) b2sL[u * kTkThreads + tid] = bv[u];
-    __syncthreads();
-    if (tid >= kWave) return;
-    // the candidates' order keys as the selection computed them (block b at b - 1)
-    uint32_t kd[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) kd[e] = keysL[min(max(sbw[e] - 1, 0), Nmax - 1)];
-    diff_wave(unit, kb, Nmax, cap, selL, b2sL, sbw, kd, luw, lu, step, bu, slu, fetch, n_fetch, evict, attend,
-              n_attend, smem_u64);
-    return;
-  }
   const int sb = slu[min(tid, kb - 1)];  // clamped: no branch around the loads
   const int n = ctx_len[unit / H];
   __builtin_amdgcn_sched_barrier(0);
@@ -279,16 +246,16 @@ __global__ __launch_bounds__(1024) void select_diff_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
     int32_t* __restrict__ b2s, int32_t* __restrict__ s2b, int32_t* __restrict__ fetch,
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
-    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int32_t* __restrict__ last_use, int step) {
+    int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap) {
   extern __shared__ unsigned long long smem_u64[];
   __shared__ TopkFastShared<kTkThreads> sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
-                        last_use, step, smem_u64, sh, dsh);
+                        smem_u64, sh, dsh);
 }
 
-// The fused selection + diff in workgroups [0, units), then the attention's
-// split combine, sixteen query rows per workgroup, in the rest.
+// The same in workgroups [0, units), then the attention's split combine,
+// sixteen query rows per workgroup, in the rest.
 template <int KPT, int D, int SMAX>
 __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len, int32_t* __restrict__ sel,
@@ -296,7 +263,7 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
     int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict, int32_t* __restrict__ attend,
     int32_t* __restrict__ n_attend, int H, int Nmax, int kb, int cap, int units,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, float* __restrict__ out, int arows,
-    int splits, int comb_total, int32_t* __restrict__ last_use, int step) {
+    int splits, int comb_total) {
   if (static_cast<int>(blockIdx.x) >= units) {
     attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, arows, splits, comb_total,
                               (blockIdx.x - units) * kTkWaves + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
@@ -306,42 +273,121 @@ __global__ __launch_bounds__(1024) void select_diff_combine_kernel(
   __shared__ TopkFastShared<kTkThreads> sh;
   __shared__ DiffShared dsh;
   select_diff_unit<KPT>(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, H, Nmax, kb, cap,
-                        last_use, step, smem_u64, sh, dsh);
+                        smem_u64, sh, dsh);
 }
 
 template <int KPT, int D, int SMAX>
 hipError_t sdc_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
   const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   const int comb_total = c.units * c.rows_attn;
   const int ncomb = (comb_total + kTkWaves - 1) / kTkWaves;
   hipLaunchKernelGGL((select_diff_combine_kernel<KPT, D, SMAX>), dim3(c.units + ncomb), dim3(kTkThreads), lds, st,
                      scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads,
-                     c.s.max_blocks, kb, cap, c.units, ws_acc, ws_ml, out, c.rows_attn, c.attn_splits, comb_total,
-                     lru.last_use, lru.step);
+                     c.s.max_blocks, kb, cap, c.units, ws_acc, ws_ml, out, c.rows_attn, c.attn_splits, comb_total);
   return hipGetLastError();
 }
 
 template <int KPT, int D>
 hipError_t sdc_s(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
   const int S = c.attn_splits;
-  if (S <= 4) return sdc_t<KPT, D, 4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  if (S <= 8) return sdc_t<KPT, D, 8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  if (S <= 16) return sdc_t<KPT, D, 16>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  return sdc_t<KPT, D, 32>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (S <= 4) return sdc_t<KPT, D, 4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (S <= 8) return sdc_t<KPT, D, 8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (S <= 16) return sdc_t<KPT, D, 16>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  return sdc_t<KPT, D, 32>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
 }
 
 template <int KPT>
 hipError_t sdc_d(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                  int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st, LruState lru) {
+                 int32_t* n_attend, const float* ws_acc, const float* ws_ml, float* out, hipStream_t st) {
   return c.s.head_dim == 128
-             ? sdc_s<KPT, 128>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru)
-             : sdc_s<KPT, 64>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+             ? sdc_s<KPT, 128>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st)
+             : sdc_s<KPT, 64>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+}
+
+// ---- budgets of at most 128 blocks: one workgroup selection per unit ----
+// (select_wg.h), with the attention's split combine (NT / 64 query rows per
+// workgroup) in the workgroups after the units' when comb_total > 0.
+template <int NT, int KPT, bool LRU, int D, int SMAX>
+__global__ __launch_bounds__(NT) void select_wg_kernel(SelectJob job, int units, int H, int Nmax, int kb, int cap,
+                                                       const float* __restrict__ ws_acc,
+                                                       const float* __restrict__ ws_ml, float* __restrict__ out,
+                                                       int arows, int splits, int comb_total) {
+  __shared__ SelectLds<NT> lds;
+  if (static_cast<int>(blockIdx.x) < units) {
+    select_diff_wg<NT, KPT, LRU>(job, blockIdx.x, H, Nmax, kb, cap, lds);
+    return;
+  }
+  attn_combine_row<D, SMAX>(ws_acc, ws_ml, out, arows, splits, comb_total,
+                            (blockIdx.x - units) * (NT / kWave) + threadIdx.x / kWave, threadIdx.x & (kWave - 1));
+}
+
+// Workgroup size by keys per unit: 512 threads up to 2048 blocks, 1024 beyond
+// (measured in the decode step at 2048 and 8192 blocks).
+template <bool LRU, int D, int SMAX>
+hipError_t swg_t(const Ctx& c, const SelectJob& job, const float* ws_acc, const float* ws_ml, float* out,
+                 int comb_total, hipStream_t st) {
+  const int N = c.s.max_blocks;
+#define OASIS_SWG(NT, KPT)                                                                                     \
+  hipLaunchKernelGGL((select_wg_kernel<NT, KPT, LRU, D, SMAX>),                                                \
+                     dim3(c.units + (comb_total + NT / kWave - 1) / (NT / kWave)), dim3(NT), 0, st, job, c.units, \
+                     c.s.kv_heads, N, c.s.budget_blocks, c.s.fetch_cap, ws_acc, ws_ml, out, c.rows_attn,        \
+                     c.attn_splits, comb_total);                                                               \
+  return hipGetLastError()
+  if (N <= 512) { OASIS_SWG(512, 1); }
+  if (N <= 1024) { OASIS_SWG(512, 2); }
+  if (N <= 2048) { OASIS_SWG(512, 4); }
+  if (N <= 4096) { OASIS_SWG(1024, 4); }
+  OASIS_SWG(1024, 8);
+#undef OASIS_SWG
+}
+
+template <bool LRU>
+hipError_t swg_l(const Ctx& c, const SelectJob& job, const void* ws, float* out, bool combine, hipStream_t st) {
+  if (!combine) return swg_t<LRU, 128, 4>(c, job, nullptr, nullptr, nullptr, 0, st);
+  const float* ws_acc = static_cast<const float*>(ws);
+  const float* ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + attn_ws_acc_bytes(c));
+  const int comb_total = c.units * c.rows_attn;
+  const int S = c.attn_splits;
+  if (c.s.head_dim == 128) {
+    if (S <= 4) return swg_t<LRU, 128, 4>(c, job, ws_acc, ws_ml, out, comb_total, st);
+    if (S <= 8) return swg_t<LRU, 128, 8>(c, job, ws_acc, ws_ml, out, comb_total, st);
+    if (S <= 16) return swg_t<LRU, 128, 16>(c, job, ws_acc, ws_ml, out, comb_total, st);
+    return swg_t<LRU, 128, 32>(c, job, ws_acc, ws_ml, out, comb_total, st);
+  }
+  if (S <= 4) return swg_t<LRU, 64, 4>(c, job, ws_acc, ws_ml, out, comb_total, st);
+  if (S <= 8) return swg_t<LRU, 64, 8>(c, job, ws_acc, ws_ml, out, comb_total, st);
+  if (S <= 16) return swg_t<LRU, 64, 16>(c, job, ws_acc, ws_ml, out, comb_total, st);
+  return swg_t<LRU, 64, 32>(c, job, ws_acc, ws_ml, out, comb_total, st);
+}
+
+hipError_t swg_d(const Ctx& c, const SelectJob& job, const void* ws, float* out, bool combine, hipStream_t st) {
+  return job.last_use != nullptr ? swg_l<true>(c, job, ws, out, combine, st)
+                                 : swg_l<false>(c, job, ws, out, combine, st);
+}
+
+SelectJob job_of(const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s, int32_t* s2b,
+                 int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
+                 const LruState& lru) {
+  SelectJob j;
+  j.scores = scores;
+  j.ctx_len = ctx_len;
+  j.sel = sel;
+  j.b2s = b2s;
+  j.s2b = s2b;
+  j.fetch = fetch;
+  j.n_fetch = n_fetch;
+  j.evict = evict;
+  j.attend = attend;
+  j.n_attend = n_attend;
+  j.last_use = lru.last_use;
+  j.step = lru.step;
+  return j;
 }
 
 template <int KPT>
@@ -354,48 +400,55 @@ hipError_t fast_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int
 template <int KPT>
 hipError_t select_diff_t(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel, int32_t* b2s,
                          int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict, int32_t* attend,
-                         int32_t* n_attend, hipStream_t st, LruState lru) {
+                         int32_t* n_attend, hipStream_t st) {
   const int kb = c.s.budget_blocks, cap = c.s.fetch_cap;
   const size_t lds = select_diff_lds_bytes(kb, c.s.max_blocks, cap);
   hipLaunchKernelGGL((select_diff_kernel<KPT>), dim3(c.units), dim3(kTkThreads), lds, st, scores, ctx_len, sel,
-                     b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap,
-                     lru.last_use, lru.step);
+                     b2s, s2b, fetch, n_fetch, evict, attend, n_attend, c.s.kv_heads, c.s.max_blocks, kb, cap);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool select_diff_fused_available(const Ctx& c) {
-  return c.s.budget_blocks - 2 <= kTkMaxWin && c.s.max_blocks <= 8 * kTkThreads;
+bool select_wg_available(const Ctx& c) {
+  return c.s.budget_blocks <= kDiffWaveMaxBudget && c.s.max_blocks <= kSelWgMaxBlocks;
 }
 
-bool select_diff_lru_available(const Ctx& c) {
-  return select_diff_fused_available(c) && c.s.budget_blocks <= kDiffWaveMaxBudget;
+bool select_diff_fused_available(const Ctx& c) {
+  return select_wg_available(c) || (c.s.budget_blocks - 2 <= kTkMaxWin && c.s.max_blocks <= 8 * kTkThreads);
 }
+
+bool select_diff_lru_available(const Ctx& c) { return select_wg_available(c); }
 
 hipError_t launch_select_diff(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                               int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                               int32_t* attend, int32_t* n_attend, hipStream_t st, LruState lru) {
-  if (lru.last_use != nullptr && !select_diff_lru_available(c)) return hipErrorInvalidValue;
+  if (select_wg_available(c))
+    return swg_d(c, job_of(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, lru), nullptr,
+                 nullptr, false, st);
+  if (lru.last_use != nullptr) return hipErrorInvalidValue;
   const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
-  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
-  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
-  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
-  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st, lru);
+  if (kpt <= 1) return select_diff_t<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  if (kpt <= 2) return select_diff_t<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  if (kpt <= 4) return select_diff_t<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
+  return select_diff_t<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, st);
 }
 
 hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                                       int32_t* b2s, int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                                       int32_t* attend, int32_t* n_attend, const void* ws, float* out,
                                       hipStream_t st, LruState lru) {
-  if (lru.last_use != nullptr && !select_diff_lru_available(c)) return hipErrorInvalidValue;
+  if (select_wg_available(c))
+    return swg_d(c, job_of(scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, lru), ws, out,
+                 true, st);
+  if (lru.last_use != nullptr) return hipErrorInvalidValue;
   const float* ws_acc = static_cast<const float*>(ws);
   const float* ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + attn_ws_acc_bytes(c));
   const int kpt = (c.s.max_blocks + kTkThreads - 1) / kTkThreads;
-  if (kpt <= 1) return sdc_d<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  if (kpt <= 2) return sdc_d<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  if (kpt <= 4) return sdc_d<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
-  return sdc_d<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st, lru);
+  if (kpt <= 1) return sdc_d<1>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (kpt <= 2) return sdc_d<2>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  if (kpt <= 4) return sdc_d<4>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
+  return sdc_d<8>(c, scores, ctx_len, sel, b2s, s2b, fetch, n_fetch, evict, attend, n_attend, ws_acc, ws_ml, out, st);
 }
 
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,

@@ -11,7 +11,7 @@
 
 #include "attn_body.h"
 #include "score_body.h"
-#include "topk_body.h"
+#include "select_wg.h"
 
 namespace oasis {
 namespace {
@@ -45,22 +45,6 @@ __device__ __forceinline__ void gather_page(const StepGather& g, int Nmax, int k
   }
 }
 
-// Largest block count and diff LDS of a carried selection (k <= 128,
-// cap <= k): candidate keys, selection bitmap, fetch/target/victim lists, free
-// slots, candidate slots and stamps (the layout diff_wave carves).
-constexpr int kCarryMaxBlocks = 8 * 1024;
-constexpr int kCarryDiffBytes =
-    kDiffWaveMaxBudget * 8 + (kCarryMaxBlocks / 32) * 4 + (3 * kDiffWaveMaxBudget + 4 * kDiffWaveMaxBudget) * 4;
-
-template <int NT>
-struct SelectLds {
-  TopkFastShared<NT> tk;
-  int32_t selL[kDiffWaveMaxBudget];                   // the selection in rank order
-  uint32_t slot_keys[kDiffWaveMaxBudget];             // order key of the block in each slot
-  unsigned long long diff[kCarryDiffBytes / 8];        // diff_wave's arrays
-  int8_t slot_of[kCarryMaxBlocks];                     // block -> slot before the step (-1: none)
-};
-
 // The LDS of a first-launch workgroup: an attention workgroup's, overlaid with
 // a selecting workgroup's when the launch carries a selection.
 template <int D, int RT, int W, bool SEL>
@@ -74,44 +58,6 @@ struct StepLds<D, RT, W, true> {
     SelectLds<64 * W> sel;
   };
 };
-
-// The top-k selection and resident-set diff of one unit of the carried state
-// by one workgroup of NT threads: the unit's scores, slot map and context
-// length in one round trip of loads; the block -> slot table is built in LDS
-// as the inverse of the slot map (every diff keeps block_to_slot its inverse,
-// so the block map row itself is not read); then topk_body.h and diff_wave,
-// exactly as the separate selection launch computes them.
-template <int NT, int KPT>
-__device__ __forceinline__ void select_diff_wg(const SelectJob& job, int unit, int H, int Nmax, int kb, int cap,
-                                               SelectLds<NT>& sh) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  int32_t* bu = job.b2s + static_cast<size_t>(unit) * Nmax;
-  int32_t* slu = job.s2b + static_cast<size_t>(unit) * kb;
-  float v[KPT];
-  topk_fast_load<NT, KPT>(job.scores + static_cast<size_t>(unit) * Nmax, Nmax, v);
-  int sbw[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) sbw[e] = slu[min(lane + e * kWave, kb - 1)];  // clamped: no branch around the loads
-  const int sb_own = slu[min(tid, kb - 1)];  // slot tid's block, for the table
-  const int n = job.ctx_len[unit / H];
-  uint32_t* tab = reinterpret_cast<uint32_t*>(sh.slot_of);
-  for (int j = tid; j < (Nmax + 3) / 4; j += NT) tab[j] = 0xFFFFFFFFu;  // every entry -1
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sh.diff + kb);
-  for (int j = tid; j < (Nmax + 31) / 32; j += NT) bitmap[j] = 0u;
-  __syncthreads();
-  if (tid < kb && sb_own >= 0 && sb_own < Nmax) sh.slot_of[sb_own] = static_cast<int8_t>(tid);
-  __syncthreads();
-  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, nullptr, sh.slot_of, sh.slot_keys);
-  __syncthreads();
-  if (tid >= kWave) return;
-  uint32_t kd[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) kd[e] = sh.slot_keys[min(lane + e * kWave, kb - 1)];
-  const int luw[2] = {0, 0};
-  diff_wave<int8_t>(unit, kb, Nmax, cap, sh.selL, sh.slot_of, sbw, kd, luw, nullptr, 0, bu, slu, job.fetch,
-                    job.n_fetch, job.evict, job.attend, job.n_attend, sh.diff);
-}
 
 // Attention (2-page ring) and scoring workgroups in one grid of workgroups of
 // W wavefronts (W = 2, or 4 for up to two attention row tiles), led by
@@ -139,7 +85,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((RTA <= 
   }
   if constexpr (SEL) {
     if (static_cast<int>(blockIdx.x) < n_gather_wg + n_select_wg) {
-      select_diff_wg<64 * W, KPT>(job, blockIdx.x - n_gather_wg, H, Nmax, kb, cap, lds.sel);
+      select_diff_wg<64 * W, KPT, false>(job, blockIdx.x - n_gather_wg, H, Nmax, kb, cap, lds.sel);
       return;
     }
   }

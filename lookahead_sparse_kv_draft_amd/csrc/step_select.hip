@@ -11,9 +11,7 @@
 namespace oasis {
 
 bool attn_score_select_available(const Ctx& c) {
-  return attn_and_score_fused_available(c) && c.attn_waves == 2 && c.s.head_dim == 128 &&
-         c.s.budget_blocks <= kDiffWaveMaxBudget && c.s.fetch_cap <= c.s.budget_blocks &&
-         c.s.max_blocks <= kCarryMaxBlocks;
+  return attn_and_score_fused_available(c) && c.attn_waves == 2 && c.s.head_dim == 128 && select_wg_available(c);
 }
 
 hipError_t launch_attn_score_select(const Ctx& c, const void* q, const void* pool, const int32_t* attend,

@@ -246,7 +246,7 @@ def test_decode_step_carry_rejects_before_any_launch():
     finally:
         L.oasis_destroy(h)
     for kw in (dict(budget_blocks=256, fetch_cap=4), dict(head_dim=64), dict(dtype=L.OASIS_F32),
-               dict(fetch_cap=32, budget_blocks=16), dict(max_blocks=9000)):
+               dict(max_blocks=9000)):
         h = L.oasis_create(**_shape(**kw))
         try:
             assert lib.oasis_decode_step_carry(h, *args, job(), None, None) == L.OASIS_EUNSUPPORTED, kw
