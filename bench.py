@@ -35,15 +35,20 @@ CALIB_ELEMS = 2**28  # float32: 1 GiB
 CSRC = os.path.join(ROOT, "lookahead_sparse_kv_draft_amd", "csrc")
 # source files of each op's kernels (a traffic measurement is valid while they are unchanged)
 # (api.cpp holds the launch shapes)
-OP_SOURCES = {"attend_and_score": ["step.hip", "attn_body.h", "score_body.h", "oasis_internal.h", "api.cpp"],
-              "select_diff_combine": ["select.hip", "diff_body.h", "block_ops.h", "attn_combine.h",
-                                      "oasis_internal.h"],
+OP_SOURCES = {"attend_and_score": ["step.hip", "step_kernel.h", "attn_body.h", "score_body.h", "select_wg.h",
+                                   "topk_body.h", "diff_body.h", "oasis_internal.h", "api.cpp"],
+              "select_diff_combine": ["select.hip", "select_wg.h", "topk_body.h", "diff_body.h", "block_ops.h",
+                                      "attn_combine.h", "oasis_internal.h"],
               "sparse_paged_decode_attn": ["attn.hip", "attn_body.h", "attn_combine.h", "oasis_internal.h"],
               "lookahead_score": ["score.hip", "score_body.h", "oasis_internal.h"],
-              "select_and_diff": ["select.hip", "diff_body.h", "block_ops.h", "oasis_internal.h"]}
-OP_KERNELS = {"attend_and_score": ["attn_score_kernel"], "select_diff_combine": ["select_diff_combine_kernel"],
+              "select_and_diff": ["select.hip", "select_wg.h", "topk_body.h", "diff_body.h", "block_ops.h",
+                                  "oasis_internal.h"]}
+# (budgets of at most 128 blocks run the workgroup selection kernels, larger ones the
+# 1024-thread kernels; only one of each pair runs for a shape)
+OP_KERNELS = {"attend_and_score": ["attn_score_kernel"],
+              "select_diff_combine": ["select_wg_combine_kernel", "select_diff_combine_kernel"],
               "sparse_paged_decode_attn": ["attn_mfma_kernel", "attn_combine_kernel"],
-              "lookahead_score": ["score_mfma_kernel"], "select_and_diff": ["select_diff_kernel"]}
+              "lookahead_score": ["score_mfma_kernel"], "select_and_diff": ["select_wg_kernel", "select_diff_kernel"]}
 # the two launches of the decode step, then the stages on their own
 OPS = ["attend_and_score", "select_diff_combine", "sparse_paged_decode_attn", "lookahead_score", "select_and_diff"]
 

@@ -215,8 +215,8 @@ __device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, c
 // decode step's default path): lane l handles selection entries and slots l and
 // l + 64, every rank is a ballot within the wavefront, so there is no barrier at
 // all (the wavefront's LDS accesses complete in order).  selL: LDS [kb], the
-// selection; b2sL: LDS [Nmax], this unit's block_to_slot row before the step
-// (int32 or int8 entries, -1 = not resident); bitmap words in `lds` already
+// selection; b2sL: LDS [Nmax], this unit's block -> slot table before the step
+// (one byte per block, -1 = not resident); bitmap words in `lds` already
 // cleared; sb: the slot map for slots l and l + 64 (-1 / any for slots >= kb);
 // kd: the selection's order keys (desc_key of the score) of the blocks in
 // those two slots, read only for resident blocks outside the selection (the
@@ -227,9 +227,8 @@ __device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, c
 // reads are stamped with `step` ([EXPL] Table 2 runs LRU eviction).
 constexpr int kDiffWaveMaxBudget = 2 * kWave;
 
-template <typename SlotT>
 __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL,
-                                          const SlotT* b2sL, const int (&sb)[2], const uint32_t (&kd)[2],
+                                          const int8_t* b2sL, const int (&sb)[2], const uint32_t (&kd)[2],
                                           const int (&luv)[2], int32_t* __restrict__ lu, int step,
                                           int32_t* __restrict__ bu,
                                  int32_t* __restrict__ slu, int32_t* __restrict__ fetch,

@@ -311,13 +311,20 @@ hipError_t sdc_d(const Ctx& c, const float* scores, const int32_t* ctx_len, int3
 }
 
 // ---- budgets of at most 128 blocks: one workgroup selection per unit ----
-// (select_wg.h), with the attention's split combine (NT / 64 query rows per
-// workgroup) in the workgroups after the units' when comb_total > 0.
+// (select_wg.h), alone, or with the attention's split combine (NT / 64 query
+// rows per workgroup) in the workgroups after the units'.
+template <int NT, int KPT, bool LRU>
+__global__ __launch_bounds__(NT) void select_wg_kernel(SelectJob job, int H, int Nmax, int kb, int cap) {
+  __shared__ SelectLds<NT> lds;
+  select_diff_wg<NT, KPT, LRU>(job, blockIdx.x, H, Nmax, kb, cap, lds);
+}
+
 template <int NT, int KPT, bool LRU, int D, int SMAX>
-__global__ __launch_bounds__(NT) void select_wg_kernel(SelectJob job, int units, int H, int Nmax, int kb, int cap,
-                                                       const float* __restrict__ ws_acc,
-                                                       const float* __restrict__ ws_ml, float* __restrict__ out,
-                                                       int arows, int splits, int comb_total) {
+__global__ __launch_bounds__(NT) void select_wg_combine_kernel(SelectJob job, int units, int H, int Nmax, int kb,
+                                                               int cap, const float* __restrict__ ws_acc,
+                                                               const float* __restrict__ ws_ml,
+                                                               float* __restrict__ out, int arows, int splits,
+                                                               int comb_total) {
   __shared__ SelectLds<NT> lds;
   if (static_cast<int>(blockIdx.x) < units) {
     select_diff_wg<NT, KPT, LRU>(job, blockIdx.x, H, Nmax, kb, cap, lds);
@@ -329,27 +336,43 @@ __global__ __launch_bounds__(NT) void select_wg_kernel(SelectJob job, int units,
 
 // Workgroup size by keys per unit: 512 threads up to 2048 blocks, 1024 beyond
 // (measured in the decode step at 2048 and 8192 blocks).
+#define OASIS_SWG_BY_SIZE(LAUNCH)                \
+  do {                                           \
+    const int N = c.s.max_blocks;                \
+    if (N <= 512) { LAUNCH(512, 1); }            \
+    if (N <= 1024) { LAUNCH(512, 2); }           \
+    if (N <= 2048) { LAUNCH(512, 4); }           \
+    if (N <= 4096) { LAUNCH(1024, 4); }          \
+    LAUNCH(1024, 8);                             \
+  } while (0)
+
 template <bool LRU, int D, int SMAX>
 hipError_t swg_t(const Ctx& c, const SelectJob& job, const float* ws_acc, const float* ws_ml, float* out,
                  int comb_total, hipStream_t st) {
-  const int N = c.s.max_blocks;
-#define OASIS_SWG(NT, KPT)                                                                                     \
-  hipLaunchKernelGGL((select_wg_kernel<NT, KPT, LRU, D, SMAX>),                                                \
+#define OASIS_SWGC(NT, KPT)                                                                                     \
+  hipLaunchKernelGGL((select_wg_combine_kernel<NT, KPT, LRU, D, SMAX>),                                          \
                      dim3(c.units + (comb_total + NT / kWave - 1) / (NT / kWave)), dim3(NT), 0, st, job, c.units, \
-                     c.s.kv_heads, N, c.s.budget_blocks, c.s.fetch_cap, ws_acc, ws_ml, out, c.rows_attn,        \
-                     c.attn_splits, comb_total);                                                               \
+                     c.s.kv_heads, c.s.max_blocks, c.s.budget_blocks, c.s.fetch_cap, ws_acc, ws_ml, out,        \
+                     c.rows_attn, c.attn_splits, comb_total);                                                   \
   return hipGetLastError()
-  if (N <= 512) { OASIS_SWG(512, 1); }
-  if (N <= 1024) { OASIS_SWG(512, 2); }
-  if (N <= 2048) { OASIS_SWG(512, 4); }
-  if (N <= 4096) { OASIS_SWG(1024, 4); }
-  OASIS_SWG(1024, 8);
-#undef OASIS_SWG
+  OASIS_SWG_BY_SIZE(OASIS_SWGC);
+#undef OASIS_SWGC
 }
 
 template <bool LRU>
+hipError_t swg_alone(const Ctx& c, const SelectJob& job, hipStream_t st) {
+#define OASIS_SWGA(NT, KPT)                                                                                 \
+  hipLaunchKernelGGL((select_wg_kernel<NT, KPT, LRU>), dim3(c.units), dim3(NT), 0, st, job, c.s.kv_heads,   \
+                     c.s.max_blocks, c.s.budget_blocks, c.s.fetch_cap);                                      \
+  return hipGetLastError()
+  OASIS_SWG_BY_SIZE(OASIS_SWGA);
+#undef OASIS_SWGA
+}
+#undef OASIS_SWG_BY_SIZE
+
+template <bool LRU>
 hipError_t swg_l(const Ctx& c, const SelectJob& job, const void* ws, float* out, bool combine, hipStream_t st) {
-  if (!combine) return swg_t<LRU, 128, 4>(c, job, nullptr, nullptr, nullptr, 0, st);
+  if (!combine) return swg_alone<LRU>(c, job, st);
   const float* ws_acc = static_cast<const float*>(ws);
   const float* ws_ml = reinterpret_cast<const float*>(static_cast<const char*>(ws) + attn_ws_acc_bytes(c));
   const int comb_total = c.units * c.rows_attn;

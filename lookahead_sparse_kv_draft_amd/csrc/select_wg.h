@@ -60,13 +60,13 @@ __device__ __forceinline__ void select_diff_wg(const SelectJob& job, int unit, i
   __syncthreads();
   if (tid < kb && sb_own >= 0 && sb_own < Nmax) sh.slot_of[sb_own] = static_cast<int8_t>(tid);
   __syncthreads();
-  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, nullptr, sh.slot_of, sh.slot_keys);
+  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, sh.slot_of, sh.slot_keys);
   __syncthreads();
   if (tid >= kWave) return;
   uint32_t kd[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) kd[e] = sh.slot_keys[min(lane + e * kWave, kb - 1)];
-  diff_wave<int8_t>(unit, kb, Nmax, cap, sh.selL, sh.slot_of, sbw, kd, luw, lu, job.step, bu, slu, job.fetch,
+  diff_wave(unit, kb, Nmax, cap, sh.selL, sh.slot_of, sbw, kd, luw, lu, job.step, bu, slu, job.fetch,
                     job.n_fetch, job.evict, job.attend, job.n_attend, sh.diff);
 }
 

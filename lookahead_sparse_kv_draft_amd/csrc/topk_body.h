@@ -77,18 +77,14 @@ __device__ __forceinline__ void topk_fast_load(const float* __restrict__ su, int
 // The selection of unit `unit` from the scores topk_fast_load returned and the
 // request's context length n (read by the caller before anything else, so its
 // round trip overlaps the scores'); written to sel and, in rank order and -1
-// padded, to the LDS array selL when it is not null.  keysL (LDS, Nmax
-// entries, or null) receives every candidate's order key at index block - 1
-// (0xFFFFFFFF past the candidates), before any early return, for a diff that
-// ranks eviction victims by the same keys.  Alternatively slot_keys (LDS, one
-// entry per slot) receives the order key of the block each slot holds, from
-// the LDS table slot_of (block -> slot, -1 = none; complete on entry): the keys
-// of the resident blocks only.
+// padded, to the LDS array selL when it is not null.  slot_keys (LDS, one entry
+// per slot, or null) receives the order key of the block each slot holds, from
+// the LDS table slot_of (block -> slot, -1 = none; complete on entry), before
+// any early return: the diff ranks eviction victims by the same keys.
 template <int NT, int KPT>
 __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int unit, int32_t* __restrict__ sel,
                                                int Nmax, int kb, int32_t* selL, TopkFastShared<NT>& sh,
-                                               uint32_t* keysL = nullptr, const int8_t* slot_of = nullptr,
-                                               uint32_t* slot_keys = nullptr) {
+                                               const int8_t* slot_of = nullptr, uint32_t* slot_keys = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int BPT = kTkBins / NT;  // consecutive histogram bins per thread
   static_assert(BPT * NT == kTkBins, "the bins are spread evenly over the threads");
@@ -117,7 +113,6 @@ __device__ __forceinline__ void topk_fast_body(const float (&v)[KPT], int n, int
   for (int u = 0; u < KPT; ++u) {
     const int c = u * NT + tid;
     key[u] = (c < C) ? desc_key(v[u]) : 0xFFFFFFFFu;
-    if (keysL != nullptr && c < Nmax) keysL[c] = key[u];
     if (slot_keys != nullptr && c + 1 < Nmax) {
       const int s = slot_of[c + 1];
       if (s >= 0) slot_keys[s] = key[u];
