@@ -638,6 +638,11 @@ def test_fetch_gather_matches_fetch_issue(dtype, d):
     # resident blocks must still be ranked as victims by their order keys
     (2, 2, [16 * 100, 16 * 37 + 5, 33, 16], "normal"),
     (2, 1, [16 * 300, 16 * 64, 16 * 3, 100], "ties"),
+    # the workgroup selection's larger sizes: 1024 threads with 4 and 8 keys each
+    (128, 32, [16 * 3000, 16 * 2100, 16 * 700, 16 * 2049], "normal"),
+    (128, 16, [131072, 16 * 5000, 16 * 4097, 16 * 300], "ties"),
+    # a cap above the budget (at most k blocks move; the lists are cap long)
+    (64, 100, [16 * 700, 16 * 64, 16 * 200, 40], "normal"),
 ])
 def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
     B, H = len(ctxs), 3
@@ -697,6 +702,7 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
 @pytest.mark.parametrize("k,cap,N,kind,steps", [
     (128, 32, 2048, "normal", 6), (128, 8, 700, "ties", 6), (16, 4, 64, "normal", 8),
     (64, 64, 300, "normal", 5), (128, 0, 500, "normal", 3), (8, 3, 40, "const", 6), (2, 2, 9, "normal", 4),
+    (128, 32, 5000, "normal", 4), (32, 50, 200, "normal", 4),
 ])
 def test_select_and_diff_lru_parity(k, cap, N, kind, steps):
     """Several steps in a row of selection + diff with least-recently-used
