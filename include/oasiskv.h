@@ -163,6 +163,19 @@ int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* pag
                            const int32_t* block_to_slot, void* stream);
 
 /*
+ * The block metadata from key rows, the form the method states it in ([EXPL]
+ * Figure 7 left: per-block min/max pooling of the keys): k_rows
+ * [B][H][max_blocks*16][d] token-major on the device (element type, 16-byte
+ * aligned).  For every request r, every block b that tokens [tok_begin,
+ * tok_end) fall in and that holds tokens below ctx_len[r] gets its metadata
+ * row from all of its tokens below ctx_len[r] (also those outside the range).
+ * Other blocks are not touched.  EINVAL unless
+ * 0 <= tok_begin <= tok_end <= max_blocks*16.
+ */
+int oasis_block_meta_build_rows(oasis_handle h, const void* k_rows, int32_t tok_begin, int32_t tok_end,
+                                const int32_t* ctx_len, void* meta, void* stream);
+
+/*
  * The block metadata in its logical layout ([EXPL] Figure 7 left: per-block,
  * per-channel key min and max): meta_logical is [B][H][max_blocks][2][d]
  * elements (device, 16-byte aligned, oasis_meta_bytes() covers it), block b's

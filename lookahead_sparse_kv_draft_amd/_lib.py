@@ -74,6 +74,7 @@ SIGNATURES = {
     "oasis_host_tier_append": (_int, [_vp, _vp, _vp, _vp, _vp]),
     "oasis_block_meta_build": (_int, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "oasis_block_meta_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "oasis_block_meta_build_rows": (_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "oasis_block_meta_export": (_int, [_vp, _vp, _vp, _vp]),
     "oasis_block_meta_import": (_int, [_vp, _vp, _vp, _vp]),
     "oasis_lookahead_score": (_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
@@ -241,6 +242,11 @@ def oasis_block_meta_build(h, pages, page_ids, count, ctx_len, meta, pool=None, 
                            stream=None):
     _call("oasis_block_meta_build", h, _ptr(pages), _ptr(page_ids), count, _ptr(ctx_len), _ptr(meta),
           _ptr(pool), _ptr(block_to_slot), _stream(stream))
+
+
+def oasis_block_meta_build_rows(h, k_rows, tok_begin, tok_end, ctx_len, meta, stream=None):
+    _call("oasis_block_meta_build_rows", h, _ptr(k_rows), tok_begin, tok_end, _ptr(ctx_len), _ptr(meta),
+          _stream(stream))
 
 
 def oasis_block_meta_export(h, meta, meta_logical, stream=None):

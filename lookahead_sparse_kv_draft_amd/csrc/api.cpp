@@ -303,6 +303,23 @@ int oasis_block_meta_build(oasis_handle h, const void* pages, const int32_t* pag
                     "oasis_block_meta_build");
 }
 
+int oasis_block_meta_build_rows(oasis_handle h, const void* k_rows, int32_t tok_begin, int32_t tok_end,
+                                const int32_t* ctx_len, void* meta, void* stream) {
+  CHECK_HANDLE(h);
+  CHECK_PTR(k_rows);
+  CHECK_PTR(ctx_len);
+  CHECK_PTR(meta);
+  CHECK_ALIGN16(k_rows);
+  CHECK_ALIGN16(meta);
+  const long long ntok = static_cast<long long>(h->c.s.max_blocks) * oasis::kBlock;
+  if (tok_begin < 0 || tok_end < tok_begin || tok_end > ntok)
+    return fail(OASIS_EINVAL, "oasis_block_meta_build_rows: token range [%d, %d) outside [0, %lld]", tok_begin,
+                tok_end, ntok);
+  return hip_status(oasis::launch_meta_rows(h->c, k_rows, tok_begin, tok_end, ctx_len, meta,
+                                            static_cast<hipStream_t>(stream)),
+                    "oasis_block_meta_build_rows");
+}
+
 int oasis_block_meta_export(oasis_handle h, const void* meta, void* meta_logical, void* stream) {
   CHECK_HANDLE(h);
   CHECK_PTR(meta);

@@ -3,6 +3,7 @@
 //
 //  meta_build  - one wavefront per staged page: min/max over the block's tokens
 //                below the context length; optionally patches the resident copy.
+//  meta_rows   - one wavefront per block of a token range, from key rows.
 //  meta_update - one wavefront per (request, KV head): absorbs the appended
 //                token into its block's min/max and writes it into the page if
 //                the block is resident.
@@ -63,6 +64,49 @@ __global__ __launch_bounds__(256) void meta_build_kernel(
       for (int i = lane; i < V4; i += kWave) dst[i] = src[i];
     }
   }
+}
+
+// The metadata of blocks [b0, b1) of every unit from key rows [units][Nmax*16][d]
+// (token-major): one wavefront per (unit, block), min/max over the block's
+// tokens below the context length; blocks at or past it are not touched.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void meta_rows_kernel(const E* __restrict__ k_rows,
+                                                        const int32_t* __restrict__ ctx_len, E* __restrict__ meta,
+                                                        int units, int H, int Nmax, int b0, int b1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int nb = b1 - b0;
+  if (w >= units * nb) return;
+  const int unit = w / nb;
+  const int b = b0 + (w - unit * nb);
+  const int n = ctx_len[unit / H];
+  const int N = min((n + kBlock - 1) / kBlock, Nmax);
+  if (b >= N) return;
+  const int ntok = min(kBlock, n - kBlock * b);
+  const E* kr = k_rows + (static_cast<size_t>(unit) * Nmax * kBlock + static_cast<size_t>(b) * kBlock) * D;
+  constexpr int CE = 16 / static_cast<int>(sizeof(E));
+  for (int c = lane; c < D; c += kWave) {
+    float mn = Elem<E>::load(kr[c]);
+    float mx = mn;
+    for (int j = 1; j < ntok; ++j) {
+      const float v = Elem<E>::load(kr[j * D + c]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    meta[meta_offset<D, CE>(unit, b, c, Nmax)] = Elem<E>::store(mn);
+    meta[meta_offset<D, CE>(unit, b, D + c, Nmax)] = Elem<E>::store(mx);
+  }
+}
+
+template <typename E, int D>
+hipError_t rows_t(const Ctx& c, const void* k_rows, const int32_t* ctx_len, void* meta, int b0, int b1,
+                  hipStream_t st) {
+  const long long waves = static_cast<long long>(c.units) * (b1 - b0);
+  if (waves <= 0) return hipSuccess;
+  hipLaunchKernelGGL((meta_rows_kernel<E, D>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const E*>(k_rows), ctx_len, static_cast<E*>(meta), c.units, c.s.kv_heads,
+                     c.s.max_blocks, b0, b1);
+  return hipGetLastError();
 }
 
 // The metadata between the library's chunk-major tiles and the logical layout
@@ -228,6 +272,17 @@ hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids
               : build_t<float, 128>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
   return bf ? build_t<uint16_t, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st)
             : build_t<float, 64>(c, pages, ids, count, ctx_len, meta, pool, b2s, st);
+}
+
+hipError_t launch_meta_rows(const Ctx& c, const void* k_rows, int tok_begin, int tok_end, const int32_t* ctx_len,
+                            void* meta, hipStream_t st) {
+  const int b0 = tok_begin / kBlock, b1 = (tok_end + kBlock - 1) / kBlock;
+  const bool bf = c.s.dtype == OASIS_BF16;
+  if (c.s.head_dim == 128)
+    return bf ? rows_t<uint16_t, 128>(c, k_rows, ctx_len, meta, b0, b1, st)
+              : rows_t<float, 128>(c, k_rows, ctx_len, meta, b0, b1, st);
+  return bf ? rows_t<uint16_t, 64>(c, k_rows, ctx_len, meta, b0, b1, st)
+            : rows_t<float, 64>(c, k_rows, ctx_len, meta, b0, b1, st);
 }
 
 hipError_t launch_admit(const Ctx& c, const void* k_rows, const void* v_rows, const int32_t* ctx_len,

@@ -61,6 +61,10 @@ hipError_t launch_meta_build(const Ctx& c, const void* pages, const int32_t* ids
                              const int32_t* ctx_len, void* meta, void* pool,
                              const int32_t* b2s, hipStream_t st);
 // The metadata from the tiles to [units][Nmax][2][d] (to_logical) or back.
+// The metadata of the blocks that tokens [tok_begin, tok_end) fall in, from key
+// rows [units][Nmax*16][d].
+hipError_t launch_meta_rows(const Ctx& c, const void* k_rows, int tok_begin, int tok_end, const int32_t* ctx_len,
+                            void* meta, hipStream_t st);
 hipError_t launch_meta_relayout(const Ctx& c, const void* src, void* dst, bool to_logical, hipStream_t st);
 hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new,
                               const int32_t* ctx_in, int32_t* ctx_out, void* meta, void* pool,

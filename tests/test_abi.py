@@ -77,6 +77,10 @@ def test_sizes_and_null_checks():
         assert lib.oasis_sparse_paged_decode_attn(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_update(h, None, None, None, None, None, None, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_build(h, None, None, 0, None, None, None, None, None) == L.OASIS_EINVAL
+        # token ranges outside [0, max_blocks * 16] (64 blocks here)
+        for tb, te in ((-1, 16), (32, 16), (0, 64 * 16 + 1)):
+            assert lib.oasis_block_meta_build_rows(h, 256, tb, te, 256, 256, None) == L.OASIS_EINVAL, (tb, te)
+        assert lib.oasis_block_meta_build_rows(h, None, 0, 16, 256, 256, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_export(h, None, 256, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_import(h, 256, None, None) == L.OASIS_EINVAL
         assert lib.oasis_block_meta_export(h, 256, 256, None) == L.OASIS_EINVAL  # not in place

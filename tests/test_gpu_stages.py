@@ -538,6 +538,51 @@ def test_meta_export_and_import(dtype, d, nmax):
     rt.close()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_meta_build_from_key_rows(dtype, d):
+    """The metadata from key rows and a token range: every block the range
+    touches equals the oracle's min/max over the block's tokens below the
+    context, the others keep what they held, and a whole-range build equals the
+    build from staged pages."""
+    B, H, Nmax = 3, 2, 40
+    ctxs = [Nmax * BLK, 16 * 21 + 5, 16 * 3]
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=Nmax, budget_blocks=4, fetch_cap=4, dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(17)
+    units = B * H
+    K = U.elem_round(dtype, rng.standard_normal((units, Nmax * BLK, d)).astype(np.float32))
+    for u in range(units):
+        rt.pack_unit(0, u, U.to_elem_np(dtype, K[u]), U.to_elem_np(dtype, K[u]))
+    rt.set_ctx(ctxs)
+    rt.build_meta(0)
+    torch.cuda.synchronize()
+    staged = rt.state[0][0].meta.clone()
+    k_rows = U.to_dev(dtype, K.reshape(B, H, Nmax * BLK, d))
+    n_tiles = units * ((Nmax + 15) // 16) * 16 * 2 * d * sh.elem_bytes
+    meta = torch.zeros_like(staged)
+    L.oasis_block_meta_build_rows(rt.h, k_rows, 0, Nmax * BLK, rt.ctx_len, meta)
+    torch.cuda.synchronize()
+    assert torch.equal(meta[:n_tiles], staged[:n_tiles])
+    # a range that starts and ends inside blocks: blocks 5 .. 12 only
+    meta2 = torch.zeros_like(staged)
+    L.oasis_block_meta_build_rows(rt.h, k_rows, 16 * 5 + 3, 16 * 12 + 1, rt.ctx_len, meta2)
+    torch.cuda.synchronize()
+    lg = torch.empty((units, Nmax, 2, d), dtype=torch.int16 if dtype == "bf16" else torch.float32, device="cuda")
+    L.oasis_block_meta_export(rt.h, meta2, lg)
+    torch.cuda.synchronize()
+    mv = (lg.view(torch.bfloat16).float() if dtype == "bf16" else lg).cpu().numpy().astype(np.float64)
+    for u in range(units):
+        n = ctxs[u // H]
+        kmin, kmax = O.block_meta(K[u].astype(np.float64), n)
+        N = kmin.shape[0]
+        for b in range(Nmax):
+            if 5 <= b <= 12 and b < N:
+                assert np.array_equal(mv[u, b, 0], kmin[b]) and np.array_equal(mv[u, b, 1], kmax[b]), (u, b)
+            else:
+                assert not mv[u, b].any(), (u, b)
+    rt.close()
+
+
 def test_fetch_issue_copies_pages():
     sh = U.make_shape(batch=2, kv_heads=2, max_blocks=40, budget_blocks=8, fetch_cap=5)
     rt = DecodeRuntime(sh)
