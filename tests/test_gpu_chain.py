@@ -275,6 +275,16 @@ def test_carry_step_matches_decode_step(name, kw):
     _decode_step_vs_separate(cfg, runs=[SyntheticRun(cfg, overlap=False, carry_select=c) for c in (True, False)])
 
 
+@pytest.mark.parametrize("name,kw", [CARRY_SHAPES[0], CARRY_SHAPES[4], CARRY_SHAPES[5]])
+def test_carry_step_matches_separate_calls(name, kw):
+    """The carried step against the separate entry points (attention, score,
+    selection and diff each on their own): every selection, list and map bit
+    for bit, the attention output up to the split order of its fp32 sums."""
+    cfg = CONFIGS[name].with_(**kw)
+    _decode_step_vs_separate(cfg, runs=[SyntheticRun(cfg, overlap=False, carry_select=True),
+                                        SyntheticRun(cfg, overlap=False, fused_step=False)])
+
+
 def _outputs_without_step_syncs(cfg, **kw):
     """All steps enqueued back to back (carried selections and inline transfers
     cross step boundaries); every layer's output copied on the stream; the
