@@ -758,22 +758,37 @@ def main():
                 cs.wait_event(ev_sel[l])
             L.oasis_sparse_paged_decode_attn(rt.h, q, st.pool, st.sel, st.b2s, rt.ctx_len, rt.out, rt.ws_ptr, cs)
             ev_attn[l].record(cs)
-            L.oasis_lookahead_score(rt.h, q, st.meta, rt.ctx_len, st.scores, ps)
+            append(l, t, st, ps)  # writes token n only, which the attention does not read
+            L.oasis_lookahead_score(rt.h, q, st.meta, ctx_score, st.scores, ps)
             ps.wait_event(ev_attn[l])
-            L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+            L.oasis_select_and_diff(rt.h, st.scores, ctx_score, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
                                     st.evict, st.attend, st.n_attend, stream=ps)
             ev_sel[l].record(ps)
+
+    # Appending workloads: every step of every layer first appends one token per
+    # request (oasis_block_meta_update at the current context length, written to
+    # the other context buffer, which the step's scoring then sees).  The timed
+    # loop does not advance the context, so each step appends at the same
+    # position: the same work as a growing context.
+    ctx_in, ctx_grown = rt.ctx[rt.ctx_cur], rt.ctx[1 - rt.ctx_cur]
+    ctx_score = ctx_grown if cfg.append else ctx_in
+
+    def append(l, t, st, cs):
+        if cfg.append:
+            L.oasis_block_meta_update(rt.h, run.k_new_dev[l, t], run.v_new_dev[l, t], ctx_in, ctx_grown, st.meta,
+                                      st.pool, st.b2s, cs)
 
     def sequential_step(i, cs):
         """One decode step over all layers: the single decode-step call per layer
         (attention beside the scoring in one launch; selection, diff and the
-        attention's split combine in the second)."""
+        attention's split combine in the second), after the layer's append."""
         rep = i % replicas
         t = i % cfg.steps
         for l in range(run.L):
             q = run.q[l, t + 1]
             st = rt.state[l][rep]
-            L.oasis_decode_step(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.s2b,
+            append(l, t, st, cs)
+            L.oasis_decode_step(rt.h, q, st.pool, st.meta, rt.ctx_len, ctx_score, st.sel, st.b2s, st.s2b,
                                 st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
                                 st.n_attend, stream=cs)
 
@@ -789,9 +804,10 @@ def main():
         for l in range(run.L):
             q = run.q[l, t + 1]
             st = rt.state[l][rep]
-            L.oasis_decode_step_carry(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.attend, st.n_attend,
+            append(l, t, st, cs)
+            L.oasis_decode_step_carry(rt.h, q, st.pool, st.meta, rt.ctx_len, ctx_score, st.attend, st.n_attend,
                                       st.scores, rt.out, rt.ws_ptr, job=pending[0], stream=cs)
-            pending[0] = (st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, st.attend,
+            pending[0] = (st.scores, ctx_score, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch, st.evict, st.attend,
                           st.n_attend)
 
     def carry_flush(cs):
@@ -818,11 +834,12 @@ def main():
             st = rt.state[l][rep]
             if not first:
                 cs.wait_event(ev_state[l][rep])
-            L.oasis_attend_and_score(rt.h, q, st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s, st.attend,
+            append(l, t, st, cs)
+            L.oasis_attend_and_score(rt.h, q, st.pool, st.meta, rt.ctx_len, ctx_score, st.sel, st.b2s, st.attend,
                                      st.n_attend, st.scores, rt.out, rt.ws_ptr, cs)
             ev_scored.record(cs)
             ps.wait_event(ev_scored)
-            L.oasis_select_and_diff(rt.h, st.scores, rt.ctx_len, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
+            L.oasis_select_and_diff(rt.h, st.scores, ctx_score, st.sel, st.b2s, st.s2b, st.fetch, st.n_fetch,
                                     st.evict, st.attend, st.n_attend, stream=ps)
             ev_state[l][rep].record(ps)
             L.oasis_attn_combine(rt.h, rt.ws_ptr, rt.out, cs)
@@ -1036,6 +1053,9 @@ def main():
     steps_total = cfg.batch * run.L * args.steps
     value = steps_total / elapsed
     ab = algorithmic_bytes(cfg, attended_before)
+    # the append per layer step: per unit the new K and V rows read, the block's
+    # metadata row read and written, the K and V rows written into a resident page
+    append_bytes = (cfg.batch * cfg.kv_heads * cfg.head_dim * cfg.elem_bytes * (2 + 4 + 2)) if cfg.append else 0
     kern = {}
     for n in names:
         gbs = ab[n] / avg[n] / 1e9
@@ -1078,7 +1098,8 @@ def main():
                       "two_streams": "per layer: attention + scoring, then the split combine, on one stream; "
                                   "the selection and diff on a second stream beside the next layer",
                       "two_streams_graph": f"HIP graph of {G} steps of the two_streams mode"}[args.mode],
-        "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"]) * run.L,
+        "hbm_bytes_per_step": (ab["attend_and_score"] + ab["select_diff_combine"] + append_bytes) * run.L,
+        "step_includes_append": bool(cfg.append),
         "decode_step_call_us": step_call_us,
         "decode_step_carry_call_us": carry_call_us,
         "headline_timing": {"clock": "HIP events on the compute stream around the K timed steps, after a "
