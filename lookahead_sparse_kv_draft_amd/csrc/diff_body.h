@@ -214,172 +214,171 @@ __device__ __forceinline__ void diff_body(int unit, int kb, int Nmax, int cap, c
 // The same step run by ONE wavefront for k <= 128 (the largest shape of the
 // decode step's default path): lane l handles selection entries and slots l and
 // l + 64, every rank is a ballot within the wavefront, so there is no barrier at
-// all (the wavefront's LDS accesses complete in order).  selL: LDS [kb], the
-// selection; b2sL: LDS [Nmax], this unit's block -> slot table before the step
-// (one byte per block, -1 = not resident); bitmap words in `lds` already
-// cleared; sb: the slot map for slots l and l + 64 (-1 / any for slots >= kb);
-// kd: the selection's order keys (desc_key of the score) of the blocks in
-// those two slots, read only for resident blocks outside the selection (the
-// diff ranks victims by the same keys as the selection).
+// all (the wavefront's LDS accesses complete in order).  A lone wavefront issues
+// about one instruction every four cycles, so the step is written for few
+// instructions and few dependent LDS round trips: the selection arrives with
+// what the top-k found out while ranking it, and each lane writes the list
+// entries it owns directly.
+//   selL: LDS [kb], the selection in rank order (-1 padded);
+//   selS: LDS [kb], the slot each selected block held before the step (-1: not
+//         resident);
+//   selF: LDS [kb], per slot: 1 when the block it holds is selected;
+//   sb:   the slot map for slots l and l + 64 (-1 / any for slots >= kb);
+//   kd:   the selection's order keys (desc_key of the score) of the blocks in
+//         those two slots, read only for resident blocks outside the selection
+//         (the diff ranks victims by the same keys as the selection).
 // Least-recently-used eviction when lu (this unit's per-slot stamps) is not
 // null: luv holds the stamps of slots l and l + 64; victims are taken oldest
 // stamp first, then in the lowest-score order, and the slots the next attention
 // reads are stamped with `step` ([EXPL] Table 2 runs LRU eviction).
 constexpr int kDiffWaveMaxBudget = 2 * kWave;
+constexpr int kDiffWavePad = 8;  // the victim ranking reads the candidates 8 at a time
+// LDS bytes diff_wave carves: candidate keys and stamps (padded), targets.
+constexpr int kDiffWaveLdsBytes = (kDiffWaveMaxBudget + kDiffWavePad) * 12 + kDiffWaveMaxBudget * 4;
 
 __device__ __forceinline__ void diff_wave(int unit, int kb, int Nmax, int cap, const int32_t* selL,
-                                          const int8_t* b2sL, const int (&sb)[2], const uint32_t (&kd)[2],
-                                          const int (&luv)[2], int32_t* __restrict__ lu, int step,
-                                          int32_t* __restrict__ bu,
-                                 int32_t* __restrict__ slu, int32_t* __restrict__ fetch,
-                                 int32_t* __restrict__ n_fetch, int32_t* __restrict__ evict,
-                                 int32_t* __restrict__ attend, int32_t* __restrict__ n_attend,
-                                 unsigned long long* lds) {
-  // at most k blocks are fetched or evicted per step: the lists in LDS need
-  // min(cap, k) entries (the fetch / evict lists in memory are cap long)
-  const int capL = min(cap, kb);
-  unsigned long long* candK = lds;
-  const int nwords = (Nmax + 31) / 32;
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(candK + kb);
-  int32_t* F = reinterpret_cast<int32_t*>(bitmap + nwords);
-  int32_t* tgt = F + capL;
-  int32_t* freeS = tgt + capL;
-  int32_t* vict = freeS + kb;
-  int32_t* victS = vict + capL;
-  int32_t* candS = victS + capL;
-  int32_t* candA = candS + kb;  // LRU: the candidates' stamps
-
+                                          const int8_t* selS, const uint8_t* selF, const int (&sb)[2],
+                                          const uint32_t (&kd)[2], const int (&luv)[2], int32_t* __restrict__ lu,
+                                          int step, int32_t* __restrict__ bu, int32_t* __restrict__ slu,
+                                          int32_t* __restrict__ fetch, int32_t* __restrict__ n_fetch,
+                                          int32_t* __restrict__ evict, int32_t* __restrict__ attend,
+                                          int32_t* __restrict__ n_attend, unsigned long long* lds) {
+  unsigned long long* candK = lds;                                                         // [kb + pad]
+  int32_t* tgt = reinterpret_cast<int32_t*>(candK + kDiffWaveMaxBudget + kDiffWavePad);   // [kb]
+  int32_t* candA = tgt + kDiffWaveMaxBudget;                                              // [kb + pad] LRU
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t below = (1ull << lane) - 1ull;
-  int b[2], res[2], mrank[2];
-  bool in[2], bok[2], sok[2], miss[2];
-  uint64_t bm[2], bf[2];
+  int b[2], res[2];
+  bool in[2], bok[2], miss[2], cnd[2];
+  uint64_t bm[2], bf[2], bc[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int i = lane + e * kWave;
+    const int ic = min(i, kb - 1);  // clamped: no branch around the reads
     in[e] = i < kb;
-    b[e] = in[e] ? selL[i] : -1;
+    const int bl = selL[ic];
+    const int rs = selS[ic];
+    const bool f = selF[ic] != 0;
+    b[e] = in[e] ? bl : -1;
     bok[e] = b[e] >= 0 && b[e] < Nmax;
-    res[e] = bok[e] ? static_cast<int>(b2sL[b[e]]) : -1;
-    sok[e] = in[e] && sb[e] >= 0 && sb[e] < Nmax;
-    if (bok[e]) atomicOr(&bitmap[b[e] >> 5], 1u << (b[e] & 31));
+    res[e] = bok[e] ? rs : -1;
     miss[e] = bok[e] && res[e] < 0;
+    cnd[e] = in[e] && sb[e] >= 0 && sb[e] < Nmax && !f;  // resident, outside the selection
     bm[e] = __ballot(miss[e]);
     bf[e] = __ballot(in[e] && sb[e] < 0);
+    bc[e] = __ballot(cnd[e]);
   }
   // 1 + 2: missing blocks in selection order, free slots in ascending order
-  const int nm0 = __popcll(bm[0]), nf0 = __popcll(bf[0]);
-  const int nmiss = nm0 + __popcll(bm[1]), nfree = nf0 + __popcll(bf[1]);
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    mrank[e] = (e ? nm0 : 0) + __popcll(bm[e] & below);
-    if (miss[e] && mrank[e] < cap) F[mrank[e]] = b[e];
-    if ((bf[e] >> lane) & 1ull) freeS[(e ? nf0 : 0) + __popcll(bf[e] & below)] = lane + e * kWave;
-  }
+  const int nm0 = __popcll(bm[0]), nf0 = __popcll(bf[0]), nc0 = __popcll(bc[0]);
+  const int nmiss = nm0 + __popcll(bm[1]), nfree = nf0 + __popcll(bf[1]), nc = nc0 + __popcll(bc[1]);
   int nF = min(cap, nmiss);
   int need = max(0, nF - nfree);
-  // lanes exchange data through LDS below: order each phase's accesses
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // Consistent maps with at most k selected blocks always leave enough
+  // victims; clamp anyway so inconsistent input stays within the buffers.
+  if (need > nc) {
+    need = nc;
+    nF = nfree + nc;
+  }
 
-  // 3. victims: resident blocks outside the selection, compacted in slot order,
-  // then placed by the number of candidates with a larger key
+  // 3. victims: resident blocks outside the selection, compacted in slot order
+  // (sentinels after the last one), each placed by the number of candidates
+  // with a larger key
+  int r[2] = {need, need};
   if (need > 0) {
-    bool cnd[2];
     unsigned long long ck[2];
-    uint64_t bc[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int sbc = sok[e] ? sb[e] : 0;  // index clamped: no branch around the read
-      cnd[e] = sok[e] && !((bitmap[sbc >> 5] >> (sbc & 31)) & 1u);
       ck[e] = ~((static_cast<unsigned long long>(kd[e]) << 32) | static_cast<uint32_t>(sb[e] + 1));
-      bc[e] = __ballot(cnd[e]);
-    }
-    const int nc0 = __popcll(bc[0]);
-    const int nc = nc0 + __popcll(bc[1]);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
       if (cnd[e]) {
         const int pos = (e ? nc0 : 0) + __popcll(bc[e] & below);
         candK[pos] = ck[e];  // complemented: a larger key ranks first
-        candS[pos] = lane + e * kWave;
         if (lu != nullptr) candA[pos] = luv[e];
       }
-    // Consistent maps with at most k selected blocks always leave enough
-    // victims; clamp anyway so inconsistent input stays within the buffers.
-    if (need > nc) {
-      need = nc;
-      nF = nfree + nc;
+    }
+    if (lane < kDiffWavePad) {
+      candK[nc + lane] = ~0ull;  // never below a candidate's key
+      if (lu != nullptr) candA[nc + lane] = 0x7FFFFFFF;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    constexpr int kBatch = 8;
     int r0 = 0, r1 = 0;
     if (lu == nullptr) {
-      for (int j = 0; j < nc; j += kBatch) {
-        unsigned long long x[kBatch];
+      for (int j = 0; j < nc; j += kDiffWavePad) {
+        unsigned long long x[kDiffWavePad];
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) x[t] = candK[min(j + t, nc - 1)];
+        for (int t = 0; t < kDiffWavePad; ++t) x[t] = candK[j + t];
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-          const bool ok = j + t < nc;
-          r0 += static_cast<int>(ok & (x[t] < ck[0]));
-          r1 += static_cast<int>(ok & (x[t] < ck[1]));
+        for (int t = 0; t < kDiffWavePad; ++t) {
+          r0 += static_cast<int>(x[t] < ck[0]);
+          r1 += static_cast<int>(x[t] < ck[1]);
         }
       }
     } else {
       // (older stamp, then the lowest-score order) ranks first
-      for (int j = 0; j < nc; j += kBatch) {
-        unsigned long long x[kBatch];
-        int a[kBatch];
+      for (int j = 0; j < nc; j += kDiffWavePad) {
+        unsigned long long x[kDiffWavePad];
+        int a[kDiffWavePad];
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-          x[t] = candK[min(j + t, nc - 1)];
-          a[t] = candA[min(j + t, nc - 1)];
+        for (int t = 0; t < kDiffWavePad; ++t) {
+          x[t] = candK[j + t];
+          a[t] = candA[j + t];
         }
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) {
-          const bool ok = j + t < nc;
-          r0 += static_cast<int>(ok & ((a[t] < luv[0]) | ((a[t] == luv[0]) & (x[t] < ck[0]))));
-          r1 += static_cast<int>(ok & ((a[t] < luv[1]) | ((a[t] == luv[1]) & (x[t] < ck[1]))));
+        for (int t = 0; t < kDiffWavePad; ++t) {
+          r0 += static_cast<int>((a[t] < luv[0]) | ((a[t] == luv[0]) & (x[t] < ck[0])));
+          r1 += static_cast<int>((a[t] < luv[1]) | ((a[t] == luv[1]) & (x[t] < ck[1])));
         }
       }
     }
-    const int r[2] = {r0, r1};
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      if (cnd[e] && r[e] < need) {
-        vict[r[e]] = sb[e];
-        victS[r[e]] = lane + e * kWave;
-      }
+    r[0] = cnd[0] ? r0 : need;
+    r[1] = cnd[1] ? r1 : need;
   }
 
-  // 4. targets, then the map updates and the lists
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int t = lane; t < nF; t += kWave) tgt[t] = (t < nfree) ? freeS[t] : victS[t - nfree];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int t = lane; t < need; t += kWave) bu[vict[t]] = -1;
-  for (int t = lane; t < nF; t += kWave) {
-    const int s = tgt[t];
-    slu[s] = F[t];
-    bu[F[t]] = s;
-  }
+  // 4. targets (free slots, then the victims' slots in rank order); each
+  // victim's lane writes its evict entry and clears its block's slot
   int32_t* fu = fetch + static_cast<size_t>(unit) * cap * 2;
   int32_t* eu = evict + static_cast<size_t>(unit) * cap;
-  for (int j = lane; j < cap; j += kWave) {
-    fu[2 * j] = (j < nF) ? F[j] : -1;
-    fu[2 * j + 1] = (j < nF) ? tgt[j] : -1;
-    eu[j] = (j < need) ? vict[j] : -1;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int slot = lane + e * kWave;
+    if ((bf[e] >> lane) & 1ull) {
+      const int fr = (e ? nf0 : 0) + __popcll(bf[e] & below);
+      if (fr < nF) tgt[fr] = slot;
+    }
+    if (r[e] < need) {
+      tgt[nfree + r[e]] = slot;
+      eu[r[e]] = sb[e];
+      bu[sb[e]] = -1;
+    }
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // 5. each fetched block's lane takes its target: fetch entry and both maps
+  int sa[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int mrank = (e ? nm0 : 0) + __popcll(bm[e] & below);
+    sa[e] = res[e];
+    if (miss[e] && mrank < nF) {
+      const int s = tgt[mrank];
+      fu[2 * mrank] = b[e];
+      fu[2 * mrank + 1] = s;
+      slu[s] = b[e];
+      bu[b[e]] = s;
+      sa[e] = s;
+    }
+  }
+  for (int j = nF + lane; j < cap; j += kWave) {
+    fu[2 * j] = -1;
+    fu[2 * j + 1] = -1;
+  }
+  for (int j = need + lane; j < cap; j += kWave) eu[j] = -1;
   if (lane == 0) n_fetch[unit] = nF;
 
-  // 5. the attended list for the next attention (selection order); with LRU
+  // 6. the attended list for the next attention (selection order); with LRU
   // its slots take this step's stamp
   if (attend != nullptr || lu != nullptr) {
-    int sa[2];
     uint64_t ba[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      sa[e] = -1;
-      if (bok[e]) sa[e] = (res[e] >= 0) ? res[e] : ((miss[e] && mrank[e] < nF) ? tgt[mrank[e]] : -1);
       ba[e] = __ballot(in[e] && sa[e] >= 0 && sa[e] < kb);
       if (lu != nullptr && ((ba[e] >> lane) & 1ull)) lu[sa[e]] = step;
     }

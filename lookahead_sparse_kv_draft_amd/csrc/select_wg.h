@@ -11,19 +11,17 @@
 
 namespace oasis {
 
-// Largest block count and diff LDS of a workgroup selection (k <= 128,
-// cap <= k): candidate keys, selection bitmap, fetch/target/victim lists, free
-// slots, candidate slots and stamps (the layout diff_wave carves).
+// Largest block count of a workgroup selection (k <= 128).
 constexpr int kSelWgMaxBlocks = 8 * 1024;
-constexpr int kSelWgDiffBytes =
-    kDiffWaveMaxBudget * 8 + (kSelWgMaxBlocks / 32) * 4 + (3 * kDiffWaveMaxBudget + 4 * kDiffWaveMaxBudget) * 4;
 
 template <int NT>
 struct SelectLds {
   TopkFastShared<NT> tk;
   int32_t selL[kDiffWaveMaxBudget];                   // the selection in rank order
   uint32_t slot_keys[kDiffWaveMaxBudget];             // order key of the block in each slot
-  unsigned long long diff[kSelWgDiffBytes / 8];        // diff_wave's arrays
+  unsigned long long diff[kDiffWaveLdsBytes / 8];      // diff_wave's arrays
+  int8_t selS[kDiffWaveMaxBudget];                     // slot of each selected block (-1: none)
+  uint8_t selF[kDiffWaveMaxBudget];                    // per slot: its block is selected
   int8_t slot_of[kSelWgMaxBlocks];                     // block -> slot before the step (-1: none)
 };
 
@@ -55,19 +53,19 @@ __device__ __forceinline__ void select_diff_wg(const SelectJob& job, int unit, i
   const int n = job.ctx_len[unit / H];
   uint32_t* tab = reinterpret_cast<uint32_t*>(sh.slot_of);
   for (int j = tid; j < (Nmax + 3) / 4; j += NT) tab[j] = 0xFFFFFFFFu;  // every entry -1
-  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sh.diff + kb);
-  for (int j = tid; j < (Nmax + 31) / 32; j += NT) bitmap[j] = 0u;
+  if (tid < kDiffWaveMaxBudget / 4) reinterpret_cast<uint32_t*>(sh.selF)[tid] = 0u;
   __syncthreads();
   if (tid < kb && sb_own >= 0 && sb_own < Nmax) sh.slot_of[sb_own] = static_cast<int8_t>(tid);
   __syncthreads();
-  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, sh.slot_of, sh.slot_keys);
+  topk_fast_body<NT, KPT>(v, n, unit, job.sel, Nmax, kb, sh.selL, sh.tk, sh.slot_of, sh.slot_keys, sh.selS,
+                          sh.selF);
   __syncthreads();
   if (tid >= kWave) return;
   uint32_t kd[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) kd[e] = sh.slot_keys[min(lane + e * kWave, kb - 1)];
-  diff_wave(unit, kb, Nmax, cap, sh.selL, sh.slot_of, sbw, kd, luw, lu, job.step, bu, slu, job.fetch,
-                    job.n_fetch, job.evict, job.attend, job.n_attend, sh.diff);
+  diff_wave(unit, kb, Nmax, cap, sh.selL, sh.selS, sh.selF, sbw, kd, luw, lu, job.step, bu, slu, job.fetch,
+            job.n_fetch, job.evict, job.attend, job.n_attend, sh.diff);
 }
 
 }  // namespace oasis
