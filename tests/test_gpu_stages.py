@@ -743,6 +743,76 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
     L.oasis_destroy(h)
 
 
+@pytest.mark.parametrize("Nmax,k,cap,kind,ctxs", [
+    (300, 64, 16, "ties", [16 * 300, 16 * 170 + 5]),          # 4 keys per thread
+    (2048, 128, 32, "ties", [16 * 2048, 16 * 1500 + 9]),      # 16 keys per thread
+    (2048, 128, 32, "const", [16 * 2048, 16 * 131]),
+    (8192, 128, 32, "ties", [16 * 8192, 16 * 6000 + 3]),      # 64 keys per thread
+    (8192, 128, 16, "const", [16 * 8192, 16 * 4100]),
+    (8192, 128, 32, "normal", [16 * 8000, 16 * 129]),
+])
+def test_carried_selection_matches_select_and_diff(Nmax, k, cap, kind, ctxs):
+    """The selection and diff carried by a decode step's first launch (128-thread
+    workgroups, 4 to 64 keys per thread) on tie-heavy and constant scores, which
+    take the radix select's later passes and its ordered tie pass: selection,
+    both maps, fetch and evict lists and the attended list bit-identical to
+    oasis_select_and_diff on the same state, and the selection the oracle's."""
+    B, H = len(ctxs), 2
+    units = B * H
+    sh = U.make_shape(batch=B, kv_heads=H, max_blocks=Nmax, budget_blocks=k, fetch_cap=cap)
+    h = sh.handle()
+    rng = _rng(31)
+    # this step's own inputs: zeros, nothing attended (its outputs are not compared)
+    d, T = sh.head_dim, sh.T
+    q = torch.zeros((B, sh.q_heads, T, d), dtype=torch.bfloat16, device="cuda")
+    pool = torch.zeros((units * k * 2 * 16 * d,), dtype=torch.bfloat16, device="cuda")
+    meta = torch.zeros((L.oasis_meta_bytes(h),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((L.oasis_workspace_bytes(h),), dtype=torch.uint8, device="cuda")
+    ctx_own = U.i32([16 * Nmax] * B)
+    att_own = torch.zeros((units, k), dtype=torch.int32, device="cuda")
+    natt_own = torch.zeros((units,), dtype=torch.int32, device="cuda")
+    sc_own = torch.zeros((units, Nmax), dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, sh.q_heads, T, d), dtype=torch.float32, device="cuda")
+    # the carried state
+    sc = np.stack([random_scores(rng, Nmax, kind) for _ in range(units)])
+    b2s0 = np.full((units, Nmax), -1, dtype=np.int32)
+    s2b0 = np.full((units, k), -1, dtype=np.int32)
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        n_res = [k, k // 2, int(rng.integers(0, k + 1)), 0][u % 4]
+        res = rng.choice(N, size=min(n_res, N), replace=False)
+        slots = rng.choice(k, size=len(res), replace=False)
+        s2b0[u, slots] = res
+        b2s0[u, res] = slots
+    sc_d, ctx_d = torch.from_numpy(sc).cuda(), U.i32(ctxs)
+    outs = []
+    for carried in (True, False):
+        sel = torch.full((units, k), -7, dtype=torch.int32, device="cuda")
+        b2s, s2b = U.i32(b2s0), U.i32(s2b0)
+        fetch = torch.full((units, cap, 2), -9, dtype=torch.int32, device="cuda")
+        nf = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+        ev = torch.full((units, cap), -9, dtype=torch.int32, device="cuda")
+        att = torch.full((units, k), -9, dtype=torch.int32, device="cuda")
+        natt = torch.full((units,), -9, dtype=torch.int32, device="cuda")
+        if carried:
+            L.oasis_decode_step_carry(h, q, pool, meta, ctx_own, ctx_own, att_own, natt_own, sc_own, out, ws,
+                                      job=(sc_d, ctx_d, sel, b2s, s2b, fetch, nf, ev, att, natt))
+        else:
+            L.oasis_select_and_diff(h, sc_d, ctx_d, sel, b2s, s2b, fetch, nf, ev, att, natt)
+        torch.cuda.synchronize()
+        na = natt.cpu().numpy()
+        am = att.cpu().numpy()
+        am = [list(am[u][: na[u]]) for u in range(units)]
+        outs.append([x.cpu().numpy() for x in (sel, b2s, s2b, fetch, nf, ev, natt)] + [am])
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert (a == b) if isinstance(a, list) else np.array_equal(a, b), i
+    sel = outs[0][0]
+    for u in range(units):
+        N = (ctxs[u // H] + BLK - 1) // BLK
+        assert list(sel[u]) == O.topk_select(sc[u].astype(np.float64), N, k), u
+    L.oasis_destroy(h)
+
+
 # ------------------------------------------------------------------ LRU eviction
 @pytest.mark.parametrize("k,cap,N,kind,steps", [
     (128, 32, 2048, "normal", 6), (128, 8, 700, "ties", 6), (16, 4, 64, "normal", 8),
