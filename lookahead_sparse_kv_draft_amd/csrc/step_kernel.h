@@ -17,37 +17,22 @@ namespace oasis {
 namespace {
 
 // One page of another layer's fetch list, copied from the device-mapped pinned
-// host tier into that layer's pool by one workgroup of NT threads: all reads of
-// a batch issued before its writes, with no branch around either (a branch kept
-// the batch out of registers).  Entries beyond n_fetch and entries out of
-// range are skipped, as in the standalone gather.
+// host tier into that layer's pool by one workgroup of NT threads, one 16-byte
+// read in flight per thread: over the host link, reading two or four chunks
+// per thread at once measured slower (more of each step's transfer exposed).
+// Entries beyond n_fetch and entries out of range are skipped, as in the
+// standalone gather.
 template <int NT>
 __device__ __forceinline__ void gather_page(const StepGather& g, int Nmax, int kb, int page16, int entry, int unit) {
-  constexpr int kBatch = 4;
   const int nf = g.n_fetch[unit];
   if (entry >= nf || entry >= g.cap) return;
   const int b = g.fetch[(static_cast<size_t>(unit) * g.cap + entry) * 2];
   const int s = g.fetch[(static_cast<size_t>(unit) * g.cap + entry) * 2 + 1];
   if (b < 0 || b >= Nmax || s < 0 || s >= kb) return;
-  // native vectors: an array of uint4 structs was left in scratch memory
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(g.host + (static_cast<size_t>(unit) * Nmax + b) * page16);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(g.pool + (static_cast<size_t>(unit) * kb + s) * page16);
-  for (int c0 = 0; c0 < page16; c0 += NT * kBatch) {
-    u32x4_t v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      // every load unconditional (index clamped inside the page), so the batch
-      // stays in registers and its loads are in flight together
-      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
-      v[u] = src[min(c, page16 - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      // lanes past the page's end rewrite its last 16 bytes with the same bytes
-      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
-      dst[min(c, page16 - 1)] = v[u];
-    }
-  }
+#pragma unroll 1
+  for (int c = static_cast<int>(threadIdx.x); c < page16; c += NT) dst[c] = src[c];
 }
 
 // The LDS of a first-launch workgroup: an attention workgroup's, overlaid with
