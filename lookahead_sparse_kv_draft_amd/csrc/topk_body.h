@@ -1,14 +1,16 @@
 // The latency-oriented top-k of one unit by one workgroup of NT threads, every
 // thread holding at most KPT keys in registers (candidate c lives in slot
-// c / NT of thread c % NT).  Shared by the selection kernels (NT = 1024, one
-// workgroup per unit) and by the decode step's first launch when it carries
-// another layer's selection (NT = 128, one workgroup per unit).  The ranking is the total order (descending score,
-// ascending block index) with -0.0 ranked as +0.0; the sink block and the
-// newest block are forced (OasisKV explainer, Figure 7 right: the draft query
-// predicts the next step's top-K blocks).
+// c / NT of thread c % NT).  Shared by the selection kernels (NT = 512 or 1024,
+// one workgroup per unit) and by the decode step's first launch when it carries
+// another layer's selection (NT = 128, one workgroup per unit).  The ranking is
+// the total order (descending score, ascending block index) with -0.0 ranked as
+// +0.0; the sink block and the newest block are forced (OasisKV explainer,
+// Figure 7 right: the draft query predicts the next step's top-K blocks).
 //
-// Serial chains are what cost time in a kernel this small, so each step is
-// spread over all threads:
+// Serial chains and instruction counts are what cost time in a kernel this
+// small (two wavefronts per SIMD issue about one instruction each per four
+// cycles), so each step is spread over all threads and the bookkeeping that is
+// the same for every thread is kept in scalar registers:
 //   * the radix digits are 10 bits (1024 histogram bins, 1024 / NT consecutive
 //     bins per thread) taken from the highest bit where the keys differ (block
 //     min/max), so the first pass already spreads the keys; the search stops as
