@@ -185,11 +185,17 @@ def cpu_baseline(cfg, target_s: float):
 
 
 def op_source_hash(op: str) -> str:
+    """Hash of the code of an op's sources: comments and whitespace removed, so
+    that only a change of the code itself invalidates measured traffic."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in OP_SOURCES[op]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
