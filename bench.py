@@ -918,7 +918,11 @@ def main():
     # event: the GPU stays busy while the host enqueues the first calls, so the
     # events time K back-to-back calls and not the host's launch latency after a
     # synchronisation (which added 10-30 us to the first step).  The spin's
-    # length is calibrated here, untimed.
+    # length is calibrated here, untimed, on a second spin (the first launch of
+    # the spin kernel also loads its code, which made the calibrated lead a
+    # quarter of its intended length).
+    torch.cuda._sleep(1_000)
+    torch.cuda.synchronize()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record(cs0)
     torch.cuda._sleep(1_000_000)
