@@ -68,6 +68,20 @@ def test_load_traffic_drops_ops_whose_sources_changed(tmp_path, monkeypatch):
     assert bench.load_traffic("absent") == {}
 
 
+def test_source_hash_covers_code_not_comments(tmp_path, monkeypatch):
+    """Measured traffic stays valid across comment and whitespace edits of an
+    op's sources and is dropped when their code changes."""
+    src = tmp_path / "score.hip"
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    monkeypatch.setitem(bench.OP_SOURCES, "lookahead_score", ["score.hip"])
+    src.write_text("// header\nint f(int x) {\n  return x + 1;  // one\n}\n")
+    h0 = bench.op_source_hash("lookahead_score")
+    src.write_text("/* a longer\n   header */\nint f(int x)   {\n\n  return x + 1;\n}\n")
+    assert bench.op_source_hash("lookahead_score") == h0
+    src.write_text("// header\nint f(int x) {\n  return x + 2;  // one\n}\n")
+    assert bench.op_source_hash("lookahead_score") != h0
+
+
 def test_counter_summary_means_per_kernel_and_counter(tmp_path):
     a, b, out = tmp_path / "a.csv", tmp_path / "b.csv", tmp_path / "c.txt"
     _write(a, "MfmaUtil", [(STEP1, 4.0), (STEP1, 6.0), (SCORE, 2.0)])
