@@ -750,6 +750,9 @@ def test_select_and_diff_matches_separate_calls_and_oracle(k, cap, ctxs, kind):
     (8192, 128, 32, "ties", [16 * 8192, 16 * 6000 + 3]),      # 64 keys per thread
     (8192, 128, 16, "const", [16 * 8192, 16 * 4100]),
     (8192, 128, 32, "normal", [16 * 8000, 16 * 129]),
+    # one to three blocks: only the forced blocks, or a single candidate
+    (300, 64, 16, "normal", [1, 16 * 2 + 1]),
+    (2048, 128, 8, "ties", [16, 17]),
 ])
 def test_carried_selection_matches_select_and_diff(Nmax, k, cap, kind, ctxs):
     """The selection and diff carried by a decode step's first launch (128-thread
