@@ -787,13 +787,18 @@ def main():
     def sequential_step(i, cs):
         """One decode step over all layers: the single decode-step call per layer
         (attention beside the scoring in one launch; selection, diff and the
-        attention's split combine in the second), after the layer's append."""
+        attention's split combine in the second; other shapes in three); with
+        an append, the call that carries the layer's token append."""
         rep = i % replicas
         t = i % cfg.steps
         for l in range(run.L):
             q = run.q[l, t + 1]
             st = rt.state[l][rep]
-            append(l, t, st, cs)
+            if cfg.append:
+                L.oasis_decode_step_append(rt.h, q, st.pool, st.meta, ctx_in, ctx_grown, st.sel, st.b2s, st.s2b,
+                                           st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict,
+                                           st.attend, st.n_attend, run.k_new_dev[l, t], run.v_new_dev[l, t], cs)
+                continue
             L.oasis_decode_step(rt.h, q, st.pool, st.meta, rt.ctx_len, ctx_score, st.sel, st.b2s, st.s2b,
                                 st.scores, rt.out, rt.ws_ptr, st.fetch, st.n_fetch, st.evict, st.attend,
                                 st.n_attend, stream=cs)
@@ -1101,7 +1106,10 @@ def main():
         "kernels": kern,
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
-                      "eager": "one decode-step call per layer (2 launches) on one stream",
+                      "eager": ("one oasis_decode_step_append call per layer on one stream (the token's "
+                                "metadata row carried by the step's attention launch and its page row by the "
+                                "scoring launch where the two run on their own)" if cfg.append else
+                                "one decode-step call per layer (2 launches) on one stream"),
                       "carry": "one call per layer (2 launches) on one stream whose first launch carries the "
                                "previous layer's selection and diff (the last layer's in the next step's first "
                                "layer; the last step's run on its own) and whose second is the split combine",

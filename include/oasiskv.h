@@ -490,6 +490,29 @@ typedef struct oasis_select_job {
 } oasis_select_job;
 
 /*
+ * A layer's decode step that also appends this step's token (long-output
+ * decode, [EXPL] Figure 7 left and Figure 8): bit-identical with
+ *   oasis_block_meta_update(k_new, v_new, ctx_in, ctx_out, meta, pool, block_to_slot)
+ *   oasis_decode_step(q, pool, meta, ctx_attn = ctx_in, ctx_score = ctx_out, ...)
+ * on `stream`, with one launch fewer where the step's attention and scoring run
+ * as launches of their own (bf16 shapes whose attention writes its output
+ * without a split combine, e.g. one attention workgroup per (request, KV
+ * head)): one workgroup per (request, KV head) after the attention's updates
+ * the token's metadata row and ctx_out (the attention reads no metadata), and
+ * one after the scoring's writes the token's K / V rows into its block's page
+ * when resident (the scoring reads no pages; the next step's attention is the
+ * first reader).  Other shapes enqueue the append kernel first.  k_new, v_new:
+ * [B][H][d] device; ctx_out (written: ctx_in + 1) must not alias ctx_in
+ * (EINVAL); pool and meta are written.  Other arguments and errors as for
+ * oasis_decode_step.
+ */
+int oasis_decode_step_append(oasis_handle h, const void* q, void* pool, void* meta, const int32_t* ctx_in,
+                             int32_t* ctx_out, int32_t* sel, int32_t* block_to_slot, int32_t* slot_to_block,
+                             float* scores, float* out, void* workspace, int32_t* fetch, int32_t* n_fetch,
+                             int32_t* evict, int32_t* attend, int32_t* n_attend, const void* k_new,
+                             const void* v_new, void* stream);
+
+/*
  * A layer's decode step whose first launch carries another state's selection
  * ([EXPL] Figure 8: a layer's prediction, selection and transfer proceed while
  * later layers compute; only that layer's next attention needs them).  Two

@@ -87,6 +87,7 @@ SIGNATURES = {
     "oasis_sparse_paged_decode_attn": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "oasis_decode_step": (_int, [_vp] * 18),
     "oasis_decode_step_gather": (_int, [_vp] * 17 + [ctypes.POINTER(oasis_transfer), _vp]),
+    "oasis_decode_step_append": (_int, [_vp] * 20),
     "oasis_decode_step_carry": (_int, [_vp] * 11 + [ctypes.POINTER(oasis_select_job),
                                                      ctypes.POINTER(oasis_transfer), _vp]),
     "oasis_sparse_paged_decode_attn_list": (_int, [_vp] * 9),
@@ -300,6 +301,13 @@ def oasis_decode_step(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot,
 def oasis_sparse_paged_decode_attn_noalloc(h, q, pool, sel, block_to_slot, ctx_len, out, stream=None):
     _call("oasis_sparse_paged_decode_attn_noalloc", h, _ptr(q), _ptr(pool), _ptr(sel), _ptr(block_to_slot),
           _ptr(ctx_len), _ptr(out), _stream(stream))
+
+
+def oasis_decode_step_append(h, q, pool, meta, ctx_in, ctx_out, sel, block_to_slot, slot_to_block, scores, out,
+                             workspace, fetch, n_fetch, evict, attend, n_attend, k_new, v_new, stream=None):
+    _call("oasis_decode_step_append", h, _ptr(q), _ptr(pool), _ptr(meta), _ptr(ctx_in), _ptr(ctx_out), _ptr(sel),
+          _ptr(block_to_slot), _ptr(slot_to_block), _ptr(scores), _ptr(out), _ptr(workspace), _ptr(fetch),
+          _ptr(n_fetch), _ptr(evict), _ptr(attend), _ptr(n_attend), _ptr(k_new), _ptr(v_new), _stream(stream))
 
 
 def oasis_decode_step_gather(h, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block, scores, out,

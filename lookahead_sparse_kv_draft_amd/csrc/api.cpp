@@ -754,15 +754,27 @@ namespace {
 
 // The decode step of one layer, optionally carrying another layer's transfer
 // (g.host != nullptr) in its first launch; arguments already validated.
+// ap: a token append the step carries (its scoring then reads the grown
+// context ctx_score = ap->ctx_out): where the attention (bf16, its output
+// written without a combine) and the scoring are launches of their own, the
+// attention launch updates the token's metadata row and the scoring launch
+// writes its page row, one workgroup per unit each; otherwise the append
+// kernel runs first.
 hipError_t decode_step_impl(const oasis::Ctx& c, const void* q, const void* pool, const void* meta,
                             const int32_t* ctx_attn, const int32_t* ctx_score, int32_t* sel, int32_t* block_to_slot,
                             int32_t* slot_to_block, float* scores, float* out, void* workspace, int32_t* fetch,
                             int32_t* n_fetch, int32_t* evict, int32_t* attend, int32_t* n_attend,
-                            const oasis::StepGather& g, hipStream_t st) {
+                            const oasis::StepGather& g, hipStream_t st, const oasis::StepAppend* ap = nullptr) {
   hipError_t e;
   if (oasis::attn_needs_combine(c) && oasis::attn_and_score_fused_available(c) &&
       oasis::select_diff_fused_available(c) && c.step_launches == 2) {
-    // two launches: (the carried transfer,) attention + scoring, then selection + diff + split combine
+    // two launches: (the carried transfer,) attention + scoring, then selection + diff + split combine;
+    // the scoring reads the appended token's metadata, so an append goes first
+    if (ap != nullptr) {
+      e = oasis::launch_meta_update(c, ap->k_new, ap->v_new, ap->ctx_in, ap->ctx_out, ap->meta, ap->pool, ap->b2s,
+                                    st);
+      if (e != hipSuccess) return e;
+    }
     e = oasis::launch_attn_and_score(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace,
                                      meta, ctx_score, scores, st, g);
     if (e == hipSuccess)
@@ -775,14 +787,20 @@ hipError_t decode_step_impl(const oasis::Ctx& c, const void* q, const void* pool
     e = oasis::launch_fetch_gather(c, g.host, g.pool, g.fetch, g.n_fetch, st);
     if (e != hipSuccess) return e;
   }
-  if (c.s.dtype == OASIS_BF16 && oasis::attn_needs_combine(c)) {
+  const bool attn_alone = !(c.s.dtype == OASIS_BF16 && oasis::attn_needs_combine(c));
+  const oasis::StepAppend* ride = (ap != nullptr && c.s.dtype == OASIS_BF16 && attn_alone) ? ap : nullptr;
+  if (ap != nullptr && ride == nullptr) {
+    e = oasis::launch_meta_update(c, ap->k_new, ap->v_new, ap->ctx_in, ap->ctx_out, ap->meta, ap->pool, ap->b2s, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!attn_alone) {
     e = oasis::launch_attn_main(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace, st);
     if (e == hipSuccess) e = oasis::launch_combine_and_score(c, workspace, out, q, meta, ctx_score, scores, st);
   } else {
     // the fp32 reference path attends from the maps (the list splits differently)
     e = oasis::launch_attn(c, q, pool, sel, block_to_slot, c.s.dtype == OASIS_BF16 ? attend : nullptr,
-                           c.s.dtype == OASIS_BF16 ? n_attend : nullptr, ctx_attn, out, workspace, st);
-    if (e == hipSuccess) e = oasis::launch_score(c, q, meta, ctx_score, scores, st);
+                           c.s.dtype == OASIS_BF16 ? n_attend : nullptr, ctx_attn, out, workspace, st, ride);
+    if (e == hipSuccess) e = oasis::launch_score(c, q, meta, ctx_score, scores, st, false, ride);
   }
   if (e == hipSuccess) {
     if (oasis::select_diff_fused_available(c)) {
@@ -926,6 +944,32 @@ int oasis_decode_step(oasis_handle h, const void* q, const void* pool, const voi
                                      scores, out, workspace, fetch, n_fetch, evict, attend, n_attend,
                                      oasis::StepGather(), static_cast<hipStream_t>(stream)),
                     "oasis_decode_step");
+}
+
+int oasis_decode_step_append(oasis_handle h, const void* q, void* pool, void* meta, const int32_t* ctx_in,
+                             int32_t* ctx_out, int32_t* sel, int32_t* block_to_slot, int32_t* slot_to_block,
+                             float* scores, float* out, void* workspace, int32_t* fetch, int32_t* n_fetch,
+                             int32_t* evict, int32_t* attend, int32_t* n_attend, const void* k_new,
+                             const void* v_new, void* stream) {
+  const int32_t* ctx_attn = ctx_in;
+  const int32_t* ctx_score = ctx_out;
+  CHECK_DECODE_STEP_ARGS("oasis_decode_step_append");
+  CHECK_PTR(k_new);
+  CHECK_PTR(v_new);
+  if (static_cast<const void*>(ctx_in) == static_cast<const void*>(ctx_out))
+    return fail(OASIS_EINVAL, "oasis_decode_step_append: ctx_out aliases ctx_in");
+  oasis::StepAppend ap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.ctx_in = ctx_in;
+  ap.ctx_out = ctx_out;
+  ap.meta = meta;
+  ap.pool = pool;
+  ap.b2s = block_to_slot;
+  return hip_status(decode_step_impl(h->c, q, pool, meta, ctx_attn, ctx_score, sel, block_to_slot, slot_to_block,
+                                     scores, out, workspace, fetch, n_fetch, evict, attend, n_attend,
+                                     oasis::StepGather(), static_cast<hipStream_t>(stream), &ap),
+                    "oasis_decode_step_append");
 }
 
 int oasis_decode_step_gather(oasis_handle h, const void* q, const void* pool, const void* meta,

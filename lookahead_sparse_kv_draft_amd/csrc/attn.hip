@@ -28,20 +28,32 @@
 #include <algorithm>
 #include <mutex>
 
+#include "append_body.h"
 #include "attn_body.h"
 #include "attn_combine.h"
 
 namespace oasis {
 namespace {
 
+// n_app_wg workgroups (one per unit, or none) after the attention's update the
+// metadata row of a token being appended (the attention reads no metadata; the
+// token's page row is written by the scoring launch that follows, which reads
+// no pages: written here, beside the attention's reads of the same pages, it
+// made the launch several microseconds longer).
 template <int D, int RT, int W, int PF>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((PF <= 2 && RT <= 3) ? 2 : 1))) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ pool,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend,
     const int32_t* __restrict__ n_attend, const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, float* __restrict__ out, int H, int rows, int Nmax, int kb,
-    int splits, int run, float scale_log2) {
+    int splits, int run, float scale_log2, StepAppend app, int n_app_wg) {
   __shared__ AttnLds<D, RT, W> lds;
+  const int n_attn_wg = static_cast<int>(gridDim.x) - n_app_wg;
+  if (static_cast<int>(blockIdx.x) >= n_attn_wg) {
+    append_meta<uint16_t, D>(static_cast<const uint16_t*>(app.k_new), app.ctx_in, app.ctx_out,
+                             static_cast<uint16_t*>(app.meta), blockIdx.x - n_attn_wg, H, Nmax, threadIdx.x, 64 * W);
+    return;
+  }
   attn_wg<D, RT, W, PF>(q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, H, rows, Nmax, kb, splits,
                         run, scale_log2, blockIdx.x, lds);
 }
@@ -163,50 +175,53 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 template <int D, int RT, int W, int PF>
 hipError_t mfma_wp(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                    const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_len, float* ws_acc,
-                   float* ws_ml, float* out, float scale_log2, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, RT, W, PF>), dim3(c.units * c.attn_splits), dim3(W * kWave), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s, attend,
+                   float* ws_ml, float* out, float scale_log2, hipStream_t st, const StepAppend* ap) {
+  const int n_app_wg = ap != nullptr ? c.units : 0;
+  hipLaunchKernelGGL((attn_mfma_kernel<D, RT, W, PF>), dim3(n_app_wg + c.units * c.attn_splits), dim3(W * kWave), 0,
+                     st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(pool), sel, b2s, attend,
                      n_attend, ctx_len,
                      ws_acc, ws_ml, out, c.s.kv_heads, c.rows_attn, c.s.max_blocks,
-                     c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2);
+                     c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2,
+                     ap != nullptr ? *ap : StepAppend(), n_app_wg);
   return hipGetLastError();
 }
 
 template <int D, int RT, int W>
 hipError_t mfma_w(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                   const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_len, float* ws_acc,
-                  float* ws_ml, float* out, float scale_log2, hipStream_t st) {
+                  float* ws_ml, float* out, float scale_log2, hipStream_t st, const StepAppend* ap) {
   switch (c.attn_pf) {
-    case 2: return mfma_wp<D, RT, W, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-    case 4: return mfma_wp<D, RT, W, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-    default: return mfma_wp<D, RT, W, 8>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    case 2: return mfma_wp<D, RT, W, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+    case 4: return mfma_wp<D, RT, W, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+    default: return mfma_wp<D, RT, W, 8>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
   }
 }
 
 template <int D, int RT>
 hipError_t mfma_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                   const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_len, float* ws_acc,
-                  float* ws_ml, float* out, float scale_log2, hipStream_t st) {
-  if (c.attn_waves == 1) return mfma_w<D, RT, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+                  float* ws_ml, float* out, float scale_log2, hipStream_t st, const StepAppend* ap) {
+  if (c.attn_waves == 1) return mfma_w<D, RT, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
   // at most 2 wavefronts for 3 or 4 row tiles (LDS of the wavefront merge)
   if (RT >= 3 || c.attn_waves == 2)
-    return mfma_w<D, RT, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-  return mfma_w<D, RT, (RT >= 3 ? 2 : 4)>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+    return mfma_w<D, RT, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+  return mfma_w<D, RT, (RT >= 3 ? 2 : 4)>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
 }
 
 template <int D>
 hipError_t main_t(const Ctx& c, const void* q, const void* pool, const int32_t* sel, const int32_t* b2s,
                   const int32_t* attend, const int32_t* n_attend, const int32_t* ctx_len, float* ws_acc,
-                  float* ws_ml, float* out, hipStream_t st) {
+                  float* ws_ml, float* out, hipStream_t st, const StepAppend* ap) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   if (c.s.dtype == OASIS_BF16) {
     switch ((c.rows_attn + 15) / 16) {
-      case 1: return mfma_t<D, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-      case 2: return mfma_t<D, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-      case 3: return mfma_t<D, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
-      default: return mfma_t<D, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st);
+      case 1: return mfma_t<D, 1>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+      case 2: return mfma_t<D, 2>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+      case 3: return mfma_t<D, 3>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
+      default: return mfma_t<D, 4>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, scale_log2, st, ap);
     }
   }
+  if (ap != nullptr) return hipErrorInvalidValue;  // the fp32 kernel carries no append
   const int rows = c.rows_attn;
   const size_t lds = (static_cast<size_t>(rows) * D + rows * kBlock + 3 * rows) * sizeof(float);
   hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(c.units * c.attn_splits), dim3(256), lds, st,
@@ -251,11 +266,12 @@ bool attn_needs_combine(const Ctx& c) {
 
 hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                             const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
-                            const int32_t* ctx_len, float* out, void* ws, hipStream_t st) {
+                            const int32_t* ctx_len, float* out, void* ws, hipStream_t st, const StepAppend* ap) {
   float* ws_acc = static_cast<float*>(ws);
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));
-  return (c.s.head_dim == 128) ? main_t<128>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, st)
-                               : main_t<64>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, st);
+  return (c.s.head_dim == 128)
+             ? main_t<128>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, st, ap)
+             : main_t<64>(c, q, pool, sel, b2s, attend, n_attend, ctx_len, ws_acc, ws_ml, out, st, ap);
 }
 
 hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t st) {
@@ -267,13 +283,13 @@ hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t s
 
 hipError_t launch_attn(const Ctx& c0, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
-                       const int32_t* ctx_len, float* out, void* ws, hipStream_t st) {
+                       const int32_t* ctx_len, float* out, void* ws, hipStream_t st, const StepAppend* ap) {
   // the attention on its own: its own split shape (the workspace fits the larger one)
   Ctx c = c0;
   c.attn_splits = c0.attn_splits_solo;
   c.attn_run = c0.attn_run_solo;
   c.attn_split_len = c0.attn_waves * c0.attn_run_solo;
-  hipError_t e = launch_attn_main(c, q, pool, sel, b2s, attend, n_attend, ctx_len, out, ws, st);
+  hipError_t e = launch_attn_main(c, q, pool, sel, b2s, attend, n_attend, ctx_len, out, ws, st, ap);
   if (e != hipSuccess || !attn_needs_combine(c)) return e;
   float* ws_acc = static_cast<float*>(ws);
   float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_acc_bytes(c));

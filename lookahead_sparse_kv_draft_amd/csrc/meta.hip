@@ -10,20 +10,10 @@
 //  admit       - one wavefront per block of a prefill on the device: page into
 //                the pinned host tier (and its pool slot if resident) plus the
 //                metadata row.
-#include "oasis_internal.h"
+#include "append_body.h"
 
 namespace oasis {
 namespace {
-
-template <typename E> struct Elem;
-template <> struct Elem<uint16_t> {
-  static __device__ __forceinline__ float load(uint16_t v) { return bf16_to_f32(v); }
-  static __device__ __forceinline__ uint16_t store(float f) { return f32_to_bf16(f); }
-};
-template <> struct Elem<float> {
-  static __device__ __forceinline__ float load(float v) { return v; }
-  static __device__ __forceinline__ float store(float f) { return f; }
-};
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void meta_build_kernel(
@@ -133,41 +123,7 @@ __global__ __launch_bounds__(64) void meta_update_kernel(
     const E* __restrict__ k_new, const E* __restrict__ v_new, const int32_t* __restrict__ ctx_in,
     int32_t* __restrict__ ctx_out, E* __restrict__ meta, E* __restrict__ pool,
     const int32_t* __restrict__ b2s, int H, int Nmax, int kb) {
-  constexpr int PAGE = 2 * kBlock * D;
-  const int unit = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int r = unit / H;
-  const int h = unit - r * H;
-  const int p = ctx_in[r];
-  const int b = p / kBlock;
-  const int j = p - b * kBlock;
-  if (p < 0 || b >= Nmax) return;
-  const size_t id = static_cast<size_t>(unit) * Nmax + b;
-  constexpr int CE = 16 / static_cast<int>(sizeof(E));
-  const E* kn = k_new + static_cast<size_t>(unit) * D;
-  const E* vn = v_new + static_cast<size_t>(unit) * D;
-  for (int c = lane; c < D; c += kWave) {
-    const E kv = kn[c];
-    E* mn = meta + meta_offset<D, CE>(unit, b, c, Nmax);
-    E* mx = meta + meta_offset<D, CE>(unit, b, D + c, Nmax);
-    if (j == 0) {
-      *mn = kv;
-      *mx = kv;
-    } else {
-      const float kf = Elem<E>::load(kv);
-      *mn = Elem<E>::store(fminf(Elem<E>::load(*mn), kf));
-      *mx = Elem<E>::store(fmaxf(Elem<E>::load(*mx), kf));
-    }
-  }
-  const int slot = b2s[id];
-  if (slot >= 0 && slot < kb) {
-    E* pg = pool + (static_cast<size_t>(unit) * kb + slot) * PAGE;
-    for (int c = lane; c < D; c += kWave) {
-      pg[j * D + c] = kn[c];                  // K row j (token-major)
-      pg[kBlock * D + c * kBlock + j] = vn[c];  // V^T column j (channel-major)
-    }
-  }
-  if (h == 0 && lane == 0) ctx_out[r] = p + 1;
+  append_token<E, D>(k_new, v_new, ctx_in, ctx_out, meta, pool, b2s, blockIdx.x, H, Nmax, kb, threadIdx.x, kWave);
 }
 
 // Admission of a prefill: one wavefront per (unit, block) below the context.

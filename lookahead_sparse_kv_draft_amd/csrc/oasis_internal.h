@@ -73,10 +73,23 @@ hipError_t launch_meta_update(const Ctx& c, const void* k_new, const void* v_new
 // and resident pool slots, plus the metadata rows.
 hipError_t launch_admit(const Ctx& c, const void* k_rows, const void* v_rows, const int32_t* ctx_len,
                         void* host_dev, void* meta, void* pool, const int32_t* b2s, hipStream_t st);
+// A token append a decode step's launches carry (bf16): the token's K / V rows
+// [B][H][d], its position per request (ctx_in) and ctx_in + 1 (ctx_out), and
+// the metadata, pool and block map it updates (as oasis_block_meta_update).
+struct StepAppend {
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int32_t* ctx_in = nullptr;
+  int32_t* ctx_out = nullptr;
+  void* meta = nullptr;
+  void* pool = nullptr;
+  const int32_t* b2s = nullptr;
+};
 // The lookahead score from the draft rows, or (verify) the same bound from the
-// verify query rows.
+// verify query rows.  With `ap` (bf16 only) one workgroup per unit after the
+// scoring writes the appended token's page row (the scoring reads no pages).
 hipError_t launch_score(const Ctx& c, const void* q, const void* meta, const int32_t* ctx_len,
-                        float* scores, hipStream_t st, bool verify = false);
+                        float* scores, hipStream_t st, bool verify = false, const StepAppend* ap = nullptr);
 hipError_t launch_topk(const Ctx& c, const float* scores, const int32_t* ctx_len, int32_t* sel,
                        hipStream_t st);
 bool select_diff_fused_available(const Ctx& c);
@@ -98,14 +111,18 @@ hipError_t launch_diff(const Ctx& c, const int32_t* sel, const float* scores, in
                        int32_t* s2b, int32_t* fetch, int32_t* n_fetch, int32_t* evict,
                        int32_t* attend, int32_t* n_attend, hipStream_t st);
 // Attention over S ∩ R given either (sel, b2s) or, when attend is not null, the
-// attended list a diff produced (sel and b2s are then ignored).
+// attended list a diff produced (sel and b2s are then ignored).  With `ap`
+// (bf16 only) one workgroup per unit after the attention updates the appended
+// token's metadata row (its page row is left to the scoring launch).
 hipError_t launch_attn(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
-                       const int32_t* ctx_len, float* out, void* ws, hipStream_t st);
+                       const int32_t* ctx_len, float* out, void* ws, hipStream_t st,
+                       const StepAppend* ap = nullptr);
 // The attention without its split combine, and whether a combine must follow.
 hipError_t launch_attn_main(const Ctx& c, const void* q, const void* pool, const int32_t* sel,
                             const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
-                            const int32_t* ctx_len, float* out, void* ws, hipStream_t st);
+                            const int32_t* ctx_len, float* out, void* ws, hipStream_t st,
+                            const StepAppend* ap = nullptr);
 bool attn_needs_combine(const Ctx& c);
 // The split combine alone (nothing to do when the attention wrote the output).
 hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t st);

@@ -217,6 +217,34 @@ def test_decode_step_gather_rejects_its_own_pool():
         L.oasis_destroy(h)
 
 
+def test_decode_step_append_rejects_before_any_launch():
+    """The step that carries the token append: missing pointers (the step's
+    own and the token's), a misaligned workspace and a grown context that
+    aliases the positions are EINVAL, on the host, before any launch."""
+    lib = L.load()
+    # q, pool, meta, ctx_in, ctx_out, sel, b2s, s2b, scores, out, workspace, fetch, n_fetch, evict, attend,
+    # n_attend, k_new, v_new (fake device addresses: nothing is launched)
+    args = list(range(256, 256 * 19, 256))
+    h = L.oasis_create(**_shape())
+    try:
+        for i in (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 16, 17):
+            a = list(args)
+            a[i] = None
+            assert lib.oasis_decode_step_append(h, *a, None) == L.OASIS_EINVAL, i
+        a = list(args)
+        a[10] = 272  # workspace not 256-byte aligned
+        assert lib.oasis_decode_step_append(h, *a, None) == L.OASIS_EINVAL
+        a = list(args)
+        a[4] = a[3]  # ctx_out aliases ctx_in
+        assert lib.oasis_decode_step_append(h, *a, None) == L.OASIS_EINVAL
+        assert "aliases" in L.oasis_last_error()
+        a = list(args)
+        a[14] = None  # attend without n_attend
+        assert lib.oasis_decode_step_append(h, *a, None) == L.OASIS_EINVAL
+    finally:
+        L.oasis_destroy(h)
+
+
 def test_decode_step_carry_rejects_before_any_launch():
     """The step that carries another state's selection: missing pointers, a job
     that is this step's own state, and a transfer reading the fetch list the

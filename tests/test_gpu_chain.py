@@ -285,6 +285,49 @@ def test_carry_step_matches_separate_calls(name, kw):
                                         SyntheticRun(cfg, overlap=False, fused_step=False)])
 
 
+@pytest.mark.parametrize("dtype,options", [
+    ("bf16", {"attn_splits": 1}),      # attention and scoring launches carry the metadata and page rows
+    ("bf16", {"step_launches": 3}),    # three launches (with a split combine: the append launch first)
+    ("bf16", None),                    # attention beside the scoring: the append launch goes first
+    ("f32", None),                     # fp32: the append launch goes first
+])
+def test_decode_step_append_matches_separate_calls(dtype, options):
+    """oasis_decode_step_append against oasis_block_meta_update followed by
+    oasis_decode_step on an identical copy of the state, over steps that cross
+    a block boundary: every output, the grown context, the metadata, the pool
+    and every list and map bit for bit."""
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    cfg = CONFIGS["qwen8b_reason"].with_(batch=2, ctx=16 * 40 + 13, steps=5, dtype=dtype, budget_tokens=16 * 16,
+                                         fetch_cap=4, planted=6)
+    print(f"{dtype} {options}", flush=True)
+    run = SyntheticRun(cfg, replicas=2, overlap=False, options=options)
+    try:
+        run.prologue()
+        rt = run.rt
+        a, b = rt.state[0][0], rt.state[0][1]
+        b.copy_from(a)
+        torch.cuda.synchronize()
+        base = torch.tensor([cfg.ctx_of(r) for r in range(cfg.batch)], dtype=torch.int32, device="cuda")
+        out_a, out_b = torch.zeros_like(rt.out), torch.zeros_like(rt.out)
+        for t in range(cfg.steps):
+            ctx_in = base + t
+            grown_a, grown_b = torch.zeros_like(ctx_in), torch.zeros_like(ctx_in)
+            q, kn, vn = run.q[0, t + 1], run.k_new_dev[0, t], run.v_new_dev[0, t]
+            L.oasis_block_meta_update(rt.h, kn, vn, ctx_in, grown_a, a.meta, a.pool, a.b2s)
+            L.oasis_decode_step(rt.h, q, a.pool, a.meta, ctx_in, grown_a, a.sel, a.b2s, a.s2b, a.scores, out_a,
+                                rt.ws_ptr, a.fetch, a.n_fetch, a.evict, a.attend, a.n_attend)
+            L.oasis_decode_step_append(rt.h, q, b.pool, b.meta, ctx_in, grown_b, b.sel, b.b2s, b.s2b, b.scores,
+                                       out_b, rt.ws_ptr, b.fetch, b.n_fetch, b.evict, b.attend, b.n_attend, kn, vn)
+            torch.cuda.synchronize()
+            assert torch.equal(out_a, out_b), t
+            assert torch.equal(grown_a, grown_b) and torch.equal(grown_a, ctx_in + 1), t
+            for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict", "attend",
+                         "n_attend"):
+                assert torch.equal(getattr(a, name), getattr(b, name)), (t, name)
+    finally:
+        run.close()
+
+
 def _outputs_without_step_syncs(cfg, **kw):
     """All steps enqueued back to back (carried selections and inline transfers
     cross step boundaries); every layer's output copied on the stream; the
