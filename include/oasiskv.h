@@ -90,6 +90,8 @@ typedef struct oasis_launch_options {
   int32_t attn_waves;     /* wavefronts per attention workgroup: 0, 1, 2 or 4 (default 2;
                              at most 2 with more than 32 attention rows) */
   int32_t attn_pf;        /* pages in flight per attention wavefront: 0, 2, 4 or 8 (default 2;
+                             4 for the attention as a launch of its own when it runs one
+                             split of 64-block runs per unit at one wavefront per SIMD;
                              capped by the registers the row count needs) */
   int32_t attn_splits;    /* attention workgroups per unit, 0..32 (default: about 512
                              attention wavefronts per launch; bounded so that a

@@ -154,10 +154,18 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   const int splits = shape_splits(512, &run);
   const int splits_solo = shape_splits(512, &run_solo);
   const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
-  // measured: a shallow ring keeps the math beside the loads
+  // measured: a shallow ring keeps the math beside the loads, except where the
+  // attention on its own gives each wavefront a whole unit's 64-block run in
+  // one split at one wavefront per SIMD: there 4 pages in flight (the batch-64
+  // reasoning workload: 60.8 against 62.4-63.3 us alone, the three-launch step
+  // 115.3 against 118.4-119.7 us; with 2 to 8 splits of 8- to 32-block runs
+  // the 4-page ring was 12-18 % slower)
   const int pf = std::min(o.attn_pf != 0 ? o.attn_pf : 2, max_pf);
+  const bool long_runs = splits_solo == 1 && run_solo >= 64 && c.units * waves <= 4 * 256;
+  const int pf_solo = std::min(o.attn_pf != 0 ? o.attn_pf : (long_runs ? 4 : 2), max_pf);
   c.attn_waves = waves;
   c.attn_pf = pf;
+  c.attn_pf_solo = pf_solo;
   c.attn_run = run;
   c.attn_split_len = waves * run;
   c.attn_splits = splits;

@@ -284,10 +284,11 @@ hipError_t launch_attn_combine(const Ctx& c, void* ws, float* out, hipStream_t s
 hipError_t launch_attn(const Ctx& c0, const void* q, const void* pool, const int32_t* sel,
                        const int32_t* b2s, const int32_t* attend, const int32_t* n_attend,
                        const int32_t* ctx_len, float* out, void* ws, hipStream_t st, const StepAppend* ap) {
-  // the attention on its own: its own split shape (the workspace fits the larger one)
+  // the attention on its own: its own split shape and ring (the workspace fits the larger one)
   Ctx c = c0;
   c.attn_splits = c0.attn_splits_solo;
   c.attn_run = c0.attn_run_solo;
+  c.attn_pf = c0.attn_pf_solo;
   c.attn_split_len = c0.attn_waves * c0.attn_run_solo;
   hipError_t e = launch_attn_main(c, q, pool, sel, b2s, attend, n_attend, ctx_len, out, ws, st, ap);
   if (e != hipSuccess || !attn_needs_combine(c)) return e;

@@ -46,8 +46,8 @@ struct Ctx {
   int attn_split_len;  // selection entries per split (attn_waves * attn_run)
   int attn_run;     // selection entries per attention wavefront (<= 64)
   // The attention on its own (not sharing the decode step's launch): its own
-  // split count and run (fewer, longer wavefronts are best there).
-  int attn_splits_solo, attn_run_solo;
+  // split count, run (fewer, longer wavefronts are best there) and ring.
+  int attn_splits_solo, attn_run_solo, attn_pf_solo;
   int attn_waves;   // wavefronts per attention workgroup (1, 2 or 4)
   int attn_pf;      // pages in flight per attention wavefront (2, 4 or 8)
   int score_tpw;    // 16-block tiles per scoring wave beside the attention in the step's launch
