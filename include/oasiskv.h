@@ -209,7 +209,10 @@ int oasis_admit(oasis_handle h, const void* k_rows, const void* v_rows, const in
  * device.  The token goes to position p = ctx_len_in[r]: the metadata row of
  * block p/16 is initialised to the token (p % 16 == 0) or absorbs it by
  * min/max; if that block is resident its pool page row is written too.
- * ctx_len_out[r] = p + 1 (ctx_len_out must not alias ctx_len_in).
+ * ctx_len_out[r] = p + 1 (ctx_len_out must not alias ctx_len_in).  A position
+ * outside [0, 16*max_blocks) is a caller error the device cannot report: that
+ * request's metadata and pages are left as they are and ctx_len_out[r] = p
+ * (the context does not grow).
  */
 int oasis_block_meta_update(oasis_handle h, const void* k_new, const void* v_new,
                             const int32_t* ctx_len_in, int32_t* ctx_len_out, void* meta,
@@ -504,7 +507,8 @@ typedef struct oasis_select_job {
  * one after the scoring's writes the token's K / V rows into its block's page
  * when resident (the scoring reads no pages; the next step's attention is the
  * first reader).  Other shapes enqueue the append kernel first.  k_new, v_new:
- * [B][H][d] device; ctx_out (written: ctx_in + 1) must not alias ctx_in
+ * [B][H][d] device; ctx_out (written: ctx_in + 1, or ctx_in for a position
+ * outside the capacity, as oasis_block_meta_update) must not alias ctx_in
  * (EINVAL); pool and meta are written.  Other arguments and errors as for
  * oasis_decode_step.
  */

@@ -22,8 +22,10 @@ template <> struct Elem<float> {
 // The token of unit `unit` goes to position p = ctx_in[request], block p / 16:
 // its metadata row is set to the token's key (p % 16 == 0) or absorbs it by
 // min / max, and ctx_out[request] = p + 1 (written by the request's first KV
-// head).  Positions outside the capacity change nothing.  Run by nthreads
-// threads (tid = 0 .. nthreads - 1), each taking channels tid, tid + nthreads, ...
+// head).  A position outside [0, 16 * Nmax) writes no metadata and leaves the
+// context as it was (ctx_out[request] = p), so what reads ctx_out next sees a
+// defined length.  Run by nthreads threads (tid = 0 .. nthreads - 1), each
+// taking channels tid, tid + nthreads, ...
 template <typename E, int D>
 __device__ __forceinline__ void append_meta(const E* __restrict__ k_new, const int32_t* __restrict__ ctx_in,
                                             int32_t* __restrict__ ctx_out, E* __restrict__ meta, int unit, int H,
@@ -33,7 +35,10 @@ __device__ __forceinline__ void append_meta(const E* __restrict__ k_new, const i
   const int p = ctx_in[r];
   const int b = p / kBlock;
   const int j = p - b * kBlock;
-  if (p < 0 || b >= Nmax) return;
+  if (p < 0 || b >= Nmax) {
+    if (h == 0 && tid == 0) ctx_out[r] = p;
+    return;
+  }
   constexpr int CE = 16 / static_cast<int>(sizeof(E));
   const E* kn = k_new + static_cast<size_t>(unit) * D;
   for (int c = tid; c < D; c += nthreads) {
@@ -53,7 +58,8 @@ __device__ __forceinline__ void append_meta(const E* __restrict__ k_new, const i
 }
 
 // The same token's K row and V column into the page of block p / 16 if the
-// block holds a slot (b2s); nothing else.  Threads as append_meta.
+// block holds a slot (b2s); nothing else (nothing at all for a position outside
+// the capacity).  Threads as append_meta.
 template <typename E, int D>
 __device__ __forceinline__ void append_page(const E* __restrict__ k_new, const E* __restrict__ v_new,
                                             const int32_t* __restrict__ ctx_in, E* __restrict__ pool,

@@ -437,8 +437,12 @@ class DecodeRuntime:
         of the same step still sees the old one; end_step() makes it current.
         The append may run beside this step's attention: it writes the metadata,
         the other context buffer and page row n % 16, none of which the attention
-        reads (it sees tokens < n).
+        reads (it sees tokens < n).  Raises ValueError if a request's context
+        is already at the capacity (max_blocks * 16 tokens).
         """
+        cap_tokens = self.shape.max_blocks * 16
+        if (self.ctx_host >= cap_tokens).any():
+            raise ValueError(f"append: a context length is at the capacity of {cap_tokens} tokens")
         st = self.state[layer][replica]
         ps = self._pred()
         self._flush_select_of(layer, replica, ps)

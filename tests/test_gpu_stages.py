@@ -497,6 +497,68 @@ def test_meta_build_and_append(dtype, d):
     rt.close()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_append_outside_capacity_keeps_the_context(dtype, d):
+    """A request whose position is at the capacity (16 * max_blocks) appends
+    nothing: no metadata, no page row, and its grown context stays the
+    position; the other requests of the same launch (one of them at the last
+    position inside the capacity) append as usual."""
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    B, H, Nmax, k = 3, 2, 4, 4
+    cap = Nmax * BLK
+    ctxs = [cap, 40, cap - 1]
+    sh = U.make_shape(batch=B, kv_heads=H, head_dim=d, max_blocks=Nmax, budget_blocks=k, fetch_cap=k,
+                      dtype=dtype)
+    rt = DecodeRuntime(sh)
+    rng = _rng(6)
+    units = B * H
+    K = U.elem_round(dtype, rng.standard_normal((units, cap, d)).astype(np.float32))
+    V = U.elem_round(dtype, rng.standard_normal((units, cap, d)).astype(np.float32))
+    for u in range(units):
+        rt.pack_unit(0, u, U.to_elem_np(dtype, K[u]), U.to_elem_np(dtype, V[u]))
+    rt.set_ctx(ctxs)
+    rt.build_meta(0)
+    st = rt.state[0][0]
+    # the block of every request's position (the last one where it is at the capacity) resident in slot 0
+    s2b = np.full((units, k), -1, dtype=np.int32)
+    b2s = np.full((units, Nmax), -1, dtype=np.int32)
+    for u in range(units):
+        b = min(ctxs[u // H], cap - 1) // BLK
+        s2b[u, 0], b2s[u, b] = b, 0
+    st.s2b.copy_(torch.from_numpy(s2b))
+    st.b2s.copy_(torch.from_numpy(b2s))
+    st.pool.zero_()
+    torch.cuda.synchronize()
+    meta0 = rt.meta_view(0).clone()
+    # new tokens: fresh rows (request 0's would go past the capacity)
+    kn = U.elem_round(dtype, rng.standard_normal((B, H, d)).astype(np.float32) * 3)
+    vn = U.elem_round(dtype, rng.standard_normal((B, H, d)).astype(np.float32))
+    ctx_in = torch.tensor(ctxs, dtype=torch.int32, device="cuda")
+    ctx_out = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    L.oasis_block_meta_update(rt.h, U.to_dev(dtype, kn), U.to_dev(dtype, vn), ctx_in, ctx_out, st.meta, st.pool,
+                              st.b2s)
+    torch.cuda.synchronize()
+    assert ctx_out.cpu().tolist() == [cap, 41, cap]
+    m = rt.meta_view(0)
+    assert torch.equal(m[0:H], meta0[0:H])  # request 0: untouched
+    mv = (m.view(torch.bfloat16).float() if dtype == "bf16" else m).cpu().numpy().astype(np.float64)
+    pages = rt.pool_pages(0).cpu().numpy()
+    for u in range(H, units):
+        n = ctxs[u // H]
+        kmin, kmax = O.block_meta(K[u].astype(np.float64), n)
+        kmin, kmax = O.block_meta_append(kmin, kmax, n, kn.reshape(units, d)[u].astype(np.float64))
+        N = kmin.shape[0]
+        assert np.array_equal(mv[u, :N, 0], kmin) and np.array_equal(mv[u, :N, 1], kmax), u
+        pg = pages[u, 0].view(np.uint16 if dtype == "bf16" else np.float32)
+        j = n % BLK
+        assert np.array_equal(pg[: BLK * d].reshape(BLK, d)[j], U.to_elem_np(dtype, kn.reshape(units, d)[u])), u
+        assert np.array_equal(pg[BLK * d:].reshape(d, BLK)[:, j], U.to_elem_np(dtype, vn.reshape(units, d)[u])), u
+    assert not pages[0:H].any()  # request 0's resident page: nothing written
+    with pytest.raises(ValueError, match="capacity"):
+        rt.append(0, U.to_dev(dtype, kn), U.to_dev(dtype, vn))
+    rt.close()
+
+
 @pytest.mark.parametrize("dtype,d,nmax", [("bf16", 128, 37), ("f32", 64, 16), ("bf16", 64, 5)])
 def test_meta_export_and_import(dtype, d, nmax):
     """The tiles built from pages, read back through the export, equal the
