@@ -285,21 +285,24 @@ def test_carry_step_matches_separate_calls(name, kw):
                                         SyntheticRun(cfg, overlap=False, fused_step=False)])
 
 
-@pytest.mark.parametrize("dtype,options", [
-    ("bf16", {"attn_splits": 1}),      # attention and scoring launches carry the metadata and page rows
-    ("bf16", {"step_launches": 3}),    # three launches (with a split combine: the append launch first)
-    ("bf16", None),                    # attention beside the scoring: the append launch goes first
-    ("f32", None),                     # fp32: the append launch goes first
+@pytest.mark.parametrize("dtype,options,full", [
+    ("bf16", {"attn_splits": 1}, False),   # attention and scoring launches carry the metadata and page rows
+    ("bf16", {"attn_splits": 1}, True),    # the same, request 0 reaching the capacity
+    ("bf16", {"step_launches": 3}, False),  # three launches (with a split combine: the append launch first)
+    ("bf16", None, False),                 # attention beside the scoring: the append launch goes first
+    ("f32", None, True),                   # fp32: the append launch goes first
 ])
-def test_decode_step_append_matches_separate_calls(dtype, options):
+def test_decode_step_append_matches_separate_calls(dtype, options, full):
     """oasis_decode_step_append against oasis_block_meta_update followed by
     oasis_decode_step on an identical copy of the state, over steps that cross
     a block boundary: every output, the grown context, the metadata, the pool
-    and every list and map bit for bit."""
+    and every list and map bit for bit.  With `full`, request 0 starts two
+    tokens below the capacity and stays at it once there: its later appends
+    leave the context as it was."""
     from lookahead_sparse_kv_draft_amd import _lib as L
     cfg = CONFIGS["qwen8b_reason"].with_(batch=2, ctx=16 * 40 + 13, steps=5, dtype=dtype, budget_tokens=16 * 16,
                                          fetch_cap=4, planted=6)
-    print(f"{dtype} {options}", flush=True)
+    print(f"{dtype} {options} {full}", flush=True)
     run = SyntheticRun(cfg, replicas=2, overlap=False, options=options)
     try:
         run.prologue()
@@ -307,10 +310,13 @@ def test_decode_step_append_matches_separate_calls(dtype, options):
         a, b = rt.state[0][0], rt.state[0][1]
         b.copy_from(a)
         torch.cuda.synchronize()
+        cap = run.shape.max_blocks * 16
         base = torch.tensor([cfg.ctx_of(r) for r in range(cfg.batch)], dtype=torch.int32, device="cuda")
+        if full:
+            base[0] = cap - 2
         out_a, out_b = torch.zeros_like(rt.out), torch.zeros_like(rt.out)
         for t in range(cfg.steps):
-            ctx_in = base + t
+            ctx_in = torch.clamp(base + t, max=cap)
             grown_a, grown_b = torch.zeros_like(ctx_in), torch.zeros_like(ctx_in)
             q, kn, vn = run.q[0, t + 1], run.k_new_dev[0, t], run.v_new_dev[0, t]
             L.oasis_block_meta_update(rt.h, kn, vn, ctx_in, grown_a, a.meta, a.pool, a.b2s)
@@ -320,7 +326,8 @@ def test_decode_step_append_matches_separate_calls(dtype, options):
                                        out_b, rt.ws_ptr, b.fetch, b.n_fetch, b.evict, b.attend, b.n_attend, kn, vn)
             torch.cuda.synchronize()
             assert torch.equal(out_a, out_b), t
-            assert torch.equal(grown_a, grown_b) and torch.equal(grown_a, ctx_in + 1), t
+            assert torch.equal(grown_a, grown_b), t
+            assert torch.equal(grown_a, torch.where(ctx_in < cap, ctx_in + 1, ctx_in)), t
             for name in ("meta", "pool", "b2s", "s2b", "scores", "sel", "fetch", "n_fetch", "evict", "attend",
                          "n_attend"):
                 assert torch.equal(getattr(a, name), getattr(b, name)), (t, name)
