@@ -88,6 +88,9 @@ def parse():
                    help="--pipeline fetch caps as fractions of the block budget k (1.0 = fetch all)")
     p.add_argument("--eviction", choices=["score", "lru", "both"], default="both",
                    help="--pipeline eviction policies: lowest score, least recently used, or both")
+    p.add_argument("--launch-options", default=None, metavar="JSON",
+                   help="the library's launch options as a JSON object (oasis_launch_options fields), "
+                        "e.g. '{\"attn_merge\": 2}'; default: the library's own choice")
     p.add_argument("--mode", choices=["auto", "graph", "overlap", "eager", "carry", "two_streams",
                                       "two_streams_graph"], default="auto",
                    help="graph: steps captured as a HIP graph on one stream; overlap: the scoring on a "
@@ -733,7 +736,8 @@ def main():
     print(f"# config {cfg.name}: state {state_bytes / 2**20:.0f} MiB per replica, {replicas} replicas",
           file=sys.stderr, flush=True)
 
-    run = SyntheticRun(cfg, replicas=replicas, overlap=args.mode == "overlap")
+    launch_options = json.loads(args.launch_options) if args.launch_options else None
+    run = SyntheticRun(cfg, replicas=replicas, overlap=args.mode == "overlap", options=launch_options)
     rt = run.rt
     run.prologue()
     for l in range(run.L):
@@ -1104,6 +1108,7 @@ def main():
                    "attended_blocks": [attended_before, attended_after]},
         "roofline": roof,
         "kernels": kern,
+        "launch_options": L.oasis_get_launch_options(rt.h),
         "step_mode": {"graph": f"HIP graph of {G} steps on one stream",
                       "overlap": f"HIP graph of {G} steps; scoring on a second stream beside the attention",
                       "eager": ("one oasis_decode_step_append call per layer on one stream (the token's "

@@ -103,6 +103,14 @@ typedef struct oasis_launch_options {
   int32_t step_launches;  /* launches per oasis_decode_step: 0 or 2 (attention beside the
                              scoring; selection + diff + split combine), or 3 (attention;
                              combine + scoring; selection + diff) */
+  int32_t attn_merge;     /* where the attention's split partials are merged in the steps whose
+                             first launch runs the attention beside the scoring: 1 by a combine
+                             after that launch (the two-launch step's second launch, the carried
+                             step's combine launch); 2 inside that launch in both steps (the
+                             last workgroup of each request and KV head to finish merges; only
+                             with 2 to 8 splits, else as 1); 3 inside it in the carried step
+                             only; 0 default: 3 with 8 splits, else 1.  The outputs are
+                             bit-identical either way. */
 } oasis_launch_options;
 
 /* Validates the shape (EINVAL / EUNSUPPORTED) and returns a handle with the
@@ -126,7 +134,10 @@ size_t oasis_page_bytes(oasis_handle h);       /* one page: 2*16*d elements */
 size_t oasis_meta_bytes(oasis_handle h);       /* B*H*ceil(max_blocks/16)*16*2*d elements */
 size_t oasis_pool_bytes(oasis_handle h);       /* B*H*budget_blocks pages */
 size_t oasis_host_tier_bytes(oasis_handle h);  /* B*H*max_blocks pages */
-/* Split partials of oasis_sparse_paged_decode_attn (device, 256-byte aligned). */
+/* The attention's workspace (device, 256-byte aligned): its split partials,
+ * then one int32 arrival counter per (request, KV head) for the split merge
+ * inside the first launch (attn_merge).  Zero the workspace once before its
+ * first use; every call leaves the counters zero again. */
 size_t oasis_workspace_bytes(oasis_handle h);
 
 /*
@@ -375,8 +386,10 @@ int oasis_sparse_paged_decode_attn_list(oasis_handle h, const void* q, const voi
  * else back to back.  The attention leaves its split partials
  * in the workspace; `out` is complete after oasis_attn_combine or
  * oasis_select_diff_combine on the same workspace (which do nothing when the
- * attention has a single split and wrote `out` itself).  sel/block_to_slot may
- * be null when attend is given.
+ * attention has a single split and wrote `out` itself), or at once where the
+ * handle merges the splits inside this launch (attn_merge 2; a combine after
+ * it rewrites the same values).  sel/block_to_slot may be null when attend is
+ * given.
  */
 int oasis_attend_and_score(oasis_handle h, const void* q, const void* pool, const void* meta,
                            const int32_t* ctx_attn, const int32_t* ctx_score, const int32_t* sel,

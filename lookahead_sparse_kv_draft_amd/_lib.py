@@ -35,7 +35,7 @@ class oasis_shape(ctypes.Structure):
 
 class oasis_launch_options(ctypes.Structure):
     _fields_ = [(f, ctypes.c_int32) for f in (
-        "attn_waves", "attn_pf", "attn_splits", "score_tpw", "step_order", "step_launches")]
+        "attn_waves", "attn_pf", "attn_splits", "score_tpw", "step_order", "step_launches", "attn_merge")]
 
 
 LAUNCH_OPTION_FIELDS = tuple(f for f, _ in oasis_launch_options._fields_)

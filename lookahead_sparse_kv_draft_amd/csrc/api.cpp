@@ -62,7 +62,7 @@ void transpose_block(const T* src, T* dst, int d) {
 
 extern "C" {
 
-int oasis_version(void) { return 1; }
+int oasis_version(void) { return 2; }
 
 const char* oasis_last_error(void) { return g_err.c_str(); }
 
@@ -111,6 +111,8 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
     return fail(OASIS_EINVAL, "oasis_create: step_order %d outside [0, 2]", o.step_order);
   if (o.step_launches != 0 && o.step_launches != 2 && o.step_launches != 3)
     return fail(OASIS_EINVAL, "oasis_create: step_launches %d (0, 2 or 3)", o.step_launches);
+  if (o.attn_merge < 0 || o.attn_merge > 3)
+    return fail(OASIS_EINVAL, "oasis_create: attn_merge %d (0, 1, 2 or 3)", o.attn_merge);
 
   oasis_ctx* h = new (std::nothrow) oasis_ctx;
   if (h == nullptr) return fail(OASIS_EINVAL, "oasis_create: out of host memory");
@@ -185,6 +187,20 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   c.score_tpw_solo = runs_for(2048);
   c.step_order = o.step_order;
   c.step_launches = o.step_launches == 3 ? 3 : 2;
+  // The split merge inside the fused first launch, where 2 to 8 splits run
+  // beside the scoring.  Each attention workgroup then waits for its
+  // device-coherent partial and an atomic before it ends, which lengthened the
+  // first launch by 2-3.5 us on every workload measured; the carried step
+  // saves its combine launch for it, which paid at 8 splits (the 128K-context
+  // 8-layer workload: 31.7 against 32.5 us per layer step) and not at 2
+  // (qwen32b_32k: 52.3 against 52.2 us), while the two-launch step, whose
+  // second launch combines beside the selection anyway, lost on both (32.7
+  // against 30.1 us at the 32K-context batch-8 step).
+  const bool merge_ok = splits >= 2 && splits <= oasis::kAttnMergeMaxSplits && s.dtype == OASIS_BF16;
+  const int merge = o.attn_merge != 0 ? o.attn_merge : (splits == oasis::kAttnMergeMaxSplits ? 3 : 1);
+  c.attn_merge = merge_ok && merge == 2;
+  c.attn_merge_carry = merge_ok && (merge == 2 || merge == 3);
+  c.ws_arrive_off = oasis::attn_ws_partials_bytes(c);
   *out = h;
   return ok();
 }
@@ -198,6 +214,7 @@ int oasis_get_launch_options(oasis_handle h, oasis_launch_options* out) {
   out->attn_splits = c.attn_splits;
   out->score_tpw = c.score_tpw;
   out->step_order = c.step_order;
+  out->attn_merge = c.attn_merge ? 2 : c.attn_merge_carry ? 3 : 1;
   out->step_launches = c.step_launches;
   return ok();
 }
@@ -785,10 +802,12 @@ hipError_t decode_step_impl(const oasis::Ctx& c, const void* q, const void* pool
     }
     e = oasis::launch_attn_and_score(c, q, pool, sel, block_to_slot, attend, n_attend, ctx_attn, out, workspace,
                                      meta, ctx_score, scores, st, g);
-    if (e == hipSuccess)
-      e = oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
-                                            evict, attend, n_attend, workspace, out, st);
-    return e;
+    if (e != hipSuccess) return e;
+    if (c.attn_merge)  // the first launch merged the splits
+      return oasis::launch_select_diff(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch, evict,
+                                       attend, n_attend, st);
+    return oasis::launch_select_diff_combine(c, scores, ctx_score, sel, block_to_slot, slot_to_block, fetch, n_fetch,
+                                             evict, attend, n_attend, workspace, out, st);
   }
   // other shapes: the carried transfer as its own launch first
   if (g.host != nullptr) {
@@ -937,9 +956,11 @@ int oasis_decode_step_carry(oasis_handle h, const void* q, const void* pool, con
   if (job != nullptr && g.host != nullptr && (job->fetch == g.fetch || job->n_fetch == g.n_fetch))
     return fail(OASIS_EINVAL, "oasis_decode_step_carry: the transfer reads the fetch list the carried diff writes");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = oasis::launch_attn_score_select(h->c, q, pool, attend, n_attend, ctx_attn, out, workspace, meta,
+  oasis::Ctx c = h->c;
+  c.attn_merge = c.attn_merge_carry;  // the carried step's own choice
+  hipError_t e = oasis::launch_attn_score_select(c, q, pool, attend, n_attend, ctx_attn, out, workspace, meta,
                                                  ctx_score, scores, job != nullptr ? &sj : nullptr, st, g);
-  if (e == hipSuccess) e = oasis::launch_attn_combine(h->c, workspace, out, st);
+  if (e == hipSuccess && !c.attn_merge) e = oasis::launch_attn_combine(c, workspace, out, st);
   return hip_status(e, "oasis_decode_step_carry");
 }
 

@@ -253,10 +253,15 @@ hipError_t combine_t(const Ctx& c, const float* ws_acc, const float* ws_ml, floa
 
 }  // namespace
 
-size_t attn_workspace_bytes(const Ctx& c) {
+size_t attn_ws_partials_bytes(const Ctx& c) {
   Ctx solo = c;
   solo.attn_splits = c.attn_splits_solo;
   return std::max(attn_ws_acc_bytes(c) + attn_ws_ml_bytes(c), attn_ws_acc_bytes(solo) + attn_ws_ml_bytes(solo));
+}
+
+size_t attn_workspace_bytes(const Ctx& c) {
+  // the partials, then one int32 arrival counter per unit (256-byte aligned)
+  return attn_ws_partials_bytes(c) + (static_cast<size_t>(c.units) * 4 + 255) / 256 * 256;
 }
 
 bool attn_needs_combine(const Ctx& c) {

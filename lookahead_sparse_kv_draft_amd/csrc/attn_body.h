@@ -31,7 +31,160 @@ struct AttnLds {
   float4 slice[NSLICE][RT][D / 16][kWave];  // wavefront accumulators in register layout
   int att[kMaxBudget];
   int wcnt[4][W];
+  int last;  // the in-launch merge: this workgroup arrived last for its unit
 };
+
+// Device-coherent (sc1: coherent across the XCDs' L2 caches) 16- and 8-byte
+// accesses for the split partials that another workgroup of the same launch
+// reads: only these take the coherent path, nothing is written back or
+// invalidated wholesale.
+constexpr int kCoherentDevice = 16;
+typedef unsigned int u32v4_t __attribute__((__vector_size__(16)));
+typedef unsigned int u32v2_t __attribute__((__vector_size__(8)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4_t, v), r, off, 0, kCoherentDevice);
+}
+__device__ __forceinline__ void store_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32v2_t, v), r, off, 0, kCoherentDevice);
+}
+__device__ __forceinline__ f32x4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentDevice));
+}
+__device__ __forceinline__ f32x2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentDevice));
+}
+
+// The split merge inside the attention's launch (arrive: one counter per unit,
+// zero before the launch; the merging workgroup leaves it zero again).
+// Wavefront 0 writes the workgroup's partial (unnormalised accumulator, row
+// max, row sum) with device-coherent stores, waits for them and counts the
+// workgroup in with a device-scope atomic; the workgroup that arrives last
+// merges every split of its unit from device-coherent loads and writes the
+// output.  The arithmetic is the split combine's (attn_combine.h): the rows'
+// maximum over the splits first, then sum_s 2^(m_s - M) acc_s and
+// sum_s 2^(m_s - M) l_s accumulated over s = 0, 1, ... in that order, so the
+// output equals the combine launch's bit for bit.  Wavefront w merges the
+// channel tiles w, w + W, ...  Needs splits <= kAttnMergeMaxSplits.
+template <int D, int RT, int W>
+__device__ __forceinline__ void merge_in_launch(const f32x4_t (&acc)[RT][D / 16], const float (&mrun)[RT],
+                                                const float (&Lwg)[RT], float* __restrict__ ws_acc,
+                                                float* __restrict__ ws_ml, float* __restrict__ out, int rows,
+                                                int splits, int unit, int wid, int32_t* __restrict__ arrive,
+                                                AttnLds<D, RT, W>& lds) {
+  constexpr int CT = D / 16;
+  constexpr int CW = (CT + W - 1) / W;
+  constexpr int SM = kAttnMergeMaxSplits;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const __amdgpu_buffer_rsrc_t racc = coherent_rsrc(ws_acc, 0x7FFFFFFF);
+  const __amdgpu_buffer_rsrc_t rml = coherent_rsrc(ws_ml, 0x7FFFFFFF);
+  if (wv == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = rt * 16 + col;
+      if (row < rows) {
+        const uint32_t p = static_cast<uint32_t>(wid * rows + row);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) store_coherent4(racc, (p * D + 16 * ct + 4 * grp) * 4u, acc[rt][ct]);
+        if (grp == 0) store_coherent2(rml, p * 8u, f32x2_t{mrun[rt], Lwg[rt]});
+      }
+    }
+    // the partial is complete at device scope before the count says so
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(arrive + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (lane == 0) lds.last = (old == splits - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (lds.last == 0) return;
+  asm volatile("" ::: "memory");  // the loads below stay after the count
+
+  // Every split's row statistics and the first SB splits' accumulators are
+  // requested together, then the rest SB splits at a time (registers allow 4
+  // with up to two row tiles, 2 with more): two round trips for 8 splits.
+  constexpr int SB = (RT <= 2) ? 4 : 2;
+  f32x2_t ml[RT][SM];
+  f32x4_t v[SB][RT][CW];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int rr = min(rt * 16 + col, rows - 1);  // padded rows read row rows-1 and write nothing
+        const uint32_t p = static_cast<uint32_t>((unit * splits + min(s0 + u, splits - 1)) * rows + rr);
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          const int ct = min(wv + W * i, CT - 1);
+          v[u][rt][i] = load_coherent4(racc, (p * D + 16 * ct + 4 * grp) * 4u);
+        }
+      }
+  };
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int rr = min(rt * 16 + col, rows - 1);
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      const uint32_t p = static_cast<uint32_t>((unit * splits + min(s, splits - 1)) * rows + rr);
+      ml[rt][s] = load_coherent2(rml, p * 8u);
+    }
+  }
+  load_batch(0);
+  // the rows' maximum over the splits, then each split's weight and the sum
+  float w[RT][SM], L[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) M = fmaxf(M, ml[rt][s][0]);  // repeats do not change the max
+    L[rt] = 0.f;
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+      w[rt][s] = (s >= splits || ml[rt][s][0] == -INFINITY) ? 0.f : exp2f(ml[rt][s][0] - M);
+      L[rt] += w[rt][s] * ml[rt][s][1];
+    }
+  }
+  f32x4_t a[RT][CW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < CW; ++i) a[rt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // accumulated in split order
+#pragma unroll
+  for (int s0 = 0; s0 < SM; s0 += SB) {
+    if (s0 >= splits) break;
+    if (s0 > 0) load_batch(s0);
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < CW; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[rt][i][j] += w[rt][s0 + u] * v[u][rt][i][j];
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + col;
+    if (row >= rows) continue;
+    const float inv = (L[rt] > 0.f) ? 1.f / L[rt] : 0.f;
+    float* orow = out + (static_cast<size_t>(unit) * rows + row) * D;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int ct = wv + W * i;
+      if (ct < CT)
+        *reinterpret_cast<float4*>(orow + 16 * ct + 4 * grp) =
+            make_float4(a[rt][i][0] * inv, a[rt][i][1] * inv, a[rt][i][2] * inv, a[rt][i][3] * inv);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(arrive + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <int D, int RT, int W, int PF>
 __device__ __forceinline__ void attn_wg(
@@ -39,7 +192,7 @@ __device__ __forceinline__ void attn_wg(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ b2s, const int32_t* __restrict__ attend,
     const int32_t* __restrict__ n_attend, const int32_t* __restrict__ ctx_len, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml, float* __restrict__ out, int H, int rows, int Nmax, int kb,
-    int splits, int run, float scale_log2, int wid, AttnLds<D, RT, W>& lds) {
+    int splits, int run, float scale_log2, int wid, AttnLds<D, RT, W>& lds, int32_t* __restrict__ arrive = nullptr) {
   constexpr int KS = D / 32;  // QK k-steps of 32 channels
   constexpr int CT = D / 16;  // PV channel tiles
   constexpr int PAGE = 2 * kBlock * D;
@@ -316,6 +469,10 @@ __device__ __forceinline__ void attn_wg(
   }
   // wavefront 0 now holds the workgroup's accumulator
 
+  if (arrive != nullptr && splits > 1) {
+    merge_in_launch<D, RT, W>(acc, mrun, Lwg, ws_acc, ws_ml, out, rows, splits, unit, wid, arrive, lds);
+    return;
+  }
   if (wv != 0) return;
   if (splits == 1) {
     float* ou = out + static_cast<size_t>(unit) * rows * D;

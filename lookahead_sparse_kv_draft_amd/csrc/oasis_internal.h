@@ -33,6 +33,9 @@ __host__ __device__ inline size_t meta_offset(int unit, int b, int e, int Nmax) 
          static_cast<size_t>(j) * CE + o;
 }
 constexpr int kAttnMaxSplits = 32;  // attention splits per unit (merge statistics kept in LDS)
+// The split merge inside the fused first launch takes at most this many
+// splits (their row statistics stay in registers).
+constexpr int kAttnMergeMaxSplits = 8;
 
 struct Ctx {
   oasis_shape s;
@@ -54,6 +57,12 @@ struct Ctx {
   int score_tpw_solo;  // the same in a scoring launch of its own
   int step_order;   // workgroup order of the fused attention + score launch (0, 1, 2)
   int step_launches;  // launches per decode step: 2 (fused attention + score) or 3
+  // The fused first launch merges the attention's splits itself (the last
+  // workgroup of a unit to finish), with one arrival counter per unit at
+  // ws_arrive_off in the workspace: in the two-launch step (attn_merge) and
+  // in the carried step (attn_merge_carry).
+  bool attn_merge, attn_merge_carry;
+  size_t ws_arrive_off;
 };
 
 // ---- kernel launchers (defined in the .hip files); return a hipError_t ----
@@ -184,6 +193,8 @@ hipError_t launch_select_diff_combine(const Ctx& c, const float* scores, const i
 hipError_t launch_combine_and_score(const Ctx& c, void* ws, float* out, const void* q, const void* meta,
                                    const int32_t* ctx_len, float* scores, hipStream_t st);
 size_t attn_workspace_bytes(const Ctx& c);
+// The split partials' part of the workspace (the arrival counters follow it).
+size_t attn_ws_partials_bytes(const Ctx& c);
 // The attention with its workspace in the library's per-GPU scratch array (no
 // allocation); attn_scratch_bytes() is that array's size.
 size_t attn_scratch_bytes();

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((RTA <= 
     float* __restrict__ out, int H, int arows, int Nmax, int kb, int splits, int run, float scale_log2,
     const uint16_t* __restrict__ meta, const int32_t* __restrict__ ctx_score, float* __restrict__ scores, int G,
     int T, int ndraft, int srows, int wpu, int tpw, int total_waves, int n_attn_wg, int n_score_wg, int order,
-    StepGather gather, int n_gather_wg, int page16, SelectJob job, int n_select_wg, int cap) {
+    StepGather gather, int n_gather_wg, int page16, SelectJob job, int n_select_wg, int cap,
+    int32_t* __restrict__ arrive) {
   constexpr bool SEL = KPT > 0;
   __shared__ StepLds<D, RTA, W, SEL> lds;
   if (static_cast<int>(blockIdx.x) < n_gather_wg) {
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((RTA <= 
   }
   if (is_attn) {
     attn_wg<D, RTA, W, 2>(q, pool, sel, b2s, attend, n_attend, ctx_attn, ws_acc, ws_ml, out, H, arows, Nmax, kb,
-                          splits, run, scale_log2, idx, lds.attn);
+                          splits, run, scale_log2, idx, lds.attn, arrive);
     return;
   }
   score_wave<D, RTS>(q, meta, ctx_score, scores, H, G, T, ndraft, 1, srows, Nmax, wpu, tpw, total_waves,
@@ -127,7 +128,9 @@ hipError_t as_t(const Ctx& c, const void* q, const void* pool, const int32_t* se
                      c.s.max_blocks, c.s.budget_blocks, c.attn_splits, c.attn_run, scale_log2,
                      static_cast<const uint16_t*>(meta), ctx_score, scores, c.s.group, c.T, c.s.n_draft,
                      c.rows_score, wpu, c.score_tpw, total, n_attn_wg, n_score_wg, c.step_order, g, n_gather_wg,
-                     page16, job != nullptr ? *job : SelectJob(), n_select_wg, c.s.fetch_cap);
+                     page16, job != nullptr ? *job : SelectJob(), n_select_wg, c.s.fetch_cap,
+                     c.attn_merge ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws_acc) + c.ws_arrive_off)
+                                  : nullptr);
   return hipGetLastError();
 }
 

@@ -231,7 +231,8 @@ class DecodeRuntime:
         self.ctx_host = np.zeros(s.batch, dtype=np.int32)
         self.out = torch.zeros((s.batch, s.q_heads, s.T, s.head_dim), dtype=torch.float32, device=self.device)
         ws = L.oasis_workspace_bytes(self.h)
-        self.ws = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+        # zeroed: the tail holds the in-launch split merge's arrival counters
+        self.ws = torch.zeros(ws + 256, dtype=torch.uint8, device=self.device)
         off = (-self.ws.data_ptr()) % 256
         self.ws_ptr = self.ws.data_ptr() + off
         self.side = torch.cuda.Stream(device=self.device)

@@ -55,10 +55,48 @@ def test_create_rejects_bad_shapes(kw, code):
     assert L.oasis_last_error()
 
 
+def test_launch_options_resolve_and_validate():
+    """The launch options a handle resolves (host only, no device call): the
+    in-launch split merge where it was asked for (or, by default, in the
+    carried step at 8 splits) and 2 to 8 splits run beside the scoring, the
+    combine otherwise (1 split, too many splits, fp32); out-of-range values
+    are EINVAL."""
+    def resolved(opts, **kw):
+        h = L.oasis_create_with_options(**_shape(**kw), options=opts)
+        try:
+            return L.oasis_get_launch_options(h)
+        finally:
+            L.oasis_destroy(h)
+
+    assert resolved(dict(attn_splits=4))["attn_merge"] == 1                  # default below 8 splits
+    assert resolved(dict(attn_splits=8))["attn_merge"] == 3                  # default at 8: carried step
+    assert resolved(dict(attn_splits=8, attn_merge=1))["attn_merge"] == 1
+    assert resolved(dict(attn_splits=4, attn_merge=2)) == dict(resolved(dict(attn_splits=4)), attn_merge=2)
+    assert resolved(dict(attn_splits=4, attn_merge=3))["attn_merge"] == 3
+    assert resolved(dict(attn_splits=8, attn_merge=2))["attn_merge"] == 2
+    assert resolved(dict(attn_splits=1, attn_merge=2))["attn_merge"] == 1    # nothing to merge
+    nine = resolved(dict(attn_splits=9, attn_merge=2), budget_blocks=72, max_blocks=128)
+    assert nine["attn_splits"] == 9 and nine["attn_merge"] == 1             # more than 8 splits
+    assert resolved(dict(attn_splits=4, attn_merge=2), dtype=L.OASIS_F32)["attn_merge"] == 1
+    for bad in (dict(attn_merge=4), dict(attn_merge=-1), dict(attn_pf=3), dict(step_launches=1)):
+        with pytest.raises(L.OasisError) as e:
+            resolved(bad)
+        assert e.value.code == L.OASIS_EINVAL, bad
+    # the workspace holds the partials and then one arrival counter per unit
+    h1 = L.oasis_create_with_options(**_shape(), options=dict(attn_splits=4))
+    h2 = L.oasis_create_with_options(**_shape(), options=dict(attn_splits=4, attn_merge=2))
+    try:
+        assert L.oasis_workspace_bytes(h1) == L.oasis_workspace_bytes(h2)
+        assert L.oasis_workspace_bytes(h1) % 256 == 0
+    finally:
+        L.oasis_destroy(h1)
+        L.oasis_destroy(h2)
+
+
 def test_sizes_and_null_checks():
     h = L.oasis_create(**_shape())
     try:
-        assert L.oasis_version() == 1
+        assert L.oasis_version() == 2
         assert L.oasis_page_bytes(h) == 2 * 16 * 128 * 2
         assert L.oasis_meta_bytes(h) == 4 * 64 * 2 * 128 * 2
         assert L.oasis_pool_bytes(h) == 4 * 16 * 8192

@@ -210,7 +210,7 @@ def test_decode_step_halves(launches):
                                         for tc in (True, False)])
 
 
-def _decode_step_vs_separate(cfg, runs=None, options=None):
+def _decode_step_vs_separate(cfg, runs=None, options=None, exact=False):
     runs = runs or [SyntheticRun(cfg, overlap=False, fused_step=f, options=options) for f in (True, False)]
     try:
         for r in runs:
@@ -221,7 +221,7 @@ def _decode_step_vs_separate(cfg, runs=None, options=None):
                 r.step(t)
                 snaps.append(_state_snapshot(r))
             for i, (a, b) in enumerate(zip(*snaps)):
-                if i == 0:
+                if i == 0 and not exact:
                     # the attention output: the standalone attention may split the
                     # attended list differently (its own split count), which only
                     # reorders fp32 sums; every discrete output must be identical
@@ -283,6 +283,34 @@ def test_carry_step_matches_separate_calls(name, kw):
     cfg = CONFIGS[name].with_(**kw)
     _decode_step_vs_separate(cfg, runs=[SyntheticRun(cfg, overlap=False, carry_select=True),
                                         SyntheticRun(cfg, overlap=False, fused_step=False)])
+
+
+@pytest.mark.parametrize("shape,splits,carry", [
+    (0, 4, False),   # three layers, 16 units, the two-launch step
+    (0, 8, True),    # the same with the carried selection, the largest split count merged in launch
+    (0, 3, True),    # a split count that is no power of two
+    (5, 2, False),   # 40 attention rows (three row tiles)
+    (5, 3, True),
+    (4, 3, True),    # appends over 20 steps
+    (2, 8, True),    # 8192 blocks per head
+])
+def test_split_merge_in_launch_matches_the_combine(shape, splits, carry):
+    """The attention's splits merged inside the fused first launch (the last
+    workgroup of each unit to finish merges, attn_merge = 2) against the same
+    split count merged by the combine (attn_merge = 1): every output, the
+    attention's included, and all state bit for bit, step after step (the
+    arrival counters return to zero after every launch, or a later step would
+    merge early, late or never)."""
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    name, kw = CARRY_SHAPES[shape]
+    cfg = CONFIGS[name].with_(**kw)
+    print(f"{name} {kw} splits {splits} carry {carry}", flush=True)
+    runs = [SyntheticRun(cfg, overlap=False, carry_select=carry, options=dict(attn_splits=splits, attn_merge=m))
+            for m in (2, 1)]
+    got = [L.oasis_get_launch_options(r.rt.h) for r in runs]
+    assert got[0]["attn_splits"] == splits and got[0]["attn_merge"] == 2, got[0]
+    assert got[1]["attn_merge"] == 1, got[1]
+    _decode_step_vs_separate(cfg, runs=runs, exact=True)
 
 
 @pytest.mark.parametrize("dtype,options,full", [

@@ -103,7 +103,7 @@ def test_score_standalone_matches_step_launch():
     attend = torch.full((units, k), -1, dtype=torch.int32, device="cuda")
     n_attend = torch.zeros(units, dtype=torch.int32, device="cuda")
     out = torch.zeros((B, H * G, 1 + D, d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(L.oasis_workspace_bytes(h) + 256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(L.oasis_workspace_bytes(h) + 256, dtype=torch.uint8, device="cuda")
     ws_ptr = ws.data_ptr() + (-ws.data_ptr()) % 256
     fused = torch.full((units, Nmax), float("nan"), device="cuda")
     L.oasis_attend_and_score(h, q_d, pool, meta_d, ctx_d, ctx_d, sel, b2s, attend, n_attend, fused, out, ws_ptr)
