@@ -313,6 +313,59 @@ def test_split_merge_in_launch_matches_the_combine(shape, splits, carry):
     _decode_step_vs_separate(cfg, runs=runs, exact=True)
 
 
+def test_split_merge_in_launch_under_graph_replay():
+    """The fused first launch with its splits merged inside it, captured as a
+    HIP graph and replayed three times, with eager calls on the same workspace
+    between the replays: every replay and every eager call gives the eager
+    output and scores bit for bit (each launch leaves the arrival counters
+    zero for the next, captured or not)."""
+    from lookahead_sparse_kv_draft_amd import _lib as L
+    name, kw = CARRY_SHAPES[0]
+    cfg = CONFIGS[name].with_(**dict(kw, layers=1))
+    run = SyntheticRun(cfg, overlap=False, options=dict(attn_splits=4, attn_merge=2))
+    try:
+        run.prologue()
+        rt = run.rt
+        st = rt.state[0][0]
+        assert L.oasis_get_launch_options(rt.h)["attn_merge"] == 2
+
+        def call(out, scores, stream):
+            L.oasis_attend_and_score(rt.h, run.q[0, 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                     st.attend, st.n_attend, scores, out, rt.ws_ptr, stream)
+
+        out_e, sc_e = torch.zeros_like(rt.out), torch.zeros_like(st.scores)
+        call(out_e, sc_e, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        out_g, sc_g = torch.zeros_like(rt.out), torch.zeros_like(st.scores)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(out_g, sc_g, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for r in range(3):
+            out_g.zero_()
+            sc_g.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_g, out_e) and torch.equal(sc_g, sc_e), r
+            out_x, sc_x = torch.zeros_like(rt.out), torch.zeros_like(st.scores)
+            call(out_x, sc_x, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            assert torch.equal(out_x, out_e) and torch.equal(sc_x, sc_e), r
+        # and the same output as the combine after the launch
+        h1 = run.shape.handle(options=dict(attn_splits=4, attn_merge=1))
+        try:
+            out_c = torch.zeros_like(rt.out)
+            L.oasis_attend_and_score(h1, run.q[0, 1], st.pool, st.meta, rt.ctx_len, rt.ctx_len, st.sel, st.b2s,
+                                     st.attend, st.n_attend, torch.zeros_like(st.scores), out_c, rt.ws_ptr)
+            L.oasis_attn_combine(h1, rt.ws_ptr, out_c)
+            torch.cuda.synchronize()
+            assert torch.equal(out_c, out_e)
+        finally:
+            L.oasis_destroy(h1)
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("dtype,options,full", [
     ("bf16", {"attn_splits": 1}, False),   # attention and scoring launches carry the metadata and page rows
     ("bf16", {"attn_splits": 1}, True),    # the same, request 0 reaching the capacity
