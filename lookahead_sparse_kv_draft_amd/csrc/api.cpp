@@ -176,15 +176,16 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
 
   // Scoring: runs of 16-block tiles per wavefront, for about 4096 wavefronts
   // where the decode step runs it beside the attention (bf16), 2048 in a launch
-  // of its own (at the 32K-context batch-8 workload the scoring alone takes
-  // 12.6 us with runs of 4 tiles against 13.4 us with 2, while the step's
-  // launch is 0.4 us faster with 2).
+  // of its own but at most 4 tiles (at the 32K-context batch-8 workload the
+  // scoring alone takes 12.6 us with runs of 4 tiles against 13.4 us with 2,
+  // while the step's launch is 0.4 us faster with 2; in the batch-64 reasoning
+  // step, whose scoring launch reads its metadata cold, 4 tiles beat 8).
   const long long tiles = units * ((s.max_blocks + 15) / 16);
   auto runs_for = [&](long long waves) {
     return o.score_tpw > 0 ? o.score_tpw : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
   };
   c.score_tpw = runs_for(step_fused ? 4096 : 2048);
-  c.score_tpw_solo = runs_for(2048);
+  c.score_tpw_solo = o.score_tpw > 0 ? o.score_tpw : std::min(runs_for(2048), 4);
   c.step_order = o.step_order;
   c.step_launches = o.step_launches == 3 ? 3 : 2;
   // The split merge inside the fused first launch, where 2 to 8 splits run
