@@ -197,7 +197,10 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   // (qwen32b_32k: 52.3 against 52.2 us), while the two-launch step, whose
   // second launch combines beside the selection anyway, lost on both (32.7
   // against 30.1 us at the 32K-context batch-8 step).
-  const bool merge_ok = splits >= 2 && splits <= oasis::kAttnMergeMaxSplits && s.dtype == OASIS_BF16;
+  // (its device-coherent accesses address the partials with 32-bit byte
+  // offsets in a view of at most 2 GiB)
+  const bool merge_ok = splits >= 2 && splits <= oasis::kAttnMergeMaxSplits && s.dtype == OASIS_BF16 &&
+                        oasis::attn_ws_partials_bytes(c) < (static_cast<size_t>(1) << 31);
   const int merge = o.attn_merge != 0 ? o.attn_merge : (splits == oasis::kAttnMergeMaxSplits ? 3 : 1);
   c.attn_merge = merge_ok && merge == 2;
   c.attn_merge_carry = merge_ok && (merge == 2 || merge == 3);

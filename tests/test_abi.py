@@ -78,6 +78,9 @@ def test_launch_options_resolve_and_validate():
     nine = resolved(dict(attn_splits=9, attn_merge=2), budget_blocks=72, max_blocks=128)
     assert nine["attn_splits"] == 9 and nine["attn_merge"] == 1             # more than 8 splits
     assert resolved(dict(attn_splits=4, attn_merge=2), dtype=L.OASIS_F32)["attn_merge"] == 1
+    # partials of 2 GiB or more (batch 65536, 8 KV heads, 20 rows, 8 splits): the combine
+    big = resolved(dict(attn_splits=8, attn_merge=2), batch=65536, kv_heads=8, budget_blocks=128, max_blocks=128)
+    assert big["attn_splits"] == 8 and big["attn_merge"] == 1
     for bad in (dict(attn_merge=4), dict(attn_merge=-1), dict(attn_pf=3), dict(step_launches=1)):
         with pytest.raises(L.OasisError) as e:
             resolved(bad)
