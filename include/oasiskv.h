@@ -94,8 +94,9 @@ typedef struct oasis_launch_options {
                              split of 64-block runs per unit at one wavefront per SIMD;
                              capped by the registers the row count needs) */
   int32_t attn_splits;    /* attention workgroups per unit, 0..32 (default: about 512
-                             attention wavefronts per launch; bounded so that a
-                             wavefront streams at most 64 blocks) */
+                             attention wavefronts per launch, beside the scoring fewer
+                             where the attention moves under half of that launch's bytes;
+                             bounded so that a wavefront streams at most 64 blocks) */
   int32_t score_tpw;      /* 16-block tiles per scoring wavefront, 0..64 (default: about
                              4096 scoring wavefronts beside the attention, 2048 alone) */
   int32_t step_order;     /* workgroup order of the step's first launch: 0 attention first
@@ -109,8 +110,7 @@ typedef struct oasis_launch_options {
                              step's combine launch); 2 inside that launch in both steps (the
                              last workgroup of each request and KV head to finish merges; only
                              with 2 to 8 splits, else as 1); 3 inside it in the carried step
-                             only; 0 default: 3 with 8 splits, else 1.  The outputs are
-                             bit-identical either way. */
+                             only; 0 default: 1.  The outputs are bit-identical either way. */
 } oasis_launch_options;
 
 /* Validates the shape (EINVAL / EUNSUPPORTED) and returns a handle with the

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -152,8 +153,16 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
     *run_out = r;
     return (kbud + r * waves - 1) / (r * waves);  // no empty split
   };
+  // Beside the scoring, the attention's wavefronts scale with its share of
+  // the launch's bytes (per unit: k pages of 32 d elements against N_max
+  // metadata rows of 2 d): about 512 from an even share up (the 32K-context
+  // workloads, where 4 and 2 splits measured best), fewer below it (the
+  // 128K-context 8-layer workload, share 0.2: 4 splits, 30.8 us per carried
+  // layer step against 31.6 us with 8 splits and 33.7 / 32.3 us with 3 / 5).
+  const double share = 16.0 * kbud / (16.0 * kbud + s.max_blocks);
+  const int target_fused = std::max(1, static_cast<int>(std::lround(512.0 * std::min(1.0, 2.0 * share))));
   int run = 0, run_solo = 0;
-  const int splits = shape_splits(512, &run);
+  const int splits = shape_splits(target_fused, &run);
   const int splits_solo = shape_splits(512, &run_solo);
   const int max_pf = (row_tiles <= 2) ? 8 : (row_tiles == 3) ? 4 : 2;  // registers (no spills)
   // measured: a shallow ring keeps the math beside the loads, except where the
@@ -189,19 +198,20 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   c.step_order = o.step_order;
   c.step_launches = o.step_launches == 3 ? 3 : 2;
   // The split merge inside the fused first launch, where 2 to 8 splits run
-  // beside the scoring.  Each attention workgroup then waits for its
-  // device-coherent partial and an atomic before it ends, which lengthened the
-  // first launch by 2-3.5 us on every workload measured; the carried step
-  // saves its combine launch for it, which paid at 8 splits (the 128K-context
-  // 8-layer workload: 31.7 against 32.5 us per layer step) and not at 2
-  // (qwen32b_32k: 52.3 against 52.2 us), while the two-launch step, whose
-  // second launch combines beside the selection anyway, lost on both (32.7
-  // against 30.1 us at the 32K-context batch-8 step).
+  // beside the scoring (an option; the default combines).  Each attention
+  // workgroup then waits for its device-coherent partial and an atomic before
+  // it ends, which lengthened the first launch by 2-3.5 us on every workload
+  // measured; the carried step saves its combine launch for it, which paid at
+  // 8 splits of the 128K-context 8-layer workload (31.7 against 32.5 us per
+  // layer step) but not at the 4 splits that shape now takes (31.4 against
+  // 30.8 us), nor at qwen32b_32k's 2 (52.3 against 52.2 us); the two-launch
+  // step, whose second launch combines beside the selection anyway, lost
+  // everywhere (32.7 against 30.1 us at the 32K-context batch-8 step).
   // (its device-coherent accesses address the partials with 32-bit byte
   // offsets in a view of at most 2 GiB)
   const bool merge_ok = splits >= 2 && splits <= oasis::kAttnMergeMaxSplits && s.dtype == OASIS_BF16 &&
                         oasis::attn_ws_partials_bytes(c) < (static_cast<size_t>(1) << 31);
-  const int merge = o.attn_merge != 0 ? o.attn_merge : (splits == oasis::kAttnMergeMaxSplits ? 3 : 1);
+  const int merge = o.attn_merge != 0 ? o.attn_merge : 1;
   c.attn_merge = merge_ok && merge == 2;
   c.attn_merge_carry = merge_ok && (merge == 2 || merge == 3);
   c.ws_arrive_off = oasis::attn_ws_partials_bytes(c);

@@ -57,10 +57,11 @@ def test_create_rejects_bad_shapes(kw, code):
 
 def test_launch_options_resolve_and_validate():
     """The launch options a handle resolves (host only, no device call): the
-    in-launch split merge where it was asked for (or, by default, in the
-    carried step at 8 splits) and 2 to 8 splits run beside the scoring, the
-    combine otherwise (1 split, too many splits, fp32); out-of-range values
-    are EINVAL."""
+    in-launch split merge where it was asked for and 2 to 8 splits run beside
+    the scoring, the combine otherwise (by default, 1 split, too many splits,
+    fp32); the default split count beside the scoring (about 512 attention
+    wavefronts, fewer where the scoring reads most of the launch's bytes);
+    out-of-range values are EINVAL."""
     def resolved(opts, **kw):
         h = L.oasis_create_with_options(**_shape(**kw), options=opts)
         try:
@@ -68,8 +69,8 @@ def test_launch_options_resolve_and_validate():
         finally:
             L.oasis_destroy(h)
 
-    assert resolved(dict(attn_splits=4))["attn_merge"] == 1                  # default below 8 splits
-    assert resolved(dict(attn_splits=8))["attn_merge"] == 3                  # default at 8: carried step
+    assert resolved(dict(attn_splits=4))["attn_merge"] == 1                  # default: the combine
+    assert resolved(dict(attn_splits=8))["attn_merge"] == 1
     assert resolved(dict(attn_splits=8, attn_merge=1))["attn_merge"] == 1
     assert resolved(dict(attn_splits=4, attn_merge=2)) == dict(resolved(dict(attn_splits=4)), attn_merge=2)
     assert resolved(dict(attn_splits=4, attn_merge=3))["attn_merge"] == 3
@@ -81,6 +82,10 @@ def test_launch_options_resolve_and_validate():
     # partials of 2 GiB or more (batch 65536, 8 KV heads, 20 rows, 8 splits): the combine
     big = resolved(dict(attn_splits=8, attn_merge=2), batch=65536, kv_heads=8, budget_blocks=128, max_blocks=128)
     assert big["attn_splits"] == 8 and big["attn_merge"] == 1
+    # 64 units, k = 128: 4 splits with 2048 blocks of metadata per unit (even
+    # share), 2 with 8192 (share 0.2: about 205 attention wavefronts)
+    assert resolved(None, batch=8, kv_heads=8, budget_blocks=128, max_blocks=2048)["attn_splits"] == 4
+    assert resolved(None, batch=8, kv_heads=8, budget_blocks=128, max_blocks=8192)["attn_splits"] == 2
     for bad in (dict(attn_merge=4), dict(attn_merge=-1), dict(attn_pf=3), dict(step_launches=1)):
         with pytest.raises(L.OasisError) as e:
             resolved(bad)
