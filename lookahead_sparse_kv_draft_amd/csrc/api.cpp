@@ -193,7 +193,13 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   auto runs_for = [&](long long waves) {
     return o.score_tpw > 0 ? o.score_tpw : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
   };
-  c.score_tpw = runs_for(step_fused ? 4096 : 2048);
+  // Beside an attention that moves at least half of the launch's bytes, runs
+  // of at most 2 tiles (qwen32b_32k: 50.6-50.7 against 51.9 us per carried
+  // layer step with 4; the 32K-context batch-8 step already had 2), else for
+  // about 4096 wavefronts (the 128K-context 8-layer step: 4 tiles 30.7
+  // against 30.8 us with 2).
+  c.score_tpw = !step_fused ? runs_for(2048)
+                : (o.score_tpw == 0 && share >= 0.5) ? std::min(2, runs_for(4096)) : runs_for(4096);
   c.score_tpw_solo = o.score_tpw > 0 ? o.score_tpw : std::min(runs_for(2048), 4);
   c.step_order = o.step_order;
   c.step_launches = o.step_launches == 3 ? 3 : 2;
