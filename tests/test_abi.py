@@ -101,6 +101,29 @@ def test_launch_options_resolve_and_validate():
         L.oasis_destroy(h2)
 
 
+@pytest.mark.parametrize("kw,splits,tpw,pf_step", [
+    # llama8b_32k: batch 8, 32q/8kv, 2048 blocks; the attention moves half of the first launch's bytes
+    (dict(batch=8, kv_heads=8, group=4, max_blocks=2048, n_draft=4), 4, 2, 2),
+    # qwen32b_32k: batch 16, 64q/8kv (40 attention rows), 2048 blocks
+    (dict(batch=16, kv_heads=8, group=8, max_blocks=2048, n_draft=4), 2, 2, 2),
+    # llama8b_128k: batch 4, 8192 blocks; the attention moves a fifth of the bytes
+    (dict(batch=4, kv_heads=8, group=4, max_blocks=8192, n_draft=4), 4, 4, 2),
+    # qwen8b_reason: batch 64, 528 blocks; one split of 64-block runs
+    (dict(batch=64, kv_heads=8, group=4, max_blocks=528, n_draft=5), 1, 2, 2),
+])
+def test_default_launch_shapes_of_the_workloads(kw, splits, tpw, pf_step):
+    """The launch shape the library picks by default for each benchmark
+    workload (attention splits and scoring runs of the fused first launch;
+    the ring stays 2 pages there), as measured best on MI355X."""
+    h = L.oasis_create_with_options(head_dim=128, budget_blocks=128, fetch_cap=32, dtype=L.OASIS_BF16, **kw)
+    try:
+        o = L.oasis_get_launch_options(h)
+    finally:
+        L.oasis_destroy(h)
+    assert (o["attn_splits"], o["score_tpw"], o["attn_pf"], o["attn_waves"], o["attn_merge"]) == \
+        (splits, tpw, pf_step, 2, 1), o
+
+
 def test_sizes_and_null_checks():
     h = L.oasis_create(**_shape())
     try:
