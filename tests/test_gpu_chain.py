@@ -285,17 +285,18 @@ def test_carry_step_matches_separate_calls(name, kw):
                                         SyntheticRun(cfg, overlap=False, fused_step=False)])
 
 
-@pytest.mark.parametrize("shape,splits,carry,waves", [
-    (0, 4, False, 2),   # three layers, 16 units, the two-launch step
-    (0, 4, False, 4),   # 4-wavefront attention workgroups (each merges 2 of the 8 channel tiles)
-    (0, 8, True, 2),    # the carried selection, the largest split count merged in launch
-    (0, 3, True, 2),    # a split count that is no power of two
-    (5, 2, False, 2),   # 40 attention rows (three row tiles)
-    (5, 3, True, 2),
-    (4, 3, True, 2),    # appends over 20 steps
-    (2, 8, True, 2),    # 8192 blocks per head
+@pytest.mark.parametrize("shape,splits,carry,waves,d", [
+    (0, 4, False, 2, 128),   # three layers, 16 units, the two-launch step
+    (0, 4, False, 4, 128),   # 4-wavefront attention workgroups (each merges 2 of the 8 channel tiles)
+    (0, 3, False, 2, 64),    # head dim 64 (4 channel tiles; the two-launch step)
+    (0, 8, True, 2, 128),    # the carried selection, the largest split count merged in launch
+    (0, 3, True, 2, 128),    # a split count that is no power of two
+    (5, 2, False, 2, 128),   # 40 attention rows (three row tiles)
+    (5, 3, True, 2, 128),
+    (4, 3, True, 2, 128),    # appends over 20 steps
+    (2, 8, True, 2, 128),    # 8192 blocks per head
 ])
-def test_split_merge_in_launch_matches_the_combine(shape, splits, carry, waves):
+def test_split_merge_in_launch_matches_the_combine(shape, splits, carry, waves, d):
     """The attention's splits merged inside the fused first launch (the last
     workgroup of each unit to finish merges, attn_merge = 2) against the same
     split count merged by the combine (attn_merge = 1): every output, the
@@ -304,8 +305,8 @@ def test_split_merge_in_launch_matches_the_combine(shape, splits, carry, waves):
     merge early, late or never)."""
     from lookahead_sparse_kv_draft_amd import _lib as L
     name, kw = CARRY_SHAPES[shape]
-    cfg = CONFIGS[name].with_(**kw)
-    print(f"{name} {kw} splits {splits} carry {carry} waves {waves}", flush=True)
+    cfg = CONFIGS[name].with_(**dict(kw, head_dim=d))
+    print(f"{name} {kw} d {d} splits {splits} carry {carry} waves {waves}", flush=True)
     runs = [SyntheticRun(cfg, overlap=False, carry_select=carry,
                          options=dict(attn_splits=splits, attn_merge=m, attn_waves=waves)) for m in (2, 1)]
     got = [L.oasis_get_launch_options(r.rt.h) for r in runs]
