@@ -194,10 +194,10 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
     return o.score_tpw > 0 ? o.score_tpw : static_cast<int>(std::max(1LL, std::min(16LL, tiles / waves)));
   };
   // Beside an attention that moves at least half of the launch's bytes, runs
-  // of at most 2 tiles (qwen32b_32k: 50.6-50.7 against 51.9 us per carried
-  // layer step with 4; the 32K-context batch-8 step already had 2), else for
-  // about 4096 wavefronts (the 128K-context 8-layer step: 4 tiles 30.7
-  // against 30.8 us with 2).
+  // of at most 2 tiles (the 32K-context 8-layer batch-16 workload: 50.6-50.7
+  // against 51.9 us per carried layer step with 4; the 32K-context batch-8
+  // step already had 2), else for about 4096 wavefronts (the 128K-context
+  // 8-layer step: 4 tiles 30.7 against 30.8 us with 2).
   c.score_tpw = !step_fused ? runs_for(2048)
                 : (o.score_tpw == 0 && share >= 0.5) ? std::min(2, runs_for(4096)) : runs_for(4096);
   c.score_tpw_solo = o.score_tpw > 0 ? o.score_tpw : std::min(runs_for(2048), 4);
@@ -210,11 +210,11 @@ int oasis_create_with_options(const oasis_shape* shape, const oasis_launch_optio
   // measured; the carried step saves its combine launch for it, which paid at
   // 8 splits of the 128K-context 8-layer workload (31.7 against 32.5 us per
   // layer step) but not at the 4 splits that shape now takes (31.4 against
-  // 30.8 us), nor at qwen32b_32k's 2 (52.3 against 52.2 us); the two-launch
-  // step, whose second launch combines beside the selection anyway, lost
-  // everywhere (32.7 against 30.1 us at the 32K-context batch-8 step).
-  // (its device-coherent accesses address the partials with 32-bit byte
-  // offsets in a view of at most 2 GiB)
+  // 30.8 us), nor at the 2 splits of the 32K-context 8-layer batch-16
+  // workload (52.3 against 52.2 us); the two-launch step, whose second launch
+  // combines beside the selection anyway, lost everywhere (32.7 against
+  // 30.1 us at the 32K-context batch-8 step).  Its device-coherent accesses
+  // address the partials with 32-bit byte offsets in a view of at most 2 GiB.
   const bool merge_ok = splits >= 2 && splits <= oasis::kAttnMergeMaxSplits && s.dtype == OASIS_BF16 &&
                         oasis::attn_ws_partials_bytes(c) < (static_cast<size_t>(1) << 31);
   const int merge = o.attn_merge != 0 ? o.attn_merge : 1;
